@@ -1,0 +1,327 @@
+"""Pins of the float64 oracle against things other than itself.
+
+Each test fixes part of the oracle with a brute-force computation, a closed form,
+an invariant of the mathematics, or a value printed on the pages.  None of them
+re-calls the oracle's own formula to check it.
+"""
+import dataclasses
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import ssb_oracle as O
+from synth import WORKLOADS, bf_pixels, cached_counts
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _geom(name, **kw):
+    g = O.OGeom.from_any(WORKLOADS[name].geometry)
+    return dataclasses.replace(g, **kw) if kw else g
+
+
+def _read_golden(fname):
+    out = {}
+    with open(os.path.join(GOLDEN, fname)) as fh:
+        for line in fh:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                k, v = line.split()
+                out[k] = int(v)
+    return out
+
+
+# ------------------------------------------------------------------ BF set (P14)
+@pytest.mark.parametrize("name,expected", [("tiny", 49), ("small", 317), ("medium", 2121), ("full", 8937)])
+def test_bf_count(name, expected):
+    g = _geom(name)
+    i, j = O.bf_indices(g)
+    assert i.size == expected
+    # independent lattice count of the disk, column by column
+    r2 = int(g.bf_r2)
+    c = int(g.det_cy)
+    count = sum(2 * math.isqrt(r2 - dy * dy) + 1 for dy in range(-math.isqrt(r2), math.isqrt(r2) + 1))
+    assert count == expected
+    # the generator's independent selection gives the same pixels in the same order
+    gi, gj = bf_pixels(WORKLOADS[name].geometry)
+    assert np.array_equal(gi, i) and np.array_equal(gj, j)
+    assert c == g.det_n // 2
+
+
+def test_full_counts_match_pages():
+    gold = _read_golden("full_bf_count.txt")
+    g = _geom("full")
+    i, _ = O.bf_indices(g)
+    assert g.scan_n == gold["scan_n"] and g.det_n == gold["det_n"]
+    assert i.size == gold["n_bf"]
+    assert i.size * g.scan_n ** 2 == gold["samples_per_eval"]
+
+
+# ------------------------------------------------------------------ transforms (P1-P4)
+def _direct_dft2(x, sign):
+    n = x.shape[0]
+    k = np.arange(n)
+    w = np.exp(sign * 2j * np.pi * np.outer(k, k) / n)
+    out = np.zeros((n, n), dtype=np.complex128)
+    for a in range(n):           # explicit double sum, row by row
+        for b in range(n):
+            out[a, b] = np.sum(x * np.outer(w[a], w[b]))
+    return out
+
+
+@pytest.fixture(scope="module")
+def tiny_counts():
+    return cached_counts(WORKLOADS["tiny"])
+
+
+def test_scan_spectrum_brute_force(tiny_counts):
+    for b in (0, 24, 48):
+        x = tiny_counts[b].astype(np.float64)
+        ref = _direct_dft2(x, -1.0)[:, :17]
+        got = O.scan_spectrum(tiny_counts[b])
+        assert np.linalg.norm(got - ref) <= 1e-12 * np.linalg.norm(ref)
+
+
+def test_object_brute_force(tiny_counts):
+    g = _geom("tiny")
+    kx, ky = O.bf_kvectors(g)
+    dc = O.dc_value(tiny_counts)
+    n = g.scan_n
+    for b in (3, 24, 40):
+        t = O.transfer(g, (40.0, 5.0, 0.3), kx[b], ky[b])
+        c = O.corrected_spectrum(O.scan_spectrum(tiny_counts[b]), t, dc)
+        full = O.full_plane(c)
+        ref = _direct_dft2(full, +1.0) / n ** 2
+        got = O.bf_object(full)
+        assert np.linalg.norm(got - ref) <= 1e-12 * np.linalg.norm(ref)
+        assert np.max(np.abs(O.bf_phase(got) - np.angle(ref))) < 1e-12
+
+
+def test_hermitian_half_plane(tiny_counts):
+    x = tiny_counts[7].astype(np.float64)
+    g = O.scan_spectrum(x)
+    n = x.shape[0]
+    u = np.arange(n)
+    for v in (0, n // 2):
+        assert np.allclose(g[(n - u) % n, v], np.conj(g[u, v]), rtol=0, atol=1e-9 * np.abs(g).max())
+    # rebuild the full plane by Hermitian symmetry and compare with a complex 2-D FFT
+    full = np.empty((n, n), dtype=np.complex128)
+    full[:, : n // 2 + 1] = g
+    for v in range(n // 2 + 1, n):
+        full[:, v] = np.conj(g[(n - u) % n, n - v])
+    ref = _direct_dft2(x, -1.0)
+    assert np.linalg.norm(full - ref) <= 1e-12 * np.linalg.norm(ref)
+
+
+def test_parseval(tiny_counts):
+    n = 32
+    for b in range(0, 49, 6):
+        x = tiny_counts[b].astype(np.float64)
+        g = O.scan_spectrum(x)
+        w = np.full(g.shape[1], 2.0)
+        w[0] = w[-1] = 1.0
+        assert abs(np.sum(w * np.abs(g) ** 2) / n ** 2 - np.sum(x * x)) <= 1e-12 * np.sum(x * x)
+
+
+def test_dc_is_exact_integer_mean(tiny_counts):
+    sums = [int(v) for v in tiny_counts.reshape(49, -1).sum(axis=1, dtype=np.uint64)]
+    for b in (0, 10, 48):
+        assert O.scan_spectrum(tiny_counts[b])[0, 0].real == float(sums[b])
+    assert O.dc_value(tiny_counts) == sum(sums) / 49
+
+
+# ------------------------------------------------------------------ aperture closed form
+def test_aperture_closed_form():
+    g = _geom("small")                     # R_a = 10 px, w = 1 px
+    assert abs(g.aperture_px - 10.0) < 1e-12
+    r = np.array([0.0, 5.0, 9.5, 9.75, 10.0, 10.25, 10.5, 11.0, 30.0])
+    a = O.aperture(g, r, 0.0 * r)
+    assert np.allclose(a, [1, 1, 1, 0.75, 0.5, 0.25, 0, 0, 0], atol=1e-15)
+    # radial: direction does not matter
+    assert np.allclose(O.aperture(g, 0.6 * r, 0.8 * r), a, atol=1e-14)
+
+
+# ------------------------------------------------------------------ zero aberration (P5)
+def test_zero_aberration_transfer_is_sign_of_sidebands():
+    g = _geom("small")
+    kx, ky = O.bf_kvectors(g)
+    qx, qy = O.q_vectors(g)
+    ra = g.aperture_px
+    for b in (0, 50, 158, 316):
+        t = O.transfer(g, (0.0, 0.0, 0.0), kx[b], ky[b], qx, qy)
+        assert np.all(t.imag == 0.0)
+        assert set(np.unique(t.real)).issubset({-1.0, 0.0, 1.0})
+        # closed form: both probe factors are exactly 1, so T = sign(a(k - q) - a(k + q))
+        rm = np.hypot(kx[b] - qx, ky[b] - qy)
+        rp = np.hypot(kx[b] + qx, ky[b] + qy)
+        am = np.clip(ra + 0.5 - rm, 0.0, 1.0)
+        ap = np.clip(ra + 0.5 - rp, 0.0, 1.0)
+        assert np.array_equal(t.real, np.sign(am - ap))
+
+
+def test_closed_form_single_sideband_cosine():
+    """One BF, counts A0 + A1 cos(2 pi u0 y / N), zero aberration: phi(y) = -atan(A1 sin / A0)."""
+    g = _geom("tiny")                      # N = 32, R_a = 4, s = 0.5
+    i, j = O.bf_indices(g)
+    b = int(np.flatnonzero((i == 5) & (j == 8))[0])   # kappa = (0, -3) px
+    n, u0, a0, a1 = 32, 4, 100.0, 30.0             # q0 = (0, 2) px: k - q0 outside, k + q0 inside
+    y = np.arange(n)
+    counts = np.repeat((a0 + a1 * np.cos(2 * np.pi * u0 * y / n))[:, None], n, axis=1)
+    dc = a0 * n * n
+    s1, s2 = O.bf_moments(g, counts[None], (0.0, 0.0, 0.0), dc, [b])
+    expect = -np.arctan(a1 * np.sin(2 * np.pi * u0 * y / n) / a0)
+    assert np.max(np.abs(s1 - expect[:, None])) < 1e-13
+    assert abs(s2 - n * np.sum(expect ** 2)) < 1e-11
+
+
+def test_closed_form_sideband_with_aberration():
+    """Same single-sideband case with defocus: C(q0) = -G(q0) exp(i(chi(k) - chi(k+q0)))."""
+    g = _geom("tiny")
+    i, j = O.bf_indices(g)
+    b = int(np.flatnonzero((i == 5) & (j == 8))[0])
+    n, u0, a0, a1 = 32, 4, 100.0, 30.0
+    y = np.arange(n)
+    counts = np.repeat((a0 + a1 * np.cos(2 * np.pi * u0 * y / n))[:, None], n, axis=1)
+    params = (25.0, 0.0, 0.0)
+    # chi written out for k = (0, -3) px, k + q0 = (0, -1), k - q0 = (0, -5)
+    lam, dk = g.wavelength_A, g.dk
+    c10 = float(np.float32(25.0)) * 10.0
+    chi = lambda r2: math.pi * lam * dk * dk * c10 * r2
+    ph = chi(9.0) - chi(1.0)
+    s1, _ = O.bf_moments(g, counts[None], params, a0 * n * n, [b])
+    # C(u0) = -(A1 N^2/2) e^{i ph}; C(-u0) = -conj(C(u0)) -> O = A0 + (A1/2)(-e^{i(ph+th)} + e^{-i(ph+th)})
+    th = 2 * np.pi * u0 * y / n
+    o = a0 + 0.5 * a1 * (-np.exp(1j * (ph + th)) + np.exp(-1j * (ph + th)))
+    assert np.max(np.abs(s1 - np.angle(o)[:, None])) < 1e-12
+
+
+# ------------------------------------------------------------------ inactive BF (P6), vacuum (P7)
+def test_inactive_bf_phase_is_zero():
+    w = WORKLOADS["tiny"]
+    counts = cached_counts(w)
+    # shrink the probe aperture to 2.5 px: BF pixels beyond 3 px have a(k_b) = 0
+    g = _geom("tiny")
+    g = dataclasses.replace(g, alpha_rad=g.alpha_rad * 2.5 / g.aperture_px)
+    kx, ky = O.bf_kvectors(g)
+    inactive = np.flatnonzero(kx ** 2 + ky ** 2 >= 9.0)
+    assert inactive.size > 10
+    dc = O.dc_value(counts)
+    for b in inactive[:5]:
+        s1, s2 = O.bf_moments(g, counts[b][None], (40.0, 5.0, 0.3), dc, [b])
+        assert np.all(s1 == 0.0) and s2 == 0.0
+    # they still count in n_bf: loss over all == moments over the active ones, normalized by 49
+    s1a, s2a = O.bf_moments(g, counts, (40.0, 5.0, 0.3), dc)
+    assert O.loss(g, counts, (40.0, 5.0, 0.3), dc) == O.loss_from_moments(s1a, s2a, 49)
+
+
+@pytest.mark.parametrize("params", [(0.0, 0.0, 0.0), (40.0, 5.0, 0.3), (-150.0, 18.0, 2.0)])
+def test_vacuum_loss_is_zero(params):
+    g = _geom("tiny")
+    counts = np.full((49, 32, 32), 200, dtype=np.uint32)
+    assert abs(O.loss(g, counts, params)) < 1e-24
+
+
+# ------------------------------------------------------------------ symmetry (P8, P9)
+def test_transfer_antihermitian():
+    g = _geom("small")
+    kx, ky = O.bf_kvectors(g)
+    qx, qy = O.q_vectors(g)
+    for b in (5, 120, 300):
+        t = O.transfer(g, (33.0, -7.0, 1.1), kx[b], ky[b], qx, qy)
+        tm = O.transfer(g, (33.0, -7.0, 1.1), kx[b], ky[b], -qx, -qy)
+        assert np.max(np.abs(tm + np.conj(t))) < 1e-12
+
+
+def test_conjugate_branch_small():
+    """Negating q (rotation by pi) and the aberrations negates every BF phase exactly.
+
+    At the small workload every Nyquist-line entry has zero transfer, so the
+    identity holds to rounding (the Notes page reports agreement within 1.13e-7
+    on real data, where Nyquist terms break it slightly).
+    """
+    w = WORKLOADS["small"]
+    counts = cached_counts(w)
+    g = _geom("small")
+    kx, ky = O.bf_kvectors(g)
+    qx, qy = O.q_vectors(g)
+    dc = O.dc_value(counts)
+    s1p = np.zeros((128, 128))
+    s1m = np.zeros((128, 128))
+    for b in range(0, 317, 3):
+        gb = O.scan_spectrum(counts[b])
+        tp = O.transfer(g, (40.0, 5.0, 0.3), kx[b], ky[b], qx, qy)
+        tm = O.transfer(g, (-40.0, -5.0, 0.3), kx[b], ky[b], -qx, -qy)
+        pp = O.bf_phase(O.bf_object(O.full_plane(O.corrected_spectrum(gb, tp, dc))))
+        pm = O.bf_phase(O.bf_object(O.full_plane(O.corrected_spectrum(gb, tm, dc))))
+        assert np.max(np.abs(pp + pm)) < 1e-12
+        s1p += pp
+        s1m += pm
+    assert np.max(np.abs(s1p + s1m)) < 1e-10
+
+
+# ------------------------------------------------------------------ object linearity (P10)
+def test_phase_of_mean_linearity(tiny_counts):
+    g = _geom("tiny")
+    kx, ky = O.bf_kvectors(g)
+    dc = O.dc_value(tiny_counts)
+    acc = np.zeros((32, 32), dtype=np.complex128)
+    for b in range(49):
+        t = O.transfer(g, (40.0, 5.0, 0.3), kx[b], ky[b])
+        acc += O.bf_object(O.full_plane(O.corrected_spectrum(O.scan_spectrum(tiny_counts[b]), t, dc)))
+    phase, psi = O.object_wave(g, tiny_counts, (40.0, 5.0, 0.3), dc)
+    assert np.max(np.abs(psi - acc / 49)) < 1e-12 * np.abs(psi).max()
+    assert np.max(np.abs(phase - np.angle(acc))) < 1e-12
+
+
+# ------------------------------------------------------------------ physics (P13)
+@pytest.fixture(scope="module")
+def small_setup():
+    w = WORKLOADS["small"]
+    counts = cached_counts(w)
+    return _geom("small"), counts, O.dc_value(counts)
+
+
+def test_defocus_minimum_at_truth(small_setup):
+    g, counts, dc = small_setup
+    grid = [20.0, 30.0, 35.0, 40.0, 45.0, 50.0, 60.0]
+    losses = [O.loss(g, counts, (c10, 5.0, 0.3), dc) for c10 in grid]
+    assert grid[int(np.argmin(losses))] == 40.0
+    assert max(losses) > 1.3 * min(losses)
+
+
+def test_astigmatism_minimum_at_truth(small_setup):
+    g, counts, dc = small_setup
+    ref = O.loss(g, counts, (40.0, 5.0, 0.3), dc)
+    for other in [(40.0, 0.0, 0.3), (40.0, 10.0, 0.3), (40.0, -5.0, 0.3),
+                  (40.0, 5.0, -0.3), (40.0, 5.0, 0.3 + math.pi / 4)]:
+        assert O.loss(g, counts, other, dc) > ref * 1.1
+
+
+# ------------------------------------------------------------------ two-pass half-plane form
+def test_two_pass_half_plane_equals_definition(tiny_counts):
+    """Column IFFT over the half plane, then the anti-Hermitian row extension and a row
+    IFFT, reproduces ifft2 of the full plane; and its imaginary part is the real inverse
+    transform (C2R) of -i times the column result, its real part set by columns 0 and N/2.
+    """
+    g = _geom("tiny")
+    n, h = 32, 16
+    kx, ky = O.bf_kvectors(g)
+    dc = O.dc_value(tiny_counts)
+    for b in (2, 30):
+        t = O.transfer(g, (-60.0, 12.0, 2.2), kx[b], ky[b])
+        c = O.corrected_spectrum(O.scan_spectrum(tiny_counts[b]), t, dc)
+        ref = O.bf_object(O.full_plane(c))
+        a = np.fft.ifft(c, axis=0)                     # (N, N/2+1) column transforms
+        row = np.empty((n, n), dtype=np.complex128)
+        row[:, : h + 1] = a
+        for v in range(h + 1, n):
+            row[:, v] = -np.conj(a[:, n - v])
+        two_pass = np.fft.ifft(row, axis=1)
+        assert np.linalg.norm(two_pass - ref) <= 1e-13 * np.linalg.norm(ref)
+        im = np.fft.irfft(-1j * a, n=n, axis=1)        # C2R: imag parts of bins 0 and N/2 ignored
+        x = np.arange(n)
+        re = (a[:, 0].real[:, None] + ((-1.0) ** x)[None, :] * a[:, h].real[:, None]) / n
+        assert np.max(np.abs(im - ref.imag)) < 1e-12 * np.abs(ref).max()
+        assert np.max(np.abs(re - ref.real)) < 1e-12 * np.abs(ref).max()
