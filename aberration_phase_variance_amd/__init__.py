@@ -1,0 +1,12 @@
+"""MI355X (gfx950) SSB phase-variance objective: HIP kernels behind a C ABI (include/ssb.h).
+
+The Python layer is a thin ctypes binding with the C ABI's names; all computation runs
+in libssb.so.  Build it with ``python -m aberration_phase_variance_amd.build``.
+"""
+from ._ssb import (EXPORTS, LIB_PATH, SSBError, load_library, make_geometry, ssb_geometry, ssb_info,
+                   ssb_last_error, ssb_loss, ssb_moments, ssb_object, ssb_prepare, ssb_query, ssb_release,
+                   ssb_set_chunk, ssb_spectrum, ssb_profile, SSB_STAGES)
+
+__all__ = ["EXPORTS", "LIB_PATH", "SSBError", "load_library", "make_geometry", "ssb_geometry", "ssb_info",
+           "ssb_last_error", "ssb_loss", "ssb_moments", "ssb_object", "ssb_prepare", "ssb_query", "ssb_release",
+           "ssb_set_chunk", "ssb_spectrum", "ssb_profile", "SSB_STAGES"]

@@ -1,0 +1,200 @@
+"""ctypes binding of libssb.so (declared in include/ssb.h): argument marshalling only.
+
+Every step of the computation runs in the HIP library.  Device buffers and
+streams may be passed as torch tensors / torch streams (used for their device
+pointers only) or as raw integer addresses.  There is no fallback: if the built
+library is missing, loading fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libssb.so")
+
+SSB_OK, SSB_EINVAL, SSB_ESHAPE, SSB_ENOMEM, SSB_EDEVICE = 0, -1, -2, -3, -4
+
+
+class SSBError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"ssb error {code}: {msg}")
+        self.code = code
+
+
+class ssb_geometry(ctypes.Structure):
+    _fields_ = [
+        ("scan_n", ctypes.c_int32),
+        ("det_n", ctypes.c_int32),
+        ("bf_r2", ctypes.c_double),
+        ("det_cy", ctypes.c_double),
+        ("det_cx", ctypes.c_double),
+        ("q_step_px", ctypes.c_double),
+        ("dk", ctypes.c_double),
+        ("wavelength_A", ctypes.c_double),
+        ("alpha_rad", ctypes.c_double),
+        ("rotation_rad", ctypes.c_double),
+        ("edge_px", ctypes.c_double),
+    ]
+
+
+class ssb_info(ctypes.Structure):
+    _fields_ = [
+        ("n_bf", ctypes.c_int64),
+        ("n_active_bf", ctypes.c_int64),
+        ("scan_n", ctypes.c_int32),
+        ("det_n", ctypes.c_int32),
+        ("spectrum_bytes", ctypes.c_int64),
+        ("dc", ctypes.c_double),
+        ("chunk_bf", ctypes.c_int64),
+    ]
+
+
+SSB_STAGES = ("pass1", "pass2", "reduce", "obj_sum", "obj_fft")
+
+
+class ssb_profile_data(ctypes.Structure):
+    _fields_ = [
+        ("ms", ctypes.c_double * len(SSB_STAGES)),
+        ("launches", ctypes.c_int64 * len(SSB_STAGES)),
+        ("units", ctypes.c_int64 * len(SSB_STAGES)),
+    ]
+
+
+EXPORTS = ("ssb_prepare", "ssb_loss", "ssb_moments", "ssb_object", "ssb_spectrum", "ssb_set_chunk",
+           "ssb_profile", "ssb_query", "ssb_release", "ssb_last_error")
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libssb.so (once) and declare its signatures.  Raises if it was not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m aberration_phase_variance_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    dp, fp = ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_float)
+    lib.ssb_prepare.argtypes = [ctypes.POINTER(ssb_geometry), vp, i64, vp, ctypes.POINTER(vp)]
+    lib.ssb_loss.argtypes = [vp, fp, i32, dp, vp, vp]
+    lib.ssb_moments.argtypes = [vp, fp, i64, i64, vp, dp, vp]
+    lib.ssb_object.argtypes = [vp, fp, vp, vp, vp]
+    lib.ssb_spectrum.argtypes = [vp, i64, vp, vp]
+    lib.ssb_set_chunk.argtypes = [vp, i64]
+    lib.ssb_profile.argtypes = [vp, ctypes.c_int, ctypes.POINTER(ssb_profile_data)]
+    lib.ssb_query.argtypes = [vp, ctypes.POINTER(ssb_info)]
+    lib.ssb_release.argtypes = [vp]
+    lib.ssb_release.restype = None
+    lib.ssb_last_error.argtypes = []
+    lib.ssb_last_error.restype = ctypes.c_char_p
+    for name in EXPORTS:
+        if name not in ("ssb_release", "ssb_last_error"):
+            getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(rc: int):
+    if rc != SSB_OK:
+        raise SSBError(rc, load_library().ssb_last_error().decode())
+
+
+def _ptr(x) -> int | None:
+    """Device address of a torch tensor, an int, or None."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return int(x.data_ptr())
+
+
+def _stream(s) -> int | None:
+    if s is None:
+        return None
+    if isinstance(s, int):
+        return s
+    return int(s.cuda_stream)
+
+
+def make_geometry(g) -> ssb_geometry:
+    get = (lambda k: g[k]) if isinstance(g, dict) else (lambda k: getattr(g, k))
+    return ssb_geometry(*[get(name) if typ is not ctypes.c_int32 else int(get(name))
+                          for name, typ in ssb_geometry._fields_])
+
+
+def _params(params, n_expected=None):
+    p = np.ascontiguousarray(np.asarray(params, dtype=np.float32).reshape(-1, 3))
+    if n_expected is not None and p.shape[0] != n_expected:
+        raise ValueError("expected a single (C10, C12, phi12) triple")
+    return p
+
+
+# ----------------------------------------------------------------- C ABI, same names
+def ssb_prepare(geometry, counts, n_bf: int, stream=None) -> int:
+    """Returns an opaque handle (int).  counts: device uint32 [n_bf][N][N] (tensor or address)."""
+    lib = load_library()
+    g = make_geometry(geometry)
+    h = ctypes.c_void_p()
+    _check(lib.ssb_prepare(ctypes.byref(g), _ptr(counts), int(n_bf), _stream(stream), ctypes.byref(h)))
+    return h.value
+
+
+def ssb_loss(handle: int, params, mean_phase=None, stream=None) -> np.ndarray:
+    """Losses (float64 [n_trials]) for host params [n_trials][3]; optional device float [N][N] mean phase."""
+    lib = load_library()
+    p = _params(params)
+    out = np.empty(p.shape[0], dtype=np.float64)
+    _check(lib.ssb_loss(handle, p.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), p.shape[0],
+                        out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), _ptr(mean_phase), _stream(stream)))
+    return out
+
+
+def ssb_moments(handle: int, params3, bf_begin: int, bf_end: int, s1, stream=None) -> float:
+    """S1 into device double [N][N] s1; returns S2."""
+    lib = load_library()
+    p = _params(params3, 1)
+    s2 = ctypes.c_double()
+    _check(lib.ssb_moments(handle, p.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), int(bf_begin), int(bf_end),
+                           _ptr(s1), ctypes.byref(s2), _stream(stream)))
+    return s2.value
+
+
+def ssb_object(handle: int, params3, phase, psi=None, stream=None) -> None:
+    lib = load_library()
+    p = _params(params3, 1)
+    _check(lib.ssb_object(handle, p.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), _ptr(phase), _ptr(psi),
+                          _stream(stream)))
+
+
+def ssb_spectrum(handle: int, bf: int, out, stream=None) -> None:
+    _check(load_library().ssb_spectrum(handle, int(bf), _ptr(out), _stream(stream)))
+
+
+def ssb_set_chunk(handle: int, chunk_bf: int) -> None:
+    _check(load_library().ssb_set_chunk(handle, int(chunk_bf)))
+
+
+def ssb_profile(handle: int, mode: int = 2) -> dict:
+    """mode 1: enable and clear, 0: disable, 2: keep.  Returns the per-stage totals."""
+    data = ssb_profile_data()
+    _check(load_library().ssb_profile(handle, int(mode), ctypes.byref(data)))
+    return {name: {"ms": data.ms[i], "launches": data.launches[i], "units": data.units[i]}
+            for i, name in enumerate(SSB_STAGES)}
+
+
+def ssb_query(handle: int) -> dict:
+    info = ssb_info()
+    _check(load_library().ssb_query(handle, ctypes.byref(info)))
+    return {name: getattr(info, name) for name, _ in ssb_info._fields_}
+
+
+def ssb_release(handle: int) -> None:
+    load_library().ssb_release(handle)
+
+
+def ssb_last_error() -> str:
+    return load_library().ssb_last_error().decode()

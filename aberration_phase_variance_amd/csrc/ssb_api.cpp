@@ -1,0 +1,565 @@
+// Host side of the C ABI declared in include/ssb.h.
+#include "../../include/ssb.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "ssb_internal.hpp"
+
+using namespace ssb;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+    if (e == hipErrorOutOfMemory) return fail(SSB_ENOMEM, "%s: %s", what, hipGetErrorString(e));
+    return fail(SSB_EDEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define SSB_HIP(call, what)                          \
+    do {                                             \
+        hipError_t e_ = (call);                      \
+        if (e_ != hipSuccess) return hip_fail(e_, what); \
+    } while (0)
+
+constexpr uint64_t kMagic = 0x5353424d49333535ull;   // "SSBMI355"
+constexpr uint64_t kDead = 0xdeadbeefdeadbeefull;
+// Intermediate budget for one chunk (all trials): bounds workspace memory.
+constexpr double kInterBudget = 12.0 * 1024 * 1024 * 1024;
+
+template <class T>
+T* align_up(char* base, size_t& off, size_t count) {
+    off = (off + 255) & ~size_t(255);
+    T* p = reinterpret_cast<T*>(base + off);
+    off += count * sizeof(T);
+    return p;
+}
+
+}  // namespace
+
+struct ssb_handle {
+    uint64_t magic;
+    ssb_geometry g;
+    int n, h;
+    int device;
+    int64_t n_bf, n_active;
+    GeomDev geo;
+    double dc;
+    int64_t chunk_user;
+    float2* gm = nullptr;
+    float2* gn = nullptr;
+    double2* kb = nullptr;
+    uint8_t* active = nullptr;
+    unsigned long long* bfsum = nullptr;
+    // loss / moments workspace
+    char* ws = nullptr;
+    size_t ws_bytes = 0;
+    // object workspace
+    char* ows = nullptr;
+    size_t ows_bytes = 0;
+    // host copy of the active flags, prefix counts for range queries
+    std::vector<int64_t> active_prefix;
+    // stage profiling
+    struct ProfRec {
+        int stage;
+        hipEvent_t a, b;
+        int64_t units;
+    };
+    bool prof_on = false;
+    std::vector<ProfRec> prof_pending;
+    std::vector<hipEvent_t> prof_pool;
+    double prof_ms[SSB_NUM_STAGES] = {};
+    int64_t prof_n[SSB_NUM_STAGES] = {};
+    int64_t prof_units[SSB_NUM_STAGES] = {};
+};
+
+namespace {
+
+bool finite_pos(double v) { return std::isfinite(v) && v > 0.0; }
+
+int check_handle(const ssb_handle* h) {
+    if (!h) return fail(SSB_EINVAL, "null handle");
+    if (h->magic != kMagic) return fail(SSB_EINVAL, "invalid or released handle");
+    return SSB_OK;
+}
+
+int check_params(const float* p, int n) {
+    for (int i = 0; i < 3 * n; ++i)
+        if (!std::isfinite(p[i])) return fail(SSB_EINVAL, "parameter %d of trial %d is not finite", i % 3, i / 3);
+    return SSB_OK;
+}
+
+hipEvent_t prof_event(ssb_handle* h) {
+    if (!h->prof_pool.empty()) {
+        hipEvent_t e = h->prof_pool.back();
+        h->prof_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+// Records events around one stage's launches when profiling is on.
+struct StageTimer {
+    ssb_handle* h;
+    int stage;
+    hipStream_t st;
+    int64_t units;
+    hipEvent_t a = nullptr, b = nullptr;
+    StageTimer(ssb_handle* h_, int stage_, hipStream_t st_, int64_t units_)
+        : h(h_), stage(stage_), st(st_), units(units_) {
+        if (!h->prof_on) return;
+        a = prof_event(h);
+        b = prof_event(h);
+        if (a && b) (void)hipEventRecord(a, st);
+    }
+    ~StageTimer() {
+        if (a && b) {
+            (void)hipEventRecord(b, st);
+            h->prof_pending.push_back({stage, a, b, units});
+        } else {
+            if (a) h->prof_pool.push_back(a);
+            if (b) h->prof_pool.push_back(b);
+        }
+    }
+};
+
+int prof_flush(ssb_handle* h) {
+    for (auto& r : h->prof_pending) {
+        float ms = 0.f;
+        hipError_t e = hipEventSynchronize(r.b);
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.a, r.b);
+        if (e != hipSuccess) return hip_fail(e, "profile events");
+        h->prof_ms[r.stage] += ms;
+        h->prof_n[r.stage] += 1;
+        h->prof_units[r.stage] += r.units;
+        h->prof_pool.push_back(r.a);
+        h->prof_pool.push_back(r.b);
+    }
+    h->prof_pending.clear();
+    return SSB_OK;
+}
+
+int64_t active_in(const ssb_handle* h, int64_t b0, int64_t b1) {
+    return h->active_prefix[b1] - h->active_prefix[b0];
+}
+
+TrialConst trial_const(const ssb_handle* h, const float* p) {
+    const double c10 = (double)p[0] * 10.0;    // nm -> Angstrom
+    const double c12 = (double)p[1] * 10.0;
+    const double phi = (double)p[2];
+    const double c2 = std::cos(2.0 * phi), s2 = std::sin(2.0 * phi);
+    const double k = 0.5 * h->g.wavelength_A * h->g.dk * h->g.dk;   // revolutions per (px^2 Angstrom)
+    TrialConst t;
+    t.mxx = k * (c10 + c12 * c2);
+    t.myy = k * (c10 - c12 * c2);
+    t.mxy = k * (c12 * s2);
+    t.pad = 0.0;
+    return t;
+}
+
+struct LossPlan {
+    int cap;       // BF capacity of one chunk (multiple of kGroupBF)
+    int gcap;      // groups per chunk
+    size_t off_im, off_in, off_ps1, off_ps2, off_s1, off_s2, off_loss, off_tc, total;
+};
+
+LossPlan plan_loss(const ssb_handle* h, int64_t nb, int n_trials) {
+    const int64_t n = h->n, hh = h->h;
+    const double plane = (double)n * (hh + 1) * sizeof(float2);
+    int64_t cap = (int64_t)(kInterBudget / (plane * n_trials));
+    cap = (cap / kGroupBF) * kGroupBF;
+    if (cap < kGroupBF) cap = kGroupBF;
+    const int64_t need = ((nb + kGroupBF - 1) / kGroupBF) * kGroupBF;
+    if (cap > need) cap = need;
+    if (h->chunk_user > 0) {
+        const int64_t u = ((h->chunk_user + kGroupBF - 1) / kGroupBF) * kGroupBF;
+        if (u < cap) cap = u;
+    }
+    LossPlan pl;
+    pl.cap = (int)cap;
+    pl.gcap = (int)(cap / kGroupBF);
+    const int rb = pass2_row_blocks(h->n);
+    size_t off = 0;
+    char* z = nullptr;
+    pl.off_im = (size_t)align_up<float2>(z, off, (size_t)n_trials * cap * n * hh);
+    pl.off_in = (size_t)align_up<float2>(z, off, (size_t)n_trials * cap * n);
+    pl.off_ps1 = (size_t)align_up<float>(z, off, (size_t)n_trials * pl.gcap * n * n);
+    pl.off_ps2 = (size_t)align_up<double>(z, off, (size_t)n_trials * pl.gcap * rb);
+    pl.off_s1 = (size_t)align_up<double>(z, off, (size_t)n_trials * n * n);
+    pl.off_s2 = (size_t)align_up<double>(z, off, (size_t)n_trials);
+    pl.off_loss = (size_t)align_up<double>(z, off, (size_t)n_trials);
+    pl.off_tc = (size_t)align_up<TrialConst>(z, off, (size_t)n_trials);
+    pl.total = off + 256;
+    return pl;
+}
+
+int ensure(char** buf, size_t* have, size_t need, const char* what) {
+    if (*have >= need) return SSB_OK;
+    if (*buf) {
+        hipError_t e = hipFree(*buf);
+        *buf = nullptr;
+        *have = 0;
+        if (e != hipSuccess) return hip_fail(e, what);
+    }
+    void* p = nullptr;
+    hipError_t e = hipMalloc(&p, need);
+    if (e != hipSuccess) return hip_fail(e, what);
+    *buf = static_cast<char*>(p);
+    *have = need;
+    return SSB_OK;
+}
+
+// Phase moments of n_trials trials over BF [b_begin, b_end): leaves S1 (double
+// [t][N][N]) and S2 (double [t]) in the workspace.
+// htc receives the host copy of the trial constants; it must outlive the
+// stream's use of it (the caller synchronizes before returning).
+int run_moments(ssb_handle* h, const float* params, int n_trials, int64_t b_begin, int64_t b_end,
+                hipStream_t st, std::vector<TrialConst>& htc, LossPlan* out_plan) {
+    const int64_t nb = b_end - b_begin;
+    LossPlan pl = plan_loss(h, nb, n_trials);
+    int rc = ensure(&h->ws, &h->ws_bytes, pl.total, "workspace allocation");
+    if (rc) return rc;
+    float2* im = reinterpret_cast<float2*>(h->ws + pl.off_im);
+    float2* in = reinterpret_cast<float2*>(h->ws + pl.off_in);
+    float* ps1 = reinterpret_cast<float*>(h->ws + pl.off_ps1);
+    double* ps2 = reinterpret_cast<double*>(h->ws + pl.off_ps2);
+    double* s1 = reinterpret_cast<double*>(h->ws + pl.off_s1);
+    double* s2 = reinterpret_cast<double*>(h->ws + pl.off_s2);
+    TrialConst* tc = reinterpret_cast<TrialConst*>(h->ws + pl.off_tc);
+
+    htc.resize(n_trials);
+    for (int t = 0; t < n_trials; ++t) htc[t] = trial_const(h, params + 3 * t);
+    SSB_HIP(hipMemcpyAsync(tc, htc.data(), sizeof(TrialConst) * n_trials, hipMemcpyHostToDevice, st),
+            "copy trial constants");
+    {
+        StageTimer tm(h, SSB_STAGE_REDUCE, st, 0);
+        SSB_HIP(launch_fill(s1, (int64_t)n_trials * h->n * h->n, st), "clear S1");
+        SSB_HIP(launch_fill(s2, n_trials, st), "clear S2");
+    }
+    for (int64_t c0 = b_begin; c0 < b_end; c0 += pl.cap) {
+        const int cb = (int)std::min<int64_t>(pl.cap, b_end - c0);
+        const int ng = (cb + kGroupBF - 1) / kGroupBF;
+        const int64_t units = active_in(h, c0, c0 + cb) * n_trials;
+        {
+            StageTimer tm(h, SSB_STAGE_PASS1, st, units);
+            SSB_HIP(launch_pass1(h->n, h->gm, h->gn, h->kb, h->active, tc, n_trials, h->geo, c0, cb, pl.cap, im,
+                                 in, st),
+                    "pass 1 launch");
+        }
+        {
+            StageTimer tm(h, SSB_STAGE_PASS2, st, units);
+            SSB_HIP(launch_pass2(h->n, im, in, pl.cap, h->active, c0, cb, n_trials, h->dc, ps1, ps2, pl.gcap, st),
+                    "pass 2 launch");
+        }
+        {
+            StageTimer tm(h, SSB_STAGE_REDUCE, st, 0);
+            SSB_HIP(launch_accum(h->n, ps1, ps2, pl.gcap, ng, n_trials, s1, s2, st), "accumulate launch");
+        }
+    }
+    if (out_plan) *out_plan = pl;
+    return SSB_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ssb_last_error(void) { return g_err.c_str(); }
+
+int ssb_prepare(const ssb_geometry* g, const uint32_t* counts, int64_t n_bf, void* stream, ssb_handle** out) {
+    g_err.clear();
+    if (!g || !counts || !out) return fail(SSB_EINVAL, "null argument");
+    *out = nullptr;
+    const int n = g->scan_n;
+    if (n != 32 && n != 64 && n != 128 && n != 256 && n != 512)
+        return fail(SSB_EINVAL, "scan_n must be a power of two in [32, 512], got %d", n);
+    if (g->det_n <= 0) return fail(SSB_EINVAL, "det_n must be positive");
+    if (!std::isfinite(g->bf_r2) || g->bf_r2 < 0.0) return fail(SSB_EINVAL, "bf_r2 must be finite and >= 0");
+    if (!std::isfinite(g->det_cy) || !std::isfinite(g->det_cx)) return fail(SSB_EINVAL, "non-finite detector center");
+    if (!finite_pos(g->q_step_px) || !finite_pos(g->dk) || !finite_pos(g->wavelength_A) ||
+        !finite_pos(g->alpha_rad) || !finite_pos(g->edge_px))
+        return fail(SSB_EINVAL, "q_step_px, dk, wavelength_A, alpha_rad and edge_px must be finite and > 0");
+    if (!std::isfinite(g->rotation_rad)) return fail(SSB_EINVAL, "non-finite rotation");
+    if (n_bf <= 0) return fail(SSB_ESHAPE, "n_bf must be positive");
+
+    // BF set (row-major) and per-BF offsets
+    const double ra = g->alpha_rad / g->wavelength_A / g->dk;
+    const double w = g->edge_px;
+    const double hi2 = (ra + 0.5 * w) * (ra + 0.5 * w);
+    std::vector<double2> kb;
+    std::vector<uint8_t> act;
+    for (int i = 0; i < g->det_n; ++i)
+        for (int j = 0; j < g->det_n; ++j) {
+            const double di = i - g->det_cy, dj = j - g->det_cx;
+            if (di * di + dj * dj <= g->bf_r2) {
+                kb.push_back(make_double2(dj, di));
+                act.push_back(dj * dj + di * di < hi2 ? 1 : 0);
+            }
+        }
+    if ((int64_t)kb.size() != n_bf)
+        return fail(SSB_ESHAPE, "n_bf = %lld but the BF rule selects %zu detector pixels", (long long)n_bf, kb.size());
+
+    hipPointerAttribute_t attr;
+    if (hipPointerGetAttributes(&attr, counts) != hipSuccess || attr.type == hipMemoryTypeHost ||
+        attr.type == hipMemoryTypeUnregistered) {
+        (void)hipGetLastError();
+        return fail(SSB_EINVAL, "counts must be a device pointer");
+    }
+
+    ssb_handle* h = new ssb_handle();
+    h->magic = kMagic;
+    h->g = *g;
+    h->n = n;
+    h->h = n / 2;
+    h->n_bf = n_bf;
+    h->n_active = 0;
+    h->active_prefix.assign(1, 0);
+    for (uint8_t a : act) {
+        h->n_active += a;
+        h->active_prefix.push_back(h->n_active);
+    }
+    h->chunk_user = 0;
+    (void)hipGetDevice(&h->device);
+    GeomDev& geo = h->geo;
+    geo.n = n;
+    geo.h = n / 2;
+    geo.s = g->q_step_px;
+    geo.crot = std::cos(g->rotation_rad);
+    geo.srot = std::sin(g->rotation_rad);
+    geo.ra = ra;
+    geo.w = w;
+    geo.lo2 = ra >= 0.5 * w ? (ra - 0.5 * w) * (ra - 0.5 * w) : -1.0;
+    geo.hi2 = hi2;
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const size_t nm = (size_t)n_bf * n * (n / 2), nn = (size_t)n_bf * n;
+    auto cleanup = [&](int rc) {
+        ssb_release(h);
+        return rc;
+    };
+    hipError_t e;
+    if ((e = hipMalloc(&h->gm, nm * sizeof(float2))) != hipSuccess) return cleanup(hip_fail(e, "spectrum allocation"));
+    if ((e = hipMalloc(&h->gn, nn * sizeof(float2))) != hipSuccess) return cleanup(hip_fail(e, "spectrum allocation"));
+    if ((e = hipMalloc(&h->kb, kb.size() * sizeof(double2))) != hipSuccess) return cleanup(hip_fail(e, "allocation"));
+    if ((e = hipMalloc(&h->active, act.size())) != hipSuccess) return cleanup(hip_fail(e, "allocation"));
+    if ((e = hipMalloc(&h->bfsum, n_bf * sizeof(unsigned long long))) != hipSuccess)
+        return cleanup(hip_fail(e, "allocation"));
+    if ((e = hipMemcpyAsync(h->kb, kb.data(), kb.size() * sizeof(double2), hipMemcpyHostToDevice, st)) != hipSuccess ||
+        (e = hipMemcpyAsync(h->active, act.data(), act.size(), hipMemcpyHostToDevice, st)) != hipSuccess ||
+        (e = hipMemsetAsync(h->bfsum, 0, n_bf * sizeof(unsigned long long), st)) != hipSuccess)
+        return cleanup(hip_fail(e, "prepare upload"));
+    if ((e = launch_g_rows(n, counts, n_bf, h->gm, h->gn, h->bfsum, st)) != hipSuccess)
+        return cleanup(hip_fail(e, "spectrum row pass"));
+    if ((e = launch_g_cols(n, h->gm, h->gn, n_bf, st)) != hipSuccess)
+        return cleanup(hip_fail(e, "spectrum column pass"));
+    std::vector<unsigned long long> sums(n_bf);
+    if ((e = hipMemcpyAsync(sums.data(), h->bfsum, n_bf * sizeof(unsigned long long), hipMemcpyDeviceToHost, st)) !=
+            hipSuccess ||
+        (e = hipStreamSynchronize(st)) != hipSuccess)
+        return cleanup(hip_fail(e, "prepare"));
+    unsigned long long tot = 0;
+    for (unsigned long long s : sums) tot += s;
+    h->dc = (double)tot / (double)n_bf;
+    // size the single-trial workspace now so a plain loss call allocates nothing
+    const LossPlan pl = plan_loss(h, n_bf, 1);
+    int rc = ensure(&h->ws, &h->ws_bytes, pl.total, "workspace allocation");
+    if (rc) return cleanup(rc);
+    *out = h;
+    return SSB_OK;
+}
+
+int ssb_loss(ssb_handle* h, const float* params, int32_t n_trials, double* losses, float* mean_phase,
+             void* stream) {
+    g_err.clear();
+    int rc = check_handle(h);
+    if (rc) return rc;
+    if (!params || !losses) return fail(SSB_EINVAL, "null params or losses");
+    if (n_trials < 1 || n_trials > 65535) return fail(SSB_EINVAL, "n_trials must be in [1, 65535]");
+    if ((rc = check_params(params, n_trials))) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    LossPlan pl;
+    std::vector<TrialConst> htc;
+    if ((rc = run_moments(h, params, n_trials, 0, h->n_bf, st, htc, &pl))) {
+        (void)hipStreamSynchronize(st);
+        return rc;
+    }
+    double* s1 = reinterpret_cast<double*>(h->ws + pl.off_s1);
+    double* s2 = reinterpret_cast<double*>(h->ws + pl.off_s2);
+    double* dl = reinterpret_cast<double*>(h->ws + pl.off_loss);
+    {
+        StageTimer tm(h, SSB_STAGE_REDUCE, st, 0);
+        SSB_HIP(launch_loss(h->n, s1, s2, n_trials, (double)h->n_bf, dl, mean_phase, st), "loss launch");
+    }
+    SSB_HIP(hipMemcpyAsync(losses, dl, sizeof(double) * n_trials, hipMemcpyDeviceToHost, st), "copy losses");
+    SSB_HIP(hipStreamSynchronize(st), "loss");
+    return SSB_OK;
+}
+
+int ssb_moments(ssb_handle* h, const float* params3, int64_t bf_begin, int64_t bf_end, double* s1, double* s2,
+                void* stream) {
+    g_err.clear();
+    int rc = check_handle(h);
+    if (rc) return rc;
+    if (!params3 || !s1 || !s2) return fail(SSB_EINVAL, "null argument");
+    if (bf_begin < 0 || bf_end > h->n_bf || bf_begin >= bf_end)
+        return fail(SSB_ESHAPE, "BF range [%lld, %lld) outside [0, %lld)", (long long)bf_begin, (long long)bf_end,
+                    (long long)h->n_bf);
+    if ((rc = check_params(params3, 1))) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    LossPlan pl;
+    std::vector<TrialConst> htc;
+    if ((rc = run_moments(h, params3, 1, bf_begin, bf_end, st, htc, &pl))) {
+        (void)hipStreamSynchronize(st);
+        return rc;
+    }
+    SSB_HIP(hipMemcpyAsync(s1, h->ws + pl.off_s1, sizeof(double) * h->n * h->n, hipMemcpyDeviceToDevice, st),
+            "copy S1");
+    SSB_HIP(hipMemcpyAsync(s2, h->ws + pl.off_s2, sizeof(double), hipMemcpyDeviceToHost, st), "copy S2");
+    SSB_HIP(hipStreamSynchronize(st), "moments");
+    return SSB_OK;
+}
+
+int ssb_object(ssb_handle* h, const float* params3, float* phase, float* psi, void* stream) {
+    g_err.clear();
+    int rc = check_handle(h);
+    if (rc) return rc;
+    if (!params3 || !phase) return fail(SSB_EINVAL, "null argument");
+    if ((rc = check_params(params3, 1))) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int n = h->n, hh = h->h;
+    const int nseg = obj_segments(h->n_bf);
+    const size_t ne = (size_t)n * (hh + 1);
+    size_t off = 0;
+    char* z = nullptr;
+    const size_t o_part = (size_t)align_up<double2>(z, off, ne * nseg);
+    const size_t o_pm = (size_t)align_up<float2>(z, off, (size_t)n * hh);
+    const size_t o_pn = (size_t)align_up<float2>(z, off, (size_t)n);
+    if ((rc = ensure(&h->ows, &h->ows_bytes, off + 256, "object workspace allocation"))) return rc;
+    double2* part = reinterpret_cast<double2*>(h->ows + o_part);
+    float2* pm = reinterpret_cast<float2*>(h->ows + o_pm);
+    float2* pn = reinterpret_cast<float2*>(h->ows + o_pn);
+    const TrialConst tc = trial_const(h, params3);   // passed by value: no host-staged copy
+    {
+        StageTimer tm(h, SSB_STAGE_OBJ_SUM, st, h->n_active);
+        SSB_HIP(launch_obj_sum(n, h->gm, h->gn, h->kb, h->active, tc, h->geo, h->n_bf, part, nseg, st),
+                "object sum");
+    }
+    {
+        StageTimer tm(h, SSB_STAGE_OBJ_FFT, st, 0);
+        SSB_HIP(launch_obj_reduce(n, part, nseg, pm, pn, st), "object reduce");
+        SSB_HIP(launch_obj_cols(n, pm, pn, st), "object columns");
+        const double dcsum = h->dc * (double)h->n_bf;
+        const double scale = 1.0 / ((double)h->n_bf * (double)n * (double)n);
+        SSB_HIP(launch_obj_rows(n, pm, pn, dcsum, scale, phase, reinterpret_cast<float2*>(psi), st), "object rows");
+    }
+    return SSB_OK;
+}
+
+int ssb_spectrum(const ssb_handle* h, int64_t bf, float* out, void* stream) {
+    g_err.clear();
+    int rc = check_handle(h);
+    if (rc) return rc;
+    if (!out) return fail(SSB_EINVAL, "null output");
+    if (bf < 0 || bf >= h->n_bf) return fail(SSB_ESHAPE, "BF index %lld outside [0, %lld)", (long long)bf,
+                                             (long long)h->n_bf);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int n = h->n, hh = h->h;
+    float2* o = reinterpret_cast<float2*>(out);
+    SSB_HIP(hipMemcpy2DAsync(o, sizeof(float2) * (hh + 1), h->gm + (size_t)bf * n * hh, sizeof(float2) * hh,
+                             sizeof(float2) * hh, n, hipMemcpyDeviceToDevice, st),
+            "copy spectrum");
+    SSB_HIP(hipMemcpy2DAsync(o + hh, sizeof(float2) * (hh + 1), h->gn + (size_t)bf * n, sizeof(float2),
+                             sizeof(float2), n, hipMemcpyDeviceToDevice, st),
+            "copy spectrum");
+    return SSB_OK;
+}
+
+int ssb_set_chunk(ssb_handle* h, int64_t chunk_bf) {
+    g_err.clear();
+    int rc = check_handle(h);
+    if (rc) return rc;
+    if (chunk_bf < 0) return fail(SSB_EINVAL, "chunk_bf must be >= 0");
+    h->chunk_user = chunk_bf;
+    return SSB_OK;
+}
+
+int ssb_profile(ssb_handle* h, int mode, ssb_profile_data* out) {
+    g_err.clear();
+    int rc = check_handle(h);
+    if (rc) return rc;
+    if (mode < 0 || mode > 2) return fail(SSB_EINVAL, "profile mode must be 0, 1 or 2");
+    if ((rc = prof_flush(h))) return rc;
+    if (out) {
+        for (int s = 0; s < SSB_NUM_STAGES; ++s) {
+            out->ms[s] = h->prof_ms[s];
+            out->launches[s] = h->prof_n[s];
+            out->units[s] = h->prof_units[s];
+        }
+    }
+    if (mode == 1) {
+        for (int s = 0; s < SSB_NUM_STAGES; ++s) {
+            h->prof_ms[s] = 0.0;
+            h->prof_n[s] = 0;
+            h->prof_units[s] = 0;
+        }
+        h->prof_on = true;
+    } else if (mode == 0) {
+        h->prof_on = false;
+    }
+    return SSB_OK;
+}
+
+int ssb_query(const ssb_handle* h, ssb_info* info) {
+    g_err.clear();
+    int rc = check_handle(h);
+    if (rc) return rc;
+    if (!info) return fail(SSB_EINVAL, "null info");
+    info->n_bf = h->n_bf;
+    info->n_active_bf = h->n_active;
+    info->scan_n = h->n;
+    info->det_n = h->g.det_n;
+    info->spectrum_bytes = (int64_t)h->n_bf * h->n * (h->h + 1) * (int64_t)sizeof(float2);
+    info->dc = h->dc;
+    info->chunk_bf = plan_loss(h, h->n_bf, 1).cap;
+    return SSB_OK;
+}
+
+void ssb_release(ssb_handle* h) {
+    if (!h || h->magic != kMagic) return;
+    h->magic = kDead;
+    (void)hipFree(h->gm);
+    (void)hipFree(h->gn);
+    (void)hipFree(h->kb);
+    (void)hipFree(h->active);
+    (void)hipFree(h->bfsum);
+    (void)hipFree(h->ws);
+    (void)hipFree(h->ows);
+    for (auto& r : h->prof_pending) {
+        (void)hipEventSynchronize(r.b);
+        (void)hipEventDestroy(r.a);
+        (void)hipEventDestroy(r.b);
+    }
+    for (hipEvent_t e : h->prof_pool) (void)hipEventDestroy(e);
+    delete h;
+}
+
+}  // extern "C"

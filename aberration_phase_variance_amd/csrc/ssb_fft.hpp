@@ -1,0 +1,143 @@
+// Wave-level radix-R Stockham FFT for gfx950 (64-lane wavefronts).
+//
+// An FFT of length N is done by a group of L = N/R lanes.  Lane j (0 <= j < L)
+// holds x[j + r L] for r = 0..R-1 in registers, both on entry and on exit
+// (natural order).  Each of the log_R(N) passes twiddles, does a radix-R DFT in
+// registers, and (except the last) exchanges through a group-private LDS buffer
+// of N complex values.  A wave holds 64/L groups.  Lanes of one group exchange
+// only with each other, so no workgroup barrier is needed, only wave-level
+// ordering of the LDS accesses.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace ssb {
+
+__device__ __forceinline__ float2 cadd(float2 a, float2 b) { return make_float2(a.x + b.x, a.y + b.y); }
+__device__ __forceinline__ float2 csub(float2 a, float2 b) { return make_float2(a.x - b.x, a.y - b.y); }
+__device__ __forceinline__ float2 cmul(float2 a, float2 b) {
+    return make_float2(a.x * b.x - a.y * b.y, a.x * b.y + a.y * b.x);
+}
+// multiply by SIGN * i
+template <int SIGN>
+__device__ __forceinline__ float2 mul_si(float2 v) {
+    return SIGN > 0 ? make_float2(-v.y, v.x) : make_float2(v.y, -v.x);
+}
+
+// Keep the compiler from moving LDS accesses across this point; the hardware
+// executes one wave's LDS operations in order.
+__device__ __forceinline__ void wave_lds_fence() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int SIGN>
+__device__ __forceinline__ void dft2(float2 (&x)[2]) {
+    float2 a = x[0];
+    x[0] = cadd(a, x[1]);
+    x[1] = csub(a, x[1]);
+}
+
+template <int SIGN>
+__device__ __forceinline__ void dft4v(float2& x0, float2& x1, float2& x2, float2& x3) {
+    float2 a = cadd(x0, x2), b = csub(x0, x2), c = cadd(x1, x3), d = mul_si<SIGN>(csub(x1, x3));
+    x0 = cadd(a, c);
+    x2 = csub(a, c);
+    x1 = cadd(b, d);
+    x3 = csub(b, d);
+}
+
+template <int SIGN>
+__device__ __forceinline__ void dft4(float2 (&x)[4]) {
+    dft4v<SIGN>(x[0], x[1], x[2], x[3]);
+}
+
+template <int SIGN>
+__device__ __forceinline__ void dft8(float2 (&x)[8]) {
+    float2 e0 = x[0], e1 = x[2], e2 = x[4], e3 = x[6];
+    float2 o0 = x[1], o1 = x[3], o2 = x[5], o3 = x[7];
+    dft4v<SIGN>(e0, e1, e2, e3);
+    dft4v<SIGN>(o0, o1, o2, o3);
+    const float c = 0.70710678118654752440f;
+    // o_k * exp(SIGN i pi k / 4)
+    float2 t1 = make_float2(c * (o1.x - SIGN * o1.y), c * (o1.y + SIGN * o1.x));
+    float2 t2 = mul_si<SIGN>(o2);
+    float2 t3 = make_float2(c * (-o3.x - SIGN * o3.y), c * (SIGN * o3.x - o3.y));
+    x[0] = cadd(e0, o0);
+    x[4] = csub(e0, o0);
+    x[1] = cadd(e1, t1);
+    x[5] = csub(e1, t1);
+    x[2] = cadd(e2, t2);
+    x[6] = csub(e2, t2);
+    x[3] = cadd(e3, t3);
+    x[7] = csub(e3, t3);
+}
+
+template <int R, int SIGN>
+__device__ __forceinline__ void dft(float2 (&x)[R]) {
+    if constexpr (R == 2) dft2<SIGN>(x);
+    else if constexpr (R == 4) dft4<SIGN>(x);
+    else dft8<SIGN>(x);
+}
+
+template <int N> struct FftShape;
+template <> struct FftShape<512> { static constexpr int R = 8, P = 3; };
+template <> struct FftShape<256> { static constexpr int R = 4, P = 4; };
+template <> struct FftShape<128> { static constexpr int R = 2, P = 7; };
+template <> struct FftShape<64>  { static constexpr int R = 4, P = 3; };
+template <> struct FftShape<32>  { static constexpr int R = 2, P = 5; };
+
+template <int N, int SIGN>
+struct WaveFFT {
+    static constexpr int R = FftShape<N>::R;
+    static constexpr int P = FftShape<N>::P;
+    static constexpr int L = N / R;        // lanes per FFT
+    static constexpr int W = 64 / L;       // FFTs per wave
+    static constexpr int NT = (P > 1 ? P - 1 : 1);
+
+    float2 tw[NT][R - 1];                  // per-lane twiddles of passes 1..P-1
+
+    // j: lane index inside the group.
+    __device__ __forceinline__ void init(int j) {
+        int ns = R;
+#pragma unroll
+        for (int p = 1; p < P; ++p) {
+            const int k = j & (ns - 1);
+#pragma unroll
+            for (int r = 1; r < R; ++r) {
+                // exp(SIGN * 2 pi i k r / (ns R)): sincospi of an exact dyadic argument
+                float s, c;
+                sincospif((float)(SIGN * 2 * k * r) / (float)(ns * R), &s, &c);
+                tw[p - 1][r - 1] = make_float2(c, s);
+            }
+            ns *= R;
+        }
+    }
+
+    // In-place transform of the group's values; buf holds N complex values private
+    // to this group (clobbered).
+    __device__ __forceinline__ void run(float2 (&x)[R], float2* buf, int j) const {
+        int ns = 1;
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            if (p > 0) {
+#pragma unroll
+                for (int r = 1; r < R; ++r) x[r] = cmul(x[r], tw[p - 1][r - 1]);
+            }
+            dft<R, SIGN>(x);
+            if (p == P - 1) break;
+            const int k = j & (ns - 1);
+            const int base = (j - k) * R + k;
+            wave_lds_fence();
+#pragma unroll
+            for (int r = 0; r < R; ++r) buf[base + r * ns] = x[r];
+            wave_lds_fence();
+#pragma unroll
+            for (int r = 0; r < R; ++r) x[r] = buf[j + r * L];
+            ns *= R;
+        }
+    }
+};
+
+}  // namespace ssb

@@ -1,0 +1,65 @@
+// Internal declarations shared by the host layer and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssb {
+
+// Reduction group: S1 partial images are summed over this many consecutive BF
+// pixels in float, then added group by group, in order, in double.  Fixed so that
+// every result is independent of chunking and batch size.
+constexpr int kGroupBF = 32;
+
+// Per-trial aberration constants: chi(k)/(2 pi) = k^T M k with k in detector
+// pixels (revolutions), M = (lambda dk^2 / 2) [[C10 + C12 c, C12 s], [C12 s, C10 - C12 c]],
+// c = cos 2 phi12, s = sin 2 phi12.
+struct TrialConst {
+    double mxx, mxy, myy, pad;
+};
+
+// Geometry as the kernels see it.
+struct GeomDev {
+    int n;            // N
+    int h;            // N / 2
+    double s;         // q step (detector pixels per scan-frequency index)
+    double crot, srot;
+    double ra;        // aperture radius (pixels)
+    double w;         // edge width (pixels)
+    double lo2;       // (ra - w/2)^2, or -1 when ra < w/2 (no flat top)
+    double hi2;       // (ra + w/2)^2
+};
+
+// Launchers (defined in ssb_kernels.hip).  All return the hipError_t of the
+// launch; grids are chunked internally to keep every dimension in range.
+hipError_t launch_g_rows(int n, const uint32_t* counts, int64_t nbf, float2* gm, float2* gn,
+                         unsigned long long* bfsum, hipStream_t st);
+hipError_t launch_g_cols(int n, float2* gm, float2* gn, int64_t nbf, hipStream_t st);
+
+// Pass 1: correction + column inverse transforms of the BF chunk [bf0, bf0 + cb)
+// for n_trials trials into the intermediate (main [t][cap][N][H], nyq [t][cap][N]).
+hipError_t launch_pass1(int n, const float2* gm, const float2* gn, const double2* kb,
+                        const uint8_t* active, const TrialConst* tc, int n_trials, GeomDev geo,
+                        int64_t bf0, int cb, int cap, float2* im, float2* in, hipStream_t st);
+// Pass 2: row transforms, atan2 and moments, one partial per 32-BF group.
+hipError_t launch_pass2(int n, const float2* im, const float2* in, int cap, const uint8_t* active,
+                        int64_t bf0, int cb, int n_trials, double dc, float* part_s1,
+                        double* part_s2, int gcap, hipStream_t st);
+int pass2_row_blocks(int n);
+hipError_t launch_accum(int n, const float* part_s1, const double* part_s2, int gcap, int ng,
+                        int n_trials, double* s1run, double* s2run, hipStream_t st);
+hipError_t launch_fill(double* p, int64_t count, hipStream_t st);
+hipError_t launch_loss(int n, const double* s1run, const double* s2run, int n_trials, double n_bf,
+                       double* loss, float* mean_phase, hipStream_t st);
+// Object: sum of corrected spectra over all BF, then one 2-D inverse transform.
+int obj_segments(int64_t nbf);
+hipError_t launch_obj_sum(int n, const float2* gm, const float2* gn, const double2* kb,
+                          const uint8_t* active, TrialConst tc, GeomDev geo, int64_t nbf,
+                          double2* part, int nseg, hipStream_t st);
+hipError_t launch_obj_reduce(int n, const double2* part, int nseg, float2* pm, float2* pn,
+                             hipStream_t st);
+hipError_t launch_obj_cols(int n, float2* pm, float2* pn, hipStream_t st);
+hipError_t launch_obj_rows(int n, const float2* pm, const float2* pn, double dcsum, double scale,
+                           float* phase, float2* psi, hipStream_t st);
+
+}  // namespace ssb

@@ -1,0 +1,242 @@
+"""Benchmark of the SSB phase-variance evaluation on one MI355X.
+
+One step = one exact phase-variance loss evaluation (one trial) of the full
+workload: 512 x 512 scan x 8,937 BF pixels, from cached complex64 spectra
+already resident in HBM.  Prints one JSON line (rank 0, one GPU).
+
+Also reported: the object redraw, the per-trial time inside a 200-trial batch,
+the spectrum build (prepare), per-stage device times measured with HIP events on
+the library's stream, the roofline of the dominant kernel, and the float64
+oracle timed on the host on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "ms per phase-variance eval + BF×scan samples/s at 512²×8,937 BF (1 GPU)"
+# Checkpoints page, "fftA intermediate and M5 hardware floor": 222.7 ms p50 per
+# evaluation of 2,342,780,928 BF x scan samples on an Apple M5 (another machine;
+# real data with 2,464 aperture-active BF, ours has all 8,937 active).
+PAGES_MS = 222.7
+PEAK_FP32_TFLOPS = 157.3    # MI355X FP32 vector (256 CU x 2.4 GHz, packed)
+PEAK_HBM_GBS = 8000.0
+
+
+def algorithmic_flops(n: int, support_share: float) -> dict:
+    """Algorithmic FLOPs per active BF plane and trial, by stage."""
+    fft = 5.0 * n * math.log2(n)                     # one complex n-point transform
+    half = n * (n // 2 + 1)
+    return {
+        # (N/2 + 1) column transforms + 45 flop per nonzero-transfer entry
+        "pass1": (n // 2 + 1) * fft + 45.0 * support_share * half,
+        # N rows as N/2 packed complex transforms + 23 flop per sample (atan2 + moments)
+        "pass2": (n // 2) * fft + 23.0 * n * n,
+    }
+
+
+def support_share(geom) -> float:
+    """Fraction of half-plane entries with nonzero transfer, averaged over every 8th BF (geometry only)."""
+    n = geom.scan_n
+    d = geom.det_n
+    ra, w = geom.aperture_px, geom.edge_px
+    hi2 = (ra + 0.5 * w) ** 2
+    i, j = np.meshgrid(np.arange(d), np.arange(d), indexing="ij")
+    sel = (i - geom.det_cy) ** 2 + (j - geom.det_cx) ** 2 <= geom.bf_r2
+    kx = (j[sel] - geom.det_cx).astype(np.float64)
+    ky = (i[sel] - geom.det_cy).astype(np.float64)
+    fy = np.fft.fftfreq(n) * n * geom.q_step_px
+    fx = np.fft.rfftfreq(n) * n * geom.q_step_px
+    tot = 0
+    picks = range(0, kx.size, 8)
+    for b in picks:
+        dxm = (kx[b] - fx)[None, :] ** 2
+        dym = (ky[b] - fy)[:, None] ** 2
+        dxp = (kx[b] + fx)[None, :] ** 2
+        dyp = (ky[b] + fy)[:, None] ** 2
+        tot += np.count_nonzero((dxm + dym < hi2) | (dxp + dyp < hi2))
+    return tot / (len(picks) * n * (n // 2 + 1))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="full", choices=["tiny", "small", "medium", "full"])
+    ap.add_argument("--batch", type=int, default=200, help="trials in the batched measurement (0 = skip)")
+    ap.add_argument("--cpu-sample-bf", type=int, default=512, help="BF pixels in the oracle CPU sample (0 = skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path shards over BF pixels "
+              "but this build runs on a single device.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import aberration_phase_variance_amd as ssb
+    from synth import WORKLOADS, make_counts_numpy, make_counts_torch, trial_params
+
+    def log(msg):
+        print(msg, file=sys.stderr, flush=True)
+
+    w = WORKLOADS[args.config]
+    g = w.geometry
+    n = g.scan_n
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    log(f"[bench] generating {w.name} counts ({w.n_bf} BF x {n}^2)")
+    t0 = time.perf_counter()
+    if n >= 256:
+        counts = make_counts_torch(w, dev)
+    else:
+        counts = torch.from_numpy(make_counts_numpy(w).view(np.int32)).to(dev)
+    torch.cuda.synchronize()
+    log(f"[bench] counts ready in {time.perf_counter() - t0:.1f} s")
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    h = ssb.ssb_prepare(g, counts, w.n_bf)
+    torch.cuda.synchronize()
+    prepare_ms = (time.perf_counter() - t0) * 1e3
+    info = ssb.ssb_query(h)
+    log(f"[bench] prepare {prepare_ms:.1f} ms, spectra {info['spectrum_bytes'] / 1e9:.2f} GB, chunk {info['chunk_bf']}")
+
+    params = np.array([w.true_params], dtype=np.float32)
+    for _ in range(args.warmup):
+        ssb.ssb_loss(h, params)
+    torch.cuda.synchronize()
+    samples = w.n_bf * n * n
+    times = []
+    t_all = time.perf_counter()
+    for _ in range(args.steps):
+        t1 = time.perf_counter()
+        loss = ssb.ssb_loss(h, params)[0]     # synchronizes the stream before returning
+        times.append((time.perf_counter() - t1) * 1e3)
+    torch.cuda.synchronize()
+    total_s = time.perf_counter() - t_all
+    ms_per_step = total_s * 1e3 / args.steps
+    log(f"[bench] loss {loss:.9f}: {ms_per_step:.3f} ms/eval (p50 {np.median(times):.3f}, min {min(times):.3f})")
+
+    # per-stage device times (HIP events on the library's stream), separate pass
+    ssb.ssb_profile(h, 1)
+    prof_steps = max(3, min(args.steps, 10))
+    for _ in range(prof_steps):
+        ssb.ssb_loss(h, params)
+    phase = torch.empty((n, n), dtype=torch.float32, device=dev)
+    for _ in range(3):
+        ssb.ssb_object(h, params[0], phase)
+    prof = ssb.ssb_profile(h, 0)
+    torch.cuda.synchronize()
+
+    # object redraw, host clock
+    ssb.ssb_object(h, params[0], phase)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    n_obj = 5
+    for _ in range(n_obj):
+        ssb.ssb_object(h, params[0], phase)
+    torch.cuda.synchronize()
+    object_ms = (time.perf_counter() - t1) * 1e3 / n_obj
+    log(f"[bench] object {object_ms:.3f} ms")
+
+    batch_ms_per_trial = None
+    if args.batch > 0:
+        bp = trial_params(w, args.batch)
+        ssb.ssb_loss(h, bp[:2])
+        t1 = time.perf_counter()
+        bl = ssb.ssb_loss(h, bp)
+        batch_ms_per_trial = (time.perf_counter() - t1) * 1e3 / args.batch
+        log(f"[bench] batch of {args.batch}: {batch_ms_per_trial:.3f} ms/trial")
+
+    # roofline of the dominant stage: algorithmic FLOPs per launch / average launch time
+    share = support_share(g)
+    fl = algorithmic_flops(n, share)
+    stage_ms = {k: prof[k]["ms"] / max(1, prof[k]["launches"]) for k in prof}
+    dom = max(("pass1", "pass2"), key=lambda k: prof[k]["ms"])
+    units_per_launch = prof[dom]["units"] / max(1, prof[dom]["launches"])
+    achieved_tflops = fl[dom] * units_per_launch / (stage_ms[dom] * 1e-3) / 1e12
+    roofline = {"bound": "alu", "kernel": dom, "achieved": round(achieved_tflops, 3),
+                "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved_tflops / PEAK_FP32_TFLOPS, 4),
+                "traffic": None,
+                "flop_per_plane": fl[dom], "planes_per_launch": units_per_launch,
+                "avg_launch_ms": round(stage_ms[dom], 4)}
+    g_bytes = info["spectrum_bytes"]
+    hbm = {"spectrum_read_gb": g_bytes / 1e9,
+           "spectrum_read_frac_of_step": round(g_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+
+    # oracle on the host: bounded BF sample of the same workload, plus GPU moments of that range
+    cpu = None
+    oracle_check = None
+    if args.cpu_sample_bf > 0:
+        from oracle import ssb_oracle as O
+
+        nb = min(args.cpu_sample_bf, w.n_bf)
+        b0 = max(0, w.n_bf // 2 - nb // 2)
+        b1 = b0 + nb
+        sample = counts[b0:b1].cpu().numpy().view(np.uint32)
+        dc = info["dc"]
+        og = O.OGeom.from_any(g)
+        log(f"[bench] oracle on BF [{b0}, {b1}) ...")
+        t1 = time.perf_counter()
+        r1, r2 = O.bf_moments(og, sample, params[0], dc, list(range(b0, b1)))
+        cpu_s = time.perf_counter() - t1
+        cpu = {"value": nb * n * n / cpu_s, "unit": "BF×scan samples/s", "cores": 1, "kind": "oracle",
+               "sample": f"float64 oracle moments of BF [{b0}, {b1}) ({nb} of {w.n_bf} BF x {n}^2 scan) at the "
+                         f"true aberrations, one host thread, {cpu_s:.1f} s",
+               "host_cores_available": len(os.sched_getaffinity(0))}
+        s1 = torch.empty((n, n), dtype=torch.float64, device=dev)
+        s2 = ssb.ssb_moments(h, params[0], b0, b1, s1)
+        s1 = s1.cpu().numpy()
+        oracle_check = {"bf_range": [b0, b1], "s2_rel_err": abs(s2 - r2) / abs(r2),
+                        "s1_max_abs_err": float(np.max(np.abs(s1 - r1)))}
+        log(f"[bench] oracle {cpu_s:.1f} s; S2 rel err {oracle_check['s2_rel_err']:.2e}")
+
+    ssb.ssb_release(h)
+    value = samples * args.steps / total_s
+    pages_rate = samples / (PAGES_MS * 1e-3) if args.config == "full" else None
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "BF×scan samples/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "strong",
+        "vs_baseline": (value / pages_rate) if pages_rate else None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: {n}x{n} scan, {g.det_n}x{g.det_n} detector, {w.n_bf} BF, "
+                               f"uint32 Poisson counts, one trial per step",
+                   "scan_n": n, "det_n": g.det_n, "n_bf": w.n_bf, "trials_per_step": 1},
+        "loss": loss,
+        "ms_p50": float(np.median(times)),
+        "ms_min": float(min(times)),
+        "object_ms": object_ms,
+        "batch_trials": args.batch,
+        "batch_ms_per_trial": batch_ms_per_trial,
+        "prepare_ms": prepare_ms,
+        "stage_ms_per_launch": {k: round(v, 4) for k, v in stage_ms.items()},
+        "support_share": share,
+        "roofline": roofline,
+        "hbm": hbm,
+        "cpu_baseline": cpu,
+        "oracle_check": oracle_check,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

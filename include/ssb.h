@@ -1,0 +1,194 @@
+/*
+ * ssb.h - C ABI of the MI355X (gfx950) single-side-band (SSB) phase-variance library.
+ *
+ * The objective follows the quantem.gpu maintainer pages "SSB performance notes"
+ * and "Later SSB performance checkpoints".  For every bright-field (BF) detector
+ * pixel b the cached scan spectrum G_b (a forward real 2-D DFT of that pixel's
+ * scan counts, Hermitian half plane) is multiplied by the SSB aberration
+ * correction T_b, extended to the full plane by C(-q) = -conj(C(q)), inverse
+ * transformed (a 2-D inverse DFT done as column then row transforms), its phase
+ * taken with atan2, and the per-scan-pixel phase moments are reduced over all BF
+ * pixels to the phase-variance loss
+ *
+ *     L = S2 / (n_bf N^2) - (1/N^2) sum_px (S1 / n_bf)^2,
+ *     S1(px) = sum_b phi_b(px),  S2 = sum_b sum_px phi_b(px)^2.
+ *
+ * The correction is T = conj(Gamma)/|Gamma| (0 where Gamma = 0) with
+ * Gamma(q) = conj(A(k)) A(k - q) - A(k) conj(A(k + q)) and the probe
+ * A(k) = a(k) exp(-i chi(k)): soft aperture a(k) = clip((R_a - |k|)/w + 1/2, 0, 1),
+ * chi = pi lambda |k|^2 C10 + pi lambda C12 ((kx^2 - ky^2) cos 2phi12 + 2 kx ky sin 2phi12).
+ * Notes page, sections "MPS zero-transfer q-space checkpoint" (both shifted
+ * apertures, zero transfer), "MPS dead inactive-write elimination checkpoint"
+ * (v8 follow-ups: two shifted-phase sincos, gamma normalization) and
+ * "Automatic whole-probe sparse-storage checkpoint" (the anti-Hermitian relation,
+ * the DC value).  The q = 0 term is the scalar DC = mean over BF of the scan sum.
+ *
+ * Conventions.  Detector pixel (i, j) is row i, column j; k_b = (j - cx, i - cy)
+ * in pixels.  The BF set is every detector pixel with (i-cy)^2 + (j-cx)^2 <= bf_r2,
+ * in row-major order; counts are passed in that order.  Scan frequency (u, v) of
+ * the half plane (u in [0, N), v in [0, N/2]) is q = Rot(rho) * s * (v, u') in
+ * detector pixels, u' = u for u < N/2 and u - N otherwise; v = N/2 is +N/2.
+ *
+ * Errors.  Every int-returning call returns SSB_OK (0) or a negative code and
+ * sets a thread-local message readable with ssb_last_error().  Nothing throws
+ * across this boundary.  A handle is not safe for concurrent calls; different
+ * handles are independent.  All device work is issued on the caller's HIP stream
+ * (NULL = the default stream).  Every call that returns host results
+ * synchronizes that stream before returning.
+ */
+#ifndef SSB_H
+#define SSB_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    SSB_OK = 0,
+    SSB_EINVAL = -1,   /* null pointer, non-finite or out-of-range argument, bad handle */
+    SSB_ESHAPE = -2,   /* n_bf does not match the BF rule, or a range is outside [0, n_bf] */
+    SSB_ENOMEM = -3,   /* a device allocation failed */
+    SSB_EDEVICE = -4   /* a HIP runtime error; the message carries hipGetErrorString */
+};
+
+/* Workload geometry.  Lengths are in detector pixels unless stated otherwise. */
+typedef struct ssb_geometry {
+    int32_t scan_n;        /* N: scan side, a power of two in [32, 512] */
+    int32_t det_n;         /* D: detector side, > 0 */
+    double bf_r2;          /* BF disk radius squared (pixels^2), >= 0 */
+    double det_cy;         /* detector center row (pixels) */
+    double det_cx;         /* detector center column (pixels) */
+    double q_step_px;      /* detector pixels per scan-frequency index: 1/(N * scan step * dk), > 0 */
+    double dk;             /* detector sampling in 1/Angstrom per pixel, > 0 */
+    double wavelength_A;   /* electron wavelength in Angstrom, > 0 */
+    double alpha_rad;      /* probe semi-angle in rad, > 0; aperture radius R_a = alpha/(lambda dk) px */
+    double rotation_rad;   /* scan-to-detector rotation rho, finite */
+    double edge_px;        /* width w of the soft aperture edge (pixels), > 0 */
+} ssb_geometry;
+
+typedef struct ssb_info {
+    int64_t n_bf;          /* logical BF pixels (all count in the normalization) */
+    int64_t n_active_bf;   /* BF pixels with a(k_b) > 0 */
+    int32_t scan_n;
+    int32_t det_n;
+    int64_t spectrum_bytes;/* device bytes of the cached half-plane spectra */
+    double dc;             /* DC value: mean over BF of the exact integer scan sums */
+    int64_t chunk_bf;      /* current cap on BF pixels per intermediate chunk */
+} ssb_info;
+
+typedef struct ssb_handle ssb_handle;
+
+/*
+ * ssb_prepare: validate the geometry, select the BF pixels, and build the cached
+ * spectra G_b = rfft2(counts_b) for every BF pixel on the device (complex64,
+ * BF-major).  Checkpoints page, "fftA intermediate and M5 hardware floor"
+ * (complex64 Hermitian G cache) and Notes page, "BF-major G_qk materialization".
+ *
+ *   g        host pointer to the geometry (copied).
+ *   counts   DEVICE pointer, uint32 [n_bf][N][N], BF-major in BF order, scan
+ *            row-major.  Counts up to 2^24 convert to float exactly.  Only read;
+ *            the caller may free it once this call returns.
+ *   n_bf     must equal the number of detector pixels selected by the BF rule.
+ *   stream   hipStream_t or NULL.
+ *   out      receives a new handle that owns all device memory it uses.
+ * Errors: SSB_EINVAL (null, non-finite or out-of-range geometry, counts not a
+ * device pointer), SSB_ESHAPE (n_bf mismatch), SSB_ENOMEM, SSB_EDEVICE.
+ */
+int ssb_prepare(const ssb_geometry* g, const uint32_t* counts, int64_t n_bf,
+                void* stream, ssb_handle** out);
+
+/*
+ * ssb_loss: phase-variance loss for n_trials aberration sets.
+ *   params      HOST float [n_trials][3] = {C10 nm, C12 nm, phi12 rad}; each value
+ *               is taken as given in float32 (the evaluation's exact input).
+ *   losses      HOST double [n_trials], written on success.
+ *   mean_phase  optional DEVICE float [N][N] receiving S1/n_bf of trial 0, or NULL.
+ * Each trial's loss is bitwise independent of n_trials, of its position in the
+ * batch and of the chunk size.  Synchronizes the stream before returning.
+ * Errors: SSB_EINVAL (null handle/params/losses, n_trials < 1, non-finite
+ * parameter), SSB_ENOMEM, SSB_EDEVICE.
+ */
+int ssb_loss(ssb_handle* h, const float* params, int32_t n_trials, double* losses,
+             float* mean_phase, void* stream);
+
+/*
+ * ssb_moments: phase moments of one trial over the BF range [bf_begin, bf_end)
+ * (one device's share when the BF set is split).  S1 = sum of phi_b per scan
+ * pixel and S2 = sum of phi_b^2 over the range, the pieces of the loss above.
+ *   params3  HOST float[3].
+ *   s1       DEVICE double [N][N], overwritten.
+ *   s2       HOST double, written on success.
+ * Synchronizes the stream.  Errors: SSB_EINVAL, SSB_ESHAPE (bad range),
+ * SSB_ENOMEM, SSB_EDEVICE.
+ */
+int ssb_moments(ssb_handle* h, const float* params3, int64_t bf_begin, int64_t bf_end,
+                double* s1, double* s2, void* stream);
+
+/*
+ * ssb_object: phase-of-mean object redraw.  psi = ifft2(full plane of
+ * mean_b C_b) and phase = atan2(Im psi, Re psi) (Notes page, "Standard-only CUDA
+ * native 512 calibration": the public output is the phase of the mean).
+ *   params3  HOST float[3].
+ *   phase    DEVICE float [N][N].
+ *   psi      optional DEVICE complex64 [N][N] (interleaved re, im) or NULL.
+ * Asynchronous on the stream.  Errors: SSB_EINVAL, SSB_ENOMEM, SSB_EDEVICE.
+ */
+int ssb_object(ssb_handle* h, const float* params3, float* phase, float* psi, void* stream);
+
+/*
+ * ssb_spectrum: copy the cached spectrum of BF pixel bf as complex64
+ * [N][N/2 + 1] (interleaved re, im, logical half-plane order) into the DEVICE
+ * buffer out.  Asynchronous.  Errors: SSB_EINVAL, SSB_ESHAPE, SSB_EDEVICE.
+ */
+int ssb_spectrum(const ssb_handle* h, int64_t bf, float* out, void* stream);
+
+/*
+ * ssb_set_chunk: cap the BF pixels whose intermediate is resident at once
+ * (rounded up to the fixed 32-BF reduction group; 0 restores the automatic
+ * choice).  Results do not depend on it; it bounds workspace memory.
+ */
+int ssb_set_chunk(ssb_handle* h, int64_t chunk_bf);
+
+/*
+ * Stage profiling.  When enabled, the library records a pair of HIP events on
+ * the caller's stream around each stage's kernel launches and accumulates their
+ * elapsed times (and the BF-plane x trial units each stage processed).
+ */
+enum {
+    SSB_STAGE_PASS1 = 0,     /* correction + column inverse transforms */
+    SSB_STAGE_PASS2 = 1,     /* row inverse transforms + atan2 + phase moments */
+    SSB_STAGE_REDUCE = 2,    /* clears, ordered S1/S2 accumulation, loss reduction */
+    SSB_STAGE_OBJ_SUM = 3,   /* object: corrected-spectrum sum over all BF */
+    SSB_STAGE_OBJ_FFT = 4,   /* object: partial reduction, 2-D inverse transform, phase */
+    SSB_NUM_STAGES = 5
+};
+
+typedef struct ssb_profile_data {
+    double ms[SSB_NUM_STAGES];         /* accumulated event time per stage */
+    int64_t launches[SSB_NUM_STAGES];  /* timed stage invocations */
+    int64_t units[SSB_NUM_STAGES];     /* active BF planes x trials processed (passes 1-2, object sum) */
+} ssb_profile_data;
+
+/*
+ * ssb_profile: mode 1 enables profiling and clears the totals, mode 0 disables it,
+ * mode 2 leaves the state unchanged.  If out is not NULL it receives the totals
+ * after waiting for every recorded event.  Errors: SSB_EINVAL, SSB_EDEVICE.
+ */
+int ssb_profile(ssb_handle* h, int mode, ssb_profile_data* out);
+
+/* ssb_query: fill *info.  Errors: SSB_EINVAL. */
+int ssb_query(const ssb_handle* h, ssb_info* info);
+
+/* ssb_release: free the handle and its device memory; NULL is a no-op. */
+void ssb_release(ssb_handle* h);
+
+/* Thread-local text of the last error on this thread ("" if none). */
+const char* ssb_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSB_H */

@@ -1,0 +1,171 @@
+"""GPU parity at the full and medium workload sizes, in the launch configuration the
+benchmark times (N = 512, 8,937 BF, default chunking).
+
+The float64 oracle cannot evaluate all 8,937 BF pixels of a 512^2 scan within a
+test's time, so at full size it checks sampled outputs one by one (cached spectra
+of single BF pixels, phase moments of BF ranges including the ragged last group)
+and properties that hold at any size (the loss equals the formula applied to the
+moments of the whole range; moments are additive over a split of the range).  A
+complete N = 512 loss and object check runs on a 317-BF sub-disk of the same counts.
+Counts come from the seeded device generator; the oracle gets the same bytes.
+"""
+import dataclasses
+import sys
+
+import numpy as np
+import pytest
+
+import aberration_phase_variance_amd as ssb
+from oracle import ssb_oracle as O
+from synth import WORKLOADS, make_counts_torch
+
+pytestmark = pytest.mark.gpu
+
+LOSS_RTOL = 1e-5
+PHASE_RMS = 1e-4
+TRUE = [40.0, 5.0, 0.3]
+
+
+def _say(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def full():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a visible GPU")
+    w = WORKLOADS["full"]
+    _say("[full] generating counts on the device")
+    counts = make_counts_torch(w, torch.device("cuda:0"))
+    h = ssb.ssb_prepare(w.geometry, counts, w.n_bf)
+    torch.cuda.synchronize()
+    yield w, counts, h
+    ssb.ssb_release(h)
+    del counts
+    torch.cuda.empty_cache()
+
+
+def _host(counts, b0, b1):
+    return counts[b0:b1].cpu().numpy().view(np.uint32)
+
+
+def _moments(h, n, params, b0, b1):
+    import torch
+    s1 = torch.empty((n, n), dtype=torch.float64, device="cuda")
+    s2 = ssb.ssb_moments(h, params, b0, b1, s1)
+    return s1.cpu().numpy(), s2
+
+
+def test_full_prepare_exact(full):
+    w, counts, h = full
+    info = ssb.ssb_query(h)
+    assert info["n_bf"] == 8937 and info["n_active_bf"] == 8937
+    assert info["scan_n"] == 512 and info["det_n"] == 192
+    total = 0
+    for b0 in range(0, w.n_bf, 1024):       # exact integer scan sums on the host
+        total += int(_host(counts, b0, min(w.n_bf, b0 + 1024)).astype(np.int64).sum())
+    assert info["dc"] == total / w.n_bf
+
+
+def test_full_spectra_sampled(full):
+    import torch
+    w, counts, h = full
+    for b in (0, 4468, 8936):
+        ref = O.scan_spectrum(_host(counts, b, b + 1)[0])
+        out = torch.empty((512, 257, 2), dtype=torch.float32, device="cuda")
+        ssb.ssb_spectrum(h, b, out)
+        o = out.cpu().numpy()
+        got = o[..., 0] + 1j * o[..., 1]
+        assert np.linalg.norm(got - ref) <= 2e-6 * np.linalg.norm(ref), b
+
+
+@pytest.mark.parametrize("b0,b1", [(0, 32), (4450, 4493), (8896, 8937)])
+def test_full_moments_sampled(full, b0, b1):
+    w, counts, h = full
+    og = O.OGeom.from_any(w.geometry)
+    dc = ssb.ssb_query(h)["dc"]
+    for params in (TRUE, [-137.0, 16.5, 2.7]):
+        s1, s2 = _moments(h, 512, params, b0, b1)
+        r1, r2 = O.bf_moments(og, _host(counts, b0, b1), params, dc, list(range(b0, b1)))
+        assert abs(s2 - r2) <= LOSS_RTOL * abs(r2), (b0, params)
+        d = s1 - r1
+        assert np.sqrt(np.mean(d * d)) <= 2e-5 * (b1 - b0) and np.max(np.abs(d)) <= 1e-3, (b0, params)
+
+
+def test_full_loss_is_formula_of_moments(full):
+    w, counts, h = full
+    for params in (TRUE, [88.0, -12.0, 1.1]):
+        loss = ssb.ssb_loss(h, [params])[0]
+        s1, s2 = _moments(h, 512, params, 0, w.n_bf)
+        assert abs(loss - O.loss_from_moments(s1, s2, w.n_bf)) <= 1e-12 * abs(loss)
+        # additivity over a split at a 32-BF group boundary
+        a1, a2 = _moments(h, 512, params, 0, 4480)
+        b1, b2 = _moments(h, 512, params, 4480, w.n_bf)
+        assert abs((a2 + b2) - s2) <= 1e-12 * s2
+        assert np.max(np.abs((a1 + b1) - s1)) <= 1e-9 * np.max(np.abs(s1))
+
+
+def test_full_batch_invariance(full):
+    w, counts, h = full
+    p = np.array([TRUE, [-150.0, 3.0, 0.9], [20.0, 19.0, 2.2]], np.float32)
+    batch = ssb.ssb_loss(h, p)
+    for k in range(3):
+        assert ssb.ssb_loss(h, p[k:k + 1])[0] == batch[k]
+
+
+@pytest.fixture(scope="module")
+def subdisk(full):
+    """The full counts restricted to the 317 BF pixels of radius <= 10 px, same 512^2 scan."""
+    import torch
+    w, counts, h = full
+    g = dataclasses.replace(w.geometry, bf_r2=100.0)
+    og_full = O.OGeom.from_any(w.geometry)
+    i, j = O.bf_indices(og_full)
+    sel = np.flatnonzero((i - 96) ** 2 + (j - 96) ** 2 <= 100)
+    sub = counts[torch.from_numpy(sel).cuda()].contiguous()
+    hs = ssb.ssb_prepare(g, sub, sel.size)
+    torch.cuda.synchronize()
+    yield g, sub.cpu().numpy().view(np.uint32), hs
+    ssb.ssb_release(hs)
+
+
+def test_n512_subdisk_loss_and_object(subdisk):
+    import torch
+    g, counts, hs = subdisk
+    og = O.OGeom.from_any(g)
+    assert counts.shape[0] == 317
+    dc = O.dc_value(counts)
+    assert ssb.ssb_query(hs)["dc"] == dc
+    for params in (TRUE, [-60.0, 9.0, 2.0]):
+        got = ssb.ssb_loss(hs, [params])[0]
+        ref = O.loss(og, counts, params, dc)
+        assert abs(got - ref) <= LOSS_RTOL * abs(ref), (params, got, ref)
+    phase = torch.empty((512, 512), dtype=torch.float32, device="cuda")
+    ssb.ssb_object(hs, TRUE, phase)
+    torch.cuda.synchronize()
+    ref_phase, _ = O.object_wave(og, counts, TRUE, dc)
+    d = np.angle(np.exp(1j * (phase.cpu().numpy() - ref_phase)))
+    assert np.sqrt(np.mean(d * d)) <= PHASE_RMS
+
+
+def test_medium_loss_and_object():
+    import torch
+    w = WORKLOADS["medium"]
+    counts = make_counts_torch(w, torch.device("cuda:0"))
+    h = ssb.ssb_prepare(w.geometry, counts, w.n_bf)
+    try:
+        host = counts.cpu().numpy().view(np.uint32)
+        og = O.OGeom.from_any(w.geometry)
+        dc = O.dc_value(host)
+        got = ssb.ssb_loss(h, [TRUE])[0]
+        ref = O.loss(og, host, TRUE, dc)
+        assert abs(got - ref) <= LOSS_RTOL * abs(ref), (got, ref)
+        phase = torch.empty((256, 256), dtype=torch.float32, device="cuda")
+        ssb.ssb_object(h, TRUE, phase)
+        torch.cuda.synchronize()
+        ref_phase, _ = O.object_wave(og, host, TRUE, dc)
+        d = np.angle(np.exp(1j * (phase.cpu().numpy() - ref_phase)))
+        assert np.sqrt(np.mean(d * d)) <= PHASE_RMS
+    finally:
+        ssb.ssb_release(h)

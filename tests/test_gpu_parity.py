@@ -1,0 +1,308 @@
+"""GPU parity: the HIP library through its C ABI against the float64 oracle.
+
+Tolerances: loss within 1e-5 relative, object phase within 1e-4 rad RMS, BF
+selection and spectrum indexing bit-exact (the targets stated for this path);
+cached spectra within 2e-6 relative L2 per BF (float32 FFT of a 2-D plane).
+"""
+import dataclasses
+import math
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import aberration_phase_variance_amd as ssb
+from oracle import ssb_oracle as O
+from synth import WORKLOADS, Workload, cached_counts, make_geometry, trial_params
+
+pytestmark = pytest.mark.gpu
+
+LOSS_RTOL = 1e-5
+PHASE_RMS = 1e-4
+SPEC_RTOL = 2e-6
+
+
+def _torch():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a visible GPU")
+    return torch
+
+
+def _say(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+class Prepared:
+    def __init__(self, geometry, counts_np=None, counts_dev=None):
+        torch = _torch()
+        self.torch = torch
+        self.g = geometry
+        if counts_dev is None:
+            counts_dev = torch.from_numpy(np.ascontiguousarray(counts_np).view(np.int32)).cuda()
+        self.n_bf = counts_dev.shape[0]
+        self.h = ssb.ssb_prepare(geometry, counts_dev, self.n_bf)
+        torch.cuda.synchronize()
+        self.n = geometry.scan_n
+
+    def loss(self, params, mean_phase=None):
+        return ssb.ssb_loss(self.h, params, mean_phase)
+
+    def obj(self, params, with_psi=True):
+        t = self.torch
+        phase = t.empty((self.n, self.n), dtype=t.float32, device="cuda")
+        psi = t.empty((self.n, self.n, 2), dtype=t.float32, device="cuda") if with_psi else None
+        ssb.ssb_object(self.h, params, phase, psi)
+        t.cuda.synchronize()
+        out_psi = None
+        if psi is not None:
+            p = psi.cpu().numpy()
+            out_psi = p[..., 0] + 1j * p[..., 1]
+        return phase.cpu().numpy(), out_psi
+
+    def moments(self, params, b0, b1):
+        t = self.torch
+        s1 = t.empty((self.n, self.n), dtype=t.float64, device="cuda")
+        s2 = ssb.ssb_moments(self.h, params, b0, b1, s1)
+        return s1.cpu().numpy(), s2
+
+    def spectrum(self, b):
+        t = self.torch
+        out = t.empty((self.n, self.n // 2 + 1, 2), dtype=t.float32, device="cuda")
+        ssb.ssb_spectrum(self.h, b, out)
+        t.cuda.synchronize()
+        o = out.cpu().numpy()
+        return o[..., 0] + 1j * o[..., 1]
+
+    def release(self):
+        ssb.ssb_release(self.h)
+        self.h = None
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    w = WORKLOADS["tiny"]
+    counts = cached_counts(w)
+    p = Prepared(w.geometry, counts)
+    yield w, counts, p
+    p.release()
+
+
+@pytest.fixture(scope="module")
+def small():
+    w = WORKLOADS["small"]
+    counts = cached_counts(w)
+    p = Prepared(w.geometry, counts)
+    yield w, counts, p
+    p.release()
+
+
+def _rel(a, b):
+    return abs(a - b) / abs(b)
+
+
+# ---------------------------------------------------------------- prepare / spectra
+@pytest.mark.parametrize("fx", ["tiny", "small"])
+def test_prepare_info_exact(fx, request):
+    w, counts, p = request.getfixturevalue(fx)
+    info = ssb.ssb_query(p.h)
+    g = O.OGeom.from_any(w.geometry)
+    kx, ky = O.bf_kvectors(g)
+    assert info["n_bf"] == w.n_bf == kx.size
+    assert info["n_active_bf"] == int(np.count_nonzero(O.aperture(g, kx, ky) > 0))
+    assert info["dc"] == O.dc_value(counts)          # exact integer mean
+    assert info["spectrum_bytes"] == w.n_bf * g.scan_n * (g.scan_n // 2 + 1) * 8
+
+
+@pytest.mark.parametrize("fx", ["tiny", "small"])
+def test_spectrum_vs_oracle(fx, request):
+    w, counts, p = request.getfixturevalue(fx)
+    for b in sorted({0, 1, w.n_bf // 2, w.n_bf - 1}):
+        ref = O.scan_spectrum(counts[b])
+        got = p.spectrum(b)
+        assert np.linalg.norm(got - ref) <= SPEC_RTOL * np.linalg.norm(ref), b
+
+
+def test_spectrum_indexing_bit_exact():
+    """Constant planes c_b = 1 + 3b: every cached spectrum is exactly (c_b N^2 at DC, 0 elsewhere)."""
+    w = WORKLOADS["small"]
+    n = w.geometry.scan_n
+    c = (1 + 3 * np.arange(w.n_bf, dtype=np.uint32))[:, None, None] * np.ones((1, n, n), np.uint32)
+    p = Prepared(w.geometry, c)
+    try:
+        for b in (0, 5, 160, w.n_bf - 1):
+            got = p.spectrum(b)
+            exp = np.zeros_like(got)
+            exp[0, 0] = float((1 + 3 * b) * n * n)
+            assert np.array_equal(got, exp), b
+        assert ssb.ssb_query(p.h)["dc"] == float(np.mean((1 + 3 * np.arange(w.n_bf)) * n * n))
+        # vacuum-like planes: every BF phase is 0, so every loss is exactly 0
+        assert np.all(p.loss([[40.0, 5.0, 0.3], [-90.0, 12.0, 2.0]]) == 0.0)
+    finally:
+        p.release()
+
+
+# ---------------------------------------------------------------- loss
+def test_loss_tiny(tiny):
+    w, counts, p = tiny
+    g = O.OGeom.from_any(w.geometry)
+    params = np.array([[40.0, 5.0, 0.3], [0.0, 0.0, 0.0], [-73.5, 14.0, 0.47], [120.0, -8.0, 2.9]], np.float32)
+    got = p.loss(params)
+    for k in range(len(params)):
+        ref = O.loss(g, counts, params[k])
+        assert _rel(got[k], ref) <= LOSS_RTOL, (k, got[k], ref)
+
+
+def test_loss_small_batch(small):
+    w, counts, p = small
+    g = O.OGeom.from_any(w.geometry)
+    dc = O.dc_value(counts)
+    params = trial_params(w, 12)
+    got = p.loss(params)
+    for k in range(len(params)):
+        ref = O.loss(g, counts, params[k], dc)
+        assert _rel(got[k], ref) <= LOSS_RTOL, (k, got[k], ref)
+
+
+def test_mean_phase_small(small):
+    w, counts, p = small
+    t = _torch()
+    g = O.OGeom.from_any(w.geometry)
+    mp = t.empty((128, 128), dtype=t.float32, device="cuda")
+    p.loss([[40.0, 5.0, 0.3]], mp)
+    ref = O.mean_phase(g, counts, (40.0, 5.0, 0.3))
+    d = mp.cpu().numpy() - ref
+    assert np.sqrt(np.mean(d * d)) < 1e-5 and np.max(np.abs(d)) < 1e-4
+
+
+def test_batch_chunk_and_repeat_invariance(small):
+    """Per-trial losses are bitwise independent of batch size, batch position, chunking and repetition."""
+    w, counts, p = small
+    a = np.array([[37.0, 4.0, 0.25]], np.float32)
+    others = trial_params(w, 6)
+    single = p.loss(a)[0]
+    batch = p.loss(np.concatenate([a, others[:2], a, others[2:]]))
+    assert batch[0] == single and batch[3] == single
+    assert np.array_equal(p.loss(others), batch[[1, 2, 4, 5, 6, 7]])
+    ssb.ssb_set_chunk(p.h, 32)
+    try:
+        assert p.loss(a)[0] == single
+        assert np.array_equal(p.loss(others), batch[[1, 2, 4, 5, 6, 7]])
+    finally:
+        ssb.ssb_set_chunk(p.h, 0)
+    assert p.loss(a)[0] == single
+
+
+def test_moments_range_small(small):
+    w, counts, p = small
+    g = O.OGeom.from_any(w.geometry)
+    dc = O.dc_value(counts)
+    b0, b1 = 37, 131                                  # not aligned to the 32-BF groups
+    s1, s2 = p.moments([40.0, 5.0, 0.3], b0, b1)
+    r1, r2 = O.bf_moments(g, counts[b0:b1], (40.0, 5.0, 0.3), dc, list(range(b0, b1)))
+    assert _rel(s2, r2) <= LOSS_RTOL
+    assert np.max(np.abs(s1 - r1)) <= 1e-4 * (b1 - b0) ** 0.5
+
+
+# ---------------------------------------------------------------- object
+@pytest.mark.parametrize("fx", ["tiny", "small"])
+def test_object_vs_oracle(fx, request):
+    w, counts, p = request.getfixturevalue(fx)
+    g = O.OGeom.from_any(w.geometry)
+    for params in ([40.0, 5.0, 0.3], [-55.0, 9.0, 1.9]):
+        phase, psi = p.obj(params)
+        ref_phase, ref_psi = O.object_wave(g, counts, params)
+        d = np.angle(np.exp(1j * (phase - ref_phase)))
+        assert np.sqrt(np.mean(d * d)) <= PHASE_RMS
+        assert np.linalg.norm(psi - ref_psi) <= 1e-5 * np.linalg.norm(ref_psi)
+
+
+# ---------------------------------------------------------------- edge cases
+def test_inactive_bf_pixels():
+    """Probe aperture smaller than the BF disk: zero-aperture BF keep phase 0 but count in n_bf."""
+    w = WORKLOADS["tiny"]
+    counts = cached_counts(w)
+    g0 = w.geometry
+    geom = dataclasses.replace(g0, alpha_rad=g0.alpha_rad * 2.5 / g0.aperture_px)
+    p = Prepared(geom, counts)
+    try:
+        og = O.OGeom.from_any(geom)
+        kx, ky = O.bf_kvectors(og)
+        n_act = int(np.count_nonzero(O.aperture(og, kx, ky) > 0))
+        assert 0 < n_act < w.n_bf
+        assert ssb.ssb_query(p.h)["n_active_bf"] == n_act
+        for params in ([40.0, 5.0, 0.3], [10.0, -3.0, 1.0]):
+            assert _rel(p.loss([params])[0], O.loss(og, counts, params)) <= LOSS_RTOL
+            phase, _ = p.obj(params, with_psi=False)
+            ref, _ = O.object_wave(og, counts, params)
+            assert np.sqrt(np.mean(np.angle(np.exp(1j * (phase - ref))) ** 2)) <= PHASE_RMS
+    finally:
+        p.release()
+
+
+def test_rotation():
+    """Rotated scan.  The edge width is 0.9 px: with 1 px the center BF pixel's |k -+ q| = |q|
+    (rotation-invariant) lands exactly on the aperture edge 10.5 px for some lattice q, a tie
+    that rounding of the rotation breaks either way."""
+    w = WORKLOADS["small"]
+    counts = cached_counts(w)
+    geom = dataclasses.replace(w.geometry, rotation_rad=0.3, edge_px=0.9)
+    og = O.OGeom.from_any(geom)
+    # no half-plane entry may sit within rounding of an aperture edge for this rotation
+    kx, ky = O.bf_kvectors(og)
+    qx, qy = O.q_vectors(og)
+    hi2 = (og.aperture_px + 0.5 * og.edge_px) ** 2
+    for s in (-1.0, 1.0):
+        r2 = (kx[:, None, None] + s * qx[None]) ** 2 + (ky[:, None, None] + s * qy[None]) ** 2
+        assert np.min(np.abs(r2 - hi2)) > 1e-9 * hi2
+    p = Prepared(geom, counts)
+    try:
+        for params in ([40.0, 5.0, 0.3], [-20.0, 15.0, 0.8]):
+            assert _rel(p.loss([params])[0], O.loss(og, counts, params)) <= LOSS_RTOL
+    finally:
+        p.release()
+
+
+def _custom_workload(n, d, r2):
+    base = WORKLOADS["tiny"]
+    g = make_geometry(n, d, r2)
+    i = np.arange(d)[:, None] - d / 2
+    j = np.arange(d)[None, :] - d / 2
+    nbf = int(np.count_nonzero(i * i + j * j <= r2))
+    return dataclasses.replace(base, name=f"n{n}", geometry=g, n_bf=nbf)
+
+
+@pytest.mark.parametrize("n,d,r2", [(64, 24, 20), (256, 40, 36)])
+def test_other_scan_sizes(n, d, r2):
+    w = _custom_workload(n, d, r2)
+    counts = cached_counts(w)
+    og = O.OGeom.from_any(w.geometry)
+    p = Prepared(w.geometry, counts)
+    try:
+        for params in ([40.0, 5.0, 0.3], [-25.0, 7.0, 2.4]):
+            assert _rel(p.loss([params])[0], O.loss(og, counts, params)) <= LOSS_RTOL
+        phase, _ = p.obj([40.0, 5.0, 0.3], with_psi=False)
+        ref, _ = O.object_wave(og, counts, [40.0, 5.0, 0.3])
+        assert np.sqrt(np.mean(np.angle(np.exp(1j * (phase - ref))) ** 2)) <= PHASE_RMS
+    finally:
+        p.release()
+
+
+def test_error_paths_on_device(small):
+    w, counts, p = small
+    t = _torch()
+    with pytest.raises(ssb.SSBError) as ei:
+        p.loss([[float("nan"), 1.0, 0.0]])
+    assert ei.value.code == ssb._ssb.SSB_EINVAL
+    s1 = t.empty((128, 128), dtype=t.float64, device="cuda")
+    for b0, b1 in ((-1, 5), (10, 10), (0, w.n_bf + 1)):
+        with pytest.raises(ssb.SSBError) as ei:
+            ssb.ssb_moments(p.h, [40.0, 5.0, 0.3], b0, b1, s1)
+        assert ei.value.code == ssb._ssb.SSB_ESHAPE
+    with pytest.raises(ssb.SSBError):
+        ssb.ssb_spectrum(p.h, w.n_bf, s1)
+    dev = t.zeros((w.n_bf - 1, 128, 128), dtype=t.int32, device="cuda")
+    with pytest.raises(ssb.SSBError) as ei:
+        ssb.ssb_prepare(w.geometry, dev, w.n_bf - 1)
+    assert ei.value.code == ssb._ssb.SSB_ESHAPE
