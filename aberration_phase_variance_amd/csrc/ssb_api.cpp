@@ -179,7 +179,7 @@ TrialConst trial_const(const ssb_handle* h, const float* p) {
 struct LossPlan {
     int cap;       // BF capacity of one chunk (multiple of kGroupBF)
     int gcap;      // groups per chunk
-    size_t off_im, off_in, off_ps1, off_ps2, off_s1, off_s2, off_loss, off_tc, total;
+    size_t off_im, off_in, off_ps1, off_ps2, off_s1, off_s2, off_loss, off_tc, off_chm, off_chn, total;
 };
 
 LossPlan plan_loss(const ssb_handle* h, int64_t nb, int n_trials) {
@@ -208,6 +208,8 @@ LossPlan plan_loss(const ssb_handle* h, int64_t nb, int n_trials) {
     pl.off_s2 = (size_t)align_up<double>(z, off, (size_t)n_trials);
     pl.off_loss = (size_t)align_up<double>(z, off, (size_t)n_trials);
     pl.off_tc = (size_t)align_up<TrialConst>(z, off, (size_t)n_trials);
+    pl.off_chm = (size_t)align_up<float2>(z, off, (size_t)n_trials * n * hh);
+    pl.off_chn = (size_t)align_up<float2>(z, off, (size_t)n_trials * n);
     pl.total = off + 256;
     return pl;
 }
@@ -245,6 +247,8 @@ int run_moments(ssb_handle* h, const float* params, int n_trials, int64_t b_begi
     double* s1 = reinterpret_cast<double*>(h->ws + pl.off_s1);
     double* s2 = reinterpret_cast<double*>(h->ws + pl.off_s2);
     TrialConst* tc = reinterpret_cast<TrialConst*>(h->ws + pl.off_tc);
+    float2* chm = reinterpret_cast<float2*>(h->ws + pl.off_chm);
+    float2* chn = reinterpret_cast<float2*>(h->ws + pl.off_chn);
 
     htc.resize(n_trials);
     for (int t = 0; t < n_trials; ++t) htc[t] = trial_const(h, params + 3 * t);
@@ -254,15 +258,17 @@ int run_moments(ssb_handle* h, const float* params, int n_trials, int64_t b_begi
         StageTimer tm(h, SSB_STAGE_REDUCE, st, 0);
         SSB_HIP(launch_fill(s1, (int64_t)n_trials * h->n * h->n, st), "clear S1");
         SSB_HIP(launch_fill(s2, n_trials, st), "clear S2");
+        SSB_HIP(launch_chiq(h->n, tc, n_trials, h->geo, chm, chn, st), "phase table launch");
     }
+
     for (int64_t c0 = b_begin; c0 < b_end; c0 += pl.cap) {
         const int cb = (int)std::min<int64_t>(pl.cap, b_end - c0);
         const int ng = (cb + kGroupBF - 1) / kGroupBF;
         const int64_t units = active_in(h, c0, c0 + cb) * n_trials;
         {
             StageTimer tm(h, SSB_STAGE_PASS1, st, units);
-            SSB_HIP(launch_pass1(h->n, h->gm, h->gn, h->kb, h->active, tc, n_trials, h->geo, c0, cb, pl.cap, im,
-                                 in, st),
+            SSB_HIP(launch_pass1(h->n, h->gm, h->gn, chm, chn, h->kb, h->active, tc, n_trials, h->geo, c0, cb,
+                                 pl.cap, im, in, st),
                     "pass 1 launch");
         }
         {
@@ -345,6 +351,11 @@ int ssb_prepare(const ssb_geometry* g, const uint32_t* counts, int64_t n_bf, voi
     geo.s = g->q_step_px;
     geo.crot = std::cos(g->rotation_rad);
     geo.srot = std::sin(g->rotation_rad);
+    geo.qvx = g->q_step_px * geo.crot;
+    geo.qux = -g->q_step_px * geo.srot;
+    geo.qvy = g->q_step_px * geo.srot;
+    geo.quy = g->q_step_px * geo.crot;
+    geo.inv_w = 1.0 / w;
     geo.ra = ra;
     geo.w = w;
     geo.lo2 = ra >= 0.5 * w ? (ra - 0.5 * w) * (ra - 0.5 * w) : -1.0;
@@ -457,7 +468,7 @@ int ssb_object(ssb_handle* h, const float* params3, float* phase, float* psi, vo
     double2* part = reinterpret_cast<double2*>(h->ows + o_part);
     float2* pm = reinterpret_cast<float2*>(h->ows + o_pm);
     float2* pn = reinterpret_cast<float2*>(h->ows + o_pn);
-    const TrialConst tc = trial_const(h, params3);   // passed by value: no host-staged copy
+    const TrialConst tc = trial_const(h, params3);   // kernel argument: no host-staged copy
     {
         StageTimer tm(h, SSB_STAGE_OBJ_SUM, st, h->n_active);
         SSB_HIP(launch_obj_sum(n, h->gm, h->gn, h->kb, h->active, tc, h->geo, h->n_bf, part, nseg, st),

@@ -88,6 +88,21 @@ template <> struct FftShape<128> { static constexpr int R = 2, P = 7; };
 template <> struct FftShape<64>  { static constexpr int R = 4, P = 3; };
 template <> struct FftShape<32>  { static constexpr int R = 2, P = 5; };
 
+// Bijective LDS index maps for the exchange after pass p.  The write and the
+// read of one exchange use the same map, so values are unchanged; the maps only
+// spread each 64-lane access across banks.  For N = 512 (radix 8) they remove
+// the bank conflicts of both exchanges (checked against 32- and 64-bank models);
+// other sizes keep the plain index.
+template <int N>
+__device__ __forceinline__ int exch_swizzle(int p, int i) {
+    if constexpr (N == 512) {
+        if (p == 0) return i ^ (((i >> 3) ^ (i >> 6)) & 7);
+        return i ^ ((((i) ^ (i >> 6)) & 7) << 3);
+    } else {
+        return i;
+    }
+}
+
 template <int N, int SIGN>
 struct WaveFFT {
     static constexpr int R = FftShape<N>::R;
@@ -131,10 +146,10 @@ struct WaveFFT {
             const int base = (j - k) * R + k;
             wave_lds_fence();
 #pragma unroll
-            for (int r = 0; r < R; ++r) buf[base + r * ns] = x[r];
+            for (int r = 0; r < R; ++r) buf[exch_swizzle<N>(p, base + r * ns)] = x[r];
             wave_lds_fence();
 #pragma unroll
-            for (int r = 0; r < R; ++r) x[r] = buf[j + r * L];
+            for (int r = 0; r < R; ++r) x[r] = buf[exch_swizzle<N>(p, j + r * L)];
             ns *= R;
         }
     }

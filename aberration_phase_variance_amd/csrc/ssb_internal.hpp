@@ -24,6 +24,9 @@ struct GeomDev {
     int h;            // N / 2
     double s;         // q step (detector pixels per scan-frequency index)
     double crot, srot;
+    // q(u', v) = (qvx v + qux u', qvy v + quy u') detector pixels, u' the signed row index
+    double qvx, qux, qvy, quy;
+    double inv_w;     // 1 / w
     double ra;        // aperture radius (pixels)
     double w;         // edge width (pixels)
     double lo2;       // (ra - w/2)^2, or -1 when ra < w/2 (no flat top)
@@ -38,9 +41,12 @@ hipError_t launch_g_cols(int n, float2* gm, float2* gn, int64_t nbf, hipStream_t
 
 // Pass 1: correction + column inverse transforms of the BF chunk [bf0, bf0 + cb)
 // for n_trials trials into the intermediate (main [t][cap][N][H], nyq [t][cap][N]).
-hipError_t launch_pass1(int n, const float2* gm, const float2* gn, const double2* kb,
-                        const uint8_t* active, const TrialConst* tc, int n_trials, GeomDev geo,
-                        int64_t bf0, int cb, int cap, float2* im, float2* in, hipStream_t st);
+// exp(2 pi i q^T M q) over the half plane for each trial: main [t][N][N/2], nyq [t][N].
+hipError_t launch_chiq(int n, const TrialConst* tc, int n_trials, GeomDev geo, float2* chm, float2* chn,
+                       hipStream_t st);
+hipError_t launch_pass1(int n, const float2* gm, const float2* gn, const float2* chm, const float2* chn,
+                        const double2* kb, const uint8_t* active, const TrialConst* tc, int n_trials,
+                        GeomDev geo, int64_t bf0, int cb, int cap, float2* im, float2* in, hipStream_t st);
 // Pass 2: row transforms, atan2 and moments, one partial per 32-BF group.
 hipError_t launch_pass2(int n, const float2* im, const float2* in, int cap, const uint8_t* active,
                         int64_t bf0, int cb, int n_trials, double dc, float* part_s1,
@@ -54,8 +60,8 @@ hipError_t launch_loss(int n, const double* s1run, const double* s2run, int n_tr
 // Object: sum of corrected spectra over all BF, then one 2-D inverse transform.
 int obj_segments(int64_t nbf);
 hipError_t launch_obj_sum(int n, const float2* gm, const float2* gn, const double2* kb,
-                          const uint8_t* active, TrialConst tc, GeomDev geo, int64_t nbf,
-                          double2* part, int nseg, hipStream_t st);
+                          const uint8_t* active, TrialConst tc, GeomDev geo, int64_t nbf, double2* part,
+                          int nseg, hipStream_t st);
 hipError_t launch_obj_reduce(int n, const double2* part, int nseg, float2* pm, float2* pn,
                              hipStream_t st);
 hipError_t launch_obj_cols(int n, float2* pm, float2* pn, hipStream_t st);

@@ -25,65 +25,130 @@ namespace ssb {
 
 namespace {
 
+// Compile-time tuning constants.
+#ifndef SSB_PASS1_TC
+#define SSB_PASS1_TC 16       // pass-1 columns per workgroup at N = 512
+#endif
+#ifndef SSB_PASS1_PRED_LOADS
+#define SSB_PASS1_PRED_LOADS 1 // pass 1 fetches only nonzero-transfer spectrum entries
+#endif
+#ifndef SSB_PASS2_MIN_WAVES
+#define SSB_PASS2_MIN_WAVES 1 // pass-2 register budget hint: minimum resident waves per SIMD
+#endif
+#ifndef SSB_PASS2_PREFETCH
+#define SSB_PASS2_PREFETCH 0  // pass 2 loads the next BF's column values during the current transform
+#endif
+
 constexpr int kTC = 16;       // columns per column-pass tile
 constexpr int kPad = 1;       // LDS row padding (complex values)
 
-enum ColMode { COL_CORRECT_INV = 0, COL_PLAIN_FWD = 1, COL_PLAIN_INV = 2 };
+enum ColMode { COL_PLAIN_FWD = 1, COL_PLAIN_INV = 2 };
 
 __device__ __forceinline__ double aperture_weight(double r2, const GeomDev& g) {
     if (r2 >= g.hi2) return 0.0;
     if (r2 <= g.lo2) return 1.0;
-    const double a = (g.ra - sqrt(r2)) / g.w + 0.5;
+    const double a = (g.ra - sqrt(r2)) * g.inv_w + 0.5;
     return fmin(fmax(a, 0.0), 1.0);
 }
 
-// C = G * T for half-plane entry (u, v) of the BF pixel at k = (kx, ky) pixels.
-// T = conj(Gamma)/|Gamma| with Gamma = a(k) e^{i delta} [(a_- - a_+) cos chi_q - i (a_- + a_+) sin chi_q],
-// where a_-+ = a(k -+ q), delta = 2 pi * 2 k^T M q and chi_q = 2 pi q^T M q: the
-// definition's two shifted probe phases chi(k) - chi(k -+ q) = +-delta - chi_q
-// regrouped, so the magnitude never comes from cancellation.  Geometry and phase
-// arguments are double; the phasors and the product are float.
-__device__ __forceinline__ float2 correct_entry(float2 gv, int u, int v, double kx, double ky,
-                                                const TrialConst& m, const GeomDev& g) {
-    const double fy = (double)(u < g.h ? u : u - g.n);
-    const double fx = (double)v;
-    const double qx0 = g.s * fx, qy0 = g.s * fy;
-    const double qx = g.crot * qx0 - g.srot * qy0;
-    const double qy = g.srot * qx0 + g.crot * qy0;
+// (cos, sin) of 2 pi r for r in [-1/2, 1/2]: quadrant from rint(4 r), then
+// sin(pi f/2) = f S(f^2) and cos(pi f/2) = C(f^2) on f in [-1/2, 1/2] with
+// polynomials fitted here (iteratively reweighted least squares, 4 and 5 terms;
+// max error 1e-7 in float).
+__device__ __forceinline__ float2 cossin_rev(float r) {
+    const float x = 4.0f * r;
+    const float q = rintf(x);
+    const float f = x - q;
+    const float s2 = f * f;
+    const float sn = f * fmaf(fmaf(fmaf(-4.592288751e-03f, s2, 7.967590541e-02f), s2, -6.459629536e-01f), s2,
+                              1.570796251e+00f);
+    const float cs = fmaf(fmaf(fmaf(fmaf(9.036316769e-04f, s2, -2.086007223e-02f), s2, 2.536692023e-01f), s2,
+                               -1.233700514e+00f),
+                          s2, 1.0f);
+    const int qi = (int)q & 3;
+    const float sb = (qi & 1) ? cs : sn;
+    const float cb = (qi & 1) ? sn : cs;
+    return make_float2(((qi + 1) & 2) ? -cb : cb, (qi & 2) ? -sb : sb);
+}
+
+// exp(-2 pi i x) for x in revolutions, reduced in double first.
+__device__ __forceinline__ float2 phasor_rev_neg(double x) {
+    const float2 cs = cossin_rev((float)(x - rint(x)));
+    return make_float2(cs.x, -cs.y);
+}
+
+// Corrected value C = G * T of one half-plane entry with scan frequency q = (qx, qy)
+// pixels, for the BF pixel at k = (kx, ky) pixels.
+//
+// T = conj(Gamma)/|Gamma|.  With chi quadratic, chi(k) - chi(k -+ q) = +-delta - chi_q
+// where delta = 2 pi * 2 k^T M q (bilinear) and chi_q = 2 pi q^T M q, so
+//   Gamma = a(k) e^{i delta} [(a_- - a_+) cos chi_q - i (a_- + a_+) sin chi_q],
+// the definition's two shifted probe factors regrouped so that |Gamma| never comes
+// from cancellation.  ed = exp(-i delta) and ch = (cos chi_q, sin chi_q) are given;
+// the support test is on exact double squared radii and both zero sidebands (zero
+// transfer) give an exact zero.
+__device__ __forceinline__ bool in_support(double qx, double qy, double kx, double ky, const GeomDev& g,
+                                           double& am, double& apl) {
     const double dxm = kx - qx, dym = ky - qy, dxp = kx + qx, dyp = ky + qy;
-    const double am = aperture_weight(dxm * dxm + dym * dym, g);
-    const double apl = aperture_weight(dxp * dxp + dyp * dyp, g);
-    if (am == 0.0 && apl == 0.0) return make_float2(0.f, 0.f);
-    const double mqx = m.mxx * qx + m.mxy * qy;
-    const double mqy = m.mxy * qx + m.myy * qy;
-    const double d = 2.0 * (kx * mqx + ky * mqy);
-    const double cq = qx * mqx + qy * mqy;
-    const float dr = (float)(d - rint(d));
-    const float cr = (float)(cq - rint(cq));
-    float sd, cd, sc, cc;
-    sincospif(2.0f * dr, &sd, &cd);
-    sincospif(2.0f * cr, &sc, &cc);
-    const float br = (float)(am - apl) * cc;   // Re conj(bracket)
-    const float bi = (float)(am + apl) * sc;   // Im conj(bracket)
+    const double r2m = dxm * dxm + dym * dym;
+    const double r2p = dxp * dxp + dyp * dyp;
+    if (r2m >= g.hi2 && r2p >= g.hi2) return false;
+    am = aperture_weight(r2m, g);
+    apl = aperture_weight(r2p, g);
+    return true;
+}
+
+__device__ __forceinline__ float2 apply_transfer(float2 gv, float2 ch, float2 ed, float am, float apl) {
+    const float br = (am - apl) * ch.x;   // Re conj(bracket)
+    const float bi = (am + apl) * ch.y;   // Im conj(bracket)
     const float mag2 = br * br + bi * bi;
     if (mag2 == 0.0f) return make_float2(0.f, 0.f);
     const float inv = rsqrtf(mag2);
-    const float tr = (cd * br + sd * bi) * inv;
-    const float ti = (cd * bi - sd * br) * inv;
+    const float tr = (ed.x * br - ed.y * bi) * inv;
+    const float ti = (ed.x * bi + ed.y * br) * inv;
     return make_float2(gv.x * tr - gv.y * ti, gv.x * ti + gv.y * tr);
 }
 
-// Column pass: one workgroup = one plane x one tile of kTC columns (or the
-// Nyquist column), one trial.  Coalesced tile load (optionally corrected) into
-// LDS, one wave-level FFT per column, coalesced store.  in == out is allowed
-// (the whole tile is read before any store).
+// (cos, sin) of 2 pi q^T M q
+__device__ __forceinline__ float2 chi_phasor(double qx, double qy, const TrialConst& m) {
+    const double cq = qx * (m.mxx * qx + m.mxy * qy) + qy * (m.mxy * qx + m.myy * qy);
+    const float2 ph = phasor_rev_neg(cq);
+    return make_float2(ph.x, -ph.y);
+}
+
+// atan2 in float: octant reduction to t = min/max in [0, 1], atan(t) = t P(t^2)
+// with a degree-8 polynomial in t^2 fitted here (iteratively reweighted least
+// squares on [0, 1] against atan; max relative error 1.4e-8 in exact arithmetic,
+// 3.3e-7 rad absolute in float including the approximate reciprocal), then the
+// octant is undone.  atan2(0, 0) = 0; NaN inputs give NaN.
+__device__ __forceinline__ float atan2_f(float y, float x) {
+    const float ax = fabsf(x), ay = fabsf(y);
+    const float mx = fmaxf(ax, ay), mn = fminf(ax, ay);
+    const float t = mx > 0.f ? mn * __builtin_amdgcn_rcpf(mx) : 0.f;
+    const float s = t * t;
+    float p = 2.903556684e-03f;
+    p = fmaf(p, s, -1.628302597e-02f);
+    p = fmaf(p, s, 4.303940013e-02f);
+    p = fmaf(p, s, -7.533679157e-02f);
+    p = fmaf(p, s, 1.065467894e-01f);
+    p = fmaf(p, s, -1.420713365e-01f);
+    p = fmaf(p, s, 1.999305487e-01f);
+    p = fmaf(p, s, -3.333309293e-01f);
+    p = fmaf(p, s, 1.0f);
+    float a = t * p;
+    a = ay > ax ? 1.57079632679489662f - a : a;
+    a = x < 0.f ? 3.14159265358979324f - a : a;
+    a = copysignf(a, y);
+    return (x != x || y != y) ? x + y : a;
+}
+
+// Plain column pass (spectrum builder, object): one workgroup = one plane x one
+// tile of kTC columns (or the Nyquist column).  Coalesced tile load into LDS, one
+// wave-level FFT per column, coalesced store.  in == out is allowed (the whole tile
+// is read before any store).
 template <int N, int MODE>
 __global__ __launch_bounds__(256) void k_cols(const float2* in_m, const float2* in_n, float2* out_m,
-                                              float2* out_n, int64_t out_tstride_m,
-                                              int64_t out_tstride_n, int64_t bf0,
-                                              const double2* __restrict__ kb,
-                                              const uint8_t* __restrict__ active,
-                                              const TrialConst* __restrict__ tc, GeomDev geo) {
+                                              float2* out_n) {
     constexpr int H = N / 2;
     constexpr int LD = N + kPad;
     constexpr int SIGN = (MODE == COL_PLAIN_FWD) ? -1 : 1;
@@ -92,40 +157,18 @@ __global__ __launch_bounds__(256) void k_cols(const float2* in_m, const float2* 
 
     const int tid = threadIdx.x;
     const int plane = blockIdx.y;
-    const int trial = blockIdx.z;
     const bool nyq = blockIdx.x == H / kTC;
     const int v0 = blockIdx.x * kTC;
-
-    double kx = 0.0, ky = 0.0;
-    TrialConst m{};
-    if constexpr (MODE == COL_CORRECT_INV) {
-        if (!active[bf0 + plane]) return;          // zero-aperture BF: phase is exactly 0
-        const double2 k = kb[bf0 + plane];
-        kx = k.x;
-        ky = k.y;
-        m = tc[trial];
-    }
     const float2* pin_m = in_m + (int64_t)plane * N * H;
     const float2* pin_n = in_n + (int64_t)plane * N;
-    float2* pout_m = out_m + (int64_t)trial * out_tstride_m + (int64_t)plane * N * H;
-    float2* pout_n = out_n + (int64_t)trial * out_tstride_n + (int64_t)plane * N;
+    float2* pout_m = out_m + (int64_t)plane * N * H;
+    float2* pout_n = out_n + (int64_t)plane * N;
 
     if (!nyq) {
         const int c = tid % kTC;
-        for (int u = tid / kTC; u < N; u += 256 / kTC) {
-            float2 gv = pin_m[(int64_t)u * H + v0 + c];
-            if constexpr (MODE == COL_CORRECT_INV) {
-                gv = (u == 0 && v0 + c == 0) ? make_float2(0.f, 0.f)
-                                             : correct_entry(gv, u, v0 + c, kx, ky, m, geo);
-            }
-            tile[c * LD + u] = gv;
-        }
+        for (int u = tid / kTC; u < N; u += 256 / kTC) tile[c * LD + u] = pin_m[(int64_t)u * H + v0 + c];
     } else {
-        for (int u = tid; u < N; u += 256) {
-            float2 gv = pin_n[u];
-            if constexpr (MODE == COL_CORRECT_INV) gv = correct_entry(gv, u, H, kx, ky, m, geo);
-            tile[u] = gv;
-        }
+        for (int u = tid; u < N; u += 256) tile[u] = pin_n[u];
     }
     __syncthreads();
 
@@ -155,46 +198,228 @@ __global__ __launch_bounds__(256) void k_cols(const float2* in_m, const float2* 
     }
 }
 
-// Assemble Z(v) = B0(v) + i B1(v), B_k = -i * (column result of row y_k),
-// extended Hermitian (B(N - v) = conj B(v)), with only real parts kept at
-// v = 0 and v = N/2; lane j gets v = j + r L.
-template <int N, int R, int L>
-__device__ __forceinline__ void assemble_row_pair(const float2* r0, const float2* r1, float2 h0, float2 h1,
-                                                  int j, float2 (&x)[R]) {
+// exp(i chi_q) = (cos, sin)(2 pi q^T M q) of every half-plane entry, per trial
+// (BF independent): main [t][N][N/2], nyq [t][N].
+template <int N>
+__global__ __launch_bounds__(256) void k_chiq(const TrialConst* __restrict__ tc, GeomDev geo,
+                                              float2* __restrict__ chm, float2* __restrict__ chn) {
     constexpr int H = N / 2;
+    constexpr int NE = N * (H + 1);
+    const int e = blockIdx.x * 256 + threadIdx.x;
+    if (e >= NE) return;
+    const int t = blockIdx.y;
+    const int u = e / (H + 1), v = e % (H + 1);
+    const double up = (double)(u < H ? u : u - N);
+    const float2 val = chi_phasor(fma(geo.qux, up, geo.qvx * v), fma(geo.quy, up, geo.qvy * v), tc[t]);
+    if (v < H) chm[((int64_t)t * N + u) * H + v] = val;
+    else chn[(int64_t)t * N + u] = val;
+}
+
+// Per-BF phase slopes of delta = v alpha + u' beta (revolutions).
+__device__ __forceinline__ void delta_slopes(double kx, double ky, const TrialConst& m, const GeomDev& g,
+                                             double& alpha, double& beta) {
+    const double px = m.mxx * kx + m.mxy * ky;
+    const double py = m.mxy * kx + m.myy * ky;
+    alpha = 2.0 * (px * g.qvx + py * g.qvy);
+    beta = 2.0 * (px * g.qux + py * g.quy);
+}
+
+// Pass 1: correction + column inverse transforms.  One workgroup = one BF pixel x
+// one tile of TC columns (or the Nyquist column) x one trial; each wave owns one
+// column's FFT.
+//   1. support test on exact double squared radii; the spectrum entries with
+//      nonzero transfer and their exp(i chi_q) from the per-trial table are
+//      loaded into registers (independent coalesced loads, all in flight
+//      together; zero-transfer entries are never fetched);
+//   2. each entry is corrected into the LDS tile;
+//   3. one wave-level inverse FFT per column;  4. coalesced store.
+// exp(-i delta) is separable: E_u(u') = exp(-2 pi i u' beta) for all rows is
+// built in LDS per workgroup, E_v(v) = exp(-2 pi i v alpha) per thread (each
+// thread keeps one column).
+constexpr int kPass1Threads = 512;
+
+template <int N, int TC>
+__global__ __launch_bounds__(kPass1Threads) void k_pass1(const float2* __restrict__ gm,
+                                                         const float2* __restrict__ gn,
+                                                         const float2* __restrict__ chm,
+                                                         const float2* __restrict__ chn,
+                                                         const double2* __restrict__ kb,
+                                                         const uint8_t* __restrict__ active,
+                                                         const TrialConst* __restrict__ tc, GeomDev geo,
+                                                         int64_t bf0, int cap, float2* __restrict__ im,
+                                                         float2* __restrict__ in) {
+    constexpr int H = N / 2;
+    constexpr int LD = N + kPad;
+    constexpr int NT = kPass1Threads;
+    constexpr int RS = NT / TC;                   // rows per sweep of the main-tile mapping
+    constexpr int PER = (N + RS - 1) / RS;        // entries per thread on a main tile (rows u < N)
+    constexpr int PERN = (N + NT - 1) / NT;       // entries per thread on the Nyquist tile
+    constexpr int PM = PER > PERN ? PER : PERN;
+    static_assert(PM <= 32, "support mask is one 32-bit word");
+    using F = WaveFFT<N, +1>;
+    __shared__ float2 tile[TC * LD];
+    __shared__ float2 eu[N];
+
+    const int tid = threadIdx.x;
+    const int bl = blockIdx.y;
+    const int t = blockIdx.z;
+    const int64_t b = bf0 + bl;
+    if (!active[b]) return;                       // zero-aperture BF: phase is exactly 0
+    const bool nyq = blockIdx.x == H / TC;
+    const int c = nyq ? 0 : tid % TC;
+    const int v = nyq ? H : blockIdx.x * TC + c;
+    const int ustart = nyq ? tid : tid / TC;
+    const int ustep = nyq ? NT : RS;
+    const int nent = nyq ? PERN : PER;
+    const double2 k = kb[b];
+    const TrialConst m = tc[t];
+    double alpha, beta;
+    delta_slopes(k.x, k.y, m, geo, alpha, beta);
+    for (int u = tid; u < N; u += NT) eu[u] = phasor_rev_neg((double)(u < H ? u : u - N) * beta);
+    const float2 ev = phasor_rev_neg((double)v * alpha);
+    const double qvx = geo.qvx * v, qvy = geo.qvy * v;
+
+    // 1. support test and loads into registers (all loads in flight together)
+    const float2* src = nyq ? gn + b * N : gm + b * N * H + v;
+    const float2* chs = nyq ? chn + (int64_t)t * N : chm + (int64_t)t * N * H + v;
+    const int sstride = nyq ? 1 : H;
+    float2 gv[PM], chv[PM];
+    float amv[PM], apv[PM];
+    unsigned sup = 0;
 #pragma unroll
-    for (int r = 0; r < R / 2; ++r) {
-        const int v = j + r * L;
-        float2 a0 = r0[v], a1 = r1[v];
-        if (v == 0) {
-            a0.x = 0.f;
-            a1.x = 0.f;
+    for (int i = 0; i < PM; ++i) {
+        const int u = ustart + i * ustep;
+        gv[i] = make_float2(0.f, 0.f);
+        chv[i] = make_float2(0.f, 0.f);
+        amv[i] = 0.f;
+        apv[i] = 0.f;
+        if (i < nent && u < N) {
+#if !SSB_PASS1_PRED_LOADS
+            gv[i] = src[u * sstride];
+            chv[i] = chs[u * sstride];
+#endif
+            const double up = (double)(u < H ? u : u - N);
+            double am, apl;
+            if ((u != 0 || v != 0) &&
+                in_support(fma(geo.qux, up, qvx), fma(geo.quy, up, qvy), k.x, k.y, geo, am, apl)) {
+                sup |= 1u << i;
+#if SSB_PASS1_PRED_LOADS
+                gv[i] = src[u * sstride];
+                chv[i] = chs[u * sstride];
+#endif
+                amv[i] = (float)am;
+                apv[i] = (float)apl;
+            }
         }
-        x[r] = make_float2(a0.y + a1.x, a1.y - a0.x);
     }
+    __syncthreads();                              // E_u complete
+
+    // 2. correction into the LDS tile
 #pragma unroll
-    for (int r = R / 2; r < R; ++r) {
-        const int v = j + r * L;
-        if (v == H) {
-            x[r] = make_float2(h0.y, h1.y);
-        } else {
-            const int w = N - v;
-            const float2 a0 = r0[w], a1 = r1[w];
-            x[r] = make_float2(a0.y - a1.x, a0.x + a1.y);
+    for (int i = 0; i < PM; ++i) {
+        const int u = ustart + i * ustep;
+        if (i < nent && u < N) {
+            float2 val = make_float2(0.f, 0.f);
+            if (sup & (1u << i)) val = apply_transfer(gv[i], chv[i], cmul(eu[u], ev), amv[i], apv[i]);
+            tile[c * LD + u] = val;
         }
+    }
+    __syncthreads();
+
+    // 3. column transforms
+    const int lane = tid & 63;
+    const int grp = (tid >> 6) * F::W + lane / F::L;
+    const int j = lane % F::L;
+    constexpr int NG = (NT / 64) * F::W;
+    F fft;
+    fft.init(j);
+    const int ncols = nyq ? 1 : TC;
+    for (int cc = grp; cc < ncols; cc += NG) {
+        float2 x[F::R];
+#pragma unroll
+        for (int r = 0; r < F::R; ++r) x[r] = tile[cc * LD + j + r * F::L];
+        fft.run(x, &tile[cc * LD], j);
+        wave_lds_fence();
+#pragma unroll
+        for (int r = 0; r < F::R; ++r) tile[cc * LD + j + r * F::L] = x[r];
+    }
+    __syncthreads();
+
+    // 4. store
+    if (!nyq) {
+        float2* om = im + ((int64_t)t * cap + bl) * N * H + v;
+#pragma unroll 4
+        for (int y = ustart; y < N; y += RS) om[(int64_t)y * H] = tile[c * LD + y];
+    } else {
+        float2* on = in + ((int64_t)t * cap + bl) * N;
+        for (int y = tid; y < N; y += NT) on[y] = tile[y];
     }
 }
 
+// Raw column-pass values a row pair needs: lane j gets v = j + r L for r < R/2
+// (direct) and the mirrored w = N - v for r >= R/2, plus the v = 0 and v = N/2
+// entries of both rows.
+template <int N, int R, int L>
+struct RowPairRaw {
+    float2 d0[R / 2], d1[R / 2], m0[R / 2], m1[R / 2];
+    float2 h0, h1, z0, z1;
+
+    __device__ __forceinline__ void load(const float2* r0, const float2* nyq, int j) {
+        constexpr int H = N / 2;
+        const float2* r1 = r0 + H;
+#pragma unroll
+        for (int r = 0; r < R / 2; ++r) {
+            d0[r] = r0[j + r * L];
+            d1[r] = r1[j + r * L];
+        }
+#pragma unroll
+        for (int r = 0; r < R / 2; ++r) {
+            const int w = H - j - r * L;            // N - (j + (r + R/2) L); w = H only for j = r = 0
+            const int ws = w == H ? 0 : w;           // that slot is taken from the Nyquist column below
+            m0[r] = r0[ws];
+            m1[r] = r1[ws];
+        }
+        h0 = nyq[0];
+        h1 = nyq[1];
+        z0 = r0[0];
+        z1 = r1[0];
+    }
+
+    // Z(v) = B0(v) + i B1(v), B_k = -i * (column result of row y_k), extended
+    // Hermitian (B(N - v) = conj B(v)) with only real parts kept at v = 0 and N/2.
+    __device__ __forceinline__ void assemble(int j, float2 (&x)[R]) const {
+        constexpr int H = N / 2;
+#pragma unroll
+        for (int r = 0; r < R / 2; ++r) {
+            float2 a0 = d0[r], a1 = d1[r];
+            if (j + r * L == 0) {
+                a0.x = 0.f;
+                a1.x = 0.f;
+            }
+            x[r] = make_float2(a0.y + a1.x, a1.y - a0.x);
+        }
+#pragma unroll
+        for (int r = 0; r < R / 2; ++r) {
+            if (j + (r + R / 2) * L == H) {
+                x[r + R / 2] = make_float2(h0.y, h1.y);
+            } else {
+                x[r + R / 2] = make_float2(m0[r].y - m1[r].x, m0[r].x + m1[r].y);
+            }
+        }
+    }
+};
+
 // Pass 2: one workgroup = 4*W row pairs x one 32-BF group x one trial.  Loops
 // over the group's BF pixels in order, accumulating per-pixel phase sums in
-// registers (float) and the squared phase (double per lane).
+// registers (float) and the squared phase (double per lane); the next BF's
+// column values are loaded while the current one is transformed.
 template <int N>
-__global__ __launch_bounds__(256) void k_pass2(const float2* __restrict__ im, const float2* __restrict__ in,
+__global__ __launch_bounds__(256, SSB_PASS2_MIN_WAVES) void k_pass2(const float2* __restrict__ im, const float2* __restrict__ in,
                                                int cap, const uint8_t* __restrict__ active, int64_t bf0,
                                                int cb, float dcf, float* __restrict__ part_s1,
                                                double* __restrict__ part_s2, int gcap) {
-    constexpr int H = N / 2;
     using F = WaveFFT<N, +1>;
+    constexpr int H = N / 2;
     constexpr int R = F::R, L = F::L;
     __shared__ float2 buf[4 * F::W][N];
     __shared__ double red[4];
@@ -221,28 +446,47 @@ __global__ __launch_bounds__(256) void k_pass2(const float2* __restrict__ im, co
     double s2 = 0.0;
     const float sgn = (j & 1) ? -1.f : 1.f;   // (-1)^x for x = j + r L, L even
 
-    for (int b = b_lo; b < b_hi; ++b) {
-        if (!active[bf0 + b]) continue;
-        const int64_t pl = (int64_t)t * cap + b;
-        const float2* r0 = im + (pl * N + y0) * H;
-        const float2* r1 = r0 + H;
-        const float2 h0 = in[pl * N + y0], h1 = in[pl * N + y0 + 1];
-        const float2 z0 = r0[0], z1 = r1[0];
+    auto next_active = [&](int b) {
+        while (b < b_hi && !active[bf0 + b]) ++b;
+        return b;
+    };
+    auto row_ptr = [&](int b) { return im + (((int64_t)t * cap + b) * N + y0) * H; };
+    auto nyq_ptr = [&](int b) { return in + ((int64_t)t * cap + b) * N + y0; };
+
+    RowPairRaw<N, R, L> cur;
+#if SSB_PASS2_PREFETCH
+    RowPairRaw<N, R, L> nxt;
+#endif
+    int b = next_active(b_lo);
+#if SSB_PASS2_PREFETCH
+    if (b < b_hi) cur.load(row_ptr(b), nyq_ptr(b), j);
+#endif
+    while (b < b_hi) {
+        const int bn = next_active(b + 1);
+#if SSB_PASS2_PREFETCH
+        if (bn < b_hi) nxt.load(row_ptr(bn), nyq_ptr(bn), j);
+#else
+        cur.load(row_ptr(b), nyq_ptr(b), j);
+#endif
         float2 x[R];
-        assemble_row_pair<N, R, L>(r0, r1, h0, h1, j, x);
+        cur.assemble(j, x);
         fft.run(x, buf[grp], j);
-        const float den0 = dcf + z0.x + sgn * h0.x;
-        const float den1 = dcf + z1.x + sgn * h1.x;
+        const float den0 = dcf + cur.z0.x + sgn * cur.h0.x;
+        const float den1 = dcf + cur.z1.x + sgn * cur.h1.x;
         float p2 = 0.f;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const float pa = atan2f(x[r].x, den0);
-            const float pb = atan2f(x[r].y, den1);
+            const float pa = atan2_f(x[r].x, den0);
+            const float pb = atan2_f(x[r].y, den1);
             s1a[r] += pa;
             s1b[r] += pb;
             p2 += pa * pa + pb * pb;
         }
         s2 += (double)p2;
+#if SSB_PASS2_PREFETCH
+        cur = nxt;
+#endif
+        b = bn;
     }
 
     float* o = part_s1 + (((int64_t)t * gcap + g) * N + y0) * N;
@@ -371,14 +615,14 @@ __global__ __launch_bounds__(256) void k_g_rows(const uint32_t* __restrict__ cou
     if (lane == 0) atomicAdd(&bfsum[b], sum);
 }
 
-// Object: sum over all BF pixels of the corrected half-plane spectrum, one
-// segment of BF pixels per grid row (double accumulation, BF order).
+// Object: sum over the BF pixels of one segment of the corrected half-plane
+// spectrum, one entry per thread, double accumulation in BF order.  Same
+// correction as pass 1; the BF-independent exp(i chi_q) is computed once per entry.
 template <int N>
 __global__ __launch_bounds__(256) void k_obj_sum(const float2* __restrict__ gm, const float2* __restrict__ gn,
                                                  const double2* __restrict__ kb,
-                                                 const uint8_t* __restrict__ active, TrialConst m,
-                                                 GeomDev geo, int64_t nbf, int seglen,
-                                                 double2* __restrict__ part) {
+                                                 const uint8_t* __restrict__ active, TrialConst m, GeomDev geo,
+                                                 int64_t nbf, int seglen, double2* __restrict__ part) {
     constexpr int H = N / 2;
     constexpr int NE = N * (H + 1);
     const int e = blockIdx.x * 256 + threadIdx.x;
@@ -388,13 +632,21 @@ __global__ __launch_bounds__(256) void k_obj_sum(const float2* __restrict__ gm, 
     const int64_t b_hi = min(nbf, b_lo + seglen);
     double ax = 0.0, ay = 0.0;
     if (!(u == 0 && v == 0)) {
+        const double up = (double)(u < H ? u : u - N);
+        const double qx = fma(geo.qux, up, geo.qvx * v), qy = fma(geo.quy, up, geo.qvy * v);
+        const float2 ch = chi_phasor(qx, qy, m);
         for (int64_t b = b_lo; b < b_hi; ++b) {
             if (!active[b]) continue;
-            const float2 gv = v < H ? gm[(b * N + u) * H + v] : gn[b * N + u];
             const double2 k = kb[b];
-            const float2 c = correct_entry(gv, u, v, k.x, k.y, m, geo);
-            ax += c.x;
-            ay += c.y;
+            double am, apl;
+            if (!in_support(qx, qy, k.x, k.y, geo, am, apl)) continue;
+            double alpha, beta;
+            delta_slopes(k.x, k.y, m, geo, alpha, beta);
+            const float2 ed = phasor_rev_neg(fma((double)v, alpha, up * beta));
+            const float2 gv = v < H ? gm[(b * N + u) * H + v] : gn[b * N + u];
+            const float2 cv = apply_transfer(gv, ch, ed, (float)am, (float)apl);
+            ax += cv.x;
+            ay += cv.y;
         }
     }
     part[(int64_t)blockIdx.y * NE + e] = make_double2(ax, ay);
@@ -432,23 +684,21 @@ __global__ __launch_bounds__(256) void k_obj_rows(const float2* __restrict__ pm,
     const int grp = (tid >> 6) * F::W + lane / L;
     const int j = lane % L;
     const int y0 = 2 * (blockIdx.x * (4 * F::W) + grp);
-    const float2* r0 = pm + y0 * H;
-    const float2* r1 = r0 + H;
-    const float2 h0 = pn[y0], h1 = pn[y0 + 1];
-    const float2 z0 = r0[0], z1 = r1[0];
+    RowPairRaw<N, R, L> raw;
+    raw.load(pm + y0 * H, pn + y0, j);
     float2 x[R];
-    assemble_row_pair<N, R, L>(r0, r1, h0, h1, j, x);
+    raw.assemble(j, x);
     F fft;
     fft.init(j);
     fft.run(x, buf[grp], j);
     const float sgn = (j & 1) ? -1.f : 1.f;
-    const float den0 = dcs + z0.x + sgn * h0.x;
-    const float den1 = dcs + z1.x + sgn * h1.x;
+    const float den0 = dcs + raw.z0.x + sgn * raw.h0.x;
+    const float den1 = dcs + raw.z1.x + sgn * raw.h1.x;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const int xx = j + r * L;
-        phase[y0 * N + xx] = atan2f(x[r].x, den0);
-        phase[(y0 + 1) * N + xx] = atan2f(x[r].y, den1);
+        phase[y0 * N + xx] = atan2_f(x[r].x, den0);
+        phase[(y0 + 1) * N + xx] = atan2_f(x[r].y, den1);
         if (psi) {
             psi[y0 * N + xx] = make_float2(den0 * scale, x[r].x * scale);
             psi[(y0 + 1) * N + xx] = make_float2(den1 * scale, x[r].y * scale);
@@ -475,18 +725,42 @@ hipError_t g_rows_n(const uint32_t* counts, int64_t nbf, float2* gm, float2* gn,
 
 template <int N, int MODE>
 hipError_t cols_n(const float2* in_m, const float2* in_n, float2* out_m, float2* out_n, int64_t planes,
-                  int trials, int64_t out_tstride_m, int64_t out_tstride_n, int64_t bf0, const double2* kb,
-                  const uint8_t* active, const TrialConst* tc, GeomDev geo, hipStream_t st) {
+                  hipStream_t st) {
     constexpr int H = N / 2;
     for (int64_t p0 = 0; p0 < planes; p0 += 65535) {
         const int np = (int)std::min<int64_t>(65535, planes - p0);
-        hipLaunchKernelGGL((k_cols<N, MODE>), dim3(H / kTC + 1, np, trials), dim3(256), 0, st,
-                           in_m + p0 * N * H, in_n + p0 * N, out_m + p0 * N * H, out_n + p0 * N,
-                           out_tstride_m, out_tstride_n, bf0 + p0, kb, active, tc, geo);
+        hipLaunchKernelGGL((k_cols<N, MODE>), dim3(H / kTC + 1, np), dim3(256), 0, st, in_m + p0 * N * H,
+                           in_n + p0 * N, out_m + p0 * N * H, out_n + p0 * N);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+// Column tile of pass 1: 16 columns (128-byte rows) for N = 512, 8 otherwise.
+template <int N> constexpr int pass1_tc() { return N >= 512 ? SSB_PASS1_TC : 8; }
+
+template <int N>
+hipError_t pass1_n(const float2* gm, const float2* gn, const float2* chm, const float2* chn, const double2* kb,
+                   const uint8_t* active, const TrialConst* tc, int n_trials, GeomDev geo, int64_t bf0, int cb,
+                   int cap, float2* im, float2* in, hipStream_t st) {
+    constexpr int H = N / 2;
+    constexpr int TC = pass1_tc<N>();
+    for (int64_t p0 = 0; p0 < cb; p0 += 65535) {
+        const int np = (int)std::min<int64_t>(65535, cb - p0);
+        hipLaunchKernelGGL((k_pass1<N, TC>), dim3(H / TC + 1, np, n_trials), dim3(kPass1Threads), 0, st, gm, gn, chm,
+                           chn, kb, active, tc, geo, bf0 + p0, cap, im + p0 * N * H, in + p0 * N);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+template <int N>
+hipError_t chiq_n(const TrialConst* tc, int n_trials, GeomDev geo, float2* chm, float2* chn, hipStream_t st) {
+    constexpr int NE = N * (N / 2 + 1);
+    hipLaunchKernelGGL(k_chiq<N>, dim3((NE + 255) / 256, n_trials), dim3(256), 0, st, tc, geo, chm, chn);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -507,19 +781,18 @@ hipError_t launch_g_rows(int n, const uint32_t* counts, int64_t nbf, float2* gm,
 }
 
 hipError_t launch_g_cols(int n, float2* gm, float2* gn, int64_t nbf, hipStream_t st) {
-    GeomDev geo{};
-    SSB_DISPATCH_N(n, (cols_n<NN, COL_PLAIN_FWD>(gm, gn, gm, gn, nbf, 1, 0, 0, 0, nullptr, nullptr, nullptr,
-                                                  geo, st)))
+    SSB_DISPATCH_N(n, (cols_n<NN, COL_PLAIN_FWD>(gm, gn, gm, gn, nbf, st)))
 }
 
-hipError_t launch_pass1(int n, const float2* gm, const float2* gn, const double2* kb, const uint8_t* active,
-                        const TrialConst* tc, int n_trials, GeomDev geo, int64_t bf0, int cb, int cap,
-                        float2* im, float2* in, hipStream_t st) {
-    const int64_t nn = n;
-    const int64_t ts_m = (int64_t)cap * nn * (nn / 2);
-    const int64_t ts_n = (int64_t)cap * nn;
-    SSB_DISPATCH_N(n, (cols_n<NN, COL_CORRECT_INV>(gm + bf0 * nn * (nn / 2), gn + bf0 * nn, im, in, cb, n_trials,
-                                                    ts_m, ts_n, bf0, kb, active, tc, geo, st)))
+hipError_t launch_chiq(int n, const TrialConst* tc, int n_trials, GeomDev geo, float2* chm, float2* chn,
+                       hipStream_t st) {
+    SSB_DISPATCH_N(n, (chiq_n<NN>(tc, n_trials, geo, chm, chn, st)))
+}
+
+hipError_t launch_pass1(int n, const float2* gm, const float2* gn, const float2* chm, const float2* chn,
+                        const double2* kb, const uint8_t* active, const TrialConst* tc, int n_trials, GeomDev geo,
+                        int64_t bf0, int cb, int cap, float2* im, float2* in, hipStream_t st) {
+    SSB_DISPATCH_N(n, (pass1_n<NN>(gm, gn, chm, chn, kb, active, tc, n_trials, geo, bf0, cb, cap, im, in, st)))
 }
 
 int pass2_row_blocks(int n) {
@@ -580,8 +853,7 @@ int obj_segments(int64_t nbf) {
 
 template <int N>
 static hipError_t obj_sum_n(const float2* gm, const float2* gn, const double2* kb, const uint8_t* active,
-                            TrialConst tc, GeomDev geo, int64_t nbf, double2* part, int nseg,
-                            hipStream_t st) {
+                            TrialConst tc, GeomDev geo, int64_t nbf, double2* part, int nseg, hipStream_t st) {
     constexpr int NE = N * (N / 2 + 1);
     const int seglen = (int)((nbf + nseg - 1) / nseg);
     hipLaunchKernelGGL(k_obj_sum<N>, dim3((NE + 255) / 256, nseg), dim3(256), 0, st, gm, gn, kb, active, tc, geo,
@@ -590,8 +862,7 @@ static hipError_t obj_sum_n(const float2* gm, const float2* gn, const double2* k
 }
 
 hipError_t launch_obj_sum(int n, const float2* gm, const float2* gn, const double2* kb, const uint8_t* active,
-                          TrialConst tc, GeomDev geo, int64_t nbf, double2* part, int nseg,
-                          hipStream_t st) {
+                          TrialConst tc, GeomDev geo, int64_t nbf, double2* part, int nseg, hipStream_t st) {
     SSB_DISPATCH_N(n, (obj_sum_n<NN>(gm, gn, kb, active, tc, geo, nbf, part, nseg, st)))
 }
 
@@ -607,9 +878,7 @@ hipError_t launch_obj_reduce(int n, const double2* part, int nseg, float2* pm, f
 }
 
 hipError_t launch_obj_cols(int n, float2* pm, float2* pn, hipStream_t st) {
-    GeomDev geo{};
-    SSB_DISPATCH_N(n, (cols_n<NN, COL_PLAIN_INV>(pm, pn, pm, pn, 1, 1, 0, 0, 0, nullptr, nullptr, nullptr, geo,
-                                                  st)))
+    SSB_DISPATCH_N(n, (cols_n<NN, COL_PLAIN_INV>(pm, pn, pm, pn, 1, st)))
 }
 
 template <int N>

@@ -76,6 +76,9 @@ def main():
     ap.add_argument("--config", default="full", choices=["tiny", "small", "medium", "full"])
     ap.add_argument("--batch", type=int, default=200, help="trials in the batched measurement (0 = skip)")
     ap.add_argument("--cpu-sample-bf", type=int, default=512, help="BF pixels in the oracle CPU sample (0 = skip)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run a plain 1 GiB device-to-device copy (3x) as a known-size reference "
+                         "for hardware byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path shards over BF pixels "
@@ -95,6 +98,13 @@ def main():
     n = g.scan_n
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
+    if args.calibrate_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)      # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     log(f"[bench] generating {w.name} counts ({w.n_bf} BF x {n}^2)")
     t0 = time.perf_counter()
     if n >= 256:
