@@ -179,21 +179,20 @@ TrialConst trial_const(const ssb_handle* h, const float* p) {
 struct LossPlan {
     int cap;       // BF capacity of one chunk (multiple of kGroupBF)
     int gcap;      // groups per chunk
-    size_t off_im, off_in, off_ps1, off_ps2, off_s1, off_s2, off_loss, off_tc, off_chm, off_chn, total;
+    size_t off_im, off_in, off_ps1, off_ps2, off_s1, off_s2, off_loss, off_lpart, off_tc, off_chm, off_chn, total;
 };
 
 LossPlan plan_loss(const ssb_handle* h, int64_t nb, int n_trials) {
     const int64_t n = h->n, hh = h->h;
     const double plane = (double)n * (hh + 1) * sizeof(float2);
-    int64_t cap = (int64_t)(kInterBudget / (plane * n_trials));
-    cap = (cap / kGroupBF) * kGroupBF;
-    if (cap < kGroupBF) cap = kGroupBF;
+    // memory bound on the chunk (intermediate for all trials of the call)
+    int64_t budget_cap = (int64_t)(kInterBudget / (plane * n_trials));
+    budget_cap = std::max<int64_t>(kGroupBF, (budget_cap / kGroupBF) * kGroupBF);
+    int64_t cap = budget_cap;
+    if (h->chunk_user > 0)
+        cap = std::min<int64_t>(cap, ((h->chunk_user + kGroupBF - 1) / kGroupBF) * kGroupBF);
     const int64_t need = ((nb + kGroupBF - 1) / kGroupBF) * kGroupBF;
     if (cap > need) cap = need;
-    if (h->chunk_user > 0) {
-        const int64_t u = ((h->chunk_user + kGroupBF - 1) / kGroupBF) * kGroupBF;
-        if (u < cap) cap = u;
-    }
     LossPlan pl;
     pl.cap = (int)cap;
     pl.gcap = (int)(cap / kGroupBF);
@@ -207,6 +206,7 @@ LossPlan plan_loss(const ssb_handle* h, int64_t nb, int n_trials) {
     pl.off_s1 = (size_t)align_up<double>(z, off, (size_t)n_trials * n * n);
     pl.off_s2 = (size_t)align_up<double>(z, off, (size_t)n_trials);
     pl.off_loss = (size_t)align_up<double>(z, off, (size_t)n_trials);
+    pl.off_lpart = (size_t)align_up<double>(z, off, (size_t)n_trials * loss_blocks());
     pl.off_tc = (size_t)align_up<TrialConst>(z, off, (size_t)n_trials);
     pl.off_chm = (size_t)align_up<float2>(z, off, (size_t)n_trials * n * hh);
     pl.off_chn = (size_t)align_up<float2>(z, off, (size_t)n_trials * n);
@@ -416,9 +416,10 @@ int ssb_loss(ssb_handle* h, const float* params, int32_t n_trials, double* losse
     double* s1 = reinterpret_cast<double*>(h->ws + pl.off_s1);
     double* s2 = reinterpret_cast<double*>(h->ws + pl.off_s2);
     double* dl = reinterpret_cast<double*>(h->ws + pl.off_loss);
+    double* lp = reinterpret_cast<double*>(h->ws + pl.off_lpart);
     {
         StageTimer tm(h, SSB_STAGE_REDUCE, st, 0);
-        SSB_HIP(launch_loss(h->n, s1, s2, n_trials, (double)h->n_bf, dl, mean_phase, st), "loss launch");
+        SSB_HIP(launch_loss(h->n, s1, s2, n_trials, (double)h->n_bf, lp, dl, mean_phase, st), "loss launch");
     }
     SSB_HIP(hipMemcpyAsync(losses, dl, sizeof(double) * n_trials, hipMemcpyDeviceToHost, st), "copy losses");
     SSB_HIP(hipStreamSynchronize(st), "loss");

@@ -55,8 +55,9 @@ int pass2_row_blocks(int n);
 hipError_t launch_accum(int n, const float* part_s1, const double* part_s2, int gcap, int ng,
                         int n_trials, double* s1run, double* s2run, hipStream_t st);
 hipError_t launch_fill(double* p, int64_t count, hipStream_t st);
+int loss_blocks();
 hipError_t launch_loss(int n, const double* s1run, const double* s2run, int n_trials, double n_bf,
-                       double* loss, float* mean_phase, hipStream_t st);
+                       double* lpart, double* loss, float* mean_phase, hipStream_t st);
 // Object: sum of corrected spectra over all BF, then one 2-D inverse transform.
 int obj_segments(int64_t nbf);
 hipError_t launch_obj_sum(int n, const float2* gm, const float2* gn, const double2* kb,

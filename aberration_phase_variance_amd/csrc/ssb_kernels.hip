@@ -514,21 +514,31 @@ __global__ __launch_bounds__(256) void k_accum_s1(const float* __restrict__ part
     s1run[t * n2 + p] = acc;
 }
 
-// S2run[t] += sum over groups g (in order) of (fixed-tree sum over row blocks).
-__global__ __launch_bounds__(64) void k_accum_s2(const double* __restrict__ part, int gcap, int ng, int rb,
-                                                 double* __restrict__ s2run) {
+// S2run[t] += sum over groups g (in order) of (sum over row blocks in order).  One
+// thread per group forms its group's sum; one thread then adds the group sums in
+// group order.  Independent of how groups are chunked.
+__global__ __launch_bounds__(256) void k_accum_s2(const double* __restrict__ part, int gcap, int ng, int rb,
+                                                  double* __restrict__ s2run) {
+    __shared__ double gs[256];
     const int t = blockIdx.x;
-    const int lane = threadIdx.x;
-    double run = s2run[t];
-    for (int g = 0; g < ng; ++g) {
-        const double* src = part + ((int64_t)t * gcap + g) * rb;
+    double run = 0.0;
+    if (threadIdx.x == 0) run = s2run[t];
+    for (int g0 = 0; g0 < ng; g0 += 256) {
+        const int g = g0 + threadIdx.x;
         double v = 0.0;
-        for (int i = lane; i < rb; i += 64) v += src[i];
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-        run += v;
+        if (g < ng) {
+            const double* src = part + ((int64_t)t * gcap + g) * rb;
+            for (int i = 0; i < rb; ++i) v += src[i];
+        }
+        gs[threadIdx.x] = v;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            const int m = min(256, ng - g0);
+            for (int i = 0; i < m; ++i) run += gs[i];
+        }
+        __syncthreads();
     }
-    if (lane == 0) s2run[t] = run;
+    if (threadIdx.x == 0) s2run[t] = run;
 }
 
 __global__ __launch_bounds__(256) void k_fill(double* p, int64_t count) {
@@ -536,26 +546,38 @@ __global__ __launch_bounds__(256) void k_fill(double* p, int64_t count) {
     if (i < count) p[i] = 0.0;
 }
 
-// loss[t] = S2/(n_bf N^2) - (1/N^2) sum_px (S1/n_bf)^2, fixed-order double reduction.
-__global__ __launch_bounds__(1024) void k_loss(const double* __restrict__ s1run, const double* __restrict__ s2run,
-                                               int64_t n2, double nbf, double* __restrict__ loss,
-                                               float* __restrict__ mean_phase) {
-    __shared__ double sh[1024];
-    const int t = blockIdx.x;
-    const int tid = threadIdx.x;
+// Per-block sums of (S1/n_bf)^2 over fixed pixel blocks (and the mean phase of
+// trial 0), then loss[t] = S2/(n_bf N^2) - (1/N^2) sum_blocks, in block order.
+constexpr int kLossBlocks = 256;
+
+__global__ __launch_bounds__(256) void k_loss_partial(const double* __restrict__ s1run, int64_t n2, double nbf,
+                                                      double* __restrict__ lpart, float* __restrict__ mean_phase) {
+    __shared__ double sh[256];
+    const int t = blockIdx.y;
+    const int64_t per = (n2 + kLossBlocks - 1) / kLossBlocks;
+    const int64_t p0 = blockIdx.x * per, p1 = min(n2, p0 + per);
     double acc = 0.0;
-    for (int64_t p = tid; p < n2; p += 1024) {
+    for (int64_t p = p0 + threadIdx.x; p < p1; p += 256) {
         const double mval = s1run[t * n2 + p] / nbf;
         acc += mval * mval;
         if (t == 0 && mean_phase) mean_phase[p] = (float)mval;
     }
-    sh[tid] = acc;
+    sh[threadIdx.x] = acc;
     __syncthreads();
-    for (int s = 512; s > 0; s >>= 1) {
-        if (tid < s) sh[tid] += sh[tid + s];
+    for (int s = 128; s > 0; s >>= 1) {
+        if (threadIdx.x < s) sh[threadIdx.x] += sh[threadIdx.x + s];
         __syncthreads();
     }
-    if (tid == 0) loss[t] = s2run[t] / (nbf * (double)n2) - sh[0] / (double)n2;
+    if (threadIdx.x == 0) lpart[(int64_t)t * kLossBlocks + blockIdx.x] = sh[0];
+}
+
+__global__ __launch_bounds__(64) void k_loss(const double* __restrict__ lpart, const double* __restrict__ s2run,
+                                             int64_t n2, double nbf, double* __restrict__ loss) {
+    const int t = blockIdx.x;
+    if (threadIdx.x != 0) return;
+    double sum = 0.0;
+    for (int i = 0; i < kLossBlocks; ++i) sum += lpart[(int64_t)t * kLossBlocks + i];
+    loss[t] = s2run[t] / (nbf * (double)n2) - sum / (double)n2;
 }
 
 // Row transform of the cached spectra: counts rows y0, y1 packed as one complex
@@ -828,7 +850,7 @@ hipError_t launch_accum(int n, const float* part_s1, const double* part_s2, int 
                        ng, n2, s1run);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_accum_s2, dim3(n_trials), dim3(64), 0, st, part_s2, gcap, ng, pass2_row_blocks(n), s2run);
+    hipLaunchKernelGGL(k_accum_s2, dim3(n_trials), dim3(256), 0, st, part_s2, gcap, ng, pass2_row_blocks(n), s2run);
     return hipGetLastError();
 }
 
@@ -838,10 +860,16 @@ hipError_t launch_fill(double* p, int64_t count, hipStream_t st) {
     return hipGetLastError();
 }
 
-hipError_t launch_loss(int n, const double* s1run, const double* s2run, int n_trials, double n_bf, double* loss,
-                       float* mean_phase, hipStream_t st) {
-    hipLaunchKernelGGL(k_loss, dim3(n_trials), dim3(1024), 0, st, s1run, s2run, (int64_t)n * n, n_bf, loss,
+int loss_blocks() { return kLossBlocks; }
+
+hipError_t launch_loss(int n, const double* s1run, const double* s2run, int n_trials, double n_bf, double* lpart,
+                       double* loss, float* mean_phase, hipStream_t st) {
+    const int64_t n2 = (int64_t)n * n;
+    hipLaunchKernelGGL(k_loss_partial, dim3(kLossBlocks, n_trials), dim3(256), 0, st, s1run, n2, n_bf, lpart,
                        mean_phase);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_loss, dim3(n_trials), dim3(64), 0, st, lpart, s2run, n2, n_bf, loss);
     return hipGetLastError();
 }
 

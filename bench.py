@@ -33,16 +33,47 @@ PEAK_FP32_TFLOPS = 157.3    # MI355X FP32 vector (256 CU x 2.4 GHz, packed)
 PEAK_HBM_GBS = 8000.0
 
 
-def algorithmic_flops(n: int, support_share: float) -> dict:
-    """Algorithmic FLOPs per active BF plane and trial, by stage."""
-    fft = 5.0 * n * math.log2(n)                     # one complex n-point transform
+def algorithmic_work(n: int, support_share: float) -> dict:
+    """Algorithmic HBM bytes and FLOPs per active BF plane and trial, by stage.
+
+    pass 1 reads the nonzero-transfer spectrum entries (complex64) and writes the
+    column-transformed plane; pass 2 reads that plane and writes one float phase
+    sum image per 32 BF.  FLOPs: 5 n log2 n per complex n-point transform, 45 per
+    nonzero-transfer correction, 23 per phase sample (atan2 and moments).
+    """
+    fft = 5.0 * n * math.log2(n)
     half = n * (n // 2 + 1)
     return {
-        # (N/2 + 1) column transforms + 45 flop per nonzero-transfer entry
-        "pass1": (n // 2 + 1) * fft + 45.0 * support_share * half,
-        # N rows as N/2 packed complex transforms + 23 flop per sample (atan2 + moments)
-        "pass2": (n // 2) * fft + 23.0 * n * n,
+        "pass1": {"bytes": 8.0 * support_share * half + 8.0 * half,
+                  "flops": (n // 2 + 1) * fft + 45.0 * support_share * half},
+        "pass2": {"bytes": 8.0 * half + 4.0 * n * n / 32.0,
+                  "flops": (n // 2) * fft + 23.0 * n * n},
     }
+
+
+def kernel_source_hash() -> str:
+    """Hash of the HIP sources the measured HBM traffic belongs to."""
+    import hashlib
+    csrc = os.path.join(ROOT, "aberration_phase_variance_amd", "csrc")
+    hsh = hashlib.sha256()
+    for name in ("ssb_kernels.hip", "ssb_fft.hpp", "ssb_internal.hpp"):
+        with open(os.path.join(csrc, name), "rb") as fh:
+            hsh.update(fh.read())
+    return hsh.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch from the committed counter summary, if it matches these sources."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    want = kernel_source_hash()
+    with open(path) as fh:
+        for line in fh:
+            parts = line.split()
+            if len(parts) >= 4 and not line.startswith("#") and parts[0] == kernel and parts[1] == want:
+                return float(parts[2]) + float(parts[3])
+    return None
 
 
 def support_share(geom) -> float:
@@ -75,7 +106,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="full", choices=["tiny", "small", "medium", "full"])
     ap.add_argument("--batch", type=int, default=200, help="trials in the batched measurement (0 = skip)")
-    ap.add_argument("--cpu-sample-bf", type=int, default=512, help="BF pixels in the oracle CPU sample (0 = skip)")
+    ap.add_argument("--cpu-sample-bf", type=int, default=1024, help="BF pixels in the oracle CPU sample (0 = skip)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB device-to-device copy (3x) as a known-size reference "
                          "for hardware byte counters")
@@ -169,18 +200,37 @@ def main():
         batch_ms_per_trial = (time.perf_counter() - t1) * 1e3 / args.batch
         log(f"[bench] batch of {args.batch}: {batch_ms_per_trial:.3f} ms/trial")
 
-    # roofline of the dominant stage: algorithmic FLOPs per launch / average launch time
+    # roofline of the dominant stage: algorithmic bytes (or FLOPs) per launch / average launch time
     share = support_share(g)
-    fl = algorithmic_flops(n, share)
+    work = algorithmic_work(n, share)
     stage_ms = {k: prof[k]["ms"] / max(1, prof[k]["launches"]) for k in prof}
     dom = max(("pass1", "pass2"), key=lambda k: prof[k]["ms"])
     units_per_launch = prof[dom]["units"] / max(1, prof[dom]["launches"])
-    achieved_tflops = fl[dom] * units_per_launch / (stage_ms[dom] * 1e-3) / 1e12
-    roofline = {"bound": "alu", "kernel": dom, "achieved": round(achieved_tflops, 3),
-                "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved_tflops / PEAK_FP32_TFLOPS, 4),
-                "traffic": None,
-                "flop_per_plane": fl[dom], "planes_per_launch": units_per_launch,
-                "avg_launch_ms": round(stage_ms[dom], 4)}
+    t_launch = stage_ms[dom] * 1e-3
+    bytes_launch = work[dom]["bytes"] * units_per_launch
+    flops_launch = work[dom]["flops"] * units_per_launch
+    hbm_bound = bytes_launch / (PEAK_HBM_GBS * 1e9) >= flops_launch / (PEAK_FP32_TFLOPS * 1e12)
+    achieved_gbs = bytes_launch / t_launch / 1e9
+    achieved_tf = flops_launch / t_launch / 1e12
+    traffic = measured_traffic(dom)
+    if hbm_bound:
+        roofline = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(achieved_gbs / PEAK_HBM_GBS, 4)}
+    else:
+        roofline = {"bound": "alu", "achieved": round(achieved_tf, 3), "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(achieved_tf / PEAK_FP32_TFLOPS, 4)}
+    roofline.update({"traffic": traffic, "kernel": dom, "avg_launch_ms": round(stage_ms[dom], 4),
+                     "planes_per_launch": units_per_launch, "algorithmic_bytes_per_launch": bytes_launch,
+                     "algorithmic_flops_per_launch": flops_launch,
+                     "flops_view": {"achieved_tflops": round(achieved_tf, 3), "peak": PEAK_FP32_TFLOPS,
+                                    "frac": round(achieved_tf / PEAK_FP32_TFLOPS, 4)},
+                     "kernel_source": kernel_source_hash()})
+    other = "pass2" if dom == "pass1" else "pass1"
+    t_other = stage_ms[other] * 1e-3
+    other_units = prof[other]["units"] / max(1, prof[other]["launches"])
+    stages_roofline = {other: {"avg_launch_ms": round(stage_ms[other], 4),
+                               "achieved_gbs": round(work[other]["bytes"] * other_units / t_other / 1e9, 1),
+                               "achieved_tflops": round(work[other]["flops"] * other_units / t_other / 1e12, 3)}}
     g_bytes = info["spectrum_bytes"]
     hbm = {"spectrum_read_gb": g_bytes / 1e9,
            "spectrum_read_frac_of_step": round(g_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
@@ -241,6 +291,7 @@ def main():
         "stage_ms_per_launch": {k: round(v, 4) for k, v in stage_ms.items()},
         "support_share": share,
         "roofline": roofline,
+        "other_stage": stages_roofline,
         "hbm": hbm,
         "cpu_baseline": cpu,
         "oracle_check": oracle_check,
