@@ -411,8 +411,9 @@ struct RowPairRaw {
 
 // Pass 2: one workgroup = 4*W row pairs x one 32-BF group x one trial.  Loops
 // over the group's BF pixels in order, accumulating per-pixel phase sums in
-// registers (float) and the squared phase (double per lane); the next BF's
-// column values are loaded while the current one is transformed.
+// registers (float) and the squared phase (double per lane).  With
+// SSB_PASS2_PREFETCH the next BF's column values are loaded while the current one
+// is transformed (off by default: the extra registers cost more than it hides).
 template <int N>
 __global__ __launch_bounds__(256, SSB_PASS2_MIN_WAVES) void k_pass2(const float2* __restrict__ im, const float2* __restrict__ in,
                                                int cap, const uint8_t* __restrict__ active, int64_t bf0,

@@ -52,13 +52,19 @@ def algorithmic_work(n: int, support_share: float) -> dict:
 
 
 def kernel_source_hash() -> str:
-    """Hash of the HIP sources the measured HBM traffic belongs to."""
+    """Hash of the HIP kernel sources the measured HBM traffic belongs to (code only:
+    comments and blank lines are dropped, so a comment edit keeps the counters valid)."""
     import hashlib
+    import re
     csrc = os.path.join(ROOT, "aberration_phase_variance_amd", "csrc")
     hsh = hashlib.sha256()
     for name in ("ssb_kernels.hip", "ssb_fft.hpp", "ssb_internal.hpp"):
-        with open(os.path.join(csrc, name), "rb") as fh:
-            hsh.update(fh.read())
+        with open(os.path.join(csrc, name)) as fh:
+            text = re.sub(r"/\*.*?\*/", "", fh.read(), flags=re.S)
+        for line in text.splitlines():
+            code = line.split("//", 1)[0].strip()
+            if code:
+                hsh.update(code.encode() + b"\n")
     return hsh.hexdigest()[:16]
 
 
