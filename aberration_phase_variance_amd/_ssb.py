@@ -49,6 +49,9 @@ class ssb_info(ctypes.Structure):
         ("spectrum_bytes", ctypes.c_int64),
         ("dc", ctypes.c_double),
         ("chunk_bf", ctypes.c_int64),
+        ("support_entries", ctypes.c_int64),
+        ("columns_written", ctypes.c_int64),
+        ("columns_read", ctypes.c_int64),
     ]
 
 

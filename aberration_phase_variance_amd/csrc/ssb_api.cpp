@@ -68,6 +68,9 @@ struct ssb_handle {
     double2* kb = nullptr;
     uint8_t* active = nullptr;
     unsigned long long* bfsum = nullptr;
+    uint4* sup = nullptr;      // correction support intervals [n_bf][N/2+1]
+    int* vend = nullptr;       // 1 + last supported column per BF [n_bf]
+    int64_t support_entries = 0, columns_written = 0, columns_read = 0;
     // loss / moments workspace
     char* ws = nullptr;
     size_t ws_bytes = 0;
@@ -267,13 +270,14 @@ int run_moments(ssb_handle* h, const float* params, int n_trials, int64_t b_begi
         const int64_t units = active_in(h, c0, c0 + cb) * n_trials;
         {
             StageTimer tm(h, SSB_STAGE_PASS1, st, units);
-            SSB_HIP(launch_pass1(h->n, h->gm, h->gn, chm, chn, h->kb, h->active, tc, n_trials, h->geo, c0, cb,
+            SSB_HIP(launch_pass1(h->n, h->gm, h->gn, chm, chn, h->kb, h->sup, h->vend, tc, n_trials, h->geo, c0, cb,
                                  pl.cap, im, in, st),
                     "pass 1 launch");
         }
         {
             StageTimer tm(h, SSB_STAGE_PASS2, st, units);
-            SSB_HIP(launch_pass2(h->n, im, in, pl.cap, h->active, c0, cb, n_trials, h->dc, ps1, ps2, pl.gcap, st),
+            SSB_HIP(launch_pass2(h->n, im, in, pl.cap, h->active, h->vend, c0, cb, n_trials, h->dc, ps1, ps2,
+                                 pl.gcap, st),
                     "pass 2 launch");
         }
         {
@@ -357,6 +361,7 @@ int ssb_prepare(const ssb_geometry* g, const uint32_t* counts, int64_t n_bf, voi
     geo.quy = g->q_step_px * geo.crot;
     geo.inv_w = 1.0 / w;
     geo.ra = ra;
+    geo.ra2 = ra * ra;
     geo.w = w;
     geo.lo2 = ra >= 0.5 * w ? (ra - 0.5 * w) * (ra - 0.5 * w) : -1.0;
     geo.hi2 = hi2;
@@ -382,6 +387,27 @@ int ssb_prepare(const ssb_geometry* g, const uint32_t* counts, int64_t n_bf, voi
         return cleanup(hip_fail(e, "spectrum row pass"));
     if ((e = launch_g_cols(n, h->gm, h->gn, n_bf, st)) != hipSuccess)
         return cleanup(hip_fail(e, "spectrum column pass"));
+    if ((e = hipMalloc(&h->sup, (size_t)n_bf * (n / 2 + 1) * sizeof(uint4))) != hipSuccess ||
+        (e = hipMalloc(&h->vend, (size_t)n_bf * sizeof(int))) != hipSuccess)
+        return cleanup(hip_fail(e, "allocation"));
+    int* nsup = nullptr;
+    if ((e = hipMalloc(&nsup, (size_t)n_bf * sizeof(int))) != hipSuccess) return cleanup(hip_fail(e, "allocation"));
+    std::vector<int> vend_h(n_bf), nsup_h(n_bf);
+    if ((e = launch_support(n, h->kb, h->active, h->geo, n_bf, h->sup, h->vend, nsup, st)) != hipSuccess ||
+        (e = hipMemcpyAsync(vend_h.data(), h->vend, n_bf * sizeof(int), hipMemcpyDeviceToHost, st)) != hipSuccess ||
+        (e = hipMemcpyAsync(nsup_h.data(), nsup, n_bf * sizeof(int), hipMemcpyDeviceToHost, st)) != hipSuccess ||
+        (e = hipStreamSynchronize(st)) != hipSuccess) {
+        (void)hipFree(nsup);
+        return cleanup(hip_fail(e, "support tables"));
+    }
+    (void)hipFree(nsup);
+    const int tile = pass1_tile(n), hh = n / 2;
+    for (int64_t b = 0; b < n_bf; ++b) {
+        const int ve = vend_h[b];
+        h->support_entries += nsup_h[b];
+        if (ve > 0) h->columns_written += std::min(hh, (ve + tile - 1) / tile * tile) + (ve > hh ? 1 : 0);
+        h->columns_read += std::min(hh, ve) + (ve > hh ? 1 : 0);
+    }
     std::vector<unsigned long long> sums(n_bf);
     if ((e = hipMemcpyAsync(sums.data(), h->bfsum, n_bf * sizeof(unsigned long long), hipMemcpyDeviceToHost, st)) !=
             hipSuccess ||
@@ -552,6 +578,9 @@ int ssb_query(const ssb_handle* h, ssb_info* info) {
     info->spectrum_bytes = (int64_t)h->n_bf * h->n * (h->h + 1) * (int64_t)sizeof(float2);
     info->dc = h->dc;
     info->chunk_bf = plan_loss(h, h->n_bf, 1).cap;
+    info->support_entries = h->support_entries;
+    info->columns_written = h->columns_written;
+    info->columns_read = h->columns_read;
     return SSB_OK;
 }
 
@@ -563,6 +592,8 @@ void ssb_release(ssb_handle* h) {
     (void)hipFree(h->kb);
     (void)hipFree(h->active);
     (void)hipFree(h->bfsum);
+    (void)hipFree(h->sup);
+    (void)hipFree(h->vend);
     (void)hipFree(h->ws);
     (void)hipFree(h->ows);
     for (auto& r : h->prof_pending) {

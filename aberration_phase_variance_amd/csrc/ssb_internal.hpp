@@ -28,6 +28,7 @@ struct GeomDev {
     double qvx, qux, qvy, quy;
     double inv_w;     // 1 / w
     double ra;        // aperture radius (pixels)
+    double ra2;       // ra^2
     double w;         // edge width (pixels)
     double lo2;       // (ra - w/2)^2, or -1 when ra < w/2 (no flat top)
     double hi2;       // (ra + w/2)^2
@@ -45,12 +46,20 @@ hipError_t launch_g_cols(int n, float2* gm, float2* gn, int64_t nbf, hipStream_t
 hipError_t launch_chiq(int n, const TrialConst* tc, int n_trials, GeomDev geo, float2* chm, float2* chn,
                        hipStream_t st);
 hipError_t launch_pass1(int n, const float2* gm, const float2* gn, const float2* chm, const float2* chn,
-                        const double2* kb, const uint8_t* active, const TrialConst* tc, int n_trials,
+                        const double2* kb, const uint4* sup, const int* vend, const TrialConst* tc, int n_trials,
                         GeomDev geo, int64_t bf0, int cb, int cap, float2* im, float2* in, hipStream_t st);
 // Pass 2: row transforms, atan2 and moments, one partial per 32-BF group.
 hipError_t launch_pass2(int n, const float2* im, const float2* in, int cap, const uint8_t* active,
-                        int64_t bf0, int cb, int n_trials, double dc, float* part_s1,
+                        const int* vend, int64_t bf0, int cb, int n_trials, double dc, float* part_s1,
                         double* part_s2, int gcap, hipStream_t st);
+// Correction support per (BF, column) from the geometry: sup [n_bf][N/2+1] of four
+// packed (lo, len) row intervals (minus/plus aperture, nonzero weight / flat top),
+// vend [n_bf] = 1 + the last column with any support (0 for an inactive BF), and
+// nsup [n_bf] = nonzero-transfer entries per BF.
+hipError_t launch_support(int n, const double2* kb, const uint8_t* active, GeomDev geo, int64_t nbf, uint4* sup,
+                          int* vend, int* nsup, hipStream_t st);
+// Columns per pass-1 tile (pass 1 writes whole tiles below vend).
+int pass1_tile(int n);
 int pass2_row_blocks(int n);
 hipError_t launch_accum(int n, const float* part_s1, const double* part_s2, int gcap, int ng,
                         int n_trials, double* s1run, double* s2run, hipStream_t st);

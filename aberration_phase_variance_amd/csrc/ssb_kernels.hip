@@ -29,9 +29,6 @@ namespace {
 #ifndef SSB_PASS1_TC
 #define SSB_PASS1_TC 16       // pass-1 columns per workgroup at N = 512
 #endif
-#ifndef SSB_PASS1_PRED_LOADS
-#define SSB_PASS1_PRED_LOADS 1 // pass 1 fetches only nonzero-transfer spectrum entries
-#endif
 #ifndef SSB_PASS2_MIN_WAVES
 #define SSB_PASS2_MIN_WAVES 1 // pass-2 register budget hint: minimum resident waves per SIMD
 #endif
@@ -77,6 +74,87 @@ __device__ __forceinline__ float2 phasor_rev_neg(double x) {
     return make_float2(cs.x, -cs.y);
 }
 
+// Squared distance |k + sg q(u', v)|^2 (pixels^2) of one shifted aperture center,
+// sg = -1 for A(k - q) and +1 for A(k + q), in double.  Every support and flat-top
+// decision of the correction is taken on this value.
+__device__ __forceinline__ double shifted_r2(double kx, double ky, double sg, int up, int v, const GeomDev& g) {
+    const double qx = fma(g.qux, (double)up, g.qvx * v);
+    const double qy = fma(g.quy, (double)up, g.qvy * v);
+    const double dx = kx + sg * qx, dy = ky + sg * qy;
+    return fma(dx, dx, dy * dy);
+}
+
+// Soft aperture weight on the edge ring (lo2 < r2 < hi2): clip((R_a - r)/w + 1/2)
+// with R_a - r = (R_a^2 - r^2)/(R_a + r), the difference taken in double.
+__device__ __forceinline__ float edge_weight(double r2, const GeomDev& g) {
+    const float num = (float)(g.ra2 - r2);
+    const float den = (float)g.ra + __builtin_amdgcn_sqrtf((float)r2);
+    const float a = fmaf(num * __builtin_amdgcn_rcpf(den), (float)g.inv_w, 0.5f);
+    return fminf(fmaxf(a, 0.f), 1.f);
+}
+
+// Signed rows u' in [-H, H) of column v where r2(u') = |k + sg q(u', v)|^2 is below
+// R2 (strict) or at most R2, as [lo, lo + len).  The set is a disk cut by a line, so
+// it is one interval; its ends come from the roots of the quadratic in u' and are
+// then settled with the exact test on shifted_r2 itself.
+template <bool STRICT>
+__device__ void row_interval(double kx, double ky, double sg, int v, int H, double R2, const GeomDev& g, int& lo,
+                             int& len) {
+    auto inside = [&](int up) {
+        const double r = shifted_r2(kx, ky, sg, up, v, g);
+        return STRICT ? r < R2 : r <= R2;
+    };
+    // r2(u') = |P + u' D|^2 with P = k + sg v qv, D = sg qu
+    const double px = kx + sg * (g.qvx * v), py = ky + sg * (g.qvy * v);
+    const double dx = sg * g.qux, dy = sg * g.quy;
+    const double dd = dx * dx + dy * dy, pd = px * dx + py * dy, pp = px * px + py * py;
+    const double disc = pd * pd - dd * (pp - R2);
+    const double c = -pd / dd;
+    double ra_ = c, rb_ = c;
+    if (disc > 0.0) {
+        const double hw = sqrt(disc) / dd;
+        ra_ = c - hw;
+        rb_ = c + hw;
+    }
+    int a = (int)fmax(fmin(ceil(ra_), (double)H), (double)(-H - 1));
+    int b = (int)fmax(fmin(floor(rb_), (double)H), (double)(-H - 1));
+    a = max(a, -H);
+    b = min(b, H - 1);
+    if (a > b) {
+        // no integer strictly between the roots: only a rounding tie can hold one
+        const int cand = (int)fmax(fmin(rint(c), (double)(H - 1)), (double)(-H));
+        if (!inside(cand)) {
+            lo = 0;
+            len = 0;
+            return;
+        }
+        a = b = cand;
+    }
+    for (int it = 0; it < 4 && a > -H && inside(a - 1); ++it) --a;
+    for (int it = 0; it < 4 && a <= b && !inside(a); ++it) ++a;
+    for (int it = 0; it < 4 && b < H - 1 && inside(b + 1); ++it) ++b;
+    for (int it = 0; it < 4 && b >= a && !inside(b); --b, ++it) {}
+    lo = a;
+    len = b >= a ? b - a + 1 : 0;
+}
+
+__device__ __forceinline__ unsigned pack_lo_len(int lo, int len) {
+    return ((unsigned)lo & 0xffffu) | ((unsigned)len << 16);
+}
+__device__ __forceinline__ int unpack_lo(unsigned p) { return (int)(short)(p & 0xffffu); }
+__device__ __forceinline__ int unpack_len(unsigned p) { return (int)(p >> 16); }
+
+// 64-bit load through a buffer resource: an offset at or past the resource's size
+// returns zero without touching memory (predicated loads with no branch).
+typedef int ssb_v2i __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+__device__ __forceinline__ float2 load_or_zero(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+constexpr int kNoLoad = (int)0x80000000;
+
 // Corrected value C = G * T of one half-plane entry with scan frequency q = (qx, qy)
 // pixels, for the BF pixel at k = (kx, ky) pixels.
 //
@@ -121,10 +199,7 @@ __device__ __forceinline__ float2 chi_phasor(double qx, double qy, const TrialCo
 // squares on [0, 1] against atan; max relative error 1.4e-8 in exact arithmetic,
 // 3.3e-7 rad absolute in float including the approximate reciprocal), then the
 // octant is undone.  atan2(0, 0) = 0; NaN inputs give NaN.
-__device__ __forceinline__ float atan2_f(float y, float x) {
-    const float ax = fabsf(x), ay = fabsf(y);
-    const float mx = fmaxf(ax, ay), mn = fminf(ax, ay);
-    const float t = mx > 0.f ? mn * __builtin_amdgcn_rcpf(mx) : 0.f;
+__device__ __forceinline__ float atan_unit(float t) {
     const float s = t * t;
     float p = 2.903556684e-03f;
     p = fmaf(p, s, -1.628302597e-02f);
@@ -135,7 +210,14 @@ __device__ __forceinline__ float atan2_f(float y, float x) {
     p = fmaf(p, s, 1.999305487e-01f);
     p = fmaf(p, s, -3.333309293e-01f);
     p = fmaf(p, s, 1.0f);
-    float a = t * p;
+    return t * p;
+}
+
+__device__ __forceinline__ float atan2_f(float y, float x) {
+    const float ax = fabsf(x), ay = fabsf(y);
+    const float mx = fmaxf(ax, ay), mn = fminf(ax, ay);
+    const float t = mx > 0.f ? mn * __builtin_amdgcn_rcpf(mx) : 0.f;
+    float a = atan_unit(t);
     a = ay > ax ? 1.57079632679489662f - a : a;
     a = x < 0.f ? 3.14159265358979324f - a : a;
     a = copysignf(a, y);
@@ -215,6 +297,64 @@ __global__ __launch_bounds__(256) void k_chiq(const TrialConst* __restrict__ tc,
     else chn[(int64_t)t * N + u] = val;
 }
 
+// Correction support of every (BF, column) pair, from the geometry alone: for each
+// shifted aperture the rows with nonzero weight (r2 < hi2) and the rows with weight
+// exactly 1 (r2 <= lo2), packed as four (lo, len) pairs:
+//   x = minus nonzero, y = plus nonzero, z = minus flat, w = plus flat.
+template <int N>
+__global__ __launch_bounds__(256) void k_support(const double2* __restrict__ kb, GeomDev geo, int64_t nbf,
+                                                 uint4* __restrict__ sup) {
+    constexpr int H = N / 2;
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= nbf * (H + 1)) return;
+    const int64_t b = e / (H + 1);
+    const int v = (int)(e % (H + 1));
+    const double2 k = kb[b];
+    int lo, len;
+    uint4 o;
+    row_interval<true>(k.x, k.y, -1.0, v, H, geo.hi2, geo, lo, len);
+    o.x = pack_lo_len(lo, len);
+    row_interval<true>(k.x, k.y, 1.0, v, H, geo.hi2, geo, lo, len);
+    o.y = pack_lo_len(lo, len);
+    if (geo.lo2 >= 0.0) {
+        row_interval<false>(k.x, k.y, -1.0, v, H, geo.lo2, geo, lo, len);
+        o.z = pack_lo_len(lo, len);
+        row_interval<false>(k.x, k.y, 1.0, v, H, geo.lo2, geo, lo, len);
+        o.w = pack_lo_len(lo, len);
+    } else {
+        o.z = 0;
+        o.w = 0;
+    }
+    sup[e] = o;
+}
+
+// vend[b] = 1 + the last column with any support (columns from vend on are all
+// zero after the correction); at least 1 for an active BF pixel, 0 for an inactive
+// one.  nsup[b] = number of half-plane entries with nonzero transfer (q = 0 aside).
+template <int N>
+__global__ __launch_bounds__(256) void k_vend(const uint4* __restrict__ sup, const uint8_t* __restrict__ active,
+                                              int64_t nbf, int* __restrict__ vend, int* __restrict__ nsup) {
+    constexpr int H = N / 2;
+    const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (b >= nbf) return;
+    int ve = 0, ns = 0;
+    if (active[b]) {
+        ve = 1;
+        for (int v = 0; v <= H; ++v) {
+            const uint4 o = sup[b * (H + 1) + v];
+            const int lm = unpack_lo(o.x), nm = unpack_len(o.x), lp = unpack_lo(o.y), np = unpack_len(o.y);
+            const int ov = max(0, min(lm + nm, lp + np) - max(lm, lp));
+            const int cnt = nm + np - ov;
+            if (cnt > 0) ve = v + 1;
+            ns += cnt;
+            // the q = 0 entry carries the DC, not a corrected value
+            if (v == 0 && ((unsigned)(0 - lm) < (unsigned)nm || (unsigned)(0 - lp) < (unsigned)np)) ns -= 1;
+        }
+    }
+    vend[b] = ve;
+    nsup[b] = ns;
+}
+
 // Per-BF phase slopes of delta = v alpha + u' beta (revolutions).
 __device__ __forceinline__ void delta_slopes(double kx, double ky, const TrialConst& m, const GeomDev& g,
                                              double& alpha, double& beta) {
@@ -226,12 +366,16 @@ __device__ __forceinline__ void delta_slopes(double kx, double ky, const TrialCo
 
 // Pass 1: correction + column inverse transforms.  One workgroup = one BF pixel x
 // one tile of TC columns (or the Nyquist column) x one trial; each wave owns one
-// column's FFT.
-//   1. support test on exact double squared radii; the spectrum entries with
-//      nonzero transfer and their exp(i chi_q) from the per-trial table are
-//      loaded into registers (independent coalesced loads, all in flight
-//      together; zero-transfer entries are never fetched);
-//   2. each entry is corrected into the LDS tile;
+// column's FFT.  Tiles at or past the BF pixel's last supported column (vend) are
+// all zero after the correction: they are neither computed nor written, and pass 2
+// does not read them.
+//   1. support from the per-column intervals (integer compares); the spectrum
+//      entries with nonzero transfer and their exp(i chi_q) (per-trial table) are
+//      loaded into registers through buffer resources, zero-transfer entries get
+//      an out-of-range offset and read as exact zeros without a memory access;
+//   2. each entry is corrected into the LDS tile: on the flat tops of the
+//      apertures the bracket is already a unit phasor, on an edge ring it is
+//      normalized;
 //   3. one wave-level inverse FFT per column;  4. coalesced store.
 // exp(-i delta) is separable: E_u(u') = exp(-2 pi i u' beta) for all rows is
 // built in LDS per workgroup, E_v(v) = exp(-2 pi i v alpha) per thread (each
@@ -244,7 +388,8 @@ __global__ __launch_bounds__(kPass1Threads) void k_pass1(const float2* __restric
                                                          const float2* __restrict__ chm,
                                                          const float2* __restrict__ chn,
                                                          const double2* __restrict__ kb,
-                                                         const uint8_t* __restrict__ active,
+                                                         const uint4* __restrict__ sup,
+                                                         const int* __restrict__ vend,
                                                          const TrialConst* __restrict__ tc, GeomDev geo,
                                                          int64_t bf0, int cap, float2* __restrict__ im,
                                                          float2* __restrict__ in) {
@@ -255,7 +400,7 @@ __global__ __launch_bounds__(kPass1Threads) void k_pass1(const float2* __restric
     constexpr int PER = (N + RS - 1) / RS;        // entries per thread on a main tile (rows u < N)
     constexpr int PERN = (N + NT - 1) / NT;       // entries per thread on the Nyquist tile
     constexpr int PM = PER > PERN ? PER : PERN;
-    static_assert(PM <= 32, "support mask is one 32-bit word");
+    static_assert(PM <= 16, "two support bits per entry in one 32-bit word");
     using F = WaveFFT<N, +1>;
     __shared__ float2 tile[TC * LD];
     __shared__ float2 eu[N];
@@ -264,10 +409,11 @@ __global__ __launch_bounds__(kPass1Threads) void k_pass1(const float2* __restric
     const int bl = blockIdx.y;
     const int t = blockIdx.z;
     const int64_t b = bf0 + bl;
-    if (!active[b]) return;                       // zero-aperture BF: phase is exactly 0
     const bool nyq = blockIdx.x == H / TC;
+    const int v0 = nyq ? H : blockIdx.x * TC;
+    if (v0 >= vend[b]) return;                    // all-zero columns (every column of an inactive BF)
     const int c = nyq ? 0 : tid % TC;
-    const int v = nyq ? H : blockIdx.x * TC + c;
+    const int v = v0 + c;
     const int ustart = nyq ? tid : tid / TC;
     const int ustep = nyq ? NT : RS;
     const int nent = nyq ? PERN : PER;
@@ -277,50 +423,71 @@ __global__ __launch_bounds__(kPass1Threads) void k_pass1(const float2* __restric
     delta_slopes(k.x, k.y, m, geo, alpha, beta);
     for (int u = tid; u < N; u += NT) eu[u] = phasor_rev_neg((double)(u < H ? u : u - N) * beta);
     const float2 ev = phasor_rev_neg((double)v * alpha);
-    const double qvx = geo.qvx * v, qvy = geo.qvy * v;
+    const uint4 sr = sup[b * (H + 1) + v];
+    const int lo_m = unpack_lo(sr.x), len_m = unpack_len(sr.x);
+    const int lo_p = unpack_lo(sr.y), len_p = unpack_len(sr.y);
 
-    // 1. support test and loads into registers (all loads in flight together)
-    const float2* src = nyq ? gn + b * N : gm + b * N * H + v;
-    const float2* chs = nyq ? chn + (int64_t)t * N : chm + (int64_t)t * N * H + v;
+    // 1. support and loads into registers (all loads in flight together)
+    const __amdgpu_buffer_rsrc_t rg = nyq ? make_rsrc(gn + b * N, N * 8) : make_rsrc(gm + b * N * H, N * H * 8);
+    const __amdgpu_buffer_rsrc_t rc =
+        nyq ? make_rsrc(chn + (int64_t)t * N, N * 8) : make_rsrc(chm + (int64_t)t * N * H, N * H * 8);
     const int sstride = nyq ? 1 : H;
+    const int vcol = nyq ? 0 : v;
     float2 gv[PM], chv[PM];
-    float amv[PM], apv[PM];
-    unsigned sup = 0;
+    unsigned bits = 0;
 #pragma unroll
     for (int i = 0; i < PM; ++i) {
         const int u = ustart + i * ustep;
-        gv[i] = make_float2(0.f, 0.f);
-        chv[i] = make_float2(0.f, 0.f);
-        amv[i] = 0.f;
-        apv[i] = 0.f;
-        if (i < nent && u < N) {
-#if !SSB_PASS1_PRED_LOADS
-            gv[i] = src[u * sstride];
-            chv[i] = chs[u * sstride];
-#endif
-            const double up = (double)(u < H ? u : u - N);
-            double am, apl;
-            if ((u != 0 || v != 0) &&
-                in_support(fma(geo.qux, up, qvx), fma(geo.quy, up, qvy), k.x, k.y, geo, am, apl)) {
-                sup |= 1u << i;
-#if SSB_PASS1_PRED_LOADS
-                gv[i] = src[u * sstride];
-                chv[i] = chs[u * sstride];
-#endif
-                amv[i] = (float)am;
-                apv[i] = (float)apl;
-            }
-        }
+        const int up = u < H ? u : u - N;
+        const bool inm = (unsigned)(up - lo_m) < (unsigned)len_m;
+        const bool inp = (unsigned)(up - lo_p) < (unsigned)len_p;
+        const bool on = i < nent && u < N && (inm || inp) && (u != 0 || v != 0);
+        const int off = on ? (u * sstride + vcol) * 8 : kNoLoad;
+        gv[i] = load_or_zero(rg, off);
+        chv[i] = load_or_zero(rc, off);
+        bits |= on ? ((inm ? 1u : 0u) | (inp ? 2u : 0u)) << (2 * i) : 0u;
     }
     __syncthreads();                              // E_u complete
 
     // 2. correction into the LDS tile
+    const int flo_m = unpack_lo(sr.z), flen_m = unpack_len(sr.z);
+    const int flo_p = unpack_lo(sr.w), flen_p = unpack_len(sr.w);
 #pragma unroll
     for (int i = 0; i < PM; ++i) {
         const int u = ustart + i * ustep;
         if (i < nent && u < N) {
             float2 val = make_float2(0.f, 0.f);
-            if (sup & (1u << i)) val = apply_transfer(gv[i], chv[i], cmul(eu[u], ev), amv[i], apv[i]);
+            const unsigned f = (bits >> (2 * i)) & 3u;
+            if (f) {
+                const int up = u < H ? u : u - N;
+                const bool inm = f & 1u, inp = f & 2u;
+                const bool edm = inm && (unsigned)(up - flo_m) >= (unsigned)flen_m;
+                const bool edp = inp && (unsigned)(up - flo_p) >= (unsigned)flen_p;
+                const float2 ch = chv[i];
+                float br, bi;
+                if (edm || edp) {
+                    // on an edge ring: bracket ((a_- - a_+) cos, (a_- + a_+) sin), normalized
+                    float am = inm ? 1.f : 0.f, apl = inp ? 1.f : 0.f;
+                    if (edm) am = edge_weight(shifted_r2(k.x, k.y, -1.0, up, v, geo), geo);
+                    if (edp) apl = edge_weight(shifted_r2(k.x, k.y, 1.0, up, v, geo), geo);
+                    br = (am - apl) * ch.x;
+                    bi = (am + apl) * ch.y;
+                    const float mag2 = fmaf(br, br, bi * bi);
+                    const float inv = mag2 > 0.f ? __builtin_amdgcn_rsqf(mag2) : 0.f;
+                    br *= inv;
+                    bi *= inv;
+                } else if (inm && inp) {
+                    // both flat tops: (0, 2 sin) -> (0, sign(sin chi_q)); zero when sin is zero
+                    br = 0.f;
+                    bi = ch.y > 0.f ? 1.f : (ch.y < 0.f ? -1.f : 0.f);
+                } else {
+                    // one flat sideband: (+-cos, sin) is already a unit phasor
+                    br = inm ? ch.x : -ch.x;
+                    bi = ch.y;
+                }
+                const float2 e = cmul(eu[u], ev);
+                val = cmul(gv[i], make_float2(e.x * br - e.y * bi, e.x * bi + e.y * br));
+            }
             tile[c * LD + u] = val;
         }
     }
@@ -364,25 +531,41 @@ struct RowPairRaw {
     float2 d0[R / 2], d1[R / 2], m0[R / 2], m1[R / 2];
     float2 h0, h1, z0, z1;
 
-    __device__ __forceinline__ void load(const float2* r0, const float2* nyq, int j) {
+    // plane: one BF pixel's column results [N][N/2]; nyqc: its Nyquist column [N].
+    // Columns at or past ve are zero (not written by pass 1) and read as zero
+    // through an out-of-range buffer offset.
+    __device__ __forceinline__ void load(const float2* plane, const float2* nyqc, int y0, int j, int ve) {
         constexpr int H = N / 2;
-        const float2* r1 = r0 + H;
+        const __amdgpu_buffer_rsrc_t rp = make_rsrc(plane, N * H * 8);
+        const int row = y0 * H * 8;
 #pragma unroll
         for (int r = 0; r < R / 2; ++r) {
-            d0[r] = r0[j + r * L];
-            d1[r] = r1[j + r * L];
+            const int col = j + r * L;
+            const int off = col < ve ? row + col * 8 : kNoLoad;
+            d0[r] = load_or_zero(rp, off);
+            d1[r] = load_or_zero(rp, off + H * 8);
         }
 #pragma unroll
         for (int r = 0; r < R / 2; ++r) {
             const int w = H - j - r * L;            // N - (j + (r + R/2) L); w = H only for j = r = 0
             const int ws = w == H ? 0 : w;           // that slot is taken from the Nyquist column below
-            m0[r] = r0[ws];
-            m1[r] = r1[ws];
+            const int off = ws < ve ? row + ws * 8 : kNoLoad;
+            m0[r] = load_or_zero(rp, off);
+            m1[r] = load_or_zero(rp, off + H * 8);
         }
-        h0 = nyq[0];
-        h1 = nyq[1];
-        z0 = r0[0];
-        z1 = r1[0];
+        const float2 zero = make_float2(0.f, 0.f);
+        h0 = zero;
+        h1 = zero;
+        if (ve > H) {
+            h0 = nyqc[y0];
+            h1 = nyqc[y0 + 1];
+        }
+        z0 = zero;
+        z1 = zero;
+        if (ve > 0) {
+            z0 = plane[y0 * H];
+            z1 = plane[(y0 + 1) * H];
+        }
     }
 
     // Z(v) = B0(v) + i B1(v), B_k = -i * (column result of row y_k), extended
@@ -416,7 +599,8 @@ struct RowPairRaw {
 // is transformed (off by default: the extra registers cost more than it hides).
 template <int N>
 __global__ __launch_bounds__(256, SSB_PASS2_MIN_WAVES) void k_pass2(const float2* __restrict__ im, const float2* __restrict__ in,
-                                               int cap, const uint8_t* __restrict__ active, int64_t bf0,
+                                               int cap, const uint8_t* __restrict__ active,
+                                               const int* __restrict__ vend, int64_t bf0,
                                                int cb, float dcf, float* __restrict__ part_s1,
                                                double* __restrict__ part_s2, int gcap) {
     using F = WaveFFT<N, +1>;
@@ -451,8 +635,8 @@ __global__ __launch_bounds__(256, SSB_PASS2_MIN_WAVES) void k_pass2(const float2
         while (b < b_hi && !active[bf0 + b]) ++b;
         return b;
     };
-    auto row_ptr = [&](int b) { return im + (((int64_t)t * cap + b) * N + y0) * H; };
-    auto nyq_ptr = [&](int b) { return in + ((int64_t)t * cap + b) * N + y0; };
+    auto plane_ptr = [&](int b) { return im + ((int64_t)t * cap + b) * N * H; };
+    auto nyq_ptr = [&](int b) { return in + ((int64_t)t * cap + b) * N; };
 
     RowPairRaw<N, R, L> cur;
 #if SSB_PASS2_PREFETCH
@@ -460,14 +644,14 @@ __global__ __launch_bounds__(256, SSB_PASS2_MIN_WAVES) void k_pass2(const float2
 #endif
     int b = next_active(b_lo);
 #if SSB_PASS2_PREFETCH
-    if (b < b_hi) cur.load(row_ptr(b), nyq_ptr(b), j);
+    if (b < b_hi) cur.load(plane_ptr(b), nyq_ptr(b), y0, j, vend[bf0 + b]);
 #endif
     while (b < b_hi) {
         const int bn = next_active(b + 1);
 #if SSB_PASS2_PREFETCH
-        if (bn < b_hi) nxt.load(row_ptr(bn), nyq_ptr(bn), j);
+        if (bn < b_hi) nxt.load(plane_ptr(bn), nyq_ptr(bn), y0, j, vend[bf0 + bn]);
 #else
-        cur.load(row_ptr(b), nyq_ptr(b), j);
+        cur.load(plane_ptr(b), nyq_ptr(b), y0, j, vend[bf0 + b]);
 #endif
         float2 x[R];
         cur.assemble(j, x);
@@ -475,13 +659,32 @@ __global__ __launch_bounds__(256, SSB_PASS2_MIN_WAVES) void k_pass2(const float2
         const float den0 = dcf + cur.z0.x + sgn * cur.h0.x;
         const float den1 = dcf + cur.z1.x + sgn * cur.h1.x;
         float p2 = 0.f;
+        // Re O > 0 and |Im O| <= Re O for every sample of the wave: atan2 is the
+        // odd polynomial of Im O / Re O, with one reciprocal per row (the real part
+        // depends on the pixel only through its parity).  Bitwise the same result
+        // as the general atan2 on those inputs.
+        bool easy = den0 > 0.f && den1 > 0.f;
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const float pa = atan2_f(x[r].x, den0);
-            const float pb = atan2_f(x[r].y, den1);
-            s1a[r] += pa;
-            s1b[r] += pb;
-            p2 += pa * pa + pb * pb;
+        for (int r = 0; r < R; ++r) easy = easy && fabsf(x[r].x) <= den0 && fabsf(x[r].y) <= den1;
+        if (__all(easy)) {
+            const float i0 = __builtin_amdgcn_rcpf(den0), i1 = __builtin_amdgcn_rcpf(den1);
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const float pa = atan_unit(x[r].x * i0);
+                const float pb = atan_unit(x[r].y * i1);
+                s1a[r] += pa;
+                s1b[r] += pb;
+                p2 += pa * pa + pb * pb;
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const float pa = atan2_f(x[r].x, den0);
+                const float pb = atan2_f(x[r].y, den1);
+                s1a[r] += pa;
+                s1b[r] += pb;
+                p2 += pa * pa + pb * pb;
+            }
         }
         s2 += (double)p2;
 #if SSB_PASS2_PREFETCH
@@ -708,7 +911,7 @@ __global__ __launch_bounds__(256) void k_obj_rows(const float2* __restrict__ pm,
     const int j = lane % L;
     const int y0 = 2 * (blockIdx.x * (4 * F::W) + grp);
     RowPairRaw<N, R, L> raw;
-    raw.load(pm + y0 * H, pn + y0, j);
+    raw.load(pm, pn, y0, j, H + 1);   // every column present
     float2 x[R];
     raw.assemble(j, x);
     F fft;
@@ -765,14 +968,14 @@ template <int N> constexpr int pass1_tc() { return N >= 512 ? SSB_PASS1_TC : 8; 
 
 template <int N>
 hipError_t pass1_n(const float2* gm, const float2* gn, const float2* chm, const float2* chn, const double2* kb,
-                   const uint8_t* active, const TrialConst* tc, int n_trials, GeomDev geo, int64_t bf0, int cb,
-                   int cap, float2* im, float2* in, hipStream_t st) {
+                   const uint4* sup, const int* vend, const TrialConst* tc, int n_trials, GeomDev geo, int64_t bf0,
+                   int cb, int cap, float2* im, float2* in, hipStream_t st) {
     constexpr int H = N / 2;
     constexpr int TC = pass1_tc<N>();
     for (int64_t p0 = 0; p0 < cb; p0 += 65535) {
         const int np = (int)std::min<int64_t>(65535, cb - p0);
         hipLaunchKernelGGL((k_pass1<N, TC>), dim3(H / TC + 1, np, n_trials), dim3(kPass1Threads), 0, st, gm, gn, chm,
-                           chn, kb, active, tc, geo, bf0 + p0, cap, im + p0 * N * H, in + p0 * N);
+                           chn, kb, sup, vend, tc, geo, bf0 + p0, cap, im + p0 * N * H, in + p0 * N);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -783,6 +986,18 @@ template <int N>
 hipError_t chiq_n(const TrialConst* tc, int n_trials, GeomDev geo, float2* chm, float2* chn, hipStream_t st) {
     constexpr int NE = N * (N / 2 + 1);
     hipLaunchKernelGGL(k_chiq<N>, dim3((NE + 255) / 256, n_trials), dim3(256), 0, st, tc, geo, chm, chn);
+    return hipGetLastError();
+}
+
+template <int N>
+hipError_t support_n(const double2* kb, const uint8_t* active, GeomDev geo, int64_t nbf, uint4* sup, int* vend,
+                     int* nsup, hipStream_t st) {
+    const int64_t ne = nbf * (N / 2 + 1);
+    hipLaunchKernelGGL(k_support<N>, dim3((unsigned)((ne + 255) / 256)), dim3(256), 0, st, kb, geo, nbf, sup);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_vend<N>, dim3((unsigned)((nbf + 255) / 256)), dim3(256), 0, st, sup, active, nbf, vend,
+                       nsup);
     return hipGetLastError();
 }
 
@@ -813,9 +1028,9 @@ hipError_t launch_chiq(int n, const TrialConst* tc, int n_trials, GeomDev geo, f
 }
 
 hipError_t launch_pass1(int n, const float2* gm, const float2* gn, const float2* chm, const float2* chn,
-                        const double2* kb, const uint8_t* active, const TrialConst* tc, int n_trials, GeomDev geo,
-                        int64_t bf0, int cb, int cap, float2* im, float2* in, hipStream_t st) {
-    SSB_DISPATCH_N(n, (pass1_n<NN>(gm, gn, chm, chn, kb, active, tc, n_trials, geo, bf0, cb, cap, im, in, st)))
+                        const double2* kb, const uint4* sup, const int* vend, const TrialConst* tc, int n_trials,
+                        GeomDev geo, int64_t bf0, int cb, int cap, float2* im, float2* in, hipStream_t st) {
+    SSB_DISPATCH_N(n, (pass1_n<NN>(gm, gn, chm, chn, kb, sup, vend, tc, n_trials, geo, bf0, cb, cap, im, in, st)))
 }
 
 int pass2_row_blocks(int n) {
@@ -829,20 +1044,27 @@ int pass2_row_blocks(int n) {
 }
 
 template <int N>
-static hipError_t pass2_n(const float2* im, const float2* in, int cap, const uint8_t* active, int64_t bf0,
-                          int cb, int n_trials, double dc, float* part_s1, double* part_s2, int gcap,
+static hipError_t pass2_n(const float2* im, const float2* in, int cap, const uint8_t* active, const int* vend,
+                          int64_t bf0, int cb, int n_trials, double dc, float* part_s1, double* part_s2, int gcap,
                           hipStream_t st) {
     const int ng = (cb + kGroupBF - 1) / kGroupBF;
     hipLaunchKernelGGL(k_pass2<N>, dim3(row_blocks<N>(), ng, n_trials), dim3(256), 0, st, im, in, cap, active,
-                       bf0, cb, (float)dc, part_s1, part_s2, gcap);
+                       vend, bf0, cb, (float)dc, part_s1, part_s2, gcap);
     return hipGetLastError();
 }
 
-hipError_t launch_pass2(int n, const float2* im, const float2* in, int cap, const uint8_t* active, int64_t bf0,
-                        int cb, int n_trials, double dc, float* part_s1, double* part_s2, int gcap,
-                        hipStream_t st) {
-    SSB_DISPATCH_N(n, (pass2_n<NN>(im, in, cap, active, bf0, cb, n_trials, dc, part_s1, part_s2, gcap, st)))
+hipError_t launch_pass2(int n, const float2* im, const float2* in, int cap, const uint8_t* active,
+                        const int* vend, int64_t bf0, int cb, int n_trials, double dc, float* part_s1,
+                        double* part_s2, int gcap, hipStream_t st) {
+    SSB_DISPATCH_N(n, (pass2_n<NN>(im, in, cap, active, vend, bf0, cb, n_trials, dc, part_s1, part_s2, gcap, st)))
 }
+
+hipError_t launch_support(int n, const double2* kb, const uint8_t* active, GeomDev geo, int64_t nbf, uint4* sup,
+                          int* vend, int* nsup, hipStream_t st) {
+    SSB_DISPATCH_N(n, (support_n<NN>(kb, active, geo, nbf, sup, vend, nsup, st)))
+}
+
+int pass1_tile(int n) { return n >= 512 ? pass1_tc<512>() : pass1_tc<256>(); }
 
 hipError_t launch_accum(int n, const float* part_s1, const double* part_s2, int gcap, int ng, int n_trials,
                         double* s1run, double* s2run, hipStream_t st) {

@@ -33,21 +33,24 @@ PEAK_FP32_TFLOPS = 157.3    # MI355X FP32 vector (256 CU x 2.4 GHz, packed)
 PEAK_HBM_GBS = 8000.0
 
 
-def algorithmic_work(n: int, support_share: float) -> dict:
+def algorithmic_work(n: int, info: dict) -> dict:
     """Algorithmic HBM bytes and FLOPs per active BF plane and trial, by stage.
 
-    pass 1 reads the nonzero-transfer spectrum entries (complex64) and writes the
-    column-transformed plane; pass 2 reads that plane and writes one float phase
-    sum image per 32 BF.  FLOPs: 5 n log2 n per complex n-point transform, 45 per
-    nonzero-transfer correction, 23 per phase sample (atan2 and moments).
+    From the library's own support tables (ssb_query): pass 1 reads the
+    nonzero-transfer spectrum entries (complex64) and writes the column results of
+    the column tiles that hold any support; pass 2 reads the nonzero columns and
+    writes one float phase-sum image per 32 BF.  FLOPs: 5 n log2 n per complex
+    n-point transform, 45 per nonzero-transfer correction, 23 per phase sample
+    (atan2 and moments).
     """
+    act = max(1, info["n_active_bf"])
+    sup = info["support_entries"] / act
+    cw = info["columns_written"] / act
+    cr = info["columns_read"] / act
     fft = 5.0 * n * math.log2(n)
-    half = n * (n // 2 + 1)
     return {
-        "pass1": {"bytes": 8.0 * support_share * half + 8.0 * half,
-                  "flops": (n // 2 + 1) * fft + 45.0 * support_share * half},
-        "pass2": {"bytes": 8.0 * half + 4.0 * n * n / 32.0,
-                  "flops": (n // 2) * fft + 23.0 * n * n},
+        "pass1": {"bytes": 8.0 * sup + 8.0 * n * cw, "flops": cw * fft + 45.0 * sup},
+        "pass2": {"bytes": 8.0 * n * cr + 4.0 * n * n / 32.0, "flops": (n // 2) * fft + 23.0 * n * n},
     }
 
 
@@ -80,29 +83,6 @@ def measured_traffic(kernel: str):
             if len(parts) >= 4 and not line.startswith("#") and parts[0] == kernel and parts[1] == want:
                 return float(parts[2]) + float(parts[3])
     return None
-
-
-def support_share(geom) -> float:
-    """Fraction of half-plane entries with nonzero transfer, averaged over every 8th BF (geometry only)."""
-    n = geom.scan_n
-    d = geom.det_n
-    ra, w = geom.aperture_px, geom.edge_px
-    hi2 = (ra + 0.5 * w) ** 2
-    i, j = np.meshgrid(np.arange(d), np.arange(d), indexing="ij")
-    sel = (i - geom.det_cy) ** 2 + (j - geom.det_cx) ** 2 <= geom.bf_r2
-    kx = (j[sel] - geom.det_cx).astype(np.float64)
-    ky = (i[sel] - geom.det_cy).astype(np.float64)
-    fy = np.fft.fftfreq(n) * n * geom.q_step_px
-    fx = np.fft.rfftfreq(n) * n * geom.q_step_px
-    tot = 0
-    picks = range(0, kx.size, 8)
-    for b in picks:
-        dxm = (kx[b] - fx)[None, :] ** 2
-        dym = (ky[b] - fy)[:, None] ** 2
-        dxp = (kx[b] + fx)[None, :] ** 2
-        dyp = (ky[b] + fy)[:, None] ** 2
-        tot += np.count_nonzero((dxm + dym < hi2) | (dxp + dyp < hi2))
-    return tot / (len(picks) * n * (n // 2 + 1))
 
 
 def main():
@@ -207,8 +187,8 @@ def main():
         log(f"[bench] batch of {args.batch}: {batch_ms_per_trial:.3f} ms/trial")
 
     # roofline of the dominant stage: algorithmic bytes (or FLOPs) per launch / average launch time
-    share = support_share(g)
-    work = algorithmic_work(n, share)
+    share = info["support_entries"] / (info["n_bf"] * n * (n // 2 + 1))
+    work = algorithmic_work(n, info)
     stage_ms = {k: prof[k]["ms"] / max(1, prof[k]["launches"]) for k in prof}
     dom = max(("pass1", "pass2"), key=lambda k: prof[k]["ms"])
     units_per_launch = prof[dom]["units"] / max(1, prof[dom]["launches"])

@@ -76,6 +76,9 @@ typedef struct ssb_info {
     int64_t spectrum_bytes;/* device bytes of the cached half-plane spectra */
     double dc;             /* DC value: mean over BF of the exact integer scan sums */
     int64_t chunk_bf;      /* current cap on BF pixels per intermediate chunk */
+    int64_t support_entries; /* half-plane entries with nonzero transfer, summed over BF (q = 0 aside) */
+    int64_t columns_written; /* column results (N values each) the column pass writes per trial, all BF */
+    int64_t columns_read;    /* column results the row pass reads per trial, all BF (zero columns skipped) */
 } ssb_info;
 
 typedef struct ssb_handle ssb_handle;

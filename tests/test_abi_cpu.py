@@ -35,10 +35,33 @@ def test_library_exports_every_declared_symbol():
     assert set(declared) == set(ssb.EXPORTS)
 
 
-def test_struct_layout_matches_header():
-    # ssb_geometry: two int32 then nine doubles -> 8 + 72 bytes
-    assert ctypes.sizeof(ssb.ssb_geometry) == 80
-    assert ctypes.sizeof(ssb.ssb_info) == 48
+def test_struct_layout_matches_header(tmp_path):
+    """Size and every field offset of the binding's structs equal what a C compiler
+    makes of include/ssb.h."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    structs = {"ssb_geometry": ssb._ssb.ssb_geometry, "ssb_info": ssb._ssb.ssb_info,
+               "ssb_profile_data": ssb._ssb.ssb_profile_data}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "ssb.h"', 'int main(void) {']
+    for name, cls in structs.items():
+        lines.append(f'printf("{name} size %zu\\n", sizeof({name}));')
+        for field, _ in cls._fields_:
+            lines.append(f'printf("{name} {field} %zu\\n", offsetof({name}, {field}));')
+    lines += ['return 0;', '}']
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    include = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    subprocess.run([cc, "-I", include, str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    got = {tuple(ln.split()[:2]): int(ln.split()[2]) for ln in out if ln.strip()}
+    for name, cls in structs.items():
+        assert got[(name, "size")] == ctypes.sizeof(cls), name
+        for field, _ in cls._fields_:
+            assert got[(name, field)] == getattr(cls, field).offset, (name, field)
 
 
 def _geom(name="tiny", **kw):

@@ -115,6 +115,34 @@ def test_prepare_info_exact(fx, request):
     assert info["spectrum_bytes"] == w.n_bf * g.scan_n * (g.scan_n // 2 + 1) * 8
 
 
+def _oracle_support_counts(g, kx, ky):
+    """Nonzero-transfer entries (q = 0 aside) and 1 + last nonzero column, per BF, from
+    the oracle's aperture: the transfer is zero exactly where both shifted apertures are."""
+    qx, qy = O.q_vectors(g)
+    nsup, vend = [], []
+    for b in range(kx.size):
+        on = (O.aperture(g, kx[b] - qx, ky[b] - qy) > 0) | (O.aperture(g, kx[b] + qx, ky[b] + qy) > 0)
+        on[0, 0] = False
+        cols = np.flatnonzero(on.any(axis=0))
+        nsup.append(int(np.count_nonzero(on)))
+        vend.append(int(cols[-1]) + 1 if cols.size else 1)
+    return np.array(nsup), np.array(vend)
+
+
+@pytest.mark.parametrize("fx", ["tiny", "small"])
+def test_support_tables_exact(fx, request):
+    """The library's per-column support intervals select exactly the oracle's
+    nonzero-transfer entries (counted) and its nonzero columns (rho = 0: exact lattice)."""
+    w, counts, p = request.getfixturevalue(fx)
+    g = O.OGeom.from_any(w.geometry)
+    kx, ky = O.bf_kvectors(g)
+    nsup, vend = _oracle_support_counts(g, kx, ky)
+    info = ssb.ssb_query(p.h)
+    h = g.scan_n // 2
+    assert info["support_entries"] == int(nsup.sum())
+    assert info["columns_read"] == int(np.minimum(vend, h).sum() + np.count_nonzero(vend > h))
+
+
 @pytest.mark.parametrize("fx", ["tiny", "small"])
 def test_spectrum_vs_oracle(fx, request):
     w, counts, p = request.getfixturevalue(fx)
