@@ -155,4 +155,57 @@ struct WaveFFT {
     }
 };
 
+// The same transform with the per-lane twiddles read from a workgroup table in
+// LDS instead of held in registers (frees 2 (R-1) complex registers per lane).
+// Table layout: for pass p = 1..P-1 (ns = R^p) a block [R-1][ns] of
+// exp(SIGN 2 pi i k r / (ns R)), r = 1..R-1, k < ns; N - R entries in all.
+template <int N, int SIGN>
+struct WaveFFTT {
+    static constexpr int R = FftShape<N>::R;
+    static constexpr int P = FftShape<N>::P;
+    static constexpr int L = N / R;
+    static constexpr int W = 64 / L;
+    static constexpr int TABLE = N - R;
+
+    __device__ static void fill(float2* tab, int tid, int nthreads) {
+        for (int e = tid; e < TABLE; e += nthreads) {
+            int base = 0, ns = R;
+            // locate the pass block holding entry e
+            while (e >= base + (R - 1) * ns) {
+                base += (R - 1) * ns;
+                ns *= R;
+            }
+            const int off = e - base;
+            const int r = off / ns + 1, k = off % ns;
+            float s, c;
+            sincospif((float)(SIGN * 2 * k * r) / (float)(ns * R), &s, &c);
+            tab[e] = make_float2(c, s);
+        }
+    }
+
+    __device__ __forceinline__ void run(float2 (&x)[R], float2* buf, int j, const float2* tab) const {
+        int ns = 1, base = 0;
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            if (p > 0) {
+                const int k = j & (ns - 1);
+#pragma unroll
+                for (int r = 1; r < R; ++r) x[r] = cmul(x[r], tab[base + (r - 1) * ns + k]);
+                base += (R - 1) * ns;
+            }
+            dft<R, SIGN>(x);
+            if (p == P - 1) break;
+            const int k = j & (ns - 1);
+            const int bb = (j - k) * R + k;
+            wave_lds_fence();
+#pragma unroll
+            for (int r = 0; r < R; ++r) buf[exch_swizzle<N>(p, bb + r * ns)] = x[r];
+            wave_lds_fence();
+#pragma unroll
+            for (int r = 0; r < R; ++r) x[r] = buf[exch_swizzle<N>(p, j + r * L)];
+            ns *= R;
+        }
+    }
+};
+
 }  // namespace ssb

@@ -27,10 +27,16 @@ namespace {
 
 // Compile-time tuning constants.
 #ifndef SSB_PASS1_TC
-#define SSB_PASS1_TC 16       // pass-1 columns per workgroup at N = 512
+#define SSB_PASS1_TC 8        // pass-1 columns per workgroup at N = 512
+#endif
+#ifndef SSB_PASS1_THREADS
+#define SSB_PASS1_THREADS 256 // pass-1 workgroup size
 #endif
 #ifndef SSB_PASS2_MIN_WAVES
 #define SSB_PASS2_MIN_WAVES 1 // pass-2 register budget hint: minimum resident waves per SIMD
+#endif
+#ifndef SSB_PASS2_TW_LDS
+#define SSB_PASS2_TW_LDS 1    // pass-2 FFT twiddles from an LDS table instead of registers
 #endif
 #ifndef SSB_PASS2_PREFETCH
 #define SSB_PASS2_PREFETCH 0  // pass 2 loads the next BF's column values during the current transform
@@ -365,8 +371,8 @@ __device__ __forceinline__ void delta_slopes(double kx, double ky, const TrialCo
 }
 
 // Pass 1: correction + column inverse transforms.  One workgroup = one BF pixel x
-// one tile of TC columns (or the Nyquist column) x one trial; each wave owns one
-// column's FFT.  Tiles at or past the BF pixel's last supported column (vend) are
+// one tile of TC columns (or the Nyquist column) x one trial; the waves share the
+// tile's column FFTs.  Tiles at or past the BF pixel's last supported column (vend) are
 // all zero after the correction: they are neither computed nor written, and pass 2
 // does not read them.
 //   1. support from the per-column intervals (integer compares); the spectrum
@@ -380,7 +386,7 @@ __device__ __forceinline__ void delta_slopes(double kx, double ky, const TrialCo
 // exp(-i delta) is separable: E_u(u') = exp(-2 pi i u' beta) for all rows is
 // built in LDS per workgroup, E_v(v) = exp(-2 pi i v alpha) per thread (each
 // thread keeps one column).
-constexpr int kPass1Threads = 512;
+constexpr int kPass1Threads = SSB_PASS1_THREADS;
 
 template <int N, int TC>
 __global__ __launch_bounds__(kPass1Threads) void k_pass1(const float2* __restrict__ gm,
@@ -406,11 +412,16 @@ __global__ __launch_bounds__(kPass1Threads) void k_pass1(const float2* __restric
     __shared__ float2 eu[N];
 
     const int tid = threadIdx.x;
-    const int bl = blockIdx.y;
-    const int t = blockIdx.z;
+    const int t = blockIdx.y;
+    // Workgroup -> (BF, tile): the H/TC main tiles of a BF, then its Nyquist tile.
+    // (Giving the two tiles that share 128-byte rows ids 8 apart, so that they run
+    // on the same XCD, halves the fetched bytes but measured slower.)
+    constexpr int NTM = H / TC;
+    const int bl = (int)(blockIdx.x / (NTM + 1));
+    const int tix = (int)(blockIdx.x % (NTM + 1));
     const int64_t b = bf0 + bl;
-    const bool nyq = blockIdx.x == H / TC;
-    const int v0 = nyq ? H : blockIdx.x * TC;
+    const bool nyq = tix == NTM;
+    const int v0 = nyq ? H : tix * TC;
     if (v0 >= vend[b]) return;                    // all-zero columns (every column of an inactive BF)
     const int c = nyq ? 0 : tid % TC;
     const int v = v0 + c;
@@ -603,7 +614,12 @@ __global__ __launch_bounds__(256, SSB_PASS2_MIN_WAVES) void k_pass2(const float2
                                                const int* __restrict__ vend, int64_t bf0,
                                                int cb, float dcf, float* __restrict__ part_s1,
                                                double* __restrict__ part_s2, int gcap) {
+#if SSB_PASS2_TW_LDS
+    using F = WaveFFTT<N, +1>;
+    __shared__ float2 twt[F::TABLE];
+#else
     using F = WaveFFT<N, +1>;
+#endif
     constexpr int H = N / 2;
     constexpr int R = F::R, L = F::L;
     __shared__ float2 buf[4 * F::W][N];
@@ -621,7 +637,12 @@ __global__ __launch_bounds__(256, SSB_PASS2_MIN_WAVES) void k_pass2(const float2
     const int b_hi = min(cb, b_lo + kGroupBF);
 
     F fft;
+#if SSB_PASS2_TW_LDS
+    F::fill(twt, tid, 256);
+    __syncthreads();
+#else
     fft.init(j);
+#endif
     float s1a[R], s1b[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -655,7 +676,11 @@ __global__ __launch_bounds__(256, SSB_PASS2_MIN_WAVES) void k_pass2(const float2
 #endif
         float2 x[R];
         cur.assemble(j, x);
+#if SSB_PASS2_TW_LDS
+        fft.run(x, buf[grp], j, twt);
+#else
         fft.run(x, buf[grp], j);
+#endif
         const float den0 = dcf + cur.z0.x + sgn * cur.h0.x;
         const float den1 = dcf + cur.z1.x + sgn * cur.h1.x;
         float p2 = 0.f;
@@ -972,14 +997,10 @@ hipError_t pass1_n(const float2* gm, const float2* gn, const float2* chm, const 
                    int cb, int cap, float2* im, float2* in, hipStream_t st) {
     constexpr int H = N / 2;
     constexpr int TC = pass1_tc<N>();
-    for (int64_t p0 = 0; p0 < cb; p0 += 65535) {
-        const int np = (int)std::min<int64_t>(65535, cb - p0);
-        hipLaunchKernelGGL((k_pass1<N, TC>), dim3(H / TC + 1, np, n_trials), dim3(kPass1Threads), 0, st, gm, gn, chm,
-                           chn, kb, sup, vend, tc, geo, bf0 + p0, cap, im + p0 * N * H, in + p0 * N);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    return hipSuccess;
+    // one launch per chunk: (H/TC + 1) tiles per BF in x, trials in y
+    hipLaunchKernelGGL((k_pass1<N, TC>), dim3((unsigned)((int64_t)cb * (H / TC + 1)), n_trials), dim3(kPass1Threads),
+                       0, st, gm, gn, chm, chn, kb, sup, vend, tc, geo, bf0, cap, im, in);
+    return hipGetLastError();
 }
 
 template <int N>
