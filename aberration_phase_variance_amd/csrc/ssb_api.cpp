@@ -498,7 +498,7 @@ int ssb_object(ssb_handle* h, const float* params3, float* phase, float* psi, vo
     const TrialConst tc = trial_const(h, params3);   // kernel argument: no host-staged copy
     {
         StageTimer tm(h, SSB_STAGE_OBJ_SUM, st, h->n_active);
-        SSB_HIP(launch_obj_sum(n, h->gm, h->gn, h->kb, h->active, tc, h->geo, h->n_bf, part, nseg, st),
+        SSB_HIP(launch_obj_sum(n, h->gm, h->gn, h->kb, h->sup, h->vend, tc, h->geo, h->n_bf, part, nseg, st),
                 "object sum");
     }
     {

@@ -69,9 +69,9 @@ hipError_t launch_loss(int n, const double* s1run, const double* s2run, int n_tr
                        double* lpart, double* loss, float* mean_phase, hipStream_t st);
 // Object: sum of corrected spectra over all BF, then one 2-D inverse transform.
 int obj_segments(int64_t nbf);
-hipError_t launch_obj_sum(int n, const float2* gm, const float2* gn, const double2* kb,
-                          const uint8_t* active, TrialConst tc, GeomDev geo, int64_t nbf, double2* part,
-                          int nseg, hipStream_t st);
+hipError_t launch_obj_sum(int n, const float2* gm, const float2* gn, const double2* kb, const uint4* sup,
+                          const int* vend, TrialConst tc, GeomDev geo, int64_t nbf, double2* part, int nseg,
+                          hipStream_t st);
 hipError_t launch_obj_reduce(int n, const double2* part, int nseg, float2* pm, float2* pn,
                              hipStream_t st);
 hipError_t launch_obj_cols(int n, float2* pm, float2* pn, hipStream_t st);

@@ -47,13 +47,6 @@ constexpr int kPad = 1;       // LDS row padding (complex values)
 
 enum ColMode { COL_PLAIN_FWD = 1, COL_PLAIN_INV = 2 };
 
-__device__ __forceinline__ double aperture_weight(double r2, const GeomDev& g) {
-    if (r2 >= g.hi2) return 0.0;
-    if (r2 <= g.lo2) return 1.0;
-    const double a = (g.ra - sqrt(r2)) * g.inv_w + 0.5;
-    return fmin(fmax(a, 0.0), 1.0);
-}
-
 // (cos, sin) of 2 pi r for r in [-1/2, 1/2]: quadrant from rint(4 r), then
 // sin(pi f/2) = f S(f^2) and cos(pi f/2) = C(f^2) on f in [-1/2, 1/2] with
 // polynomials fitted here (iteratively reweighted least squares, 4 and 5 terms;
@@ -160,38 +153,6 @@ __device__ __forceinline__ float2 load_or_zero(__amdgpu_buffer_rsrc_t r, int off
     return __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
 }
 constexpr int kNoLoad = (int)0x80000000;
-
-// Corrected value C = G * T of one half-plane entry with scan frequency q = (qx, qy)
-// pixels, for the BF pixel at k = (kx, ky) pixels.
-//
-// T = conj(Gamma)/|Gamma|.  With chi quadratic, chi(k) - chi(k -+ q) = +-delta - chi_q
-// where delta = 2 pi * 2 k^T M q (bilinear) and chi_q = 2 pi q^T M q, so
-//   Gamma = a(k) e^{i delta} [(a_- - a_+) cos chi_q - i (a_- + a_+) sin chi_q],
-// the definition's two shifted probe factors regrouped so that |Gamma| never comes
-// from cancellation.  ed = exp(-i delta) and ch = (cos chi_q, sin chi_q) are given;
-// the support test is on exact double squared radii and both zero sidebands (zero
-// transfer) give an exact zero.
-__device__ __forceinline__ bool in_support(double qx, double qy, double kx, double ky, const GeomDev& g,
-                                           double& am, double& apl) {
-    const double dxm = kx - qx, dym = ky - qy, dxp = kx + qx, dyp = ky + qy;
-    const double r2m = dxm * dxm + dym * dym;
-    const double r2p = dxp * dxp + dyp * dyp;
-    if (r2m >= g.hi2 && r2p >= g.hi2) return false;
-    am = aperture_weight(r2m, g);
-    apl = aperture_weight(r2p, g);
-    return true;
-}
-
-__device__ __forceinline__ float2 apply_transfer(float2 gv, float2 ch, float2 ed, float am, float apl) {
-    const float br = (am - apl) * ch.x;   // Re conj(bracket)
-    const float bi = (am + apl) * ch.y;   // Im conj(bracket)
-    const float mag2 = br * br + bi * bi;
-    if (mag2 == 0.0f) return make_float2(0.f, 0.f);
-    const float inv = rsqrtf(mag2);
-    const float tr = (ed.x * br - ed.y * bi) * inv;
-    const float ti = (ed.x * bi + ed.y * br) * inv;
-    return make_float2(gv.x * tr - gv.y * ti, gv.x * ti + gv.y * tr);
-}
 
 // (cos, sin) of 2 pi q^T M q
 __device__ __forceinline__ float2 chi_phasor(double qx, double qy, const TrialConst& m) {
@@ -370,6 +331,46 @@ __device__ __forceinline__ void delta_slopes(double kx, double ky, const TrialCo
     beta = 2.0 * (px * g.qux + py * g.quy);
 }
 
+// Corrected value C = G T of one half-plane entry, T = conj(Gamma)/|Gamma|.  With chi
+// quadratic, chi(k) - chi(k -+ q) = +-delta - chi_q where delta = 2 pi * 2 k^T M q
+// (bilinear) and chi_q = 2 pi q^T M q, so
+//   Gamma = a(k) e^{i delta} [(a_- - a_+) cos chi_q - i (a_- + a_+) sin chi_q],
+// the definition's two shifted probe factors regrouped so that |Gamma| never comes
+// from cancellation, and a(k) > 0 drops out of T.
+// Inputs: the support flags (inm: A(k - q) has
+// nonzero weight, inp: A(k + q) does; edm/edp: that weight is on the edge ring, not
+// the flat top), the spectrum value g, exp(i chi_q) = ch and e = exp(-i delta).
+// On the flat tops the bracket ((a_- - a_+) cos chi_q, (a_- + a_+) sin chi_q) is
+// already a unit phasor: (+-cos, sin) for one sideband, (0, sign sin) for two (zero
+// when sin chi_q is zero); on an edge ring it is evaluated and normalized.
+__device__ __forceinline__ float2 correct_entry(float2 g, float2 ch, float2 e, bool inm, bool inp, bool edm,
+                                                bool edp, int up, int v, double kx, double ky, const GeomDev& geo) {
+    float br, bi;
+    if (edm || edp) {
+        // keep the rarely needed double-precision distances inside this branch (an
+        // empty asm makes the row index opaque, so nothing here is hoisted out of a
+        // caller's loop where it would hold registers)
+        int upo = up;
+        asm volatile("" : "+v"(upo));
+        float am = inm ? 1.f : 0.f, apl = inp ? 1.f : 0.f;
+        if (edm) am = edge_weight(shifted_r2(kx, ky, -1.0, upo, v, geo), geo);
+        if (edp) apl = edge_weight(shifted_r2(kx, ky, 1.0, upo, v, geo), geo);
+        br = (am - apl) * ch.x;
+        bi = (am + apl) * ch.y;
+        const float mag2 = fmaf(br, br, bi * bi);
+        const float inv = mag2 > 0.f ? __builtin_amdgcn_rsqf(mag2) : 0.f;
+        br *= inv;
+        bi *= inv;
+    } else if (inm && inp) {
+        br = 0.f;
+        bi = ch.y > 0.f ? 1.f : (ch.y < 0.f ? -1.f : 0.f);
+    } else {
+        br = inm ? ch.x : -ch.x;
+        bi = ch.y;
+    }
+    return cmul(g, make_float2(e.x * br - e.y * bi, e.x * bi + e.y * br));
+}
+
 // Pass 1: correction + column inverse transforms.  One workgroup = one BF pixel x
 // one tile of TC columns (or the Nyquist column) x one trial; the waves share the
 // tile's column FFTs.  Tiles at or past the BF pixel's last supported column (vend) are
@@ -474,30 +475,7 @@ __global__ __launch_bounds__(kPass1Threads) void k_pass1(const float2* __restric
                 const bool inm = f & 1u, inp = f & 2u;
                 const bool edm = inm && (unsigned)(up - flo_m) >= (unsigned)flen_m;
                 const bool edp = inp && (unsigned)(up - flo_p) >= (unsigned)flen_p;
-                const float2 ch = chv[i];
-                float br, bi;
-                if (edm || edp) {
-                    // on an edge ring: bracket ((a_- - a_+) cos, (a_- + a_+) sin), normalized
-                    float am = inm ? 1.f : 0.f, apl = inp ? 1.f : 0.f;
-                    if (edm) am = edge_weight(shifted_r2(k.x, k.y, -1.0, up, v, geo), geo);
-                    if (edp) apl = edge_weight(shifted_r2(k.x, k.y, 1.0, up, v, geo), geo);
-                    br = (am - apl) * ch.x;
-                    bi = (am + apl) * ch.y;
-                    const float mag2 = fmaf(br, br, bi * bi);
-                    const float inv = mag2 > 0.f ? __builtin_amdgcn_rsqf(mag2) : 0.f;
-                    br *= inv;
-                    bi *= inv;
-                } else if (inm && inp) {
-                    // both flat tops: (0, 2 sin) -> (0, sign(sin chi_q)); zero when sin is zero
-                    br = 0.f;
-                    bi = ch.y > 0.f ? 1.f : (ch.y < 0.f ? -1.f : 0.f);
-                } else {
-                    // one flat sideband: (+-cos, sin) is already a unit phasor
-                    br = inm ? ch.x : -ch.x;
-                    bi = ch.y;
-                }
-                const float2 e = cmul(eu[u], ev);
-                val = cmul(gv[i], make_float2(e.x * br - e.y * bi, e.x * bi + e.y * br));
+                val = correct_entry(gv[i], chv[i], cmul(eu[u], ev), inm, inp, edm, edp, up, v, k.x, k.y, geo);
             }
             tile[c * LD + u] = val;
         }
@@ -867,40 +845,123 @@ __global__ __launch_bounds__(256) void k_g_rows(const uint32_t* __restrict__ cou
 }
 
 // Object: sum over the BF pixels of one segment of the corrected half-plane
-// spectrum, one entry per thread, double accumulation in BF order.  Same
-// correction as pass 1; the BF-independent exp(i chi_q) is computed once per entry.
-template <int N>
-__global__ __launch_bounds__(256) void k_obj_sum(const float2* __restrict__ gm, const float2* __restrict__ gn,
-                                                 const double2* __restrict__ kb,
-                                                 const uint8_t* __restrict__ active, TrialConst m, GeomDev geo,
-                                                 int64_t nbf, int seglen, double2* __restrict__ part) {
+// spectrum.  One workgroup = one column tile (as in pass 1) x one BF segment; each
+// thread keeps its tile entries' running sums in registers (float, at most a
+// segment's worth of terms) and loops over the segment's BF pixels in order:
+// support from the per-column intervals, predicated loads, the same correction as
+// pass 1 (exp(-i delta) from a per-BF row table in LDS, double buffered, and a
+// per-thread column phasor; exp(i chi_q) once per entry).  Tiles at or past a BF
+// pixel's last supported column skip it.  Partials per segment in double.
+constexpr int kObjThreads = 512;
+
+template <int N, int TC>
+__global__ __launch_bounds__(kObjThreads) void k_obj_sum(const float2* __restrict__ gm,
+                                                         const float2* __restrict__ gn,
+                                                         const double2* __restrict__ kb,
+                                                         const uint4* __restrict__ sup,
+                                                         const int* __restrict__ vend, TrialConst m, GeomDev geo,
+                                                         int64_t nbf, int seglen, double2* __restrict__ part) {
     constexpr int H = N / 2;
     constexpr int NE = N * (H + 1);
-    const int e = blockIdx.x * 256 + threadIdx.x;
-    if (e >= NE) return;
-    const int u = e / (H + 1), v = e % (H + 1);
+    constexpr int NT = kObjThreads;
+    constexpr int RS = NT / TC;
+    constexpr int PER = (N + RS - 1) / RS;
+    constexpr int PERN = (N + NT - 1) / NT;
+    constexpr int PM = PER > PERN ? PER : PERN;
+    __shared__ float2 eu[2][N];
+
+    const int tid = threadIdx.x;
+    const int tix = blockIdx.x;
+    const bool nyq = tix == H / TC;
+    const int c = nyq ? 0 : tid % TC;
+    const int v0 = nyq ? H : tix * TC;
+    const int v = v0 + c;
+    const int ustart = nyq ? tid : tid / TC;
+    const int ustep = nyq ? NT : RS;
+    const int nent = nyq ? PERN : PER;
+    const int sstride = nyq ? 1 : H;
+    const int vcol = nyq ? 0 : v;
     const int64_t b_lo = (int64_t)blockIdx.y * seglen;
     const int64_t b_hi = min(nbf, b_lo + seglen);
-    double ax = 0.0, ay = 0.0;
-    if (!(u == 0 && v == 0)) {
-        const double up = (double)(u < H ? u : u - N);
-        const double qx = fma(geo.qux, up, geo.qvx * v), qy = fma(geo.quy, up, geo.qvy * v);
-        const float2 ch = chi_phasor(qx, qy, m);
-        for (int64_t b = b_lo; b < b_hi; ++b) {
-            if (!active[b]) continue;
-            const double2 k = kb[b];
-            double am, apl;
-            if (!in_support(qx, qy, k.x, k.y, geo, am, apl)) continue;
-            double alpha, beta;
-            delta_slopes(k.x, k.y, m, geo, alpha, beta);
-            const float2 ed = phasor_rev_neg(fma((double)v, alpha, up * beta));
-            const float2 gv = v < H ? gm[(b * N + u) * H + v] : gn[b * N + u];
-            const float2 cv = apply_transfer(gv, ch, ed, (float)am, (float)apl);
-            ax += cv.x;
-            ay += cv.y;
-        }
+
+    float2 chv[PM], acc[PM];
+#pragma unroll
+    for (int i = 0; i < PM; ++i) {
+        const int u = ustart + i * ustep;
+        const int up = u < H ? u : u - N;
+        chv[i] = chi_phasor(fma(geo.qux, (double)up, geo.qvx * v), fma(geo.quy, (double)up, geo.qvy * v), m);
+        acc[i] = make_float2(0.f, 0.f);
     }
-    part[(int64_t)blockIdx.y * NE + e] = make_double2(ax, ay);
+
+    // BF pixels with support in this tile, in order; the next one's column support
+    // and k are fetched while the current one is corrected
+    auto next_bf = [&](int64_t b) {
+        while (b < b_hi && v0 >= vend[b]) ++b;    // no support in this tile (or an inactive BF)
+        return b;
+    };
+    int buf = 0;
+    int64_t b = next_bf(b_lo);
+    uint4 srn = make_uint4(0, 0, 0, 0);
+    double2 kn = make_double2(0.0, 0.0);
+    if (b < b_hi) {
+        srn = sup[b * (H + 1) + v];
+        kn = kb[b];
+    }
+    while (b < b_hi) {
+        const uint4 sr = srn;
+        const double2 k = kn;
+        const int64_t bn = next_bf(b + 1);
+        if (bn < b_hi) {
+            srn = sup[bn * (H + 1) + v];
+            kn = kb[bn];
+        }
+        const int lo_m = unpack_lo(sr.x), len_m = unpack_len(sr.x);
+        const int lo_p = unpack_lo(sr.y), len_p = unpack_len(sr.y);
+        const int flo_m = unpack_lo(sr.z), flen_m = unpack_len(sr.z);
+        const int flo_p = unpack_lo(sr.w), flen_p = unpack_len(sr.w);
+        const __amdgpu_buffer_rsrc_t rg = nyq ? make_rsrc(gn + b * N, N * 8) : make_rsrc(gm + b * N * H, N * H * 8);
+        float2 gv[PM];
+        unsigned bits = 0;
+#pragma unroll
+        for (int i = 0; i < PM; ++i) {
+            const int u = ustart + i * ustep;
+            const int up = u < H ? u : u - N;
+            const bool inm = (unsigned)(up - lo_m) < (unsigned)len_m;
+            const bool inp = (unsigned)(up - lo_p) < (unsigned)len_p;
+            const bool on = i < nent && u < N && (inm || inp) && (u != 0 || v != 0);
+            gv[i] = load_or_zero(rg, on ? (u * sstride + vcol) * 8 : kNoLoad);
+            bits |= on ? ((inm ? 1u : 0u) | (inp ? 2u : 0u)) << (2 * i) : 0u;
+        }
+        // phase ramps of this BF while its spectrum loads are in flight
+        double alpha, beta;
+        delta_slopes(k.x, k.y, m, geo, alpha, beta);
+        for (int u = tid; u < N; u += NT) eu[buf][u] = phasor_rev_neg((double)(u < H ? u : u - N) * beta);
+        const float2 ev = phasor_rev_neg((double)v * alpha);
+        __syncthreads();                          // row table of this BF complete (double buffered)
+#pragma unroll
+        for (int i = 0; i < PM; ++i) {
+            const unsigned f = (bits >> (2 * i)) & 3u;
+            if (f) {
+                const int u = ustart + i * ustep;
+                const int up = u < H ? u : u - N;
+                const bool inm = f & 1u, inp = f & 2u;
+                const bool edm = inm && (unsigned)(up - flo_m) >= (unsigned)flen_m;
+                const bool edp = inp && (unsigned)(up - flo_p) >= (unsigned)flen_p;
+                const float2 cv =
+                    correct_entry(gv[i], chv[i], cmul(eu[buf][u], ev), inm, inp, edm, edp, up, v, k.x, k.y, geo);
+                acc[i].x += cv.x;
+                acc[i].y += cv.y;
+            }
+        }
+        buf ^= 1;
+        b = bn;
+    }
+#pragma unroll
+    for (int i = 0; i < PM; ++i) {
+        const int u = ustart + i * ustep;
+        if (i < nent && u < N)
+            part[(int64_t)blockIdx.y * NE + (int64_t)u * (H + 1) + v] = make_double2(acc[i].x, acc[i].y);
+    }
 }
 
 template <int N>
@@ -1124,18 +1185,20 @@ int obj_segments(int64_t nbf) {
 }
 
 template <int N>
-static hipError_t obj_sum_n(const float2* gm, const float2* gn, const double2* kb, const uint8_t* active,
-                            TrialConst tc, GeomDev geo, int64_t nbf, double2* part, int nseg, hipStream_t st) {
-    constexpr int NE = N * (N / 2 + 1);
+static hipError_t obj_sum_n(const float2* gm, const float2* gn, const double2* kb, const uint4* sup,
+                            const int* vend, TrialConst tc, GeomDev geo, int64_t nbf, double2* part, int nseg,
+                            hipStream_t st) {
+    constexpr int TC = pass1_tc<N>();
     const int seglen = (int)((nbf + nseg - 1) / nseg);
-    hipLaunchKernelGGL(k_obj_sum<N>, dim3((NE + 255) / 256, nseg), dim3(256), 0, st, gm, gn, kb, active, tc, geo,
-                       nbf, seglen, part);
+    hipLaunchKernelGGL((k_obj_sum<N, TC>), dim3(N / 2 / TC + 1, nseg), dim3(kObjThreads), 0, st, gm, gn, kb, sup,
+                       vend, tc, geo, nbf, seglen, part);
     return hipGetLastError();
 }
 
-hipError_t launch_obj_sum(int n, const float2* gm, const float2* gn, const double2* kb, const uint8_t* active,
-                          TrialConst tc, GeomDev geo, int64_t nbf, double2* part, int nseg, hipStream_t st) {
-    SSB_DISPATCH_N(n, (obj_sum_n<NN>(gm, gn, kb, active, tc, geo, nbf, part, nseg, st)))
+hipError_t launch_obj_sum(int n, const float2* gm, const float2* gn, const double2* kb, const uint4* sup,
+                          const int* vend, TrialConst tc, GeomDev geo, int64_t nbf, double2* part, int nseg,
+                          hipStream_t st) {
+    SSB_DISPATCH_N(n, (obj_sum_n<NN>(gm, gn, kb, sup, vend, tc, geo, nbf, part, nseg, st)))
 }
 
 template <int N>
