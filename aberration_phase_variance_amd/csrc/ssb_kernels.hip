@@ -401,7 +401,7 @@ __global__ __launch_bounds__(kPass1Threads) void k_pass1(const float2* __restric
                                                          int64_t bf0, int cap, float2* __restrict__ im,
                                                          float2* __restrict__ in) {
     constexpr int H = N / 2;
-    constexpr int LD = N + kPad;
+    constexpr int LD = N + 16 / TC;           // row pitch: the 16 lanes of one b64 LDS cycle hit distinct banks
     constexpr int NT = kPass1Threads;
     constexpr int RS = NT / TC;                   // rows per sweep of the main-tile mapping
     constexpr int PER = (N + RS - 1) / RS;        // entries per thread on a main tile (rows u < N)

@@ -247,6 +247,41 @@ def test_object_vs_oracle(fx, request):
 
 
 # ---------------------------------------------------------------- edge cases
+@pytest.mark.parametrize("fx", ["tiny", "small"])
+def test_zero_aberration(fx, request):
+    """theta = 0: chi vanishes, so sin chi_q is exactly 0 and every entry with both
+    sidebands on their flat tops has zero transfer; one-sideband entries keep T = +-1."""
+    w, counts, p = request.getfixturevalue(fx)
+    g = O.OGeom.from_any(w.geometry)
+    zero = [0.0, 0.0, 0.0]
+    assert _rel(p.loss([zero])[0], O.loss(g, counts, zero)) <= LOSS_RTOL
+    r1, r2 = O.bf_moments(g, counts, zero, O.dc_value(counts))
+    s1, s2 = p.moments(zero, 0, w.n_bf)
+    assert _rel(s2, r2) <= LOSS_RTOL
+    assert np.sqrt(np.mean((s1 - r1) ** 2)) <= 2e-5 * w.n_bf
+    phase, _ = p.obj(zero, with_psi=False)
+    ref, _ = O.object_wave(g, counts, zero)
+    assert np.sqrt(np.mean(np.angle(np.exp(1j * (phase - ref))) ** 2)) <= PHASE_RMS
+
+
+@pytest.mark.parametrize("params", [[40.0, 5.0, 0.3], [-75.0, 12.0, 2.2]])
+def test_vacuum_counts(params):
+    """Constant counts: every scan spectrum is zero away from q = 0, so every phase and
+    the loss are zero for any aberrations (the oracle gives exactly 0)."""
+    w = WORKLOADS["small"]
+    counts = np.full((w.n_bf, 128, 128), 200, dtype=np.uint32)
+    p = Prepared(w.geometry, counts)
+    try:
+        # float transforms of a constant plane cancel to zero up to roundoff
+        assert abs(p.loss([params])[0]) <= 1e-18
+        s1, s2 = p.moments(params, 0, w.n_bf)
+        assert s2 <= 1e-12 and np.max(np.abs(s1)) <= 1e-6
+        phase, _ = p.obj(params, with_psi=False)
+        assert np.max(np.abs(phase)) <= 1e-6
+    finally:
+        p.release()
+
+
 def test_inactive_bf_pixels():
     """Probe aperture smaller than the BF disk: zero-aperture BF keep phase 0 but count in n_bf."""
     w = WORKLOADS["tiny"]
