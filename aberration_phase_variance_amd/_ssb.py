@@ -66,8 +66,38 @@ class ssb_profile_data(ctypes.Structure):
     ]
 
 
+class ssb_fit_options(ctypes.Structure):
+    _fields_ = [
+        ("fatol", ctypes.c_double),
+        ("xatol", ctypes.c_double),
+        ("step_frac", ctypes.c_double),
+        ("step_floor", ctypes.c_double * 3),
+        ("max_evals", ctypes.c_int32),
+        ("max_iter", ctypes.c_int32),
+    ]
+
+
+class ssb_fit_result(ctypes.Structure):
+    _fields_ = [
+        ("best", ctypes.c_double * 3),
+        ("loss", ctypes.c_double),
+        ("batch_best", ctypes.c_int32),
+        ("requests", ctypes.c_int32),
+        ("evals", ctypes.c_int32),
+        ("iterations", ctypes.c_int32),
+        ("converged", ctypes.c_int32),
+        ("pad", ctypes.c_int32),
+        ("batch_loss", ctypes.c_double),
+    ]
+
+
+SSB_OBJECTIVE = ctypes.CFUNCTYPE(ctypes.c_double, ctypes.POINTER(ctypes.c_float), ctypes.c_void_p)
+
+FIT_DEFAULTS = {"fatol": 3e-6, "xatol": 0.1, "step_frac": 0.05, "step_floor": (0.01, 2.0, 0.04),
+                "max_evals": 0, "max_iter": 0}
+
 EXPORTS = ("ssb_prepare", "ssb_loss", "ssb_moments", "ssb_object", "ssb_spectrum", "ssb_set_chunk",
-           "ssb_profile", "ssb_query", "ssb_release", "ssb_last_error")
+           "ssb_profile", "ssb_query", "ssb_release", "ssb_last_error", "ssb_nelder_mead", "ssb_fit")
 
 _lib = None
 
@@ -94,6 +124,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ssb_release.restype = None
     lib.ssb_last_error.argtypes = []
     lib.ssb_last_error.restype = ctypes.c_char_p
+    lib.ssb_nelder_mead.argtypes = [dp, ctypes.POINTER(ssb_fit_options), SSB_OBJECTIVE, vp,
+                                    ctypes.POINTER(ssb_fit_result), dp, i32]
+    lib.ssb_fit.argtypes = [vp, fp, i32, ctypes.POINTER(ssb_fit_options), ctypes.POINTER(ssb_fit_result), dp, i32,
+                            vp]
     for name in EXPORTS:
         if name not in ("ssb_release", "ssb_last_error"):
             getattr(lib, name).restype = ctypes.c_int
@@ -201,3 +235,48 @@ def ssb_release(handle: int) -> None:
 
 def ssb_last_error() -> str:
     return load_library().ssb_last_error().decode()
+
+
+def _fit_options(opts) -> ssb_fit_options:
+    o = dict(FIT_DEFAULTS)
+    o.update(opts or {})
+    return ssb_fit_options(o["fatol"], o["xatol"], o["step_frac"], (ctypes.c_double * 3)(*o["step_floor"]),
+                           int(o["max_evals"]), int(o["max_iter"]))
+
+
+def _fit_dict(res: ssb_fit_result, trace: np.ndarray) -> dict:
+    out = {name: getattr(res, name) for name, _ in ssb_fit_result._fields_ if name != "pad"}
+    out["best"] = list(res.best)
+    out["trace"] = trace[:min(res.evals, trace.shape[0])].copy()
+    return out
+
+
+def ssb_nelder_mead(x0, objective, options=None, trace_cap: int = 4096) -> dict:
+    """Refinement on a Python objective f(params3 float32 ndarray) -> float (host only).
+    Returns the result fields plus 'trace' (evals x 4: float32 params, loss)."""
+    lib = load_library()
+    x = (ctypes.c_double * 3)(*[float(v) for v in x0])
+
+    def cb(p, _ctx):
+        return float(objective(np.array([p[0], p[1], p[2]], dtype=np.float32)))
+
+    fn = SSB_OBJECTIVE(cb)
+    res = ssb_fit_result()
+    trace = np.zeros((trace_cap, 4), dtype=np.float64)
+    opt = _fit_options(options)
+    _check(lib.ssb_nelder_mead(x, ctypes.byref(opt), fn, None, ctypes.byref(res),
+                               trace.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), trace_cap))
+    return _fit_dict(res, trace)
+
+
+def ssb_fit(handle: int, trials, options=None, trace_cap: int = 4096, stream=None) -> dict:
+    """Batch of host trials [n][3], then refinement from the best one (see ssb.h)."""
+    lib = load_library()
+    p = _params(trials)
+    res = ssb_fit_result()
+    trace = np.zeros((trace_cap, 4), dtype=np.float64)
+    opt = _fit_options(options)
+    _check(lib.ssb_fit(handle, p.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), p.shape[0], ctypes.byref(opt),
+                       ctypes.byref(res), trace.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), trace_cap,
+                       _stream(stream)))
+    return _fit_dict(res, trace)

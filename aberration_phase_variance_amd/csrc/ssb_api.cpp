@@ -291,6 +291,15 @@ int run_moments(ssb_handle* h, const float* params, int n_trials, int64_t b_begi
 
 }  // namespace
 
+namespace ssb {
+// Shared with the fit driver (ssb_fit.cpp): the thread-local error text.
+int set_error(int code, const std::string& msg) {
+    g_err = msg;
+    return code;
+}
+void clear_error() { g_err.clear(); }
+}  // namespace ssb
+
 extern "C" {
 
 const char* ssb_last_error(void) { return g_err.c_str(); }

@@ -178,6 +178,7 @@ def main():
     log(f"[bench] object {object_ms:.3f} ms")
 
     batch_ms_per_trial = None
+    fit = None
     if args.batch > 0:
         bp = trial_params(w, args.batch)
         ssb.ssb_loss(h, bp[:2])
@@ -185,6 +186,15 @@ def main():
         bl = ssb.ssb_loss(h, bp)
         batch_ms_per_trial = (time.perf_counter() - t1) * 1e3 / args.batch
         log(f"[bench] batch of {args.batch}: {batch_ms_per_trial:.3f} ms/trial")
+        # the whole fit: the same batch, then Nelder-Mead refinement from its best trial
+        t1 = time.perf_counter()
+        fr = ssb.ssb_fit(h, bp)
+        fit_ms = (time.perf_counter() - t1) * 1e3
+        fit = {"ms": fit_ms, "trials": args.batch, "refine_evals": fr["evals"], "refine_requests": fr["requests"],
+               "converged": bool(fr["converged"]), "batch_best": fr["batch_best"], "batch_loss": fr["batch_loss"],
+               "best": fr["best"], "loss": fr["loss"], "true": list(w.true_params)}
+        log(f"[bench] fit: {fit_ms:.1f} ms ({args.batch} trials + {fr['evals']} refinement evaluations), "
+            f"best {[round(v, 3) for v in fr['best']]} loss {fr['loss']:.9f}")
 
     # roofline of the dominant stage: algorithmic bytes (or FLOPs) per launch / average launch time
     share = info["support_entries"] / (info["n_bf"] * n * (n // 2 + 1))
@@ -273,6 +283,7 @@ def main():
         "object_ms": object_ms,
         "batch_trials": args.batch,
         "batch_ms_per_trial": batch_ms_per_trial,
+        "fit": fit,
         "prepare_ms": prepare_ms,
         "stage_ms_per_launch": {k: round(v, 4) for k, v in stage_ms.items()},
         "support_share": share,

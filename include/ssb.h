@@ -182,6 +182,66 @@ typedef struct ssb_profile_data {
  */
 int ssb_profile(ssb_handle* h, int mode, ssb_profile_data* out);
 
+/*
+ * Aberration fit: a batch of trial parameter sets, then Nelder-Mead refinement of
+ * the exact loss from the batch's best trial (Notes page, "MPS wider
+ * exact-simplex checkpoint" and "Final exact MPS optimizer handoff": axis steps of
+ * 5% of each starting value with floors of 2 nm on C12 and 0.04 rad on phi12,
+ * rounded to two decimals; stop when the simplex's loss spread is at most fatol
+ * and its coordinate spread at most xatol; a request whose float32 inputs equal an
+ * earlier evaluation's reuses that loss instead of evaluating again).
+ *
+ * The simplex moves are the standard ones: reflection 1, expansion 2, outside and
+ * inside contraction 1/2, shrink 1/2 towards the best vertex; vertices are kept
+ * sorted by loss (ties keep their order).
+ */
+typedef struct ssb_fit_options {
+    double fatol;          /* loss spread tolerance (default 3e-6) */
+    double xatol;          /* coordinate spread tolerance, max over the three coordinates (default 0.1) */
+    double step_frac;      /* initial axis step as a fraction of the start value (default 0.05) */
+    double step_floor[3];  /* minimum |step| per axis: C10 nm, C12 nm, phi12 rad (default 0.01, 2.0, 0.04) */
+    int32_t max_evals;     /* cap on physical loss evaluations in the refinement, 0 = none */
+    int32_t max_iter;      /* cap on simplex iterations, 0 = 600 */
+} ssb_fit_options;
+
+typedef struct ssb_fit_result {
+    double best[3];        /* refined (C10 nm, C12 nm, phi12 rad) as the simplex holds them */
+    double loss;           /* exact loss at float32(best) */
+    int32_t batch_best;    /* index of the batch trial the refinement started from (first minimum) */
+    int32_t requests;      /* loss requests made by the simplex */
+    int32_t evals;         /* physical evaluations among them (the rest were memoized) */
+    int32_t iterations;    /* simplex iterations */
+    int32_t converged;     /* 1 if the tolerances were met, 0 if a cap stopped it */
+    int32_t pad;
+    double batch_loss;     /* loss of that batch trial */
+} ssb_fit_result;
+
+/* Loss of one float32 parameter triple, for ssb_nelder_mead.  Returns the loss;
+ * a non-finite value aborts the minimization with SSB_EINVAL. */
+typedef double (*ssb_objective)(const float* params3, void* ctx);
+
+/*
+ * ssb_nelder_mead: the refinement above on any objective (host only).
+ *   x0      HOST double[3] start.
+ *   opt     options (NULL = defaults).
+ *   f, ctx  objective; called once per distinct float32 triple.
+ *   res     result (batch_best = -1, batch_loss = the start's loss).
+ *   trace   optional HOST double [trace_cap][4]: (float32 C10, C12, phi12, loss) of
+ *           each physical evaluation in order; the count is res->evals.
+ * Errors: SSB_EINVAL (null argument, non-finite start or objective value).
+ */
+int ssb_nelder_mead(const double* x0, const ssb_fit_options* opt, ssb_objective f, void* ctx,
+                    ssb_fit_result* res, double* trace, int32_t trace_cap);
+
+/*
+ * ssb_fit: evaluate the HOST float trials [n_trials][3] as one batch (ssb_loss),
+ * then refine from the first trial with the lowest loss with ssb_nelder_mead on
+ * ssb_loss.  trace as above (refinement evaluations only).  Synchronizes the stream.
+ * Errors: those of ssb_loss and ssb_nelder_mead.
+ */
+int ssb_fit(ssb_handle* h, const float* trials, int32_t n_trials, const ssb_fit_options* opt,
+            ssb_fit_result* res, double* trace, int32_t trace_cap, void* stream);
+
 /* ssb_query: fill *info.  Errors: SSB_EINVAL. */
 int ssb_query(const ssb_handle* h, ssb_info* info);
 

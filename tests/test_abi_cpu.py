@@ -44,7 +44,8 @@ def test_struct_layout_matches_header(tmp_path):
     if cc is None:
         pytest.skip("no C compiler")
     structs = {"ssb_geometry": ssb._ssb.ssb_geometry, "ssb_info": ssb._ssb.ssb_info,
-               "ssb_profile_data": ssb._ssb.ssb_profile_data}
+               "ssb_profile_data": ssb._ssb.ssb_profile_data, "ssb_fit_options": ssb._ssb.ssb_fit_options,
+               "ssb_fit_result": ssb._ssb.ssb_fit_result}
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "ssb.h"', 'int main(void) {']
     for name, cls in structs.items():
         lines.append(f'printf("{name} size %zu\\n", sizeof({name}));')

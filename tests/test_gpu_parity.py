@@ -282,6 +282,28 @@ def test_vacuum_counts(params):
         p.release()
 
 
+def test_fit_small(small):
+    """Batch + refinement through ssb_fit: the batch's best trial is the oracle's, the
+    refinement's first evaluation repeats it bitwise, sampled refinement points match
+    the oracle, and the returned loss is the lowest evaluated."""
+    w, counts, p = small
+    g = O.OGeom.from_any(w.geometry)
+    dc = O.dc_value(counts)
+    trials = trial_params(w, 16)
+    _say("[fit] ssb_fit small, 16 trials + refinement capped at 24 evaluations")
+    r = ssb.ssb_fit(p.h, trials, {"max_evals": 24})
+    ref = np.array([O.loss(g, counts, t, dc) for t in trials])
+    assert r["batch_best"] == int(np.argmin(ref))
+    assert _rel(r["batch_loss"], ref.min()) <= LOSS_RTOL
+    t = r["trace"]
+    assert r["evals"] == t.shape[0] and 4 < r["evals"] <= 24 and r["requests"] >= r["evals"]
+    np.testing.assert_array_equal(t[0, :3], trials[r["batch_best"]])
+    assert t[0, 3] == r["batch_loss"]                  # single-trial call = batch call, bitwise
+    assert r["loss"] == t[:, 3].min()
+    for i in sorted({1, int(np.argmin(t[:, 3])), t.shape[0] - 1}):
+        assert _rel(t[i, 3], O.loss(g, counts, t[i, :3].astype(np.float32), dc)) <= LOSS_RTOL, i
+
+
 def test_inactive_bf_pixels():
     """Probe aperture smaller than the BF disk: zero-aperture BF keep phase 0 but count in n_bf."""
     w = WORKLOADS["tiny"]
