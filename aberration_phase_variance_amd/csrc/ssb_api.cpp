@@ -70,6 +70,7 @@ struct ssb_handle {
     unsigned long long* bfsum = nullptr;
     uint4* sup = nullptr;      // correction support intervals [n_bf][N/2+1]
     int* vend = nullptr;       // 1 + last supported column per BF [n_bf]
+    float2* tw = nullptr;      // FFT twiddle tables: inverse sign, then forward sign
     int64_t support_entries = 0, columns_written = 0, columns_read = 0;
     // loss / moments workspace
     char* ws = nullptr;
@@ -277,7 +278,7 @@ int run_moments(ssb_handle* h, const float* params, int n_trials, int64_t b_begi
         {
             StageTimer tm(h, SSB_STAGE_PASS2, st, units);
             SSB_HIP(launch_pass2(h->n, im, in, pl.cap, h->active, h->vend, c0, cb, n_trials, h->dc, ps1, ps2,
-                                 pl.gcap, st),
+                                 pl.gcap, h->tw, st),
                     "pass 2 launch");
         }
         {
@@ -392,9 +393,14 @@ int ssb_prepare(const ssb_geometry* g, const uint32_t* counts, int64_t n_bf, voi
         (e = hipMemcpyAsync(h->active, act.data(), act.size(), hipMemcpyHostToDevice, st)) != hipSuccess ||
         (e = hipMemsetAsync(h->bfsum, 0, n_bf * sizeof(unsigned long long), st)) != hipSuccess)
         return cleanup(hip_fail(e, "prepare upload"));
-    if ((e = launch_g_rows(n, counts, n_bf, h->gm, h->gn, h->bfsum, st)) != hipSuccess)
+    const int ntw = twiddle_count(n);
+    if ((e = hipMalloc(&h->tw, 2 * (size_t)ntw * sizeof(float2))) != hipSuccess)
+        return cleanup(hip_fail(e, "allocation"));
+    if ((e = launch_twiddles(n, h->tw, h->tw + ntw, st)) != hipSuccess)
+        return cleanup(hip_fail(e, "twiddle tables"));
+    if ((e = launch_g_rows(n, counts, n_bf, h->gm, h->gn, h->bfsum, h->tw + ntw, st)) != hipSuccess)
         return cleanup(hip_fail(e, "spectrum row pass"));
-    if ((e = launch_g_cols(n, h->gm, h->gn, n_bf, st)) != hipSuccess)
+    if ((e = launch_g_cols(n, h->gm, h->gn, n_bf, h->tw + ntw, st)) != hipSuccess)
         return cleanup(hip_fail(e, "spectrum column pass"));
     if ((e = hipMalloc(&h->sup, (size_t)n_bf * (n / 2 + 1) * sizeof(uint4))) != hipSuccess ||
         (e = hipMalloc(&h->vend, (size_t)n_bf * sizeof(int))) != hipSuccess)
@@ -513,10 +519,11 @@ int ssb_object(ssb_handle* h, const float* params3, float* phase, float* psi, vo
     {
         StageTimer tm(h, SSB_STAGE_OBJ_FFT, st, 0);
         SSB_HIP(launch_obj_reduce(n, part, nseg, pm, pn, st), "object reduce");
-        SSB_HIP(launch_obj_cols(n, pm, pn, st), "object columns");
+        SSB_HIP(launch_obj_cols(n, pm, pn, h->tw, st), "object columns");
         const double dcsum = h->dc * (double)h->n_bf;
         const double scale = 1.0 / ((double)h->n_bf * (double)n * (double)n);
-        SSB_HIP(launch_obj_rows(n, pm, pn, dcsum, scale, phase, reinterpret_cast<float2*>(psi), st), "object rows");
+        SSB_HIP(launch_obj_rows(n, pm, pn, dcsum, scale, phase, reinterpret_cast<float2*>(psi), h->tw, st),
+                "object rows");
     }
     return SSB_OK;
 }
@@ -603,6 +610,7 @@ void ssb_release(ssb_handle* h) {
     (void)hipFree(h->bfsum);
     (void)hipFree(h->sup);
     (void)hipFree(h->vend);
+    (void)hipFree(h->tw);
     (void)hipFree(h->ws);
     (void)hipFree(h->ows);
     for (auto& r : h->prof_pending) {

@@ -130,6 +130,20 @@ struct WaveFFT {
         }
     }
 
+    // The same twiddles read from a table in global memory laid out as WaveFFTT's
+    // (filled once with WaveFFTT<N, SIGN>::fill): no transcendentals per workgroup.
+    __device__ __forceinline__ void load(const float2* __restrict__ tab, int j) {
+        int ns = R, base = 0;
+#pragma unroll
+        for (int p = 1; p < P; ++p) {
+            const int k = j & (ns - 1);
+#pragma unroll
+            for (int r = 1; r < R; ++r) tw[p - 1][r - 1] = tab[base + (r - 1) * ns + k];
+            base += (R - 1) * ns;
+            ns *= R;
+        }
+    }
+
     // In-place transform of the group's values; buf holds N complex values private
     // to this group (clobbered).
     __device__ __forceinline__ void run(float2 (&x)[R], float2* buf, int j) const {

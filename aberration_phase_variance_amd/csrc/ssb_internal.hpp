@@ -36,9 +36,14 @@ struct GeomDev {
 
 // Launchers (defined in ssb_kernels.hip).  All return the hipError_t of the
 // launch; grids are chunked internally to keep every dimension in range.
+// FFT twiddle tables (inverse and forward sign, twiddle_count(n) entries each),
+// filled once per handle; the transforms below read their twiddles from them
+// (pass 1 computes its own: measured faster there).
+int twiddle_count(int n);
+hipError_t launch_twiddles(int n, float2* tw_inv, float2* tw_fwd, hipStream_t st);
 hipError_t launch_g_rows(int n, const uint32_t* counts, int64_t nbf, float2* gm, float2* gn,
-                         unsigned long long* bfsum, hipStream_t st);
-hipError_t launch_g_cols(int n, float2* gm, float2* gn, int64_t nbf, hipStream_t st);
+                         unsigned long long* bfsum, const float2* tw_fwd, hipStream_t st);
+hipError_t launch_g_cols(int n, float2* gm, float2* gn, int64_t nbf, const float2* tw_fwd, hipStream_t st);
 
 // Pass 1: correction + column inverse transforms of the BF chunk [bf0, bf0 + cb)
 // for n_trials trials into the intermediate (main [t][cap][N][H], nyq [t][cap][N]).
@@ -51,7 +56,7 @@ hipError_t launch_pass1(int n, const float2* gm, const float2* gn, const float2*
 // Pass 2: row transforms, atan2 and moments, one partial per 32-BF group.
 hipError_t launch_pass2(int n, const float2* im, const float2* in, int cap, const uint8_t* active,
                         const int* vend, int64_t bf0, int cb, int n_trials, double dc, float* part_s1,
-                        double* part_s2, int gcap, hipStream_t st);
+                        double* part_s2, int gcap, const float2* tw_inv, hipStream_t st);
 // Correction support per (BF, column) from the geometry: sup [n_bf][N/2+1] of four
 // packed (lo, len) row intervals (minus/plus aperture, nonzero weight / flat top),
 // vend [n_bf] = 1 + the last column with any support (0 for an inactive BF), and
@@ -74,8 +79,8 @@ hipError_t launch_obj_sum(int n, const float2* gm, const float2* gn, const doubl
                           hipStream_t st);
 hipError_t launch_obj_reduce(int n, const double2* part, int nseg, float2* pm, float2* pn,
                              hipStream_t st);
-hipError_t launch_obj_cols(int n, float2* pm, float2* pn, hipStream_t st);
+hipError_t launch_obj_cols(int n, float2* pm, float2* pn, const float2* tw_inv, hipStream_t st);
 hipError_t launch_obj_rows(int n, const float2* pm, const float2* pn, double dcsum, double scale,
-                           float* phase, float2* psi, hipStream_t st);
+                           float* phase, float2* psi, const float2* tw_inv, hipStream_t st);
 
 }  // namespace ssb

@@ -35,9 +35,6 @@ namespace {
 #ifndef SSB_PASS2_MIN_WAVES
 #define SSB_PASS2_MIN_WAVES 1 // pass-2 register budget hint: minimum resident waves per SIMD
 #endif
-#ifndef SSB_PASS2_TW_LDS
-#define SSB_PASS2_TW_LDS 1    // pass-2 FFT twiddles from an LDS table instead of registers
-#endif
 #ifndef SSB_PASS2_PREFETCH
 #define SSB_PASS2_PREFETCH 0  // pass 2 loads the next BF's column values during the current transform
 #endif
@@ -197,7 +194,7 @@ __device__ __forceinline__ float atan2_f(float y, float x) {
 // is read before any store).
 template <int N, int MODE>
 __global__ __launch_bounds__(256) void k_cols(const float2* in_m, const float2* in_n, float2* out_m,
-                                              float2* out_n) {
+                                              float2* out_n, const float2* __restrict__ twt) {
     constexpr int H = N / 2;
     constexpr int LD = N + kPad;
     constexpr int SIGN = (MODE == COL_PLAIN_FWD) ? -1 : 1;
@@ -226,7 +223,7 @@ __global__ __launch_bounds__(256) void k_cols(const float2* in_m, const float2* 
     const int j = lane % F::L;
     constexpr int NG = 4 * F::W;
     F fft;
-    fft.init(j);
+    fft.load(twt, j);
     const int ncols = nyq ? 1 : kTC;
     for (int c = grp; c < ncols; c += NG) {
         float2 x[F::R];
@@ -322,6 +319,12 @@ __global__ __launch_bounds__(256) void k_vend(const uint4* __restrict__ sup, con
     nsup[b] = ns;
 }
 
+// Twiddle table of the wave-level FFT (WaveFFTT layout), filled once per handle.
+template <int N, int SIGN>
+__global__ __launch_bounds__(256) void k_twiddles(float2* __restrict__ tab) {
+    WaveFFTT<N, SIGN>::fill(tab, threadIdx.x, 256);
+}
+
 // Per-BF phase slopes of delta = v alpha + u' beta (revolutions).
 __device__ __forceinline__ void delta_slopes(double kx, double ky, const TrialConst& m, const GeomDev& g,
                                              double& alpha, double& beta) {
@@ -389,6 +392,110 @@ __device__ __forceinline__ float2 correct_entry(float2 g, float2 ch, float2 e, b
 // thread keeps one column).
 constexpr int kPass1Threads = SSB_PASS1_THREADS;
 
+// One pass-1 tile; NYQ selects the Nyquist column at compile time so that every
+// row index, LDS address and load offset of the unrolled entry loops is a
+// compile-time step from the thread's first row.
+template <int N, int TC, bool NYQ>
+__device__ __forceinline__ void pass1_tile(const float2* __restrict__ gsrc, const float2* __restrict__ chsrc,
+                                           const double2 k, const uint4 sr, const TrialConst& m, const GeomDev& geo,
+                                           float2* __restrict__ out, float2* tile, float2* eu, int v0) {
+    constexpr int H = N / 2;
+    constexpr int LD = N + 16 / TC;           // row pitch: the 16 lanes of one b64 LDS cycle hit distinct banks
+    constexpr int NT = kPass1Threads;
+    constexpr int RS = NYQ ? NT : NT / TC;    // rows per sweep
+    constexpr int PM = (N + RS - 1) / RS;     // entries per thread
+    constexpr int SSTRIDE = NYQ ? 1 : H;      // row stride of the source plane
+    static_assert(PM <= 16, "two support bits per entry in one 32-bit word");
+    using F = WaveFFT<N, +1>;
+
+    const int tid = threadIdx.x;
+    const int c = NYQ ? 0 : tid % TC;
+    const int v = v0 + c;
+    const int ustart = NYQ ? tid : tid / TC;
+    double alpha, beta;
+    delta_slopes(k.x, k.y, m, geo, alpha, beta);
+    for (int u = tid; u < N; u += NT) eu[u] = phasor_rev_neg((double)(u < H ? u : u - N) * beta);
+    const float2 ev = phasor_rev_neg((double)v * alpha);
+    const int lo_m = unpack_lo(sr.x), len_m = unpack_len(sr.x);
+    const int lo_p = unpack_lo(sr.y), len_p = unpack_len(sr.y);
+
+    // 1. support and loads into registers (all loads in flight together)
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(gsrc, (NYQ ? N : N * H) * 8);
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(chsrc, (NYQ ? N : N * H) * 8);
+    const int off0 = (ustart * SSTRIDE + (NYQ ? 0 : v)) * 8;
+    float2 gv[PM], chv[PM];
+    unsigned bits = 0;
+#pragma unroll
+    for (int i = 0; i < PM; ++i) {
+        const int u = ustart + i * RS;
+        // on a main tile u < N always, and with two or more sweeps u < H exactly for i < PM/2
+        const int up = (NYQ || RS > H) ? (u < H ? u : u - N) : (i < PM / 2 ? u : u - N);
+        const bool inm = (unsigned)(up - lo_m) < (unsigned)len_m;
+        const bool inp = (unsigned)(up - lo_p) < (unsigned)len_p;
+        const bool on = (NYQ ? u < N : true) && (inm || inp) && (u != 0 || v != 0);
+        const int off = on ? off0 + i * RS * SSTRIDE * 8 : kNoLoad;
+        gv[i] = load_or_zero(rg, off);
+        chv[i] = load_or_zero(rc, off);
+        bits |= on ? ((inm ? 1u : 0u) | (inp ? 2u : 0u)) << (2 * i) : 0u;
+    }
+    __syncthreads();                              // E_u complete
+
+    // 2. correction into the LDS tile
+    const int flo_m = unpack_lo(sr.z), flen_m = unpack_len(sr.z);
+    const int flo_p = unpack_lo(sr.w), flen_p = unpack_len(sr.w);
+    float2* trow = tile + c * LD + ustart;
+    const float2* erow = eu + ustart;
+#pragma unroll
+    for (int i = 0; i < PM; ++i) {
+        const int u = ustart + i * RS;
+        if (NYQ ? u < N : true) {
+            float2 val = make_float2(0.f, 0.f);
+            const unsigned f = (bits >> (2 * i)) & 3u;
+            if (f) {
+                const int up = (NYQ || RS > H) ? (u < H ? u : u - N) : (i < PM / 2 ? u : u - N);
+                const bool inm = f & 1u, inp = f & 2u;
+                const bool edm = inm && (unsigned)(up - flo_m) >= (unsigned)flen_m;
+                const bool edp = inp && (unsigned)(up - flo_p) >= (unsigned)flen_p;
+                val = correct_entry(gv[i], chv[i], cmul(erow[i * RS], ev), inm, inp, edm, edp, up, v, k.x, k.y,
+                                    geo);
+            }
+            trow[i * RS] = val;
+        }
+    }
+    __syncthreads();
+
+    // 3. column transforms.  The twiddles are computed here rather than loaded
+    // from the shared table: loaded at this point their latency is exposed, loaded
+    // early they hold registers through the correction (both measured slower),
+    // while this arithmetic fills issue slots of waves waiting on memory.
+    const int lane = tid & 63;
+    const int grp = (tid >> 6) * F::W + lane / F::L;
+    const int j = lane % F::L;
+    constexpr int NG = (NT / 64) * F::W;
+    constexpr int NCOLS = NYQ ? 1 : TC;
+    F fft;
+    fft.init(j);
+    for (int cc = grp; cc < NCOLS; cc += NG) {
+        float2 x[F::R];
+#pragma unroll
+        for (int r = 0; r < F::R; ++r) x[r] = tile[cc * LD + j + r * F::L];
+        fft.run(x, &tile[cc * LD], j);
+        wave_lds_fence();
+#pragma unroll
+        for (int r = 0; r < F::R; ++r) tile[cc * LD + j + r * F::L] = x[r];
+    }
+    __syncthreads();
+
+    // 4. store (out: the plane's first row at this tile's column, or the Nyquist column)
+    if (!NYQ) {
+        float2* om = out + c;
+#pragma unroll 4
+        for (int y = ustart; y < N; y += RS) om[(int64_t)y * H] = tile[c * LD + y];
+    } else {
+        for (int y = tid; y < N; y += NT) out[y] = tile[y];
+    }
+}
+
 template <int N, int TC>
 __global__ __launch_bounds__(kPass1Threads) void k_pass1(const float2* __restrict__ gm,
                                                          const float2* __restrict__ gn,
@@ -401,18 +508,10 @@ __global__ __launch_bounds__(kPass1Threads) void k_pass1(const float2* __restric
                                                          int64_t bf0, int cap, float2* __restrict__ im,
                                                          float2* __restrict__ in) {
     constexpr int H = N / 2;
-    constexpr int LD = N + 16 / TC;           // row pitch: the 16 lanes of one b64 LDS cycle hit distinct banks
-    constexpr int NT = kPass1Threads;
-    constexpr int RS = NT / TC;                   // rows per sweep of the main-tile mapping
-    constexpr int PER = (N + RS - 1) / RS;        // entries per thread on a main tile (rows u < N)
-    constexpr int PERN = (N + NT - 1) / NT;       // entries per thread on the Nyquist tile
-    constexpr int PM = PER > PERN ? PER : PERN;
-    static_assert(PM <= 16, "two support bits per entry in one 32-bit word");
-    using F = WaveFFT<N, +1>;
+    constexpr int LD = N + 16 / TC;
     __shared__ float2 tile[TC * LD];
     __shared__ float2 eu[N];
 
-    const int tid = threadIdx.x;
     const int t = blockIdx.y;
     // Workgroup -> (BF, tile): the H/TC main tiles of a BF, then its Nyquist tile.
     // (Giving the two tiles that share 128-byte rows ids 8 apart, so that they run
@@ -424,91 +523,15 @@ __global__ __launch_bounds__(kPass1Threads) void k_pass1(const float2* __restric
     const bool nyq = tix == NTM;
     const int v0 = nyq ? H : tix * TC;
     if (v0 >= vend[b]) return;                    // all-zero columns (every column of an inactive BF)
-    const int c = nyq ? 0 : tid % TC;
-    const int v = v0 + c;
-    const int ustart = nyq ? tid : tid / TC;
-    const int ustep = nyq ? NT : RS;
-    const int nent = nyq ? PERN : PER;
     const double2 k = kb[b];
     const TrialConst m = tc[t];
-    double alpha, beta;
-    delta_slopes(k.x, k.y, m, geo, alpha, beta);
-    for (int u = tid; u < N; u += NT) eu[u] = phasor_rev_neg((double)(u < H ? u : u - N) * beta);
-    const float2 ev = phasor_rev_neg((double)v * alpha);
-    const uint4 sr = sup[b * (H + 1) + v];
-    const int lo_m = unpack_lo(sr.x), len_m = unpack_len(sr.x);
-    const int lo_p = unpack_lo(sr.y), len_p = unpack_len(sr.y);
-
-    // 1. support and loads into registers (all loads in flight together)
-    const __amdgpu_buffer_rsrc_t rg = nyq ? make_rsrc(gn + b * N, N * 8) : make_rsrc(gm + b * N * H, N * H * 8);
-    const __amdgpu_buffer_rsrc_t rc =
-        nyq ? make_rsrc(chn + (int64_t)t * N, N * 8) : make_rsrc(chm + (int64_t)t * N * H, N * H * 8);
-    const int sstride = nyq ? 1 : H;
-    const int vcol = nyq ? 0 : v;
-    float2 gv[PM], chv[PM];
-    unsigned bits = 0;
-#pragma unroll
-    for (int i = 0; i < PM; ++i) {
-        const int u = ustart + i * ustep;
-        const int up = u < H ? u : u - N;
-        const bool inm = (unsigned)(up - lo_m) < (unsigned)len_m;
-        const bool inp = (unsigned)(up - lo_p) < (unsigned)len_p;
-        const bool on = i < nent && u < N && (inm || inp) && (u != 0 || v != 0);
-        const int off = on ? (u * sstride + vcol) * 8 : kNoLoad;
-        gv[i] = load_or_zero(rg, off);
-        chv[i] = load_or_zero(rc, off);
-        bits |= on ? ((inm ? 1u : 0u) | (inp ? 2u : 0u)) << (2 * i) : 0u;
-    }
-    __syncthreads();                              // E_u complete
-
-    // 2. correction into the LDS tile
-    const int flo_m = unpack_lo(sr.z), flen_m = unpack_len(sr.z);
-    const int flo_p = unpack_lo(sr.w), flen_p = unpack_len(sr.w);
-#pragma unroll
-    for (int i = 0; i < PM; ++i) {
-        const int u = ustart + i * ustep;
-        if (i < nent && u < N) {
-            float2 val = make_float2(0.f, 0.f);
-            const unsigned f = (bits >> (2 * i)) & 3u;
-            if (f) {
-                const int up = u < H ? u : u - N;
-                const bool inm = f & 1u, inp = f & 2u;
-                const bool edm = inm && (unsigned)(up - flo_m) >= (unsigned)flen_m;
-                const bool edp = inp && (unsigned)(up - flo_p) >= (unsigned)flen_p;
-                val = correct_entry(gv[i], chv[i], cmul(eu[u], ev), inm, inp, edm, edp, up, v, k.x, k.y, geo);
-            }
-            tile[c * LD + u] = val;
-        }
-    }
-    __syncthreads();
-
-    // 3. column transforms
-    const int lane = tid & 63;
-    const int grp = (tid >> 6) * F::W + lane / F::L;
-    const int j = lane % F::L;
-    constexpr int NG = (NT / 64) * F::W;
-    F fft;
-    fft.init(j);
-    const int ncols = nyq ? 1 : TC;
-    for (int cc = grp; cc < ncols; cc += NG) {
-        float2 x[F::R];
-#pragma unroll
-        for (int r = 0; r < F::R; ++r) x[r] = tile[cc * LD + j + r * F::L];
-        fft.run(x, &tile[cc * LD], j);
-        wave_lds_fence();
-#pragma unroll
-        for (int r = 0; r < F::R; ++r) tile[cc * LD + j + r * F::L] = x[r];
-    }
-    __syncthreads();
-
-    // 4. store
     if (!nyq) {
-        float2* om = im + ((int64_t)t * cap + bl) * N * H + v;
-#pragma unroll 4
-        for (int y = ustart; y < N; y += RS) om[(int64_t)y * H] = tile[c * LD + y];
+        const int v = v0 + (int)threadIdx.x % TC;
+        pass1_tile<N, TC, false>(gm + b * N * H, chm + (int64_t)t * N * H, k, sup[b * (H + 1) + v], m, geo,
+                                 im + ((int64_t)t * cap + bl) * N * H + v0, tile, eu, v0);
     } else {
-        float2* on = in + ((int64_t)t * cap + bl) * N;
-        for (int y = tid; y < N; y += NT) on[y] = tile[y];
+        pass1_tile<N, TC, true>(gn + b * N, chn + (int64_t)t * N, k, sup[b * (H + 1) + H], m, geo,
+                                in + ((int64_t)t * cap + bl) * N, tile, eu, v0);
     }
 }
 
@@ -591,13 +614,11 @@ __global__ __launch_bounds__(256, SSB_PASS2_MIN_WAVES) void k_pass2(const float2
                                                int cap, const uint8_t* __restrict__ active,
                                                const int* __restrict__ vend, int64_t bf0,
                                                int cb, float dcf, float* __restrict__ part_s1,
-                                               double* __restrict__ part_s2, int gcap) {
-#if SSB_PASS2_TW_LDS
+                                               double* __restrict__ part_s2, int gcap,
+                                               const float2* __restrict__ gtw) {
+    // FFT twiddles from an LDS copy of the table (not registers: 4 waves per SIMD)
     using F = WaveFFTT<N, +1>;
     __shared__ float2 twt[F::TABLE];
-#else
-    using F = WaveFFT<N, +1>;
-#endif
     constexpr int H = N / 2;
     constexpr int R = F::R, L = F::L;
     __shared__ float2 buf[4 * F::W][N];
@@ -615,12 +636,8 @@ __global__ __launch_bounds__(256, SSB_PASS2_MIN_WAVES) void k_pass2(const float2
     const int b_hi = min(cb, b_lo + kGroupBF);
 
     F fft;
-#if SSB_PASS2_TW_LDS
-    F::fill(twt, tid, 256);
+    for (int e = tid; e < F::TABLE; e += 256) twt[e] = gtw[e];
     __syncthreads();
-#else
-    fft.init(j);
-#endif
     float s1a[R], s1b[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -654,11 +671,7 @@ __global__ __launch_bounds__(256, SSB_PASS2_MIN_WAVES) void k_pass2(const float2
 #endif
         float2 x[R];
         cur.assemble(j, x);
-#if SSB_PASS2_TW_LDS
         fft.run(x, buf[grp], j, twt);
-#else
-        fft.run(x, buf[grp], j);
-#endif
         const float den0 = dcf + cur.z0.x + sgn * cur.h0.x;
         const float den1 = dcf + cur.z1.x + sgn * cur.h1.x;
         float p2 = 0.f;
@@ -793,7 +806,8 @@ __global__ __launch_bounds__(64) void k_loss(const double* __restrict__ lpart, c
 template <int N>
 __global__ __launch_bounds__(256) void k_g_rows(const uint32_t* __restrict__ counts, int64_t b0,
                                                 float2* __restrict__ gm, float2* __restrict__ gn,
-                                                unsigned long long* __restrict__ bfsum) {
+                                                unsigned long long* __restrict__ bfsum,
+                                                const float2* __restrict__ twt) {
     constexpr int H = N / 2;
     using F = WaveFFT<N, -1>;
     constexpr int R = F::R, L = F::L;
@@ -817,7 +831,7 @@ __global__ __launch_bounds__(256) void k_g_rows(const uint32_t* __restrict__ cou
         x[r] = make_float2((float)i0, (float)i1);
     }
     F fft;
-    fft.init(j);
+    fft.load(twt, j);
     fft.run(x, buf[grp], j);
     wave_lds_fence();
 #pragma unroll
@@ -986,7 +1000,7 @@ __global__ __launch_bounds__(256) void k_obj_reduce(const double2* __restrict__ 
 template <int N>
 __global__ __launch_bounds__(256) void k_obj_rows(const float2* __restrict__ pm, const float2* __restrict__ pn,
                                                   float dcs, float scale, float* __restrict__ phase,
-                                                  float2* __restrict__ psi) {
+                                                  float2* __restrict__ psi, const float2* __restrict__ twt) {
     constexpr int H = N / 2;
     using F = WaveFFT<N, +1>;
     constexpr int R = F::R, L = F::L;
@@ -1001,7 +1015,7 @@ __global__ __launch_bounds__(256) void k_obj_rows(const float2* __restrict__ pm,
     float2 x[R];
     raw.assemble(j, x);
     F fft;
-    fft.init(j);
+    fft.load(twt, j);
     fft.run(x, buf[grp], j);
     const float sgn = (j & 1) ? -1.f : 1.f;
     const float den0 = dcs + raw.z0.x + sgn * raw.h0.x;
@@ -1025,10 +1039,10 @@ int row_blocks() {
 
 template <int N>
 hipError_t g_rows_n(const uint32_t* counts, int64_t nbf, float2* gm, float2* gn, unsigned long long* bfsum,
-                    hipStream_t st) {
+                    const float2* tw, hipStream_t st) {
     for (int64_t b0 = 0; b0 < nbf; b0 += 65535) {
         const int nb = (int)std::min<int64_t>(65535, nbf - b0);
-        hipLaunchKernelGGL(k_g_rows<N>, dim3(row_blocks<N>(), nb), dim3(256), 0, st, counts, b0, gm, gn, bfsum);
+        hipLaunchKernelGGL(k_g_rows<N>, dim3(row_blocks<N>(), nb), dim3(256), 0, st, counts, b0, gm, gn, bfsum, tw);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -1037,12 +1051,12 @@ hipError_t g_rows_n(const uint32_t* counts, int64_t nbf, float2* gm, float2* gn,
 
 template <int N, int MODE>
 hipError_t cols_n(const float2* in_m, const float2* in_n, float2* out_m, float2* out_n, int64_t planes,
-                  hipStream_t st) {
+                  const float2* tw, hipStream_t st) {
     constexpr int H = N / 2;
     for (int64_t p0 = 0; p0 < planes; p0 += 65535) {
         const int np = (int)std::min<int64_t>(65535, planes - p0);
         hipLaunchKernelGGL((k_cols<N, MODE>), dim3(H / kTC + 1, np), dim3(256), 0, st, in_m + p0 * N * H,
-                           in_n + p0 * N, out_m + p0 * N * H, out_n + p0 * N);
+                           in_n + p0 * N, out_m + p0 * N * H, out_n + p0 * N, tw);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -1096,12 +1110,35 @@ hipError_t support_n(const double2* kb, const uint8_t* active, GeomDev geo, int6
     }
 
 hipError_t launch_g_rows(int n, const uint32_t* counts, int64_t nbf, float2* gm, float2* gn,
-                         unsigned long long* bfsum, hipStream_t st) {
-    SSB_DISPATCH_N(n, (g_rows_n<NN>(counts, nbf, gm, gn, bfsum, st)))
+                         unsigned long long* bfsum, const float2* tw_fwd, hipStream_t st) {
+    SSB_DISPATCH_N(n, (g_rows_n<NN>(counts, nbf, gm, gn, bfsum, tw_fwd, st)))
 }
 
-hipError_t launch_g_cols(int n, float2* gm, float2* gn, int64_t nbf, hipStream_t st) {
-    SSB_DISPATCH_N(n, (cols_n<NN, COL_PLAIN_FWD>(gm, gn, gm, gn, nbf, st)))
+hipError_t launch_g_cols(int n, float2* gm, float2* gn, int64_t nbf, const float2* tw_fwd, hipStream_t st) {
+    SSB_DISPATCH_N(n, (cols_n<NN, COL_PLAIN_FWD>(gm, gn, gm, gn, nbf, tw_fwd, st)))
+}
+
+int twiddle_count(int n) {
+    switch (n) {
+        case 32: return WaveFFTT<32, 1>::TABLE;
+        case 64: return WaveFFTT<64, 1>::TABLE;
+        case 128: return WaveFFTT<128, 1>::TABLE;
+        case 256: return WaveFFTT<256, 1>::TABLE;
+        default: return WaveFFTT<512, 1>::TABLE;
+    }
+}
+
+template <int N>
+static hipError_t twiddles_n(float2* tw_inv, float2* tw_fwd, hipStream_t st) {
+    hipLaunchKernelGGL((k_twiddles<N, 1>), dim3(1), dim3(256), 0, st, tw_inv);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_twiddles<N, -1>), dim3(1), dim3(256), 0, st, tw_fwd);
+    return hipGetLastError();
+}
+
+hipError_t launch_twiddles(int n, float2* tw_inv, float2* tw_fwd, hipStream_t st) {
+    SSB_DISPATCH_N(n, (twiddles_n<NN>(tw_inv, tw_fwd, st)))
 }
 
 hipError_t launch_chiq(int n, const TrialConst* tc, int n_trials, GeomDev geo, float2* chm, float2* chn,
@@ -1128,17 +1165,18 @@ int pass2_row_blocks(int n) {
 template <int N>
 static hipError_t pass2_n(const float2* im, const float2* in, int cap, const uint8_t* active, const int* vend,
                           int64_t bf0, int cb, int n_trials, double dc, float* part_s1, double* part_s2, int gcap,
-                          hipStream_t st) {
+                          const float2* tw, hipStream_t st) {
     const int ng = (cb + kGroupBF - 1) / kGroupBF;
     hipLaunchKernelGGL(k_pass2<N>, dim3(row_blocks<N>(), ng, n_trials), dim3(256), 0, st, im, in, cap, active,
-                       vend, bf0, cb, (float)dc, part_s1, part_s2, gcap);
+                       vend, bf0, cb, (float)dc, part_s1, part_s2, gcap, tw);
     return hipGetLastError();
 }
 
 hipError_t launch_pass2(int n, const float2* im, const float2* in, int cap, const uint8_t* active,
                         const int* vend, int64_t bf0, int cb, int n_trials, double dc, float* part_s1,
-                        double* part_s2, int gcap, hipStream_t st) {
-    SSB_DISPATCH_N(n, (pass2_n<NN>(im, in, cap, active, vend, bf0, cb, n_trials, dc, part_s1, part_s2, gcap, st)))
+                        double* part_s2, int gcap, const float2* tw_inv, hipStream_t st) {
+    SSB_DISPATCH_N(n, (pass2_n<NN>(im, in, cap, active, vend, bf0, cb, n_trials, dc, part_s1, part_s2, gcap, tw_inv,
+                                   st)))
 }
 
 hipError_t launch_support(int n, const double2* kb, const uint8_t* active, GeomDev geo, int64_t nbf, uint4* sup,
@@ -1212,21 +1250,21 @@ hipError_t launch_obj_reduce(int n, const double2* part, int nseg, float2* pm, f
     SSB_DISPATCH_N(n, (obj_reduce_n<NN>(part, nseg, pm, pn, st)))
 }
 
-hipError_t launch_obj_cols(int n, float2* pm, float2* pn, hipStream_t st) {
-    SSB_DISPATCH_N(n, (cols_n<NN, COL_PLAIN_INV>(pm, pn, pm, pn, 1, st)))
+hipError_t launch_obj_cols(int n, float2* pm, float2* pn, const float2* tw_inv, hipStream_t st) {
+    SSB_DISPATCH_N(n, (cols_n<NN, COL_PLAIN_INV>(pm, pn, pm, pn, 1, tw_inv, st)))
 }
 
 template <int N>
 static hipError_t obj_rows_n(const float2* pm, const float2* pn, double dcsum, double scale, float* phase,
-                             float2* psi, hipStream_t st) {
+                             float2* psi, const float2* tw, hipStream_t st) {
     hipLaunchKernelGGL(k_obj_rows<N>, dim3(row_blocks<N>()), dim3(256), 0, st, pm, pn, (float)dcsum, (float)scale,
-                       phase, psi);
+                       phase, psi, tw);
     return hipGetLastError();
 }
 
 hipError_t launch_obj_rows(int n, const float2* pm, const float2* pn, double dcsum, double scale, float* phase,
-                           float2* psi, hipStream_t st) {
-    SSB_DISPATCH_N(n, (obj_rows_n<NN>(pm, pn, dcsum, scale, phase, psi, st)))
+                           float2* psi, const float2* tw_inv, hipStream_t st) {
+    SSB_DISPATCH_N(n, (obj_rows_n<NN>(pm, pn, dcsum, scale, phase, psi, tw_inv, st)))
 }
 
 }  // namespace ssb
