@@ -130,6 +130,29 @@ struct WaveFFT {
         }
     }
 
+    // The same twiddles for radix 8 from three sincospi per pass (r = 1, 2, 4) and
+    // complex products for r = 3, 5, 6, 7 (two roundings more on those).
+    __device__ __forceinline__ void init_products(int j) {
+        static_assert(R == 8, "radix-8 products");
+        int ns = R;
+#pragma unroll
+        for (int p = 1; p < P; ++p) {
+            const int k = j & (ns - 1);
+            float2 w1, w2, w4;
+            sincospif((float)(SIGN * 2 * k) / (float)(ns * R), &w1.y, &w1.x);
+            sincospif((float)(SIGN * 4 * k) / (float)(ns * R), &w2.y, &w2.x);
+            sincospif((float)(SIGN * 8 * k) / (float)(ns * R), &w4.y, &w4.x);
+            tw[p - 1][0] = w1;
+            tw[p - 1][1] = w2;
+            tw[p - 1][2] = cmul(w1, w2);
+            tw[p - 1][3] = w4;
+            tw[p - 1][4] = cmul(w4, w1);
+            tw[p - 1][5] = cmul(w4, w2);
+            tw[p - 1][6] = cmul(w4, tw[p - 1][2]);
+            ns *= R;
+        }
+    }
+
     // The same twiddles read from a table in global memory laid out as WaveFFTT's
     // (filled once with WaveFFTT<N, SIGN>::fill): no transcendentals per workgroup.
     __device__ __forceinline__ void load(const float2* __restrict__ tab, int j) {

@@ -467,14 +467,16 @@ __device__ __forceinline__ void pass1_tile(const float2* __restrict__ gsrc, cons
     // 3. column transforms.  The twiddles are computed here rather than loaded
     // from the shared table: loaded at this point their latency is exposed, loaded
     // early they hold registers through the correction (both measured slower),
-    // while this arithmetic fills issue slots of waves waiting on memory.
+    // while this arithmetic fills issue slots of waves waiting on memory.  For
+    // radix 8 only r = 1, 2, 4 take a sincospi; r = 3, 5, 6, 7 are their products.
     const int lane = tid & 63;
     const int grp = (tid >> 6) * F::W + lane / F::L;
     const int j = lane % F::L;
     constexpr int NG = (NT / 64) * F::W;
     constexpr int NCOLS = NYQ ? 1 : TC;
     F fft;
-    fft.init(j);
+    if constexpr (F::R == 8) fft.init_products(j);   // radix 8: three sincospi per pass, the rest products
+    else fft.init(j);
     for (int cc = grp; cc < NCOLS; cc += NG) {
         float2 x[F::R];
 #pragma unroll
