@@ -3,11 +3,13 @@
 The Python layer is a thin ctypes binding with the C ABI's names; all computation runs
 in libssb.so.  Build it with ``python -m aberration_phase_variance_amd.build``.
 """
-from ._ssb import (EXPORTS, FIT_DEFAULTS, LIB_PATH, SSBError, load_library, make_geometry, ssb_fit,
+from ._ssb import (EXPORTS, FIT_DEFAULTS, LIB_PATH, SSBError, load_library, make_geometry, ssb_detector_sum,
+                   ssb_fit, ssb_fit_probe, ssb_gather_bf,
                    ssb_geometry, ssb_info, ssb_last_error, ssb_loss, ssb_moments, ssb_nelder_mead, ssb_object,
                    ssb_prepare, ssb_query, ssb_release, ssb_set_chunk, ssb_spectrum, ssb_profile, SSB_STAGES)
 
-__all__ = ["EXPORTS", "FIT_DEFAULTS", "LIB_PATH", "SSBError", "load_library", "make_geometry", "ssb_fit",
+__all__ = ["EXPORTS", "FIT_DEFAULTS", "LIB_PATH", "SSBError", "load_library", "make_geometry", "ssb_detector_sum",
+           "ssb_fit", "ssb_fit_probe", "ssb_gather_bf",
            "ssb_geometry", "ssb_info", "ssb_last_error", "ssb_loss", "ssb_moments", "ssb_nelder_mead",
            "ssb_object", "ssb_prepare", "ssb_query", "ssb_release", "ssb_set_chunk", "ssb_spectrum",
            "ssb_profile", "SSB_STAGES"]

@@ -96,8 +96,21 @@ SSB_OBJECTIVE = ctypes.CFUNCTYPE(ctypes.c_double, ctypes.POINTER(ctypes.c_float)
 FIT_DEFAULTS = {"fatol": 3e-6, "xatol": 0.1, "step_frac": 0.05, "step_floor": (0.01, 2.0, 0.04),
                 "max_evals": 0, "max_iter": 0}
 
+class ssb_probe_fit(ctypes.Structure):
+    _fields_ = [
+        ("det_cy", ctypes.c_double),
+        ("det_cx", ctypes.c_double),
+        ("bf_r2", ctypes.c_double),
+        ("threshold", ctypes.c_double),
+        ("n_disk", ctypes.c_int64),
+        ("n_bf", ctypes.c_int64),
+        ("n_zero", ctypes.c_int64),
+    ]
+
+
 EXPORTS = ("ssb_prepare", "ssb_loss", "ssb_moments", "ssb_object", "ssb_spectrum", "ssb_set_chunk",
-           "ssb_profile", "ssb_query", "ssb_release", "ssb_last_error", "ssb_nelder_mead", "ssb_fit")
+           "ssb_profile", "ssb_query", "ssb_release", "ssb_last_error", "ssb_nelder_mead", "ssb_fit",
+           "ssb_detector_sum", "ssb_fit_probe", "ssb_gather_bf")
 
 _lib = None
 
@@ -128,6 +141,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                     ctypes.POINTER(ssb_fit_result), dp, i32]
     lib.ssb_fit.argtypes = [vp, fp, i32, ctypes.POINTER(ssb_fit_options), ctypes.POINTER(ssb_fit_result), dp, i32,
                             vp]
+    lib.ssb_detector_sum.argtypes = [vp, i32, i32, vp, vp]
+    lib.ssb_fit_probe.argtypes = [ctypes.POINTER(ctypes.c_uint64), i32, i32, ctypes.POINTER(ssb_probe_fit)]
+    lib.ssb_gather_bf.argtypes = [vp, ctypes.POINTER(ssb_geometry), vp, i64, vp]
     for name in EXPORTS:
         if name not in ("ssb_release", "ssb_last_error"):
             getattr(lib, name).restype = ctypes.c_int
@@ -280,3 +296,23 @@ def ssb_fit(handle: int, trials, options=None, trace_cap: int = 4096, stream=Non
                        ctypes.byref(res), trace.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), trace_cap,
                        _stream(stream)))
     return _fit_dict(res, trace)
+
+
+def ssb_detector_sum(frames, scan_n: int, det_n: int, sums, stream=None) -> None:
+    """sums (device uint64 [det_n^2]) = exact sum of the device uint32 frames [scan_n^2][det_n^2]."""
+    _check(load_library().ssb_detector_sum(_ptr(frames), int(scan_n), int(det_n), _ptr(sums), _stream(stream)))
+
+
+def ssb_fit_probe(sums, scan_n: int, det_n: int) -> dict:
+    """Probe-disk fit from host sums (array-like of uint64, det_n^2 values)."""
+    s = np.ascontiguousarray(np.asarray(sums, dtype=np.uint64).reshape(-1))
+    out = ssb_probe_fit()
+    _check(load_library().ssb_fit_probe(s.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)), int(scan_n), int(det_n),
+                                        ctypes.byref(out)))
+    return {name: getattr(out, name) for name, _ in ssb_probe_fit._fields_}
+
+
+def ssb_gather_bf(frames, geometry, counts, n_bf: int, stream=None) -> None:
+    """counts (device uint32 [n_bf][N][N]) = the BF pixels of the device frames, BF-major."""
+    g = make_geometry(geometry)
+    _check(load_library().ssb_gather_bf(_ptr(frames), ctypes.byref(g), _ptr(counts), int(n_bf), _stream(stream)))

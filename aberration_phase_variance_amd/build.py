@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libssb.so")
-SOURCES = ["ssb_kernels.hip", "ssb_api.cpp", "ssb_fit.cpp"]
+SOURCES = ["ssb_kernels.hip", "ssb_api.cpp", "ssb_fit.cpp", "ssb_detector.hip"]
 ARCH = "gfx950"
 
 

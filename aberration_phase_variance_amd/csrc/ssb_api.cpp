@@ -14,6 +14,19 @@
 
 using namespace ssb;
 
+namespace ssb {
+bool in_bf_disk(const ssb_geometry* g, int i, int j);
+}
+
+namespace {
+// |k|^2 < hi2 with the squares rounded separately (the oracle's rounding).
+bool active_pixel(double di, double dj, double hi2) {
+#pragma clang fp contract(off)
+    const double a = di * di, b = dj * dj;
+    return a + b < hi2;
+}
+}  // namespace
+
 namespace {
 
 thread_local std::string g_err;
@@ -293,6 +306,15 @@ int run_moments(ssb_handle* h, const float* params, int n_trials, int64_t b_begi
 }  // namespace
 
 namespace ssb {
+// BF rule: (i - cy)^2 + (j - cx)^2 <= bf_r2, squares rounded separately and then
+// added (no fused multiply-add), which is also the rounding of the oracle.
+bool in_bf_disk(const ssb_geometry* g, int i, int j) {
+#pragma clang fp contract(off)
+    const double di = i - g->det_cy, dj = j - g->det_cx;
+    const double a = di * di, b = dj * dj;
+    return a + b <= g->bf_r2;
+}
+
 // Shared with the fit driver (ssb_fit.cpp): the thread-local error text.
 int set_error(int code, const std::string& msg) {
     g_err = msg;
@@ -330,9 +352,9 @@ int ssb_prepare(const ssb_geometry* g, const uint32_t* counts, int64_t n_bf, voi
     for (int i = 0; i < g->det_n; ++i)
         for (int j = 0; j < g->det_n; ++j) {
             const double di = i - g->det_cy, dj = j - g->det_cx;
-            if (di * di + dj * dj <= g->bf_r2) {
+            if (ssb::in_bf_disk(g, i, j)) {
                 kb.push_back(make_double2(dj, di));
-                act.push_back(dj * dj + di * di < hi2 ? 1 : 0);
+                act.push_back(active_pixel(di, dj, hi2) ? 1 : 0);
             }
         }
     if ((int64_t)kb.size() != n_bf)

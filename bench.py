@@ -93,6 +93,8 @@ def main():
     ap.add_argument("--config", default="full", choices=["tiny", "small", "medium", "full"])
     ap.add_argument("--batch", type=int, default=200, help="trials in the batched measurement (0 = skip)")
     ap.add_argument("--cpu-sample-bf", type=int, default=1024, help="BF pixels in the oracle CPU sample (0 = skip)")
+    ap.add_argument("--detector", type=int, default=1,
+                    help="also time the detector side on full frames (detector sum, probe fit, BF gather); 0 = skip")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB device-to-device copy (3x) as a known-size reference "
                          "for hardware byte counters")
@@ -259,6 +261,47 @@ def main():
         log(f"[bench] oracle {cpu_s:.1f} s; S2 rel err {oracle_check['s2_rel_err']:.2e}")
 
     ssb.ssb_release(h)
+    del counts
+    torch.cuda.empty_cache()
+
+    detector = None
+    if args.detector:
+        import dataclasses
+
+        from synth import make_frames_torch
+        log(f"[bench] generating {w.name} detector frames ({n * n} x {g.det_n}^2)")
+        frames = make_frames_torch(w, dev)
+        torch.cuda.synchronize()
+        d2 = g.det_n * g.det_n
+        sums = torch.empty(d2, dtype=torch.int64, device=dev)
+        ssb.ssb_detector_sum(frames, n, g.det_n, sums)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 5
+        e0.record()
+        for _ in range(reps):
+            ssb.ssb_detector_sum(frames, n, g.det_n, sums)      # the library's null stream = torch's current
+        e1.record()
+        torch.cuda.synchronize()
+        sum_ms = e0.elapsed_time(e1) / reps
+        fit = ssb.ssb_fit_probe(sums.cpu().numpy().view(np.uint64), n, g.det_n)
+        geom = dataclasses.replace(g, det_cy=fit["det_cy"], det_cx=fit["det_cx"], bf_r2=fit["bf_r2"])
+        bfc = torch.empty((fit["n_bf"], n, n), dtype=torch.int32, device=dev)
+        ssb.ssb_gather_bf(frames, geom, bfc, fit["n_bf"])
+        t1 = time.perf_counter()
+        for _ in range(3):
+            ssb.ssb_gather_bf(frames, geom, bfc, fit["n_bf"])   # synchronizes
+        gather_ms = (time.perf_counter() - t1) * 1e3 / 3
+        frame_bytes = n * n * d2 * 4
+        detector = {"frames": [n * n, d2], "frame_bytes": frame_bytes,
+                    "detector_sum_ms": sum_ms, "detector_sum_gbs": frame_bytes / sum_ms / 1e6,
+                    "detector_sum_hbm_frac": round(frame_bytes / sum_ms / 1e6 / PEAK_HBM_GBS, 4),
+                    "fit": fit, "gather_ms_host_clock": gather_ms,
+                    "gather_gbs": 2 * fit["n_bf"] * n * n * 4 / gather_ms / 1e6}
+        log(f"[bench] detector sum {sum_ms:.3f} ms ({detector['detector_sum_gbs']:.0f} GB/s), fit n_bf "
+            f"{fit['n_bf']} r^2 {fit['bf_r2']:.2f}, gather {gather_ms:.3f} ms")
+        del frames, bfc, sums
+        torch.cuda.empty_cache()
+
     value = samples * args.steps / total_s
     pages_rate = samples / (PAGES_MS * 1e-3) if args.config == "full" else None
     line = {
@@ -291,6 +334,7 @@ def main():
         "other_stage": stages_roofline,
         "hbm": hbm,
         "cpu_baseline": cpu,
+        "detector": detector,
         "oracle_check": oracle_check,
     }
     print(json.dumps(line), flush=True)

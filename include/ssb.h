@@ -183,6 +183,58 @@ typedef struct ssb_profile_data {
 int ssb_profile(ssb_handle* h, int mode, ssb_profile_data* out);
 
 /*
+ * Detector side, before ssb_prepare: the mean diffraction pattern as an exact
+ * integer detector sum over every scan frame, the probe-disk fit that selects the
+ * BF pixels, and the gather of those pixels into BF-major counts (Notes page,
+ * sections "Cross-backend and native-size validation notes": mean diffraction
+ * pattern, mean-plus-standard-deviation probe fit and disk crop on the device;
+ * "Automatic full-probe MPS optimizer": the fitted center and radius select the
+ * positive-count pixels of the disk; "Automatic-probe detector-sum reduction":
+ * exact integer sums from frame-block partials).
+ *
+ * Frames are DEVICE uint32 [scan_n * scan_n][det_n * det_n]: frame y * scan_n + x
+ * is the whole detector at scan position (y, x), row-major (row i, column j).
+ */
+
+/*
+ * ssb_detector_sum: sums[p] = sum over all frames of frame[p], exact (uint64).
+ *   frames  DEVICE uint32 frames as above (only read).
+ *   sums    DEVICE uint64 [det_n * det_n], overwritten.
+ * Asynchronous on the stream.  Errors: SSB_EINVAL (null or host pointer,
+ * scan_n < 1 or det_n < 1), SSB_EDEVICE.
+ */
+int ssb_detector_sum(const uint32_t* frames, int32_t scan_n, int32_t det_n, uint64_t* sums, void* stream);
+
+typedef struct ssb_probe_fit {
+    double det_cy, det_cx;  /* disk center: unweighted centroid of the mask (pixels) */
+    double bf_r2;           /* disk radius squared: mask area / pi (pixels^2) */
+    double threshold;       /* mean + population std of the mean pattern over all pixels */
+    int64_t n_disk;         /* mask pixels: mean pattern strictly above the threshold */
+    int64_t n_bf;           /* pixels with (i-cy)^2 + (j-cx)^2 <= bf_r2 and a positive sum */
+    int64_t n_zero;         /* pixels inside that disk with a zero sum (not BF) */
+} ssb_probe_fit;
+
+/*
+ * ssb_fit_probe: the probe-disk fit on the host from HOST sums [det_n * det_n]
+ * (ssb_detector_sum's output copied back); the mean pattern is sums / scan_n^2.
+ * The BF set is the disk rule of ssb_geometry with (det_cy, det_cx, bf_r2) from
+ * the fit when n_zero is 0 (then n_bf is what ssb_prepare expects).
+ * Errors: SSB_EINVAL (null, sizes < 1, no pixel above the threshold).
+ */
+int ssb_fit_probe(const uint64_t* sums, int32_t scan_n, int32_t det_n, ssb_probe_fit* out);
+
+/*
+ * ssb_gather_bf: BF-major counts [n_bf][scan_n][scan_n] (the layout ssb_prepare
+ * takes, BF pixels in row-major detector order by the geometry's disk rule) from
+ * the DEVICE frames.  counts is a DEVICE buffer, overwritten.  Only scan_n, det_n,
+ * det_cy, det_cx and bf_r2 of the geometry are used.  Synchronizes the stream
+ * (a temporary device list of the BF pixels is freed before returning).
+ * Errors: SSB_EINVAL (null or host pointer, bad geometry), SSB_ESHAPE (n_bf differs
+ * from the rule's count), SSB_ENOMEM, SSB_EDEVICE.
+ */
+int ssb_gather_bf(const uint32_t* frames, const ssb_geometry* g, uint32_t* counts, int64_t n_bf, void* stream);
+
+/*
  * Aberration fit: a batch of trial parameter sets, then Nelder-Mead refinement of
  * the exact loss from the batch's best trial (Notes page, "MPS wider
  * exact-simplex checkpoint" and "Final exact MPS optimizer handoff": axis steps of

@@ -138,6 +138,56 @@ def make_counts_torch(w: Workload, device, rows_per_chunk: int = 16):
     return counts
 
 
+def make_frames_numpy(w: Workload) -> np.ndarray:
+    """uint32 detector frames [N^2][D^2]: frame y0 N + x0 is the whole D x D detector
+    (fftshifted, row-major) at scan position (y0, x0); same forward model as the BF
+    counts, Poisson draws over every detector pixel (rows y0, then x0, then pixel)."""
+    g = w.geometry
+    n, d = g.scan_n, g.det_n
+    t = np.exp(1j * w.object_strength * object_phase(w))
+    probe = probe_window(w)
+    r = _window_offsets(d)
+    rng = np.random.Generator(np.random.PCG64(w.poisson_seed))
+    frames = np.empty((n * n, d * d), dtype=np.uint32)
+    x0 = np.arange(n)
+    cols = (x0[:, None] + r[None, :]) % n
+    for y0 in range(n):
+        rows = (y0 + r) % n
+        patch = t[rows][:, cols]                               # (D, N, D)
+        det = np.fft.fft2(probe[:, None, :] * patch, axes=(0, 2))
+        inten = np.fft.fftshift(np.abs(det) ** 2, axes=(0, 2))  # detector order
+        draws = rng.poisson(w.dose * inten.transpose(1, 0, 2).reshape(n, d * d))
+        frames[y0 * n:(y0 + 1) * n] = draws.astype(np.uint32)
+    return frames
+
+
+def make_frames_torch(w: Workload, device, rows_per_chunk: int = 8):
+    """The frames on a torch device (complex64 model, seeded torch generator); int32
+    tensor [N^2][D^2] holding the uint32 counts."""
+    import torch
+
+    g = w.geometry
+    n, d = g.scan_n, g.det_n
+    t = torch.from_numpy(np.exp(1j * w.object_strength * object_phase(w)).astype(np.complex64)).to(device)
+    probe = torch.from_numpy(probe_window(w).astype(np.complex64)).to(device)
+    r = torch.from_numpy(_window_offsets(d)).to(device)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(w.poisson_seed)
+    frames = torch.empty((n * n, d * d), dtype=torch.int32, device=device)
+    x0 = torch.arange(n, device=device)
+    cols = (x0[:, None] + r[None, :]) % n
+    for y_start in range(0, n, rows_per_chunk):
+        ys = torch.arange(y_start, min(n, y_start + rows_per_chunk), device=device)
+        rows = (ys[:, None] + r[None, :]) % n
+        patch = t[rows[:, None, :, None], cols[None, :, None, :]]   # (Y, N, D, D)
+        det = torch.fft.fft2(probe[None, None] * patch)
+        inten = torch.fft.fftshift(det.abs().square(), dim=(2, 3)).reshape(ys.numel() * n, d * d)
+        draws = torch.poisson(w.dose * inten.double(), generator=gen)
+        frames[y_start * n:(y_start + ys.numel()) * n] = draws.to(torch.int32)
+        del patch, det, inten, draws
+    return frames
+
+
 def _cache_dir() -> str:
     return os.environ.get("SSB_SYNTH_CACHE", os.path.join("/tmp", "ssb_synth_cache"))
 

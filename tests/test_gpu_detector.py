@@ -1,0 +1,119 @@
+"""GPU parity of the detector side (ssb_detector_sum, ssb_gather_bf) and of the whole
+automatic-BF chain (frames -> detector sum -> probe fit -> gather -> prepare -> loss)
+against the detector oracle and the loss oracle.  Integer results are bit-exact."""
+import dataclasses
+import sys
+
+import numpy as np
+import pytest
+
+import aberration_phase_variance_amd as ssb
+from oracle import ssb_detector as OD
+from oracle import ssb_oracle as O
+from synth import WORKLOADS, make_frames_numpy
+
+pytestmark = pytest.mark.gpu
+
+
+def _torch():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a visible GPU")
+    return torch
+
+
+def _say(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def _dev_u32(t, arr):
+    return t.from_numpy(np.ascontiguousarray(arr).view(np.int32)).cuda()
+
+
+def _sums(t, frames_dev, n, d):
+    s = t.empty(d * d, dtype=t.int64, device="cuda")
+    ssb.ssb_detector_sum(frames_dev, n, d, s)
+    t.cuda.synchronize()
+    return s.cpu().numpy().view(np.uint64)
+
+
+@pytest.fixture(scope="module")
+def small_frames():
+    w = WORKLOADS["small"]
+    return w, make_frames_numpy(w)
+
+
+def test_detector_sum_exact(small_frames):
+    t = _torch()
+    w, frames = small_frames
+    g = w.geometry
+    _say("[detector] sum, small frames")
+    got = _sums(t, _dev_u32(t, frames), g.scan_n, g.det_n)
+    np.testing.assert_array_equal(got, OD.detector_sum(frames))
+
+
+@pytest.mark.parametrize("n,d", [(40, 15), (16, 8)])
+def test_detector_sum_large_values(n, d):
+    """Values near 2^32 (sums beyond 32 bits) and a pixel count that is not a multiple
+    of four (the one-pixel-per-lane path)."""
+    t = _torch()
+    rng = np.random.default_rng(n * d)
+    frames = rng.integers(0, 2 ** 32, size=(n * n, d * d), dtype=np.uint64).astype(np.uint32)
+    frames[:, 0] = 2 ** 32 - 1
+    got = _sums(t, _dev_u32(t, frames), n, d)
+    np.testing.assert_array_equal(got, OD.detector_sum(frames))
+
+
+def test_gather_exact(small_frames):
+    t = _torch()
+    w, frames = small_frames
+    g = w.geometry
+    sums = OD.detector_sum(frames)
+    fit = OD.fit_probe(sums, g.scan_n, g.det_n)
+    geom = dataclasses.replace(g, det_cy=fit["cy"], det_cx=fit["cx"], bf_r2=fit["bf_r2"])
+    bi, bj = OD.bf_pixels(sums.reshape(g.det_n, g.det_n), fit["cy"], fit["cx"], fit["bf_r2"])
+    ref = OD.gather_bf(frames, g.scan_n, g.det_n, bi, bj)
+    out = t.empty((bi.size, g.scan_n, g.scan_n), dtype=t.int32, device="cuda")
+    ssb.ssb_gather_bf(_dev_u32(t, frames), geom, out, bi.size)
+    np.testing.assert_array_equal(out.cpu().numpy().view(np.uint32), ref)
+    with pytest.raises(ssb.SSBError) as e:
+        ssb.ssb_gather_bf(_dev_u32(t, frames), geom, out, bi.size + 1)
+    assert e.value.code == ssb._ssb.SSB_ESHAPE
+
+
+def test_automatic_bf_chain(small_frames):
+    """Frames to loss with the fitted BF disk, every step in the library, against the
+    oracle chain on the same frames."""
+    t = _torch()
+    w, frames = small_frames
+    g = w.geometry
+    _say("[detector] automatic BF chain, small")
+    fdev = _dev_u32(t, frames)
+    sums = _sums(t, fdev, g.scan_n, g.det_n)
+    fit = ssb.ssb_fit_probe(sums, g.scan_n, g.det_n)
+    assert fit["n_zero"] == 0
+    geom = dataclasses.replace(g, det_cy=fit["det_cy"], det_cx=fit["det_cx"], bf_r2=fit["bf_r2"])
+    counts = t.empty((fit["n_bf"], g.scan_n, g.scan_n), dtype=t.int32, device="cuda")
+    ssb.ssb_gather_bf(fdev, geom, counts, fit["n_bf"])
+    h = ssb.ssb_prepare(geom, counts, fit["n_bf"])
+    try:
+        ofit = OD.fit_probe(OD.detector_sum(frames), g.scan_n, g.det_n)
+        og = O.OGeom.from_any(dataclasses.replace(g, det_cy=ofit["cy"], det_cx=ofit["cx"], bf_r2=ofit["bf_r2"]))
+        bi, bj = O.bf_indices(og)
+        assert bi.size == fit["n_bf"]
+        ocounts = OD.gather_bf(frames, g.scan_n, g.det_n, bi, bj)
+        for params in ([40.0, 5.0, 0.3], [-20.0, 5.0, 0.3]):
+            got = ssb.ssb_loss(h, [params])[0]
+            ref = O.loss(og, ocounts, params)
+            assert abs(got - ref) <= 1e-5 * abs(ref), (params, got, ref)
+    finally:
+        ssb.ssb_release(h)
+
+
+def test_detector_errors():
+    t = _torch()
+    s = t.empty(64, dtype=t.int64, device="cuda")
+    host = np.zeros((16, 64), dtype=np.uint32)
+    with pytest.raises(ssb.SSBError) as e:
+        ssb.ssb_detector_sum(host.ctypes.data, 4, 8, s)
+    assert e.value.code == ssb._ssb.SSB_EINVAL
