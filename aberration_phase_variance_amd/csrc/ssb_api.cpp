@@ -560,9 +560,12 @@ int ssb_spectrum(const ssb_handle* h, int64_t bf, float* out, void* stream) {
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int n = h->n, hh = h->h;
     float2* o = reinterpret_cast<float2*>(out);
-    SSB_HIP(hipMemcpy2DAsync(o, sizeof(float2) * (hh + 1), h->gm + (size_t)bf * n * hh, sizeof(float2) * hh,
-                             sizeof(float2) * hh, n, hipMemcpyDeviceToDevice, st),
-            "copy spectrum");
+    // the cache is tile-major ([N/2/8][N][8] per BF): one strided copy per 8-column tile
+    for (int tile = 0; tile < hh / kTileW; ++tile)
+        SSB_HIP(hipMemcpy2DAsync(o + tile * kTileW, sizeof(float2) * (hh + 1),
+                                 h->gm + (size_t)bf * n * hh + (size_t)tile * n * kTileW, sizeof(float2) * kTileW,
+                                 sizeof(float2) * kTileW, n, hipMemcpyDeviceToDevice, st),
+                "copy spectrum");
     SSB_HIP(hipMemcpy2DAsync(o + hh, sizeof(float2) * (hh + 1), h->gn + (size_t)bf * n, sizeof(float2),
                              sizeof(float2), n, hipMemcpyDeviceToDevice, st),
             "copy spectrum");

@@ -19,6 +19,15 @@ struct TrialConst {
 };
 
 // Geometry as the kernels see it.
+// Half-plane layout of the spectrum cache, the per-trial chi_q table, the column
+// results and the object's plane: the columns v < N/2 in tiles of kTileW,
+// [tile][row u][kTileW] (one tile of one plane is N * kTileW contiguous complex
+// values); the Nyquist column v = N/2 is a separate [N] array.
+constexpr int kTileW = 8;
+__host__ __device__ constexpr int64_t tm_index(int n, int u, int v) {
+    return ((int64_t)(v / kTileW) * n + u) * kTileW + (v % kTileW);
+}
+
 struct GeomDev {
     int n;            // N
     int h;            // N / 2

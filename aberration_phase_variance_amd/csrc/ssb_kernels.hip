@@ -1,11 +1,13 @@
 // HIP kernels of the SSB phase-variance path for gfx950.
 //
 // Layouts (complex64 = float2):
-//   G cache        main [n_bf][N][N/2]   (v = 0 .. N/2-1), nyq [n_bf][N]   (v = N/2)
-//   intermediate   main [trial][cap][N][N/2],             nyq [trial][cap][N]
+//   G cache        main [n_bf][N/2/8][N][8]   (v = 0 .. N/2-1 in tiles of 8 columns),
+//                  nyq [n_bf][N]              (v = N/2)
+//   intermediate   main [trial][cap][N/2/8][N][8],  nyq [trial][cap][N]
 //   S1 partials    float [trial][gcap][N][N] (one image per 32-BF group)
-// Splitting the Nyquist column off keeps every main row a power-of-two run of
-// complex values (2 KiB at N = 512), so rows and column tiles stay aligned.
+// The tile-major main planes make one 8-column tile of one BF pixel a contiguous
+// 32 KiB block at N = 512 (the unit pass 1 reads and writes), and two consecutive
+// rows of a tile share one 128-byte line (the unit pass 2 reads).
 //
 // The per-BF 2-D inverse transform follows the two-pass structure the pages
 // describe (Checkpoints page, "fftA intermediate and M5 hardware floor": a
@@ -26,9 +28,6 @@ namespace ssb {
 namespace {
 
 // Compile-time tuning constants.
-#ifndef SSB_PASS1_TC
-#define SSB_PASS1_TC 8        // pass-1 columns per workgroup at N = 512
-#endif
 #ifndef SSB_PASS1_THREADS
 #define SSB_PASS1_THREADS 256 // pass-1 workgroup size
 #endif
@@ -212,7 +211,7 @@ __global__ __launch_bounds__(256) void k_cols(const float2* in_m, const float2* 
 
     if (!nyq) {
         const int c = tid % kTC;
-        for (int u = tid / kTC; u < N; u += 256 / kTC) tile[c * LD + u] = pin_m[(int64_t)u * H + v0 + c];
+        for (int u = tid / kTC; u < N; u += 256 / kTC) tile[c * LD + u] = pin_m[tm_index(N, u, v0 + c)];
     } else {
         for (int u = tid; u < N; u += 256) tile[u] = pin_n[u];
     }
@@ -238,14 +237,14 @@ __global__ __launch_bounds__(256) void k_cols(const float2* in_m, const float2* 
 
     if (!nyq) {
         const int c = tid % kTC;
-        for (int y = tid / kTC; y < N; y += 256 / kTC) pout_m[(int64_t)y * H + v0 + c] = tile[c * LD + y];
+        for (int y = tid / kTC; y < N; y += 256 / kTC) pout_m[tm_index(N, y, v0 + c)] = tile[c * LD + y];
     } else {
         for (int y = tid; y < N; y += 256) pout_n[y] = tile[y];
     }
 }
 
 // exp(i chi_q) = (cos, sin)(2 pi q^T M q) of every half-plane entry, per trial
-// (BF independent): main [t][N][N/2], nyq [t][N].
+// (BF independent): main [t] x tile-major [N/2/8][N][8], nyq [t][N].
 template <int N>
 __global__ __launch_bounds__(256) void k_chiq(const TrialConst* __restrict__ tc, GeomDev geo,
                                               float2* __restrict__ chm, float2* __restrict__ chn) {
@@ -257,7 +256,7 @@ __global__ __launch_bounds__(256) void k_chiq(const TrialConst* __restrict__ tc,
     const int u = e / (H + 1), v = e % (H + 1);
     const double up = (double)(u < H ? u : u - N);
     const float2 val = chi_phasor(fma(geo.qux, up, geo.qvx * v), fma(geo.quy, up, geo.qvy * v), tc[t]);
-    if (v < H) chm[((int64_t)t * N + u) * H + v] = val;
+    if (v < H) chm[(int64_t)t * N * H + tm_index(N, u, v)] = val;
     else chn[(int64_t)t * N + u] = val;
 }
 
@@ -404,7 +403,8 @@ __device__ __forceinline__ void pass1_tile(const float2* __restrict__ gsrc, cons
     constexpr int NT = kPass1Threads;
     constexpr int RS = NYQ ? NT : NT / TC;    // rows per sweep
     constexpr int PM = (N + RS - 1) / RS;     // entries per thread
-    constexpr int SSTRIDE = NYQ ? 1 : H;      // row stride of the source plane
+    constexpr int SSTRIDE = NYQ ? 1 : TC;     // row stride inside the source tile
+    static_assert(NYQ || TC == kTileW, "pass-1 tiles are the layout's tiles");
     static_assert(PM <= 16, "two support bits per entry in one 32-bit word");
     using F = WaveFFT<N, +1>;
 
@@ -420,9 +420,10 @@ __device__ __forceinline__ void pass1_tile(const float2* __restrict__ gsrc, cons
     const int lo_p = unpack_lo(sr.y), len_p = unpack_len(sr.y);
 
     // 1. support and loads into registers (all loads in flight together)
-    const __amdgpu_buffer_rsrc_t rg = make_rsrc(gsrc, (NYQ ? N : N * H) * 8);
-    const __amdgpu_buffer_rsrc_t rc = make_rsrc(chsrc, (NYQ ? N : N * H) * 8);
-    const int off0 = (ustart * SSTRIDE + (NYQ ? 0 : v)) * 8;
+    // gsrc / chsrc: this tile's block (main: [N][TC] tile-major) or the Nyquist column
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(gsrc, N * (NYQ ? 1 : TC) * 8);
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(chsrc, N * (NYQ ? 1 : TC) * 8);
+    const int off0 = (ustart * SSTRIDE + c) * 8;
     float2 gv[PM], chv[PM];
     unsigned bits = 0;
 #pragma unroll
@@ -488,11 +489,11 @@ __device__ __forceinline__ void pass1_tile(const float2* __restrict__ gsrc, cons
     }
     __syncthreads();
 
-    // 4. store (out: the plane's first row at this tile's column, or the Nyquist column)
+    // 4. store (out: this tile's block of the column-result plane, or the Nyquist column)
     if (!NYQ) {
         float2* om = out + c;
 #pragma unroll 4
-        for (int y = ustart; y < N; y += RS) om[(int64_t)y * H] = tile[c * LD + y];
+        for (int y = ustart; y < N; y += RS) om[(int64_t)y * TC] = tile[c * LD + y];
     } else {
         for (int y = tid; y < N; y += NT) out[y] = tile[y];
     }
@@ -529,8 +530,9 @@ __global__ __launch_bounds__(kPass1Threads) void k_pass1(const float2* __restric
     const TrialConst m = tc[t];
     if (!nyq) {
         const int v = v0 + (int)threadIdx.x % TC;
-        pass1_tile<N, TC, false>(gm + b * N * H, chm + (int64_t)t * N * H, k, sup[b * (H + 1) + v], m, geo,
-                                 im + ((int64_t)t * cap + bl) * N * H + v0, tile, eu, v0);
+        const int64_t tb = (int64_t)tix * N * TC;        // this tile's block in a plane
+        pass1_tile<N, TC, false>(gm + b * N * H + tb, chm + (int64_t)t * N * H + tb, k, sup[b * (H + 1) + v], m, geo,
+                                 im + ((int64_t)t * cap + bl) * N * H + tb, tile, eu, v0);
     } else {
         pass1_tile<N, TC, true>(gn + b * N, chn + (int64_t)t * N, k, sup[b * (H + 1) + H], m, geo,
                                 in + ((int64_t)t * cap + bl) * N, tile, eu, v0);
@@ -545,27 +547,27 @@ struct RowPairRaw {
     float2 d0[R / 2], d1[R / 2], m0[R / 2], m1[R / 2];
     float2 h0, h1, z0, z1;
 
-    // plane: one BF pixel's column results [N][N/2]; nyqc: its Nyquist column [N].
-    // Columns at or past ve are zero (not written by pass 1) and read as zero
-    // through an out-of-range buffer offset.
+    // plane: one BF pixel's column results (tile-major [N/2/8][N][8]); nyqc: its
+    // Nyquist column [N].  Columns at or past ve are zero (not written by pass 1) and
+    // read as zero through an out-of-range buffer offset.  Row y0 + 1 of a tile
+    // follows row y0 (the same 128-byte line).
     __device__ __forceinline__ void load(const float2* plane, const float2* nyqc, int y0, int j, int ve) {
         constexpr int H = N / 2;
         const __amdgpu_buffer_rsrc_t rp = make_rsrc(plane, N * H * 8);
-        const int row = y0 * H * 8;
 #pragma unroll
         for (int r = 0; r < R / 2; ++r) {
             const int col = j + r * L;
-            const int off = col < ve ? row + col * 8 : kNoLoad;
+            const int off = col < ve ? (int)tm_index(N, y0, col) * 8 : kNoLoad;
             d0[r] = load_or_zero(rp, off);
-            d1[r] = load_or_zero(rp, off + H * 8);
+            d1[r] = load_or_zero(rp, off + kTileW * 8);
         }
 #pragma unroll
         for (int r = 0; r < R / 2; ++r) {
             const int w = H - j - r * L;            // N - (j + (r + R/2) L); w = H only for j = r = 0
             const int ws = w == H ? 0 : w;           // that slot is taken from the Nyquist column below
-            const int off = ws < ve ? row + ws * 8 : kNoLoad;
+            const int off = ws < ve ? (int)tm_index(N, y0, ws) * 8 : kNoLoad;
             m0[r] = load_or_zero(rp, off);
-            m1[r] = load_or_zero(rp, off + H * 8);
+            m1[r] = load_or_zero(rp, off + kTileW * 8);
         }
         const float2 zero = make_float2(0.f, 0.f);
         h0 = zero;
@@ -577,8 +579,8 @@ struct RowPairRaw {
         z0 = zero;
         z1 = zero;
         if (ve > 0) {
-            z0 = plane[y0 * H];
-            z1 = plane[(y0 + 1) * H];
+            z0 = plane[tm_index(N, y0, 0)];
+            z1 = plane[tm_index(N, y0 + 1, 0)];
         }
     }
 
@@ -839,16 +841,17 @@ __global__ __launch_bounds__(256) void k_g_rows(const uint32_t* __restrict__ cou
 #pragma unroll
     for (int r = 0; r < R; ++r) buf[grp][j + r * L] = x[r];
     wave_lds_fence();
-    float2* g0 = gm + (b * N + y0) * H;
-    float2* g1 = g0 + H;
+    float2* g0 = gm + b * N * H;
 #pragma unroll
     for (int r = 0; r < R / 2; ++r) {
         const int v = j + r * L;
         const float2 z = x[r];
         const float2 zm = buf[grp][(N - v) & (N - 1)];
-        // X0 = (Z(v) + conj Z(N-v))/2, X1 = (Z(v) - conj Z(N-v))/(2i)
-        g0[v] = make_float2(0.5f * (z.x + zm.x), 0.5f * (z.y - zm.y));
-        g1[v] = make_float2(0.5f * (z.y + zm.y), -0.5f * (z.x - zm.x));
+        // X0 = (Z(v) + conj Z(N-v))/2, X1 = (Z(v) - conj Z(N-v))/(2i); rows y0, y0 + 1
+        // of a tile are adjacent (one 128-byte line per 8 columns)
+        const int64_t e = tm_index(N, y0, v);
+        g0[e] = make_float2(0.5f * (z.x + zm.x), 0.5f * (z.y - zm.y));
+        g0[e + kTileW] = make_float2(0.5f * (z.y + zm.y), -0.5f * (z.x - zm.x));
     }
     if (j == 0) {
         const float2 z = x[R / 2];            // v = N/2
@@ -895,8 +898,9 @@ __global__ __launch_bounds__(kObjThreads) void k_obj_sum(const float2* __restric
     const int ustart = nyq ? tid : tid / TC;
     const int ustep = nyq ? NT : RS;
     const int nent = nyq ? PERN : PER;
-    const int sstride = nyq ? 1 : H;
-    const int vcol = nyq ? 0 : v;
+    static_assert(TC == kTileW, "object tiles are the layout's tiles");
+    const int sstride = nyq ? 1 : TC;             // row stride inside the tile block
+    const int64_t tb = (int64_t)tix * N * TC;      // this tile's block in a plane
     const int64_t b_lo = (int64_t)blockIdx.y * seglen;
     const int64_t b_hi = min(nbf, b_lo + seglen);
 
@@ -935,7 +939,8 @@ __global__ __launch_bounds__(kObjThreads) void k_obj_sum(const float2* __restric
         const int lo_p = unpack_lo(sr.y), len_p = unpack_len(sr.y);
         const int flo_m = unpack_lo(sr.z), flen_m = unpack_len(sr.z);
         const int flo_p = unpack_lo(sr.w), flen_p = unpack_len(sr.w);
-        const __amdgpu_buffer_rsrc_t rg = nyq ? make_rsrc(gn + b * N, N * 8) : make_rsrc(gm + b * N * H, N * H * 8);
+        const __amdgpu_buffer_rsrc_t rg =
+            nyq ? make_rsrc(gn + b * N, N * 8) : make_rsrc(gm + b * N * H + tb, N * TC * 8);
         float2 gv[PM];
         unsigned bits = 0;
 #pragma unroll
@@ -945,7 +950,7 @@ __global__ __launch_bounds__(kObjThreads) void k_obj_sum(const float2* __restric
             const bool inm = (unsigned)(up - lo_m) < (unsigned)len_m;
             const bool inp = (unsigned)(up - lo_p) < (unsigned)len_p;
             const bool on = i < nent && u < N && (inm || inp) && (u != 0 || v != 0);
-            gv[i] = load_or_zero(rg, on ? (u * sstride + vcol) * 8 : kNoLoad);
+            gv[i] = load_or_zero(rg, on ? (u * sstride + c) * 8 : kNoLoad);
             bits |= on ? ((inm ? 1u : 0u) | (inp ? 2u : 0u)) << (2 * i) : 0u;
         }
         // phase ramps of this BF while its spectrum loads are in flight
@@ -995,7 +1000,7 @@ __global__ __launch_bounds__(256) void k_obj_reduce(const double2* __restrict__ 
     }
     const int u = e / (H + 1), v = e % (H + 1);
     const float2 val = make_float2((float)ax, (float)ay);
-    if (v < H) pm[u * H + v] = val;
+    if (v < H) pm[tm_index(N, u, v)] = val;
     else pn[u] = val;
 }
 
@@ -1065,8 +1070,8 @@ hipError_t cols_n(const float2* in_m, const float2* in_n, float2* out_m, float2*
     return hipSuccess;
 }
 
-// Column tile of pass 1: 16 columns (128-byte rows) for N = 512, 8 otherwise.
-template <int N> constexpr int pass1_tc() { return N >= 512 ? SSB_PASS1_TC : 8; }
+// Column tile of pass 1 and of the object sum: one tile of the tile-major layout.
+template <int N> constexpr int pass1_tc() { return kTileW; }
 
 template <int N>
 hipError_t pass1_n(const float2* gm, const float2* gn, const float2* chm, const float2* chn, const double2* kb,
