@@ -332,8 +332,8 @@ int ssb_prepare(const ssb_geometry* g, const uint32_t* counts, int64_t n_bf, voi
     if (!g || !counts || !out) return fail(SSB_EINVAL, "null argument");
     *out = nullptr;
     const int n = g->scan_n;
-    if (n != 32 && n != 64 && n != 128 && n != 256 && n != 512)
-        return fail(SSB_EINVAL, "scan_n must be a power of two in [32, 512], got %d", n);
+    if (n != 32 && n != 64 && n != 128 && n != 256 && n != 512 && n != 1024)
+        return fail(SSB_EINVAL, "scan_n must be a power of two in [32, 1024], got %d", n);
     if (g->det_n <= 0) return fail(SSB_EINVAL, "det_n must be positive");
     if (!std::isfinite(g->bf_r2) || g->bf_r2 < 0.0) return fail(SSB_EINVAL, "bf_r2 must be finite and >= 0");
     if (!std::isfinite(g->det_cy) || !std::isfinite(g->det_cx)) return fail(SSB_EINVAL, "non-finite detector center");

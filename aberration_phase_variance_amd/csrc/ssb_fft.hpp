@@ -87,6 +87,7 @@ template <> struct FftShape<256> { static constexpr int R = 4, P = 4; };
 template <> struct FftShape<128> { static constexpr int R = 2, P = 7; };
 template <> struct FftShape<64>  { static constexpr int R = 4, P = 3; };
 template <> struct FftShape<32>  { static constexpr int R = 2, P = 5; };
+template <> struct FftShape<1024> { static constexpr int R = 16, P = 3; };   // radices 16, 8, 8 (below)
 
 // Bijective LDS index maps for the exchange after pass p.  The write and the
 // read of one exchange use the same map, so values are unchanged; the maps only
@@ -242,6 +243,200 @@ struct WaveFFTT {
             for (int r = 0; r < R; ++r) x[r] = buf[exch_swizzle<N>(p, j + r * L)];
             ns *= R;
         }
+    }
+};
+
+// ---------------------------------------------------------------- N = 1024
+// One wave per transform, lane j holds x[j + 64 r] for r < 16, in and out.  Mixed
+// radices 16, 8, 8 in self-sorting (Stockham) form: pass 0 is a radix-16 DFT of the
+// lane's own values; passes 1 and 2 are radix 8 on 128 virtual lanes jv = j + 64 h
+// (h = 0, 1), the lane's values with r = h + 2 r'.  Pass p reads a[jv + (N/R_p) r],
+// twiddles by exp(SIGN 2 pi i k r / (ns R_p)) with k = jv mod ns, applies the DFT and
+// writes position (jv - k) R_p + k + r ns, ns being the product of the earlier
+// radices; the last pass leaves X[jv + 128 r'] in the lane.
+
+// radix-16 DFT in registers: 4 x radix 4 over n1 (n = 4 n1 + n2), twiddles
+// exp(SIGN 2 pi i n2 k1 / 16), 4 x radix 4 over n2 (k = k1 + 4 k2)
+template <int SIGN>
+__device__ __forceinline__ void dft16(float2 (&x)[16]) {
+    const float c1 = 0.92387953251128675613f, s1 = 0.38268343236508977173f, h2 = 0.70710678118654752440f;
+    // w[m] = exp(SIGN 2 pi i m / 16) for the products m = n2 k1 that occur
+    auto w16 = [&](int m) -> float2 {
+        switch (m) {
+            case 1: return make_float2(c1, SIGN * s1);
+            case 2: return make_float2(h2, SIGN * h2);
+            case 3: return make_float2(s1, SIGN * c1);
+            case 4: return make_float2(0.f, (float)SIGN);
+            case 6: return make_float2(-h2, SIGN * h2);
+            default: return make_float2(-c1, -SIGN * s1);   // m = 9
+        }
+    };
+#pragma unroll
+    for (int n2 = 0; n2 < 4; ++n2) dft4v<SIGN>(x[n2], x[4 + n2], x[8 + n2], x[12 + n2]);
+    // now x[4 k1 + n2] holds y[n2][k1]
+#pragma unroll
+    for (int n2 = 1; n2 < 4; ++n2)
+#pragma unroll
+        for (int k1 = 1; k1 < 4; ++k1) x[4 * k1 + n2] = cmul(x[4 * k1 + n2], w16(n2 * k1));
+    float2 y[16];
+#pragma unroll
+    for (int k1 = 0; k1 < 4; ++k1) {
+        float2 a0 = x[4 * k1], a1 = x[4 * k1 + 1], a2 = x[4 * k1 + 2], a3 = x[4 * k1 + 3];
+        dft4v<SIGN>(a0, a1, a2, a3);
+        y[k1] = a0;
+        y[k1 + 4] = a1;
+        y[k1 + 8] = a2;
+        y[k1 + 12] = a3;
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) x[k] = y[k];
+}
+
+// LDS index map of the N = 1024 exchanges (bijective: bits 5-9 stay, so bit 4 and
+// then bits 0-3 can be undone): bits 4-7 XOR into bits 0-3 and bits 7, 8 into bit 4.
+// All four access patterns (stride-16 writes of pass 0, the two radix-8 reads, the
+// blocked writes of pass 1) then hit distinct banks per 16 and per 32 lanes.
+__device__ __forceinline__ int swz1024(int i) { return i ^ ((i >> 4) & 15) ^ ((((i >> 7) ^ (i >> 8)) & 1) << 4); }
+
+template <int SIGN>
+__device__ __forceinline__ void fft1024_run(float2 (&x)[16], float2* buf, int j, const float2 (&t1)[7],
+                                            const float2 (&t2a)[7], const float2 (&t2b)[7]) {
+    dft16<SIGN>(x);
+    wave_lds_fence();
+#pragma unroll
+    for (int r = 0; r < 16; ++r) buf[swz1024(j * 16 + r)] = x[r];
+    wave_lds_fence();
+    // pass 1: radix 8, ns = 16
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int r = 0; r < 8; ++r) x[8 * h + r] = buf[swz1024(j + 64 * h + 128 * r)];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        float2 (&y)[8] = *reinterpret_cast<float2 (*)[8]>(&x[8 * h]);
+#pragma unroll
+        for (int r = 1; r < 8; ++r) y[r] = cmul(y[r], t1[r - 1]);
+        dft8<SIGN>(y);
+    }
+    wave_lds_fence();
+    const int k = j & 15;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int jv = j + 64 * h;
+        const int base = (jv - k) * 8 + k;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) buf[swz1024(base + 16 * r)] = x[8 * h + r];
+    }
+    wave_lds_fence();
+    // pass 2: radix 8, ns = 128, k = jv
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int r = 0; r < 8; ++r) x[8 * h + r] = buf[swz1024(j + 64 * h + 128 * r)];
+    float2 out[16];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        float2 (&y)[8] = *reinterpret_cast<float2 (*)[8]>(&x[8 * h]);
+#pragma unroll
+        for (int r = 1; r < 8; ++r) y[r] = cmul(y[r], h == 0 ? t2a[r - 1] : t2b[r - 1]);
+        dft8<SIGN>(y);
+#pragma unroll
+        for (int r = 0; r < 8; ++r) out[h + 2 * r] = y[r];
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x[r] = out[r];
+}
+
+// Twiddle table of the N = 1024 transform: pass 1 block [r-1][16] (k < 16, over 128),
+// then pass 2 block [r-1][128] (k < 128, over 1024); 1,008 entries.
+template <int SIGN>
+struct WaveFFTT<1024, SIGN> {
+    static constexpr int N = 1024, R = 16, P = 3, L = 64, W = 1;
+    static constexpr int TABLE = 7 * 16 + 7 * 128;
+
+    __device__ static void fill(float2* tab, int tid, int nthreads) {
+        for (int e = tid; e < TABLE; e += nthreads) {
+            int r, k, den;
+            if (e < 112) {
+                r = e / 16 + 1;
+                k = e % 16;
+                den = 128;
+            } else {
+                r = (e - 112) / 128 + 1;
+                k = (e - 112) % 128;
+                den = 1024;
+            }
+            float s, c;
+            sincospif((float)(SIGN * 2 * k * r) / (float)den, &s, &c);
+            tab[e] = make_float2(c, s);
+        }
+    }
+
+    __device__ __forceinline__ void run(float2 (&x)[16], float2* buf, int j, const float2* tab) const {
+        float2 t1[7], t2a[7], t2b[7];
+#pragma unroll
+        for (int r = 1; r < 8; ++r) {
+            t1[r - 1] = tab[(r - 1) * 16 + (j & 15)];
+            t2a[r - 1] = tab[112 + (r - 1) * 128 + j];
+            t2b[r - 1] = tab[112 + (r - 1) * 128 + j + 64];
+        }
+        fft1024_run<SIGN>(x, buf, j, t1, t2a, t2b);
+    }
+};
+
+template <int SIGN>
+struct WaveFFT<1024, SIGN> {
+    static constexpr int N = 1024, R = 16, P = 3, L = 64, W = 1;
+    float2 t1[7], t2a[7], t2b[7];
+
+    __device__ __forceinline__ void init(int j) {
+#pragma unroll
+        for (int r = 1; r < 8; ++r) {
+            float s, c;
+            sincospif((float)(SIGN * 2 * (j & 15) * r) / 128.0f, &s, &c);
+            t1[r - 1] = make_float2(c, s);
+            sincospif((float)(SIGN * 2 * j * r) / 1024.0f, &s, &c);
+            t2a[r - 1] = make_float2(c, s);
+            sincospif((float)(SIGN * 2 * (j + 64) * r) / 1024.0f, &s, &c);
+            t2b[r - 1] = make_float2(c, s);
+        }
+    }
+    // The same twiddles from six sincospi: r = 1, 2, 4 of each pass directly, the
+    // other r as their products, and the h = 1 block of pass 2 as the h = 0 block
+    // times the constants exp(SIGN i pi r / 8).
+    __device__ __forceinline__ void init_products(int j) {
+        auto fill7 = [](float2 (&t)[7], int k, float den) {
+            float2 w1, w2, w4;
+            sincospif((float)(SIGN * 2 * k) / den, &w1.y, &w1.x);
+            sincospif((float)(SIGN * 4 * k) / den, &w2.y, &w2.x);
+            sincospif((float)(SIGN * 8 * k) / den, &w4.y, &w4.x);
+            t[0] = w1;
+            t[1] = w2;
+            t[2] = cmul(w1, w2);
+            t[3] = w4;
+            t[4] = cmul(w4, w1);
+            t[5] = cmul(w4, w2);
+            t[6] = cmul(w4, t[2]);
+        };
+        fill7(t1, j & 15, 128.0f);
+        fill7(t2a, j, 1024.0f);
+        const float c1 = 0.92387953251128675613f, s1 = 0.38268343236508977173f, h2 = 0.70710678118654752440f;
+        const float2 c[7] = {make_float2(c1, SIGN * s1), make_float2(h2, SIGN * h2), make_float2(s1, SIGN * c1),
+                             make_float2(0.f, (float)SIGN),  make_float2(-s1, SIGN * c1),
+                             make_float2(-h2, SIGN * h2),   make_float2(-c1, SIGN * s1)};
+#pragma unroll
+        for (int r = 0; r < 7; ++r) t2b[r] = cmul(t2a[r], c[r]);
+    }
+    __device__ __forceinline__ void load(const float2* __restrict__ tab, int j) {
+#pragma unroll
+        for (int r = 1; r < 8; ++r) {
+            t1[r - 1] = tab[(r - 1) * 16 + (j & 15)];
+            t2a[r - 1] = tab[112 + (r - 1) * 128 + j];
+            t2b[r - 1] = tab[112 + (r - 1) * 128 + j + 64];
+        }
+    }
+    __device__ __forceinline__ void run(float2 (&x)[16], float2* buf, int j) const {
+        fft1024_run<SIGN>(x, buf, j, t1, t2a, t2b);
     }
 };
 

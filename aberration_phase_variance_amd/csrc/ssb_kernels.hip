@@ -38,7 +38,8 @@ namespace {
 #define SSB_PASS2_PREFETCH 0  // pass 2 loads the next BF's column values during the current transform
 #endif
 
-constexpr int kTC = 16;       // columns per column-pass tile
+// columns per column-pass tile (LDS: kTC x (N + 1) complex values)
+template <int N> constexpr int cols_tc() { return N >= 1024 ? 8 : 16; }
 constexpr int kPad = 1;       // LDS row padding (complex values)
 
 enum ColMode { COL_PLAIN_FWD = 1, COL_PLAIN_INV = 2 };
@@ -198,6 +199,7 @@ __global__ __launch_bounds__(256) void k_cols(const float2* in_m, const float2* 
     constexpr int LD = N + kPad;
     constexpr int SIGN = (MODE == COL_PLAIN_FWD) ? -1 : 1;
     using F = WaveFFT<N, SIGN>;
+    constexpr int kTC = cols_tc<N>();
     __shared__ float2 tile[kTC * LD];
 
     const int tid = threadIdx.x;
@@ -382,6 +384,7 @@ __device__ __forceinline__ float2 correct_entry(float2 g, float2 ch, float2 e, b
 //      entries with nonzero transfer and their exp(i chi_q) (per-trial table) are
 //      loaded into registers through buffer resources, zero-transfer entries get
 //      an out-of-range offset and read as exact zeros without a memory access;
+//      the BF pixel's phase ramps are built while those loads are in flight;
 //   2. each entry is corrected into the LDS tile: on the flat tops of the
 //      apertures the bracket is already a unit phasor, on an edge ring it is
 //      normalized;
@@ -389,7 +392,9 @@ __device__ __forceinline__ float2 correct_entry(float2 g, float2 ch, float2 e, b
 // exp(-i delta) is separable: E_u(u') = exp(-2 pi i u' beta) for all rows is
 // built in LDS per workgroup, E_v(v) = exp(-2 pi i v alpha) per thread (each
 // thread keeps one column).
-constexpr int kPass1Threads = SSB_PASS1_THREADS;
+// 1024-point columns take 512 threads: a thread's share of the tile (N TC / threads
+// entries) stays at 16, the most the per-thread support word holds.
+template <int N> constexpr int pass1_threads() { return N >= 1024 ? 512 : SSB_PASS1_THREADS; }
 
 // One pass-1 tile; NYQ selects the Nyquist column at compile time so that every
 // row index, LDS address and load offset of the unrolled entry loops is a
@@ -400,7 +405,7 @@ __device__ __forceinline__ void pass1_tile(const float2* __restrict__ gsrc, cons
                                            float2* __restrict__ out, float2* tile, float2* eu, int v0) {
     constexpr int H = N / 2;
     constexpr int LD = N + 16 / TC;           // row pitch: the 16 lanes of one b64 LDS cycle hit distinct banks
-    constexpr int NT = kPass1Threads;
+    constexpr int NT = pass1_threads<N>();
     constexpr int RS = NYQ ? NT : NT / TC;    // rows per sweep
     constexpr int PM = (N + RS - 1) / RS;     // entries per thread
     constexpr int SSTRIDE = NYQ ? 1 : TC;     // row stride inside the source tile
@@ -412,10 +417,6 @@ __device__ __forceinline__ void pass1_tile(const float2* __restrict__ gsrc, cons
     const int c = NYQ ? 0 : tid % TC;
     const int v = v0 + c;
     const int ustart = NYQ ? tid : tid / TC;
-    double alpha, beta;
-    delta_slopes(k.x, k.y, m, geo, alpha, beta);
-    for (int u = tid; u < N; u += NT) eu[u] = phasor_rev_neg((double)(u < H ? u : u - N) * beta);
-    const float2 ev = phasor_rev_neg((double)v * alpha);
     const int lo_m = unpack_lo(sr.x), len_m = unpack_len(sr.x);
     const int lo_p = unpack_lo(sr.y), len_p = unpack_len(sr.y);
 
@@ -439,6 +440,11 @@ __device__ __forceinline__ void pass1_tile(const float2* __restrict__ gsrc, cons
         chv[i] = load_or_zero(rc, off);
         bits |= on ? ((inm ? 1u : 0u) | (inp ? 2u : 0u)) << (2 * i) : 0u;
     }
+    // the phase ramps of this BF pixel while the loads are in flight
+    double alpha, beta;
+    delta_slopes(k.x, k.y, m, geo, alpha, beta);
+    for (int u = tid; u < N; u += NT) eu[u] = phasor_rev_neg((double)(u < H ? u : u - N) * beta);
+    const float2 ev = phasor_rev_neg((double)v * alpha);
     __syncthreads();                              // E_u complete
 
     // 2. correction into the LDS tile
@@ -476,7 +482,7 @@ __device__ __forceinline__ void pass1_tile(const float2* __restrict__ gsrc, cons
     constexpr int NG = (NT / 64) * F::W;
     constexpr int NCOLS = NYQ ? 1 : TC;
     F fft;
-    if constexpr (F::R == 8) fft.init_products(j);   // radix 8: three sincospi per pass, the rest products
+    if constexpr (F::R == 8 || N == 1024) fft.init_products(j);   // sincospi for r = 1, 2, 4, the rest products
     else fft.init(j);
     for (int cc = grp; cc < NCOLS; cc += NG) {
         float2 x[F::R];
@@ -500,7 +506,7 @@ __device__ __forceinline__ void pass1_tile(const float2* __restrict__ gsrc, cons
 }
 
 template <int N, int TC>
-__global__ __launch_bounds__(kPass1Threads) void k_pass1(const float2* __restrict__ gm,
+__global__ __launch_bounds__(pass1_threads<N>()) void k_pass1(const float2* __restrict__ gm,
                                                          const float2* __restrict__ gn,
                                                          const float2* __restrict__ chm,
                                                          const float2* __restrict__ chn,
@@ -1062,7 +1068,7 @@ hipError_t cols_n(const float2* in_m, const float2* in_n, float2* out_m, float2*
     constexpr int H = N / 2;
     for (int64_t p0 = 0; p0 < planes; p0 += 65535) {
         const int np = (int)std::min<int64_t>(65535, planes - p0);
-        hipLaunchKernelGGL((k_cols<N, MODE>), dim3(H / kTC + 1, np), dim3(256), 0, st, in_m + p0 * N * H,
+        hipLaunchKernelGGL((k_cols<N, MODE>), dim3(H / cols_tc<N>() + 1, np), dim3(256), 0, st, in_m + p0 * N * H,
                            in_n + p0 * N, out_m + p0 * N * H, out_n + p0 * N, tw);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -1080,7 +1086,7 @@ hipError_t pass1_n(const float2* gm, const float2* gn, const float2* chm, const 
     constexpr int H = N / 2;
     constexpr int TC = pass1_tc<N>();
     // one launch per chunk: (H/TC + 1) tiles per BF in x, trials in y
-    hipLaunchKernelGGL((k_pass1<N, TC>), dim3((unsigned)((int64_t)cb * (H / TC + 1)), n_trials), dim3(kPass1Threads),
+    hipLaunchKernelGGL((k_pass1<N, TC>), dim3((unsigned)((int64_t)cb * (H / TC + 1)), n_trials), dim3(pass1_threads<N>()),
                        0, st, gm, gn, chm, chn, kb, sup, vend, tc, geo, bf0, cap, im, in);
     return hipGetLastError();
 }
@@ -1113,6 +1119,7 @@ hipError_t support_n(const double2* kb, const uint8_t* active, GeomDev geo, int6
         case 128: { constexpr int NN = 128; return CALL; } \
         case 256: { constexpr int NN = 256; return CALL; } \
         case 512: { constexpr int NN = 512; return CALL; } \
+        case 1024: { constexpr int NN = 1024; return CALL; } \
         default: return hipErrorInvalidValue;               \
     }
 
@@ -1131,6 +1138,7 @@ int twiddle_count(int n) {
         case 64: return WaveFFTT<64, 1>::TABLE;
         case 128: return WaveFFTT<128, 1>::TABLE;
         case 256: return WaveFFTT<256, 1>::TABLE;
+        case 1024: return WaveFFTT<1024, 1>::TABLE;
         default: return WaveFFTT<512, 1>::TABLE;
     }
 }
@@ -1165,6 +1173,7 @@ int pass2_row_blocks(int n) {
         case 64: return row_blocks<64>();
         case 128: return row_blocks<128>();
         case 256: return row_blocks<256>();
+        case 1024: return row_blocks<1024>();
         default: return row_blocks<512>();
     }
 }

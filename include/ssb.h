@@ -55,7 +55,7 @@ enum {
 
 /* Workload geometry.  Lengths are in detector pixels unless stated otherwise. */
 typedef struct ssb_geometry {
-    int32_t scan_n;        /* N: scan side, a power of two in [32, 512] */
+    int32_t scan_n;        /* N: scan side, a power of two in [32, 1024] */
     int32_t det_n;         /* D: detector side, > 0 */
     double bf_r2;          /* BF disk radius squared (pixels^2), >= 0 */
     double det_cy;         /* detector center row (pixels) */

@@ -6,7 +6,12 @@ checkpoints") measure on: the full one is a 512 x 512 scan with a
 192 x 192 detector and 8,937 bright-field (BF) pixels (checkpoints page,
 section "2026-09-11 full-aperture Apple M5 floor checkpoint").  The smaller
 ones keep the same optics and scale the scan and detector down so a float64
-CPU oracle finishes in seconds.
+CPU oracle finishes in seconds.  A fifth, ``full1024``, is the 1024 x 1024
+scan of the size-scaling runs (notes page, "128 GB Apple M5 Max size-scaling
+follow-up"): same optics, detector and BF set as the full one, the scan field
+twice as wide at the same step.  Those runs zero-pad the 512 spectra instead,
+which integer counts cannot express; the transform length, the BF count and
+the 4.2 MB spectrum per BF pixel are the same.
 
 Everything here is plain numbers: the beam energy, the probe semi-angle,
 the BF disk, and the derived sampling.  Nothing in this module evaluates the
@@ -120,6 +125,11 @@ WORKLOADS = {
     "medium": _workload("medium", 256, 96, 676, 2121, 200, (-100.0, 100.0)),
     # the full field: 512^2 scan x 8,937 BF
     "full": _workload("full", 512, 192, 2837, 8937, 200, (-200.0, 200.0), (-20.0, 20.0), (0.0, math.pi)),
+    # the 1024^2 scan of the size-scaling runs: the full workload's optics, detector and
+    # 8,937 BF, scanned over a field twice as wide at the same step (1024-point
+    # transforms, 4.2 MB of spectrum per BF pixel)
+    "full1024": _workload("full1024", 1024, 192, 2837, 8937, 200, (-200.0, 200.0), (-20.0, 20.0),
+                          (0.0, math.pi)),
 }
 
 

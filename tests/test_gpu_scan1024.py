@@ -1,0 +1,152 @@
+"""GPU parity at scan size 1024 (1,024-point transforms): the full workload's optics,
+detector and 8,937 BF pixels over a 1024^2 scan, in the launch configuration the
+benchmark times (default chunking).
+
+As at N = 512 the float64 oracle checks sampled outputs one by one (cached spectra of
+single BF pixels, phase moments of BF ranges including the ragged last 32-BF group)
+and properties that hold at any size (the loss is the formula applied to the moments
+of the whole range; batch invariance).  A complete loss and object check runs on the
+29 BF pixels within 3 px of the disk center, same counts.  Counts come from the
+seeded device generator; the oracle gets the same bytes.
+"""
+import dataclasses
+import sys
+
+import numpy as np
+import pytest
+
+import aberration_phase_variance_amd as ssb
+from oracle import ssb_oracle as O
+from synth import WORKLOADS, make_counts_torch
+
+pytestmark = pytest.mark.gpu
+
+LOSS_RTOL = 1e-5
+PHASE_RMS = 1e-4
+TRUE = [40.0, 5.0, 0.3]
+N = 1024
+
+
+def _say(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def full1024():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a visible GPU")
+    w = WORKLOADS["full1024"]
+    _say("[scan1024] generating 1024^2 x 8,937 counts on the device")
+    counts = make_counts_torch(w, torch.device("cuda:0"))
+    torch.cuda.synchronize()
+    _say("[scan1024] ssb_prepare")
+    h = ssb.ssb_prepare(w.geometry, counts, w.n_bf)
+    torch.cuda.synchronize()
+    yield w, counts, h
+    ssb.ssb_release(h)
+    del counts
+    torch.cuda.empty_cache()
+
+
+def _host(counts, b0, b1):
+    return counts[b0:b1].cpu().numpy().view(np.uint32)
+
+
+def _moments(h, params, b0, b1):
+    import torch
+    s1 = torch.empty((N, N), dtype=torch.float64, device="cuda")
+    s2 = ssb.ssb_moments(h, params, b0, b1, s1)
+    return s1.cpu().numpy(), s2
+
+
+def test_1024_prepare_exact(full1024):
+    import torch
+    w, counts, h = full1024
+    info = ssb.ssb_query(h)
+    assert info["n_bf"] == 8937 and info["n_active_bf"] == 8937
+    assert info["scan_n"] == N and info["det_n"] == 192
+    assert info["spectrum_bytes"] == 8937 * N * (N // 2 + 1) * 8
+    # exact integer total in int64 (torch's reduction, not the library's)
+    total = sum(int(counts[b0:b0 + 512].to(torch.int64).sum()) for b0 in range(0, w.n_bf, 512))
+    assert info["dc"] == total / w.n_bf
+
+
+def test_1024_spectra_sampled(full1024):
+    import torch
+    w, counts, h = full1024
+    for b in (0, 4468, 8936):
+        ref = O.scan_spectrum(_host(counts, b, b + 1)[0])
+        out = torch.empty((N, N // 2 + 1, 2), dtype=torch.float32, device="cuda")
+        ssb.ssb_spectrum(h, b, out)
+        o = out.cpu().numpy()
+        got = o[..., 0] + 1j * o[..., 1]
+        assert np.linalg.norm(got - ref) <= 2e-6 * np.linalg.norm(ref), b
+
+
+@pytest.mark.parametrize("b0,b1,params", [
+    (0, 32, TRUE),
+    (0, 32, [-137.0, 16.5, 2.7]),
+    (8896, 8937, [61.0, -7.5, 0.4]),      # crosses into the ragged last group (8928..8936)
+])
+def test_1024_moments_sampled(full1024, b0, b1, params):
+    w, counts, h = full1024
+    og = O.OGeom.from_any(w.geometry)
+    dc = ssb.ssb_query(h)["dc"]
+    _say(f"[scan1024] moments BF {b0}..{b1} at {params}")
+    s1, s2 = _moments(h, params, b0, b1)
+    r1, r2 = O.bf_moments(og, _host(counts, b0, b1), params, dc, list(range(b0, b1)))
+    assert abs(s2 - r2) <= LOSS_RTOL * abs(r2), (b0, params)
+    d = s1 - r1
+    assert np.sqrt(np.mean(d * d)) <= 2e-5 * (b1 - b0) and np.max(np.abs(d)) <= 1e-3, (b0, params)
+
+
+def test_1024_loss_is_formula_of_moments(full1024):
+    w, counts, h = full1024
+    for params in (TRUE, [88.0, -12.0, 1.1]):
+        loss = ssb.ssb_loss(h, [params])[0]
+        s1, s2 = _moments(h, params, 0, w.n_bf)
+        assert abs(loss - O.loss_from_moments(s1, s2, w.n_bf)) <= 1e-12 * abs(loss)
+
+
+def test_1024_batch_invariance(full1024):
+    w, counts, h = full1024
+    p = np.array([TRUE, [-150.0, 3.0, 0.9], [20.0, 19.0, 2.2]], np.float32)
+    batch = ssb.ssb_loss(h, p)
+    for k in range(3):
+        assert ssb.ssb_loss(h, p[k:k + 1])[0] == batch[k]
+
+
+@pytest.fixture(scope="module")
+def subdisk1024(full1024):
+    """The 1024^2 counts restricted to the 29 BF pixels of radius <= 3 px."""
+    import torch
+    w, counts, h = full1024
+    g = dataclasses.replace(w.geometry, bf_r2=9.0)
+    i, j = O.bf_indices(O.OGeom.from_any(w.geometry))
+    sel = np.flatnonzero((i - 96) ** 2 + (j - 96) ** 2 <= 9)
+    sub = counts[torch.from_numpy(sel).cuda()].contiguous()
+    hs = ssb.ssb_prepare(g, sub, sel.size)
+    torch.cuda.synchronize()
+    yield g, sub.cpu().numpy().view(np.uint32), hs
+    ssb.ssb_release(hs)
+
+
+def test_1024_subdisk_loss_and_object(subdisk1024):
+    import torch
+    g, counts, hs = subdisk1024
+    og = O.OGeom.from_any(g)
+    assert counts.shape[0] == 29
+    dc = O.dc_value(counts)
+    assert ssb.ssb_query(hs)["dc"] == dc
+    for params in (TRUE, [-60.0, 9.0, 2.0]):
+        _say(f"[scan1024] sub-disk loss at {params}")
+        got = ssb.ssb_loss(hs, [params])[0]
+        ref = O.loss(og, counts, params, dc)
+        assert abs(got - ref) <= LOSS_RTOL * abs(ref), (params, got, ref)
+    phase = torch.empty((N, N), dtype=torch.float32, device="cuda")
+    ssb.ssb_object(hs, TRUE, phase)
+    torch.cuda.synchronize()
+    ref_phase, _ = O.object_wave(og, counts, TRUE, dc)
+    d = np.angle(np.exp(1j * (phase.cpu().numpy() - ref_phase)))
+    assert np.sqrt(np.mean(d * d)) <= PHASE_RMS
