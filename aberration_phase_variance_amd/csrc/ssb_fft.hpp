@@ -89,6 +89,9 @@ template <> struct FftShape<64>  { static constexpr int R = 4, P = 3; };
 template <> struct FftShape<32>  { static constexpr int R = 2, P = 5; };
 template <> struct FftShape<1024> { static constexpr int R = 16, P = 3; };   // radices 16, 8, 8 (below)
 
+// LDS scratch (complex values) one transform's exchanges need.
+template <int N> constexpr int fft_scratch() { return N == 1024 ? N + N / 16 : N; }
+
 // Bijective LDS index maps for the exchange after pass p.  The write and the
 // read of one exchange use the same map, so values are unchanged; the maps only
 // spread each 64-lane access across banks.  For N = 512 (radix 8) they remove
@@ -292,53 +295,107 @@ __device__ __forceinline__ void dft16(float2 (&x)[16]) {
     for (int k = 0; k < 16; ++k) x[k] = y[k];
 }
 
-// LDS index map of the N = 1024 exchanges (bijective: bits 5-9 stay, so bit 4 and
-// then bits 0-3 can be undone): bits 4-7 XOR into bits 0-3 and bits 7, 8 into bit 4.
-// All four access patterns (stride-16 writes of pass 0, the two radix-8 reads, the
-// blocked writes of pass 1) then hit distinct banks per 16 and per 32 lanes.
-__device__ __forceinline__ int swz1024(int i) { return i ^ ((i >> 4) & 15) ^ ((((i >> 7) ^ (i >> 8)) & 1) << 4); }
+// LDS index map of the N = 1024 exchanges: one pad slot after every 16 values,
+// p(i) = i + i / 16, so a transform needs N + N/16 slots (fft_scratch).  Every
+// exchange address is then a per-lane base plus a per-register constant (the
+// instruction's immediate offset), and the stride-16 writes of pass 0 (17 j + r)
+// spread over the banks.  The transform below writes p out per access pattern
+// (base + constant), which the compiler cannot derive from p itself:
+//   pass-0 write  p(16 j + r)                       = 17 j + r
+//   radix-8 reads p(j + 64 h + 128 r)               = (j + j/16) + 68 h + 136 r
+//   pass-1 write  p(128 (j/16 + 4 h) + j%16 + 16 r) = (136 (j/16) + j%16) + 544 h + 17 r
+
+// Twiddles of the N = 1024 passes.  Pass 1: t[r-1] = exp(SIGN 2 pi i k r / 128),
+// k = j mod 16.  Pass 2: exp(SIGN 2 pi i jv r / 1024) for jv = j (ta) and j + 64 (tb).
+// Either from the table laid out as WaveFFTT<1024>'s, or from six sincospi (r = 1,
+// 2, 4 directly, the other r as products; tb = ta times exp(SIGN i pi r / 8)).
+template <int SIGN>
+__device__ __forceinline__ void tw1024_products(float2 (&t)[7], int k, float den) {
+    float2 w1, w2, w4;
+    sincospif((float)(SIGN * 2 * k) / den, &w1.y, &w1.x);
+    sincospif((float)(SIGN * 4 * k) / den, &w2.y, &w2.x);
+    sincospif((float)(SIGN * 8 * k) / den, &w4.y, &w4.x);
+    t[0] = w1;
+    t[1] = w2;
+    t[2] = cmul(w1, w2);
+    t[3] = w4;
+    t[4] = cmul(w4, w1);
+    t[5] = cmul(w4, w2);
+    t[6] = cmul(w4, t[2]);
+}
 
 template <int SIGN>
-__device__ __forceinline__ void fft1024_run(float2 (&x)[16], float2* buf, int j, const float2 (&t1)[7],
-                                            const float2 (&t2a)[7], const float2 (&t2b)[7]) {
+__device__ __forceinline__ void tw1024_shift64(const float2 (&ta)[7], float2 (&tb)[7]) {
+    const float c1 = 0.92387953251128675613f, s1 = 0.38268343236508977173f, h2 = 0.70710678118654752440f;
+    const float2 c[7] = {make_float2(c1, SIGN * s1), make_float2(h2, SIGN * h2), make_float2(s1, SIGN * c1),
+                         make_float2(0.f, (float)SIGN),  make_float2(-s1, SIGN * c1),
+                         make_float2(-h2, SIGN * h2),   make_float2(-c1, SIGN * s1)};
+#pragma unroll
+    for (int r = 0; r < 7; ++r) tb[r] = cmul(ta[r], c[r]);
+}
+
+template <class T>
+__device__ __forceinline__ void tw1024_load1(const T* tab, int j, float2 (&t)[7]) {
+#pragma unroll
+    for (int r = 1; r < 8; ++r) t[r - 1] = tab[(r - 1) * 16 + (j & 15)];
+}
+template <class T>
+__device__ __forceinline__ void tw1024_load2(const T* tab, int j, float2 (&ta)[7], float2 (&tb)[7]) {
+#pragma unroll
+    for (int r = 1; r < 8; ++r) {
+        ta[r - 1] = tab[112 + (r - 1) * 128 + j];
+        tb[r - 1] = tab[112 + (r - 1) * 128 + j + 64];
+    }
+}
+
+// The transform; get1(t) and get2(ta, tb) produce each pass's twiddles right before
+// that pass, so that at most one pass's twiddles are live.
+template <int SIGN, class Get1, class Get2>
+__device__ __forceinline__ void fft1024_run(float2 (&x)[16], float2* buf, int j, Get1 get1, Get2 get2) {
     dft16<SIGN>(x);
     wave_lds_fence();
 #pragma unroll
-    for (int r = 0; r < 16; ++r) buf[swz1024(j * 16 + r)] = x[r];
+    for (int r = 0; r < 16; ++r) buf[17 * j + r] = x[r];
     wave_lds_fence();
     // pass 1: radix 8, ns = 16
+    const float2* rd = buf + j + (j >> 4);
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int r = 0; r < 8; ++r) x[8 * h + r] = buf[swz1024(j + 64 * h + 128 * r)];
+        for (int r = 0; r < 8; ++r) x[8 * h + r] = rd[68 * h + 136 * r];
+    {
+        float2 t1[7];
+        get1(t1);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        float2 (&y)[8] = *reinterpret_cast<float2 (*)[8]>(&x[8 * h]);
+        for (int h = 0; h < 2; ++h) {
+            float2 y[8];
 #pragma unroll
-        for (int r = 1; r < 8; ++r) y[r] = cmul(y[r], t1[r - 1]);
-        dft8<SIGN>(y);
+            for (int r = 0; r < 8; ++r) y[r] = r == 0 ? x[8 * h] : cmul(x[8 * h + r], t1[r - 1]);
+            dft8<SIGN>(y);
+#pragma unroll
+            for (int r = 0; r < 8; ++r) x[8 * h + r] = y[r];
+        }
     }
     wave_lds_fence();
-    const int k = j & 15;
+    float2* wr = buf + 136 * (j >> 4) + (j & 15);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int jv = j + 64 * h;
-        const int base = (jv - k) * 8 + k;
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int r = 0; r < 8; ++r) buf[swz1024(base + 16 * r)] = x[8 * h + r];
-    }
+        for (int r = 0; r < 8; ++r) wr[544 * h + 17 * r] = x[8 * h + r];
     wave_lds_fence();
     // pass 2: radix 8, ns = 128, k = jv
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int r = 0; r < 8; ++r) x[8 * h + r] = buf[swz1024(j + 64 * h + 128 * r)];
+        for (int r = 0; r < 8; ++r) x[8 * h + r] = rd[68 * h + 136 * r];
+    float2 t2a[7], t2b[7];
+    get2(t2a, t2b);
     float2 out[16];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        float2 (&y)[8] = *reinterpret_cast<float2 (*)[8]>(&x[8 * h]);
+        float2 y[8];
 #pragma unroll
-        for (int r = 1; r < 8; ++r) y[r] = cmul(y[r], h == 0 ? t2a[r - 1] : t2b[r - 1]);
+        for (int r = 0; r < 8; ++r) y[r] = r == 0 ? x[8 * h] : cmul(x[8 * h + r], h == 0 ? t2a[r - 1] : t2b[r - 1]);
         dft8<SIGN>(y);
 #pragma unroll
         for (int r = 0; r < 8; ++r) out[h + 2 * r] = y[r];
@@ -372,71 +429,39 @@ struct WaveFFTT<1024, SIGN> {
         }
     }
 
+    // tab: the table (in LDS for the row pass), read pass by pass
     __device__ __forceinline__ void run(float2 (&x)[16], float2* buf, int j, const float2* tab) const {
-        float2 t1[7], t2a[7], t2b[7];
-#pragma unroll
-        for (int r = 1; r < 8; ++r) {
-            t1[r - 1] = tab[(r - 1) * 16 + (j & 15)];
-            t2a[r - 1] = tab[112 + (r - 1) * 128 + j];
-            t2b[r - 1] = tab[112 + (r - 1) * 128 + j + 64];
-        }
-        fft1024_run<SIGN>(x, buf, j, t1, t2a, t2b);
+        fft1024_run<SIGN>(
+            x, buf, j, [&](float2 (&t)[7]) { tw1024_load1(tab, j, t); },
+            [&](float2 (&ta)[7], float2 (&tb)[7]) { tw1024_load2(tab, j, ta, tb); });
     }
 };
 
+// Register form: load() takes the table from global memory pass by pass during
+// run(); init() / init_products() select twiddles computed from six sincospi
+// inside run() instead.
 template <int SIGN>
 struct WaveFFT<1024, SIGN> {
     static constexpr int N = 1024, R = 16, P = 3, L = 64, W = 1;
-    float2 t1[7], t2a[7], t2b[7];
+    const float2* tab = nullptr;
 
-    __device__ __forceinline__ void init(int j) {
-#pragma unroll
-        for (int r = 1; r < 8; ++r) {
-            float s, c;
-            sincospif((float)(SIGN * 2 * (j & 15) * r) / 128.0f, &s, &c);
-            t1[r - 1] = make_float2(c, s);
-            sincospif((float)(SIGN * 2 * j * r) / 1024.0f, &s, &c);
-            t2a[r - 1] = make_float2(c, s);
-            sincospif((float)(SIGN * 2 * (j + 64) * r) / 1024.0f, &s, &c);
-            t2b[r - 1] = make_float2(c, s);
-        }
-    }
-    // The same twiddles from six sincospi: r = 1, 2, 4 of each pass directly, the
-    // other r as their products, and the h = 1 block of pass 2 as the h = 0 block
-    // times the constants exp(SIGN i pi r / 8).
-    __device__ __forceinline__ void init_products(int j) {
-        auto fill7 = [](float2 (&t)[7], int k, float den) {
-            float2 w1, w2, w4;
-            sincospif((float)(SIGN * 2 * k) / den, &w1.y, &w1.x);
-            sincospif((float)(SIGN * 4 * k) / den, &w2.y, &w2.x);
-            sincospif((float)(SIGN * 8 * k) / den, &w4.y, &w4.x);
-            t[0] = w1;
-            t[1] = w2;
-            t[2] = cmul(w1, w2);
-            t[3] = w4;
-            t[4] = cmul(w4, w1);
-            t[5] = cmul(w4, w2);
-            t[6] = cmul(w4, t[2]);
-        };
-        fill7(t1, j & 15, 128.0f);
-        fill7(t2a, j, 1024.0f);
-        const float c1 = 0.92387953251128675613f, s1 = 0.38268343236508977173f, h2 = 0.70710678118654752440f;
-        const float2 c[7] = {make_float2(c1, SIGN * s1), make_float2(h2, SIGN * h2), make_float2(s1, SIGN * c1),
-                             make_float2(0.f, (float)SIGN),  make_float2(-s1, SIGN * c1),
-                             make_float2(-h2, SIGN * h2),   make_float2(-c1, SIGN * s1)};
-#pragma unroll
-        for (int r = 0; r < 7; ++r) t2b[r] = cmul(t2a[r], c[r]);
-    }
-    __device__ __forceinline__ void load(const float2* __restrict__ tab, int j) {
-#pragma unroll
-        for (int r = 1; r < 8; ++r) {
-            t1[r - 1] = tab[(r - 1) * 16 + (j & 15)];
-            t2a[r - 1] = tab[112 + (r - 1) * 128 + j];
-            t2b[r - 1] = tab[112 + (r - 1) * 128 + j + 64];
-        }
-    }
+    __device__ __forceinline__ void init(int) { tab = nullptr; }
+    __device__ __forceinline__ void init_products(int) { tab = nullptr; }
+    __device__ __forceinline__ void load(const float2* __restrict__ t, int) { tab = t; }
     __device__ __forceinline__ void run(float2 (&x)[16], float2* buf, int j) const {
-        fft1024_run<SIGN>(x, buf, j, t1, t2a, t2b);
+        if (tab) {
+            const float2* t = tab;
+            fft1024_run<SIGN>(
+                x, buf, j, [&](float2 (&t1)[7]) { tw1024_load1(t, j, t1); },
+                [&](float2 (&ta)[7], float2 (&tb)[7]) { tw1024_load2(t, j, ta, tb); });
+        } else {
+            fft1024_run<SIGN>(
+                x, buf, j, [&](float2 (&t1)[7]) { tw1024_products<SIGN>(t1, j & 15, 128.0f); },
+                [&](float2 (&ta)[7], float2 (&tb)[7]) {
+                    tw1024_products<SIGN>(ta, j, 1024.0f);
+                    tw1024_shift64<SIGN>(ta, tb);
+                });
+        }
     }
 };
 

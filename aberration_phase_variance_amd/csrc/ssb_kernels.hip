@@ -196,7 +196,7 @@ template <int N, int MODE>
 __global__ __launch_bounds__(256) void k_cols(const float2* in_m, const float2* in_n, float2* out_m,
                                               float2* out_n, const float2* __restrict__ twt) {
     constexpr int H = N / 2;
-    constexpr int LD = N + kPad;
+    constexpr int LD = fft_scratch<N>() + kPad;   // a column's slot is also its transform's scratch
     constexpr int SIGN = (MODE == COL_PLAIN_FWD) ? -1 : 1;
     using F = WaveFFT<N, SIGN>;
     constexpr int kTC = cols_tc<N>();
@@ -404,7 +404,9 @@ __device__ __forceinline__ void pass1_tile(const float2* __restrict__ gsrc, cons
                                            const double2 k, const uint4 sr, const TrialConst& m, const GeomDev& geo,
                                            float2* __restrict__ out, float2* tile, float2* eu, int v0) {
     constexpr int H = N / 2;
-    constexpr int LD = N + 16 / TC;           // row pitch: the 16 lanes of one b64 LDS cycle hit distinct banks
+    // column pitch (a column's slot is also its transform's scratch): the 16 lanes of
+    // one b64 LDS cycle hit distinct banks
+    constexpr int LD = fft_scratch<N>() + 16 / TC;
     constexpr int NT = pass1_threads<N>();
     constexpr int RS = NYQ ? NT : NT / TC;    // rows per sweep
     constexpr int PM = (N + RS - 1) / RS;     // entries per thread
@@ -517,7 +519,7 @@ __global__ __launch_bounds__(pass1_threads<N>()) void k_pass1(const float2* __re
                                                          int64_t bf0, int cap, float2* __restrict__ im,
                                                          float2* __restrict__ in) {
     constexpr int H = N / 2;
-    constexpr int LD = N + 16 / TC;
+    constexpr int LD = fft_scratch<N>() + 16 / TC;
     __shared__ float2 tile[TC * LD];
     __shared__ float2 eu[N];
 
@@ -554,26 +556,36 @@ struct RowPairRaw {
     float2 h0, h1, z0, z1;
 
     // plane: one BF pixel's column results (tile-major [N/2/8][N][8]); nyqc: its
-    // Nyquist column [N].  Columns at or past ve are zero (not written by pass 1) and
-    // read as zero through an out-of-range buffer offset.  Row y0 + 1 of a tile
-    // follows row y0 (the same 128-byte line).
+    // Nyquist column [N].  Tiles past the last supported column (ve) were not written
+    // by pass 1: the buffer resource ends at the last written tile, so their loads
+    // return zero without a memory access (columns at or past ve inside that tile
+    // hold pass 1's zeros).  Row y0 + 1 of a tile follows row y0 (the same 128-byte
+    // line).  Column j + r L sits r (L/8) tiles after column j, so every load is a
+    // per-lane base plus a constant.
     __device__ __forceinline__ void load(const float2* plane, const float2* nyqc, int y0, int j, int ve) {
         constexpr int H = N / 2;
-        const __amdgpu_buffer_rsrc_t rp = make_rsrc(plane, N * H * 8);
+        static_assert(L % kTileW == 0, "a lane group spans whole tiles");
+        constexpr int TILE = N * kTileW * 8;             // bytes of one tile of a plane
+        constexpr int RSTEP = (L / kTileW) * TILE;       // bytes from column v to column v + L
+        const int ntile = min((ve + kTileW - 1) / kTileW, H / kTileW);
+        const __amdgpu_buffer_rsrc_t rp = make_rsrc(plane, ntile * TILE);
+        // bases: column j, and the lowest mirrored column H - j - (R/2 - 1) L (>= 1).
+        // The empty asm makes them opaque, so the 2 R offsets derived from them are
+        // formed at each call rather than hoisted out of the caller's loop.
+        int od = (int)tm_index(N, y0, j) * 8;
+        int om = (int)tm_index(N, y0, H - j - (R / 2 - 1) * L) * 8;
+        asm volatile("" : "+v"(od), "+v"(om));
 #pragma unroll
         for (int r = 0; r < R / 2; ++r) {
-            const int col = j + r * L;
-            const int off = col < ve ? (int)tm_index(N, y0, col) * 8 : kNoLoad;
-            d0[r] = load_or_zero(rp, off);
-            d1[r] = load_or_zero(rp, off + kTileW * 8);
+            d0[r] = load_or_zero(rp, od + r * RSTEP);
+            d1[r] = load_or_zero(rp, od + r * RSTEP + kTileW * 8);
         }
+        // mirrored column w = H - j - r L (w = H for j = r = 0 lies past the plane,
+        // reads zero and is replaced by the Nyquist column in assemble)
 #pragma unroll
         for (int r = 0; r < R / 2; ++r) {
-            const int w = H - j - r * L;            // N - (j + (r + R/2) L); w = H only for j = r = 0
-            const int ws = w == H ? 0 : w;           // that slot is taken from the Nyquist column below
-            const int off = ws < ve ? (int)tm_index(N, y0, ws) * 8 : kNoLoad;
-            m0[r] = load_or_zero(rp, off);
-            m1[r] = load_or_zero(rp, off + kTileW * 8);
+            m0[r] = load_or_zero(rp, om + (R / 2 - 1 - r) * RSTEP);
+            m1[r] = load_or_zero(rp, om + (R / 2 - 1 - r) * RSTEP + kTileW * 8);
         }
         const float2 zero = make_float2(0.f, 0.f);
         h0 = zero;
@@ -631,7 +643,7 @@ __global__ __launch_bounds__(256, SSB_PASS2_MIN_WAVES) void k_pass2(const float2
     __shared__ float2 twt[F::TABLE];
     constexpr int H = N / 2;
     constexpr int R = F::R, L = F::L;
-    __shared__ float2 buf[4 * F::W][N];
+    __shared__ float2 buf[4 * F::W][fft_scratch<N>()];
     __shared__ double red[4];
 
     const int tid = threadIdx.x;
@@ -821,7 +833,7 @@ __global__ __launch_bounds__(256) void k_g_rows(const uint32_t* __restrict__ cou
     constexpr int H = N / 2;
     using F = WaveFFT<N, -1>;
     constexpr int R = F::R, L = F::L;
-    __shared__ float2 buf[4 * F::W][N];
+    __shared__ float2 buf[4 * F::W][fft_scratch<N>()];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -1017,7 +1029,7 @@ __global__ __launch_bounds__(256) void k_obj_rows(const float2* __restrict__ pm,
     constexpr int H = N / 2;
     using F = WaveFFT<N, +1>;
     constexpr int R = F::R, L = F::L;
-    __shared__ float2 buf[4 * F::W][N];
+    __shared__ float2 buf[4 * F::W][fft_scratch<N>()];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int grp = (tid >> 6) * F::W + lane / L;

@@ -54,6 +54,22 @@ def algorithmic_work(n: int, info: dict) -> dict:
     }
 
 
+def stage_rates(n: int, info: dict, prof: dict) -> dict:
+    """Average launch time, algorithmic bytes and FLOPs per launch, and the rates they
+    give, for pass 1 and pass 2 (launch counts and planes from ssb_profile)."""
+    work = algorithmic_work(n, info)
+    out = {}
+    for k in ("pass1", "pass2"):
+        launches = max(1, prof[k]["launches"])
+        t = prof[k]["ms"] / launches * 1e-3
+        units = prof[k]["units"] / launches
+        b = work[k]["bytes"] * units
+        f = work[k]["flops"] * units
+        out[k] = {"avg_launch_ms": t * 1e3, "planes_per_launch": units, "bytes": b, "flops": f,
+                  "gbs": b / t / 1e9, "tflops": f / t / 1e12}
+    return out
+
+
 def kernel_source_hash() -> str:
     """Hash of the HIP kernel sources the measured HBM traffic belongs to (code only:
     comments and blank lines are dropped, so a comment edit keeps the counters valid)."""
@@ -90,11 +106,13 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="full", choices=["tiny", "small", "medium", "full"])
+    ap.add_argument("--config", default="full", choices=["tiny", "small", "medium", "full", "full1024"])
     ap.add_argument("--batch", type=int, default=200, help="trials in the batched measurement (0 = skip)")
     ap.add_argument("--cpu-sample-bf", type=int, default=1024, help="BF pixels in the oracle CPU sample (0 = skip)")
     ap.add_argument("--detector", type=int, default=1,
                     help="also time the detector side on full frames (detector sum, probe fit, BF gather); 0 = skip")
+    ap.add_argument("--scan1024", type=int, default=1,
+                    help="also time the 1024^2 scan workload (8,937 BF, 1024-point transforms); 0 = skip")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB device-to-device copy (3x) as a known-size reference "
                          "for hardware byte counters")
@@ -283,24 +301,81 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         sum_ms = e0.elapsed_time(e1) / reps
-        fit = ssb.ssb_fit_probe(sums.cpu().numpy().view(np.uint64), n, g.det_n)
-        geom = dataclasses.replace(g, det_cy=fit["det_cy"], det_cx=fit["det_cx"], bf_r2=fit["bf_r2"])
-        bfc = torch.empty((fit["n_bf"], n, n), dtype=torch.int32, device=dev)
-        ssb.ssb_gather_bf(frames, geom, bfc, fit["n_bf"])
+        pfit = ssb.ssb_fit_probe(sums.cpu().numpy().view(np.uint64), n, g.det_n)
+        geom = dataclasses.replace(g, det_cy=pfit["det_cy"], det_cx=pfit["det_cx"], bf_r2=pfit["bf_r2"])
+        bfc = torch.empty((pfit["n_bf"], n, n), dtype=torch.int32, device=dev)
+        ssb.ssb_gather_bf(frames, geom, bfc, pfit["n_bf"])
         t1 = time.perf_counter()
         for _ in range(3):
-            ssb.ssb_gather_bf(frames, geom, bfc, fit["n_bf"])   # synchronizes
+            ssb.ssb_gather_bf(frames, geom, bfc, pfit["n_bf"])   # synchronizes
         gather_ms = (time.perf_counter() - t1) * 1e3 / 3
         frame_bytes = n * n * d2 * 4
         detector = {"frames": [n * n, d2], "frame_bytes": frame_bytes,
                     "detector_sum_ms": sum_ms, "detector_sum_gbs": frame_bytes / sum_ms / 1e6,
                     "detector_sum_hbm_frac": round(frame_bytes / sum_ms / 1e6 / PEAK_HBM_GBS, 4),
-                    "fit": fit, "gather_ms_host_clock": gather_ms,
-                    "gather_gbs": 2 * fit["n_bf"] * n * n * 4 / gather_ms / 1e6}
+                    "fit": pfit, "gather_ms_host_clock": gather_ms,
+                    "gather_gbs": 2 * pfit["n_bf"] * n * n * 4 / gather_ms / 1e6}
         log(f"[bench] detector sum {sum_ms:.3f} ms ({detector['detector_sum_gbs']:.0f} GB/s), fit n_bf "
-            f"{fit['n_bf']} r^2 {fit['bf_r2']:.2f}, gather {gather_ms:.3f} ms")
+            f"{pfit['n_bf']} r^2 {pfit['bf_r2']:.2f}, gather {gather_ms:.3f} ms")
         del frames, bfc, sums
         torch.cuda.empty_cache()
+
+    scan1024 = None
+    if args.scan1024 and args.config == "full":
+        w2 = WORKLOADS["full1024"]
+        n2 = w2.geometry.scan_n
+        log(f"[bench] generating {w2.name} counts ({w2.n_bf} BF x {n2}^2)")
+        counts2 = make_counts_torch(w2, dev)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        h2 = ssb.ssb_prepare(w2.geometry, counts2, w2.n_bf)
+        torch.cuda.synchronize()
+        prep2 = (time.perf_counter() - t0) * 1e3
+        del counts2
+        torch.cuda.empty_cache()
+        info2 = ssb.ssb_query(h2)
+        p2 = np.array([w2.true_params], dtype=np.float32)
+        for _ in range(args.warmup):
+            ssb.ssb_loss(h2, p2)
+        torch.cuda.synchronize()
+        steps2 = max(3, min(args.steps, 10))
+        t1 = time.perf_counter()
+        for _ in range(steps2):
+            loss2 = ssb.ssb_loss(h2, p2)[0]
+        ms2 = (time.perf_counter() - t1) * 1e3 / steps2
+        ssb.ssb_profile(h2, 1)
+        for _ in range(3):
+            ssb.ssb_loss(h2, p2)
+        prof2 = ssb.ssb_profile(h2, 0)
+        phase2 = torch.empty((n2, n2), dtype=torch.float32, device=dev)
+        ssb.ssb_object(h2, p2[0], phase2)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for _ in range(3):
+            ssb.ssb_object(h2, p2[0], phase2)
+        torch.cuda.synchronize()
+        obj2 = (time.perf_counter() - t1) * 1e3 / 3
+        ssb.ssb_release(h2)
+        del phase2
+        torch.cuda.empty_cache()
+        r2 = stage_rates(n2, info2, prof2)
+        dom2 = max(("pass1", "pass2"), key=lambda k: r2[k]["avg_launch_ms"])
+        scan1024 = {
+            "workload": f"{w2.name}: {n2}x{n2} scan, {w2.geometry.det_n}x{w2.geometry.det_n} detector, "
+                        f"{w2.n_bf} BF, one trial per evaluation",
+            "ms_per_eval": ms2, "samples_per_s": w2.n_bf * n2 * n2 / (ms2 * 1e-3), "loss": loss2,
+            "object_ms": obj2, "prepare_ms": prep2, "spectrum_gb": info2["spectrum_bytes"] / 1e9,
+            "chunk_bf": info2["chunk_bf"],
+            "roofline": {"bound": "hbm", "kernel": dom2, "achieved": round(r2[dom2]["gbs"], 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(r2[dom2]["gbs"] / PEAK_HBM_GBS, 4)},
+            "stages": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in r2[k].items()}
+                       for k in r2},
+            # notes page, "128 GB Apple M5 Max size-scaling follow-up": scalar evaluator
+            # 168.5 ms at 1024 on 2,476 compact planes of Fourier-resized evidence
+            "pages_context_ms": 168.538,
+        }
+        log(f"[bench] scan 1024: {ms2:.3f} ms/eval, pass1 {r2['pass1']['avg_launch_ms']:.3f} ms, "
+            f"pass2 {r2['pass2']['avg_launch_ms']:.3f} ms, object {obj2:.3f} ms")
 
     value = samples * args.steps / total_s
     pages_rate = samples / (PAGES_MS * 1e-3) if args.config == "full" else None
@@ -335,6 +410,7 @@ def main():
         "hbm": hbm,
         "cpu_baseline": cpu,
         "detector": detector,
+        "scan1024": scan1024,
         "oracle_check": oracle_check,
     }
     print(json.dumps(line), flush=True)
