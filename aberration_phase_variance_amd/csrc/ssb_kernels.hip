@@ -889,10 +889,11 @@ __global__ __launch_bounds__(256) void k_g_rows(const uint32_t* __restrict__ cou
 // pass 1 (exp(-i delta) from a per-BF row table in LDS, double buffered, and a
 // per-thread column phasor; exp(i chi_q) once per entry).  Tiles at or past a BF
 // pixel's last supported column skip it.  Partials per segment in double.
-constexpr int kObjThreads = 512;
+// 1024 threads at N = 1024 keep a thread's share of the tile at 8 entries, as at 512.
+template <int N> constexpr int obj_threads() { return N >= 1024 ? 1024 : 512; }
 
 template <int N, int TC>
-__global__ __launch_bounds__(kObjThreads) void k_obj_sum(const float2* __restrict__ gm,
+__global__ __launch_bounds__(obj_threads<N>()) void k_obj_sum(const float2* __restrict__ gm,
                                                          const float2* __restrict__ gn,
                                                          const double2* __restrict__ kb,
                                                          const uint4* __restrict__ sup,
@@ -900,7 +901,7 @@ __global__ __launch_bounds__(kObjThreads) void k_obj_sum(const float2* __restric
                                                          int64_t nbf, int seglen, double2* __restrict__ part) {
     constexpr int H = N / 2;
     constexpr int NE = N * (H + 1);
-    constexpr int NT = kObjThreads;
+    constexpr int NT = obj_threads<N>();
     constexpr int RS = NT / TC;
     constexpr int PER = (N + RS - 1) / RS;
     constexpr int PERN = (N + NT - 1) / NT;
@@ -1256,7 +1257,7 @@ static hipError_t obj_sum_n(const float2* gm, const float2* gn, const double2* k
                             hipStream_t st) {
     constexpr int TC = pass1_tc<N>();
     const int seglen = (int)((nbf + nseg - 1) / nseg);
-    hipLaunchKernelGGL((k_obj_sum<N, TC>), dim3(N / 2 / TC + 1, nseg), dim3(kObjThreads), 0, st, gm, gn, kb, sup,
+    hipLaunchKernelGGL((k_obj_sum<N, TC>), dim3(N / 2 / TC + 1, nseg), dim3(obj_threads<N>()), 0, st, gm, gn, kb, sup,
                        vend, tc, geo, nbf, seglen, part);
     return hipGetLastError();
 }
