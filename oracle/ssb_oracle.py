@@ -42,6 +42,16 @@ O12 S1 = sum_b phi_b (per scan pixel), S2 = sum_b sum_px phi_b^2;
     squared-phase partials: Notes, "Pack-aware column dispatch" passage).
 O13 Object: psi = ifft2(full plane of mean_b C_b), phase = angle(psi)
     ("phase-of-mean" output: Notes, "Standard-only CUDA native 512 calibration").
+
+Full-plane variant (functions with ``full_plane`` in their names).  Notes,
+"Automatic whole-probe sparse-storage checkpoint": the accepted evaluator
+corrects every entry of the N x N plane on its own; building the columns past
+N/2 from the anti-Hermitian relation (O9) moved the loss in the fourth digit,
+mostly through the Nyquist column, which has no positive-frequency partner.
+F5  q(u, v) = s * (v_signed, u_signed), fftfreq on both axes (v = N/2 -> -N/2).
+F3  G_b = fft2 of the counts (the whole complex plane).
+F8  C_b = G_b T on every entry, C_b(0, 0) = DC.
+F10 O_b = ifft2(C_b); phase, moments, loss and object as in O11-O13.
 """
 from __future__ import annotations
 
@@ -269,4 +279,71 @@ def object_wave(g, counts: np.ndarray, params3, dc: float | None = None):
         t = transfer(g, params3, kx_all[b], ky_all[b], qx, qy)
         acc += corrected_spectrum(scan_spectrum(counts[b]), t, dc)
     psi = bf_object(full_plane(acc / counts.shape[0]))
+    return bf_phase(psi), psi
+
+
+# ---------------------------------------------------------------- full-plane variant
+def q_vectors_full(g: OGeom):
+    """Scan frequencies of the full plane in detector pixels, rotated: (qx, qy), each (N, N).
+    Both axes signed as fftfreq, so u = N/2 and v = N/2 both map to -N/2."""
+    n = g.scan_n
+    f = np.fft.fftfreq(n) * n
+    sx = g.q_step_px * f[None, :] + 0.0 * f[:, None]
+    sy = g.q_step_px * f[:, None] + 0.0 * f[None, :]
+    if g.rotation_rad == 0.0:
+        return sx, sy
+    c, s = math.cos(g.rotation_rad), math.sin(g.rotation_rad)
+    return c * sx - s * sy, s * sx + c * sy
+
+
+def scan_spectrum_full(counts_b: np.ndarray) -> np.ndarray:
+    """Forward complex 2-D DFT of one BF pixel's scan counts, the whole (N, N) plane."""
+    return np.fft.fft2(np.asarray(counts_b, dtype=np.float64))
+
+
+def corrected_full_plane(g: OGeom, counts_b, params3, kbx, kby, dc, qx=None, qy=None):
+    """C_b on every entry of the full plane (each corrected on its own), DC at q = 0."""
+    if qx is None:
+        qx, qy = q_vectors_full(g)
+    c = scan_spectrum_full(counts_b) * transfer(g, params3, kbx, kby, qx, qy)
+    c[0, 0] = dc
+    return c
+
+
+def bf_moments_full_plane(g, counts: np.ndarray, params3, dc: float, bf_list=None):
+    """S1 (N, N) and S2 of the full-plane variant over the listed BF pixels (as bf_moments)."""
+    g = OGeom.from_any(g)
+    kx_all, ky_all = bf_kvectors(g)
+    if bf_list is None:
+        bf_list = np.arange(kx_all.size)
+    qx, qy = q_vectors_full(g)
+    n = g.scan_n
+    s1 = np.zeros((n, n), dtype=np.float64)
+    s2 = 0.0
+    for k, b in enumerate(bf_list):
+        c = corrected_full_plane(g, counts[k], params3, kx_all[b], ky_all[b], dc, qx, qy)
+        phi = bf_phase(bf_object(c))
+        s1 += phi
+        s2 += float(np.sum(phi * phi))
+    return s1, s2
+
+
+def loss_full_plane(g, counts: np.ndarray, params3, dc: float | None = None) -> float:
+    if dc is None:
+        dc = dc_value(counts)
+    s1, s2 = bf_moments_full_plane(g, counts, params3, dc)
+    return loss_from_moments(s1, s2, counts.shape[0])
+
+
+def object_wave_full_plane(g, counts: np.ndarray, params3, dc: float | None = None):
+    """Phase-of-mean object of the full-plane variant: psi = ifft2(mean_b C_b); (phase, psi)."""
+    g = OGeom.from_any(g)
+    if dc is None:
+        dc = dc_value(counts)
+    kx_all, ky_all = bf_kvectors(g)
+    qx, qy = q_vectors_full(g)
+    acc = np.zeros((g.scan_n, g.scan_n), dtype=np.complex128)
+    for b in range(counts.shape[0]):
+        acc += corrected_full_plane(g, counts[b], params3, kx_all[b], ky_all[b], dc, qx, qy)
+    psi = bf_object(acc / counts.shape[0])
     return bf_phase(psi), psi
