@@ -52,6 +52,8 @@ class ssb_info(ctypes.Structure):
         ("support_entries", ctypes.c_int64),
         ("columns_written", ctypes.c_int64),
         ("columns_read", ctypes.c_int64),
+        ("variant", ctypes.c_int32),
+        ("pad", ctypes.c_int32),
     ]
 
 
@@ -110,7 +112,7 @@ class ssb_probe_fit(ctypes.Structure):
 
 EXPORTS = ("ssb_prepare", "ssb_loss", "ssb_moments", "ssb_object", "ssb_spectrum", "ssb_set_chunk",
            "ssb_profile", "ssb_query", "ssb_release", "ssb_last_error", "ssb_nelder_mead", "ssb_fit",
-           "ssb_detector_sum", "ssb_fit_probe", "ssb_gather_bf")
+           "ssb_detector_sum", "ssb_fit_probe", "ssb_gather_bf", "ssb_set_variant")
 
 _lib = None
 
@@ -131,6 +133,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ssb_object.argtypes = [vp, fp, vp, vp, vp]
     lib.ssb_spectrum.argtypes = [vp, i64, vp, vp]
     lib.ssb_set_chunk.argtypes = [vp, i64]
+    lib.ssb_set_variant.argtypes = [vp, i32]
     lib.ssb_profile.argtypes = [vp, ctypes.c_int, ctypes.POINTER(ssb_profile_data)]
     lib.ssb_query.argtypes = [vp, ctypes.POINTER(ssb_info)]
     lib.ssb_release.argtypes = [vp]
@@ -229,6 +232,16 @@ def ssb_spectrum(handle: int, bf: int, out, stream=None) -> None:
 
 def ssb_set_chunk(handle: int, chunk_bf: int) -> None:
     _check(load_library().ssb_set_chunk(handle, int(chunk_bf)))
+
+
+SSB_VARIANT_HALF_PLANE = 0
+SSB_VARIANT_FULL_PLANE = 1
+
+
+def ssb_set_variant(handle: int, variant: int) -> None:
+    """0: corrected half plane with the anti-Hermitian extension (default); 1: every entry
+    of the full plane corrected on its own."""
+    _check(load_library().ssb_set_variant(handle, int(variant)))
 
 
 def ssb_profile(handle: int, mode: int = 2) -> dict:

@@ -76,6 +76,7 @@ struct ssb_handle {
     GeomDev geo;
     double dc;
     int64_t chunk_user;
+    int variant;          // SSB_VARIANT_HALF_PLANE or SSB_VARIANT_FULL_PLANE
     float2* gm = nullptr;
     float2* gn = nullptr;
     double2* kb = nullptr;
@@ -196,7 +197,9 @@ TrialConst trial_const(const ssb_handle* h, const float* p) {
 struct LossPlan {
     int cap;       // BF capacity of one chunk (multiple of kGroupBF)
     int gcap;      // groups per chunk
-    size_t off_im, off_in, off_ps1, off_ps2, off_s1, off_s2, off_loss, off_lpart, off_tc, off_chm, off_chn, total;
+    size_t off_im, off_in, off_ps1, off_ps2, off_s1, off_s2, off_loss, off_lpart, off_tc, off_chm, off_chn;
+    size_t off_na, off_nb;   // full-plane variant only (else 0)
+    size_t total;
 };
 
 LossPlan plan_loss(const ssb_handle* h, int64_t nb, int n_trials) {
@@ -227,6 +230,11 @@ LossPlan plan_loss(const ssb_handle* h, int64_t nb, int n_trials) {
     pl.off_tc = (size_t)align_up<TrialConst>(z, off, (size_t)n_trials);
     pl.off_chm = (size_t)align_up<float2>(z, off, (size_t)n_trials * n * hh);
     pl.off_chn = (size_t)align_up<float2>(z, off, (size_t)n_trials * n);
+    pl.off_na = pl.off_nb = 0;
+    if (h->variant == SSB_VARIANT_FULL_PLANE) {
+        pl.off_na = (size_t)align_up<float2>(z, off, (size_t)n_trials * cap * n);
+        pl.off_nb = (size_t)align_up<float2>(z, off, (size_t)n_trials * cap * n);
+    }
     pl.total = off + 256;
     return pl;
 }
@@ -266,6 +274,9 @@ int run_moments(ssb_handle* h, const float* params, int n_trials, int64_t b_begi
     TrialConst* tc = reinterpret_cast<TrialConst*>(h->ws + pl.off_tc);
     float2* chm = reinterpret_cast<float2*>(h->ws + pl.off_chm);
     float2* chn = reinterpret_cast<float2*>(h->ws + pl.off_chn);
+    const bool fp = h->variant == SSB_VARIANT_FULL_PLANE;
+    float2* nyq_a = fp ? reinterpret_cast<float2*>(h->ws + pl.off_na) : nullptr;
+    float2* nyq_b = fp ? reinterpret_cast<float2*>(h->ws + pl.off_nb) : nullptr;
 
     htc.resize(n_trials);
     for (int t = 0; t < n_trials; ++t) htc[t] = trial_const(h, params + 3 * t);
@@ -287,11 +298,15 @@ int run_moments(ssb_handle* h, const float* params, int n_trials, int64_t b_begi
             SSB_HIP(launch_pass1(h->n, h->gm, h->gn, chm, chn, h->kb, h->sup, h->vend, tc, n_trials, h->geo, c0, cb,
                                  pl.cap, im, in, st),
                     "pass 1 launch");
+            if (fp)
+                SSB_HIP(launch_nyq_lines(h->n, h->gm, h->gn, h->kb, h->active, tc, n_trials, h->geo, c0, cb, pl.cap,
+                                         nyq_a, nyq_b, h->tw, st),
+                        "Nyquist-line launch");
         }
         {
             StageTimer tm(h, SSB_STAGE_PASS2, st, units);
             SSB_HIP(launch_pass2(h->n, im, in, pl.cap, h->active, h->vend, c0, cb, n_trials, h->dc, ps1, ps2,
-                                 pl.gcap, h->tw, st),
+                                 pl.gcap, h->tw, nyq_a, nyq_b, st),
                     "pass 2 launch");
         }
         {
@@ -380,6 +395,7 @@ int ssb_prepare(const ssb_geometry* g, const uint32_t* counts, int64_t n_bf, voi
         h->active_prefix.push_back(h->n_active);
     }
     h->chunk_user = 0;
+    h->variant = SSB_VARIANT_HALF_PLANE;
     (void)hipGetDevice(&h->device);
     GeomDev& geo = h->geo;
     geo.n = n;
@@ -528,15 +544,23 @@ int ssb_object(ssb_handle* h, const float* params3, float* phase, float* psi, vo
     const size_t o_part = (size_t)align_up<double2>(z, off, ne * nseg);
     const size_t o_pm = (size_t)align_up<float2>(z, off, (size_t)n * hh);
     const size_t o_pn = (size_t)align_up<float2>(z, off, (size_t)n);
+    const bool fp = h->variant == SSB_VARIANT_FULL_PLANE;
+    const size_t o_npart = fp ? (size_t)align_up<double2>(z, off, (size_t)2 * n * nseg) : 0;
+    const size_t o_nab = fp ? (size_t)align_up<float2>(z, off, (size_t)2 * n) : 0;
     if ((rc = ensure(&h->ows, &h->ows_bytes, off + 256, "object workspace allocation"))) return rc;
     double2* part = reinterpret_cast<double2*>(h->ows + o_part);
     float2* pm = reinterpret_cast<float2*>(h->ows + o_pm);
     float2* pn = reinterpret_cast<float2*>(h->ows + o_pn);
+    float2* nab = fp ? reinterpret_cast<float2*>(h->ows + o_nab) : nullptr;
     const TrialConst tc = trial_const(h, params3);   // kernel argument: no host-staged copy
     {
         StageTimer tm(h, SSB_STAGE_OBJ_SUM, st, h->n_active);
         SSB_HIP(launch_obj_sum(n, h->gm, h->gn, h->kb, h->sup, h->vend, tc, h->geo, h->n_bf, part, nseg, st),
                 "object sum");
+        if (fp)
+            SSB_HIP(launch_obj_nyq(n, h->gm, h->gn, h->kb, h->vend, tc, h->geo, h->n_bf,
+                                   reinterpret_cast<double2*>(h->ows + o_npart), nseg, nab, h->tw, st),
+                    "object Nyquist lines");
     }
     {
         StageTimer tm(h, SSB_STAGE_OBJ_FFT, st, 0);
@@ -544,7 +568,7 @@ int ssb_object(ssb_handle* h, const float* params3, float* phase, float* psi, vo
         SSB_HIP(launch_obj_cols(n, pm, pn, h->tw, st), "object columns");
         const double dcsum = h->dc * (double)h->n_bf;
         const double scale = 1.0 / ((double)h->n_bf * (double)n * (double)n);
-        SSB_HIP(launch_obj_rows(n, pm, pn, dcsum, scale, phase, reinterpret_cast<float2*>(psi), h->tw, st),
+        SSB_HIP(launch_obj_rows(n, pm, pn, dcsum, scale, phase, reinterpret_cast<float2*>(psi), h->tw, nab, st),
                 "object rows");
     }
     return SSB_OK;
@@ -578,6 +602,17 @@ int ssb_set_chunk(ssb_handle* h, int64_t chunk_bf) {
     if (rc) return rc;
     if (chunk_bf < 0) return fail(SSB_EINVAL, "chunk_bf must be >= 0");
     h->chunk_user = chunk_bf;
+    return SSB_OK;
+}
+
+int ssb_set_variant(ssb_handle* h, int32_t variant) {
+    g_err.clear();
+    int rc = check_handle(h);
+    if (rc) return rc;
+    if (variant != SSB_VARIANT_HALF_PLANE && variant != SSB_VARIANT_FULL_PLANE)
+        return fail(SSB_EINVAL, "variant must be SSB_VARIANT_HALF_PLANE (0) or SSB_VARIANT_FULL_PLANE (1), got %d",
+                    (int)variant);
+    h->variant = variant;
     return SSB_OK;
 }
 
@@ -622,6 +657,8 @@ int ssb_query(const ssb_handle* h, ssb_info* info) {
     info->support_entries = h->support_entries;
     info->columns_written = h->columns_written;
     info->columns_read = h->columns_read;
+    info->variant = h->variant;
+    info->pad = 0;
     return SSB_OK;
 }
 

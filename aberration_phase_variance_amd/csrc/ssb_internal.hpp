@@ -65,7 +65,13 @@ hipError_t launch_pass1(int n, const float2* gm, const float2* gn, const float2*
 // Pass 2: row transforms, atan2 and moments, one partial per 32-BF group.
 hipError_t launch_pass2(int n, const float2* im, const float2* in, int cap, const uint8_t* active,
                         const int* vend, int64_t bf0, int cb, int n_trials, double dc, float* part_s1,
-                        double* part_s2, int gcap, const float2* tw_inv, hipStream_t st);
+                        double* part_s2, int gcap, const float2* tw_inv, const float2* na, const float2* nb,
+                        hipStream_t st);
+// Full-plane variant: the Nyquist-line terms A, B ([t][cap][N] each) of the chunk's
+// BF pixels (pass 2 adds them when na is not null).
+hipError_t launch_nyq_lines(int n, const float2* gm, const float2* gn, const double2* kb, const uint8_t* active,
+                            const TrialConst* tc, int n_trials, GeomDev geo, int64_t bf0, int cb, int cap, float2* na,
+                            float2* nb, const float2* tw_inv, hipStream_t st);
 // Correction support per (BF, column) from the geometry: sup [n_bf][N/2+1] of four
 // packed (lo, len) row intervals (minus/plus aperture, nonzero weight / flat top),
 // vend [n_bf] = 1 + the last column with any support (0 for an inactive BF), and
@@ -89,7 +95,12 @@ hipError_t launch_obj_sum(int n, const float2* gm, const float2* gn, const doubl
 hipError_t launch_obj_reduce(int n, const double2* part, int nseg, float2* pm, float2* pn,
                              hipStream_t st);
 hipError_t launch_obj_cols(int n, float2* pm, float2* pn, const float2* tw_inv, hipStream_t st);
-hipError_t launch_obj_rows(int n, const float2* pm, const float2* pn, double dcsum, double scale,
-                           float* phase, float2* psi, const float2* tw_inv, hipStream_t st);
+hipError_t launch_obj_rows(int n, const float2* pm, const float2* pn, double dcsum, double scale, float* phase,
+                           float2* psi, const float2* tw_inv, const float2* nab, hipStream_t st);
+// Full-plane object: BF sums of the Nyquist-line terms, nab = [A | B] (2N complex);
+// part holds nseg x 2N double2 partials.
+hipError_t launch_obj_nyq(int n, const float2* gm, const float2* gn, const double2* kb, const int* vend,
+                          TrialConst tc, GeomDev geo, int64_t nbf, double2* part, int nseg, float2* nab,
+                          const float2* tw_inv, hipStream_t st);
 
 }  // namespace ssb

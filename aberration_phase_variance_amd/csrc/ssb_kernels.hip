@@ -375,6 +375,98 @@ __device__ __forceinline__ float2 correct_entry(float2 g, float2 ch, float2 e, b
     return cmul(g, make_float2(e.x * br - e.y * bi, e.x * bi + e.y * br));
 }
 
+// Corrected value of the entry at signed row up and signed column v, any lattice
+// point (including the column -N/2 and the row +N/2, which the half-plane tables do
+// not hold): support and flat-top flags from the shifted distances themselves (the
+// rule the support tables encode), exp(i chi_q) in double, E_u(up) E_v(v).  The same
+// bits as the table path for an entry both can form.
+__device__ float2 correct_direct(float2 g, int up, int v, double kx, double ky, const TrialConst& m,
+                                 const GeomDev& geo, double alpha, double beta) {
+    const double rm = shifted_r2(kx, ky, -1.0, up, v, geo);
+    const double rp = shifted_r2(kx, ky, 1.0, up, v, geo);
+    const bool inm = rm < geo.hi2, inp = rp < geo.hi2;
+    if (!inm && !inp) return make_float2(0.f, 0.f);
+    const bool edm = inm && !(geo.lo2 >= 0.0 && rm <= geo.lo2);
+    const bool edp = inp && !(geo.lo2 >= 0.0 && rp <= geo.lo2);
+    const float2 ch = chi_phasor(fma(geo.qux, (double)up, geo.qvx * v), fma(geo.quy, (double)up, geo.qvy * v), m);
+    const float2 e = cmul(phasor_rev_neg((double)up * beta), phasor_rev_neg((double)v * alpha));
+    return correct_entry(g, ch, e, inm, inp, edm, edp, up, v, kx, ky, geo);
+}
+
+// Full-plane variant, the Nyquist lines of one BF pixel.  Correcting every entry of
+// the N x N plane on its own differs from the half plane's anti-Hermitian extension
+// only on the Nyquist column and row: off them, -q of a lattice q is again a lattice
+// point, G(-q) = conj G(q) and T(-q) = -conj T(q).  The object therefore gains
+//   (-1)^x A(y) + (-1)^y B(x)    (unnormalized, as the row pass's values),
+// A = inverse transform over u of dC(u) = G(u, N/2) [T(u, -N/2) - T(u, +N/2)], and
+// B = inverse transform over v of dR(v) = conj(G(N/2, v') [T(-N/2, v') - T(+N/2, v')])
+// at v = N - v' for v' = 1 .. N/2 - 1 (zero elsewhere).  (u, v) are the signed
+// row and column of q.
+__device__ __forceinline__ float2 nyq_col_delta(float2 g, int up, double kx, double ky, const TrialConst& m,
+                                                const GeomDev& geo, double alpha, double beta) {
+    const int H = geo.h;
+    const float2 a = correct_direct(g, up, -H, kx, ky, m, geo, alpha, beta);
+    const float2 b = correct_direct(g, up, H, kx, ky, m, geo, alpha, beta);
+    return make_float2(a.x - b.x, a.y - b.y);
+}
+__device__ __forceinline__ float2 nyq_row_delta(float2 g, int vp, double kx, double ky, const TrialConst& m,
+                                                const GeomDev& geo, double alpha, double beta) {
+    const int H = geo.h;
+    const float2 a = correct_direct(g, -H, vp, kx, ky, m, geo, alpha, beta);
+    const float2 b = correct_direct(g, H, vp, kx, ky, m, geo, alpha, beta);
+    return make_float2(a.x - b.x, -(a.y - b.y));
+}
+
+// A and B of every BF pixel of a chunk and trial: one workgroup per (BF, trial);
+// the deltas in LDS, then two wave-level inverse transforms.  Out: na, nb
+// [t][cap][N] (natural order).
+template <int N>
+__global__ __launch_bounds__(256) void k_nyq_lines(const float2* __restrict__ gm, const float2* __restrict__ gn,
+                                                   const double2* __restrict__ kb,
+                                                   const uint8_t* __restrict__ active,
+                                                   const TrialConst* __restrict__ tc, GeomDev geo, int64_t bf0,
+                                                   int cap, float2* __restrict__ na, float2* __restrict__ nb,
+                                                   const float2* __restrict__ twt) {
+    constexpr int H = N / 2;
+    using F = WaveFFT<N, +1>;
+    __shared__ float2 lc[fft_scratch<N>()];
+    __shared__ float2 lr[fft_scratch<N>()];
+    const int bl = blockIdx.x, t = blockIdx.y;
+    const int64_t b = bf0 + bl;
+    if (!active[b]) return;                       // pass 2 skips inactive BF pixels
+    const double2 k = kb[b];
+    const TrialConst m = tc[t];
+    double alpha, beta;
+    delta_slopes(k.x, k.y, m, geo, alpha, beta);
+    const int tid = threadIdx.x;
+    for (int u = tid; u < N; u += 256)
+        lc[u] = nyq_col_delta(gn[b * N + u], u < H ? u : u - N, k.x, k.y, m, geo, alpha, beta);
+    for (int v = tid; v < N; v += 256) {
+        float2 d = make_float2(0.f, 0.f);
+        if (v > H) {
+            const int vp = N - v;
+            d = nyq_row_delta(gm[b * N * H + tm_index(N, H, vp)], vp, k.x, k.y, m, geo, alpha, beta);
+        }
+        lr[v] = d;
+    }
+    __syncthreads();
+    const int lane = tid & 63;
+    const int grp = (tid >> 6) * F::W + lane / F::L;
+    const int j = lane % F::L;
+    if (grp < 2) {
+        float2* src = grp == 0 ? lc : lr;
+        float2* dst = (grp == 0 ? na : nb) + ((int64_t)t * cap + bl) * N;
+        F fft;
+        fft.load(twt, j);
+        float2 x[F::R];
+#pragma unroll
+        for (int r = 0; r < F::R; ++r) x[r] = src[j + r * F::L];
+        fft.run(x, src, j);
+#pragma unroll
+        for (int r = 0; r < F::R; ++r) dst[j + r * F::L] = x[r];
+    }
+}
+
 // Pass 1: correction + column inverse transforms.  One workgroup = one BF pixel x
 // one tile of TC columns (or the Nyquist column) x one trial; the waves share the
 // tile's column FFTs.  Tiles at or past the BF pixel's last supported column (vend) are
@@ -631,13 +723,17 @@ struct RowPairRaw {
 // registers (float) and the squared phase (double per lane).  With
 // SSB_PASS2_PREFETCH the next BF's column values are loaded while the current one
 // is transformed (off by default: the extra registers cost more than it hides).
-template <int N>
+// FP: the full-plane variant; each BF pixel's object gains (-1)^x A(y) + (-1)^y B(x)
+// from na, nb [t][cap][N] (k_nyq_lines), so the real part varies along a row and
+// every sample takes the general atan2.
+template <int N, bool FP>
 __global__ __launch_bounds__(256, SSB_PASS2_MIN_WAVES) void k_pass2(const float2* __restrict__ im, const float2* __restrict__ in,
                                                int cap, const uint8_t* __restrict__ active,
                                                const int* __restrict__ vend, int64_t bf0,
                                                int cb, float dcf, float* __restrict__ part_s1,
                                                double* __restrict__ part_s2, int gcap,
-                                               const float2* __restrict__ gtw) {
+                                               const float2* __restrict__ gtw,
+                                               const float2* __restrict__ na, const float2* __restrict__ nb) {
     // FFT twiddles from an LDS copy of the table (not registers: 4 waves per SIMD)
     using F = WaveFFTT<N, +1>;
     __shared__ float2 twt[F::TABLE];
@@ -693,35 +789,57 @@ __global__ __launch_bounds__(256, SSB_PASS2_MIN_WAVES) void k_pass2(const float2
 #endif
         float2 x[R];
         cur.assemble(j, x);
+        float2 av0, av1, bv[FP ? R : 1];
+        if constexpr (FP) {
+            const int64_t o = ((int64_t)t * cap + b) * N;
+            av0 = na[o + y0];
+            av1 = na[o + y0 + 1];
+#pragma unroll
+            for (int r = 0; r < R; ++r) bv[r] = nb[o + j + r * L];
+        }
         fft.run(x, buf[grp], j, twt);
         const float den0 = dcf + cur.z0.x + sgn * cur.h0.x;
         const float den1 = dcf + cur.z1.x + sgn * cur.h1.x;
         float p2 = 0.f;
-        // Re O > 0 and |Im O| <= Re O for every sample of the wave: atan2 is the
-        // odd polynomial of Im O / Re O, with one reciprocal per row (the real part
-        // depends on the pixel only through its parity).  Bitwise the same result
-        // as the general atan2 on those inputs.
-        bool easy = den0 > 0.f && den1 > 0.f;
-#pragma unroll
-        for (int r = 0; r < R; ++r) easy = easy && fabsf(x[r].x) <= den0 && fabsf(x[r].y) <= den1;
-        if (__all(easy)) {
-            const float i0 = __builtin_amdgcn_rcpf(den0), i1 = __builtin_amdgcn_rcpf(den1);
+        if constexpr (FP) {
+            // rows y0 (even: (-1)^y = +1) and y0 + 1 (odd: -1)
+            const float r0 = fmaf(sgn, av0.x, den0), i0 = sgn * av0.y;
+            const float r1 = fmaf(sgn, av1.x, den1), i1 = sgn * av1.y;
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                const float pa = atan_unit(x[r].x * i0);
-                const float pb = atan_unit(x[r].y * i1);
+                const float pa = atan2_f(x[r].x + i0 + bv[r].y, r0 + bv[r].x);
+                const float pb = atan2_f(x[r].y + i1 - bv[r].y, r1 - bv[r].x);
                 s1a[r] += pa;
                 s1b[r] += pb;
                 p2 += pa * pa + pb * pb;
             }
         } else {
+            // Re O > 0 and |Im O| <= Re O for every sample of the wave: atan2 is the
+            // odd polynomial of Im O / Re O, with one reciprocal per row (the real part
+            // depends on the pixel only through its parity).  Bitwise the same result
+            // as the general atan2 on those inputs.
+            bool easy = den0 > 0.f && den1 > 0.f;
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const float pa = atan2_f(x[r].x, den0);
-                const float pb = atan2_f(x[r].y, den1);
-                s1a[r] += pa;
-                s1b[r] += pb;
-                p2 += pa * pa + pb * pb;
+            for (int r = 0; r < R; ++r) easy = easy && fabsf(x[r].x) <= den0 && fabsf(x[r].y) <= den1;
+            if (__all(easy)) {
+                const float i0 = __builtin_amdgcn_rcpf(den0), i1 = __builtin_amdgcn_rcpf(den1);
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const float pa = atan_unit(x[r].x * i0);
+                    const float pb = atan_unit(x[r].y * i1);
+                    s1a[r] += pa;
+                    s1b[r] += pb;
+                    p2 += pa * pa + pb * pb;
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const float pa = atan2_f(x[r].x, den0);
+                    const float pb = atan2_f(x[r].y, den1);
+                    s1a[r] += pa;
+                    s1b[r] += pb;
+                    p2 += pa * pa + pb * pb;
+                }
             }
         }
         s2 += (double)p2;
@@ -1023,10 +1141,13 @@ __global__ __launch_bounds__(256) void k_obj_reduce(const double2* __restrict__ 
     else pn[u] = val;
 }
 
-template <int N>
+// FP: the full-plane variant adds (-1)^x A(y) + (-1)^y B(x) from nab = [A | B]
+// (BF sums, k_obj_nyq_fin).
+template <int N, bool FP>
 __global__ __launch_bounds__(256) void k_obj_rows(const float2* __restrict__ pm, const float2* __restrict__ pn,
                                                   float dcs, float scale, float* __restrict__ phase,
-                                                  float2* __restrict__ psi, const float2* __restrict__ twt) {
+                                                  float2* __restrict__ psi, const float2* __restrict__ twt,
+                                                  const float2* __restrict__ nab) {
     constexpr int H = N / 2;
     using F = WaveFFT<N, +1>;
     constexpr int R = F::R, L = F::L;
@@ -1049,12 +1170,105 @@ __global__ __launch_bounds__(256) void k_obj_rows(const float2* __restrict__ pm,
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const int xx = j + r * L;
-        phase[y0 * N + xx] = atan2_f(x[r].x, den0);
-        phase[(y0 + 1) * N + xx] = atan2_f(x[r].y, den1);
-        if (psi) {
-            psi[y0 * N + xx] = make_float2(den0 * scale, x[r].x * scale);
-            psi[(y0 + 1) * N + xx] = make_float2(den1 * scale, x[r].y * scale);
+        float re0 = den0, im0 = x[r].x, re1 = den1, im1 = x[r].y;
+        if constexpr (FP) {
+            const float2 a0 = nab[y0], a1 = nab[y0 + 1], bx = nab[N + xx];
+            re0 = fmaf(sgn, a0.x, re0) + bx.x;
+            im0 = fmaf(sgn, a0.y, im0) + bx.y;
+            re1 = fmaf(sgn, a1.x, re1) - bx.x;
+            im1 = fmaf(sgn, a1.y, im1) - bx.y;
         }
+        phase[y0 * N + xx] = atan2_f(im0, re0);
+        phase[(y0 + 1) * N + xx] = atan2_f(im1, re1);
+        if (psi) {
+            psi[y0 * N + xx] = make_float2(re0 * scale, im0 * scale);
+            psi[(y0 + 1) * N + xx] = make_float2(re1 * scale, im1 * scale);
+        }
+    }
+}
+
+// Full-plane object: per BF segment (in order) the sums of dC(u) and dR(v) (the
+// Nyquist-line differences, as k_nyq_lines forms them), float per segment, in
+// double partials part [seg][2N] = [dC | dR].
+template <int N>
+__global__ __launch_bounds__(256) void k_obj_nyq(const float2* __restrict__ gm, const float2* __restrict__ gn,
+                                                 const double2* __restrict__ kb, const int* __restrict__ vend,
+                                                 TrialConst m, GeomDev geo, int64_t nbf, int seglen,
+                                                 double2* __restrict__ part) {
+    constexpr int H = N / 2;
+    constexpr int PC = (N + 255) / 256;
+    const int tid = threadIdx.x;
+    const int64_t b_lo = (int64_t)blockIdx.x * seglen;
+    const int64_t b_hi = min(nbf, b_lo + seglen);
+    float2 ac[PC], ar[PC];
+#pragma unroll
+    for (int i = 0; i < PC; ++i) {
+        ac[i] = make_float2(0.f, 0.f);
+        ar[i] = make_float2(0.f, 0.f);
+    }
+    for (int64_t b = b_lo; b < b_hi; ++b) {
+        if (vend[b] == 0) continue;               // inactive BF pixel: zero transfer
+        const double2 k = kb[b];
+        double alpha, beta;
+        delta_slopes(k.x, k.y, m, geo, alpha, beta);
+#pragma unroll
+        for (int i = 0; i < PC; ++i) {
+            const int u = tid + i * 256;
+            if (u < N) {
+                const float2 dc = nyq_col_delta(gn[b * N + u], u < H ? u : u - N, k.x, k.y, m, geo, alpha, beta);
+                ac[i].x += dc.x;
+                ac[i].y += dc.y;
+                if (u > H) {
+                    const int vp = N - u;
+                    const float2 dr = nyq_row_delta(gm[b * N * H + tm_index(N, H, vp)], vp, k.x, k.y, m, geo,
+                                                    alpha, beta);
+                    ar[i].x += dr.x;
+                    ar[i].y += dr.y;
+                }
+            }
+        }
+    }
+    double2* o = part + (int64_t)blockIdx.x * 2 * N;
+#pragma unroll
+    for (int i = 0; i < PC; ++i) {
+        const int u = tid + i * 256;
+        if (u < N) {
+            o[u] = make_double2(ac[i].x, ac[i].y);
+            o[N + u] = make_double2(ar[i].x, ar[i].y);
+        }
+    }
+}
+
+// Sum of the segment partials (in order, double), then A and B by two inverse
+// transforms: nab = [A (N) | B (N)].
+template <int N>
+__global__ __launch_bounds__(256) void k_obj_nyq_fin(const double2* __restrict__ part, int nseg,
+                                                     float2* __restrict__ nab, const float2* __restrict__ twt) {
+    using F = WaveFFT<N, +1>;
+    __shared__ float2 l2[2][fft_scratch<N>()];
+    const int tid = threadIdx.x;
+    for (int e = tid; e < 2 * N; e += 256) {
+        double ax = 0.0, ay = 0.0;
+        for (int sg = 0; sg < nseg; ++sg) {
+            const double2 p = part[(int64_t)sg * 2 * N + e];
+            ax += p.x;
+            ay += p.y;
+        }
+        l2[e / N][e % N] = make_float2((float)ax, (float)ay);
+    }
+    __syncthreads();
+    const int lane = tid & 63;
+    const int grp = (tid >> 6) * F::W + lane / F::L;
+    const int j = lane % F::L;
+    if (grp < 2) {
+        F fft;
+        fft.load(twt, j);
+        float2 x[F::R];
+#pragma unroll
+        for (int r = 0; r < F::R; ++r) x[r] = l2[grp][j + r * F::L];
+        fft.run(x, l2[grp], j);
+#pragma unroll
+        for (int r = 0; r < F::R; ++r) nab[grp * N + j + r * F::L] = x[r];
     }
 }
 
@@ -1194,18 +1408,39 @@ int pass2_row_blocks(int n) {
 template <int N>
 static hipError_t pass2_n(const float2* im, const float2* in, int cap, const uint8_t* active, const int* vend,
                           int64_t bf0, int cb, int n_trials, double dc, float* part_s1, double* part_s2, int gcap,
-                          const float2* tw, hipStream_t st) {
+                          const float2* tw, const float2* na, const float2* nb, hipStream_t st) {
     const int ng = (cb + kGroupBF - 1) / kGroupBF;
-    hipLaunchKernelGGL(k_pass2<N>, dim3(row_blocks<N>(), ng, n_trials), dim3(256), 0, st, im, in, cap, active,
-                       vend, bf0, cb, (float)dc, part_s1, part_s2, gcap, tw);
+    const dim3 grid(row_blocks<N>(), ng, n_trials);
+    if (na)
+        hipLaunchKernelGGL((k_pass2<N, true>), grid, dim3(256), 0, st, im, in, cap, active, vend, bf0, cb, (float)dc,
+                           part_s1, part_s2, gcap, tw, na, nb);
+    else
+        hipLaunchKernelGGL((k_pass2<N, false>), grid, dim3(256), 0, st, im, in, cap, active, vend, bf0, cb,
+                           (float)dc, part_s1, part_s2, gcap, tw, na, nb);
     return hipGetLastError();
 }
 
 hipError_t launch_pass2(int n, const float2* im, const float2* in, int cap, const uint8_t* active,
                         const int* vend, int64_t bf0, int cb, int n_trials, double dc, float* part_s1,
-                        double* part_s2, int gcap, const float2* tw_inv, hipStream_t st) {
+                        double* part_s2, int gcap, const float2* tw_inv, const float2* na, const float2* nb,
+                        hipStream_t st) {
     SSB_DISPATCH_N(n, (pass2_n<NN>(im, in, cap, active, vend, bf0, cb, n_trials, dc, part_s1, part_s2, gcap, tw_inv,
-                                   st)))
+                                   na, nb, st)))
+}
+
+template <int N>
+static hipError_t nyq_lines_n(const float2* gm, const float2* gn, const double2* kb, const uint8_t* active,
+                              const TrialConst* tc, int n_trials, GeomDev geo, int64_t bf0, int cb, int cap,
+                              float2* na, float2* nb, const float2* tw, hipStream_t st) {
+    hipLaunchKernelGGL(k_nyq_lines<N>, dim3(cb, n_trials), dim3(256), 0, st, gm, gn, kb, active, tc, geo, bf0, cap,
+                       na, nb, tw);
+    return hipGetLastError();
+}
+
+hipError_t launch_nyq_lines(int n, const float2* gm, const float2* gn, const double2* kb, const uint8_t* active,
+                            const TrialConst* tc, int n_trials, GeomDev geo, int64_t bf0, int cb, int cap, float2* na,
+                            float2* nb, const float2* tw_inv, hipStream_t st) {
+    SSB_DISPATCH_N(n, (nyq_lines_n<NN>(gm, gn, kb, active, tc, n_trials, geo, bf0, cb, cap, na, nb, tw_inv, st)))
 }
 
 hipError_t launch_support(int n, const double2* kb, const uint8_t* active, GeomDev geo, int64_t nbf, uint4* sup,
@@ -1285,15 +1520,37 @@ hipError_t launch_obj_cols(int n, float2* pm, float2* pn, const float2* tw_inv, 
 
 template <int N>
 static hipError_t obj_rows_n(const float2* pm, const float2* pn, double dcsum, double scale, float* phase,
-                             float2* psi, const float2* tw, hipStream_t st) {
-    hipLaunchKernelGGL(k_obj_rows<N>, dim3(row_blocks<N>()), dim3(256), 0, st, pm, pn, (float)dcsum, (float)scale,
-                       phase, psi, tw);
+                             float2* psi, const float2* tw, const float2* nab, hipStream_t st) {
+    if (nab)
+        hipLaunchKernelGGL((k_obj_rows<N, true>), dim3(row_blocks<N>()), dim3(256), 0, st, pm, pn, (float)dcsum,
+                           (float)scale, phase, psi, tw, nab);
+    else
+        hipLaunchKernelGGL((k_obj_rows<N, false>), dim3(row_blocks<N>()), dim3(256), 0, st, pm, pn, (float)dcsum,
+                           (float)scale, phase, psi, tw, nab);
     return hipGetLastError();
 }
 
 hipError_t launch_obj_rows(int n, const float2* pm, const float2* pn, double dcsum, double scale, float* phase,
-                           float2* psi, const float2* tw_inv, hipStream_t st) {
-    SSB_DISPATCH_N(n, (obj_rows_n<NN>(pm, pn, dcsum, scale, phase, psi, tw_inv, st)))
+                           float2* psi, const float2* tw_inv, const float2* nab, hipStream_t st) {
+    SSB_DISPATCH_N(n, (obj_rows_n<NN>(pm, pn, dcsum, scale, phase, psi, tw_inv, nab, st)))
+}
+
+template <int N>
+static hipError_t obj_nyq_n(const float2* gm, const float2* gn, const double2* kb, const int* vend, TrialConst tc,
+                            GeomDev geo, int64_t nbf, double2* part, int nseg, float2* nab, const float2* tw,
+                            hipStream_t st) {
+    const int seglen = (int)((nbf + nseg - 1) / nseg);
+    hipLaunchKernelGGL(k_obj_nyq<N>, dim3(nseg), dim3(256), 0, st, gm, gn, kb, vend, tc, geo, nbf, seglen, part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_obj_nyq_fin<N>, dim3(1), dim3(256), 0, st, part, nseg, nab, tw);
+    return hipGetLastError();
+}
+
+hipError_t launch_obj_nyq(int n, const float2* gm, const float2* gn, const double2* kb, const int* vend,
+                          TrialConst tc, GeomDev geo, int64_t nbf, double2* part, int nseg, float2* nab,
+                          const float2* tw_inv, hipStream_t st) {
+    SSB_DISPATCH_N(n, (obj_nyq_n<NN>(gm, gn, kb, vend, tc, geo, nbf, part, nseg, nab, tw_inv, st)))
 }
 
 }  // namespace ssb

@@ -79,6 +79,8 @@ typedef struct ssb_info {
     int64_t support_entries; /* half-plane entries with nonzero transfer, summed over BF (q = 0 aside) */
     int64_t columns_written; /* column results (N values each) the column pass writes per trial, all BF */
     int64_t columns_read;    /* column results the row pass reads per trial, all BF (zero columns skipped) */
+    int32_t variant;         /* SSB_VARIANT_HALF_PLANE or SSB_VARIANT_FULL_PLANE (ssb_set_variant) */
+    int32_t pad;
 } ssb_info;
 
 typedef struct ssb_handle ssb_handle;
@@ -154,6 +156,24 @@ int ssb_spectrum(const ssb_handle* h, int64_t bf, float* out, void* stream);
  * depend on it (bitwise); it bounds workspace memory.
  */
 int ssb_set_chunk(ssb_handle* h, int64_t chunk_bf);
+
+/*
+ * ssb_set_variant: which corrected plane ssb_loss, ssb_moments and ssb_object
+ * transform (per handle; default SSB_VARIANT_HALF_PLANE).
+ *
+ *   SSB_VARIANT_HALF_PLANE  the corrected half plane v = 0 .. N/2, extended to the
+ *       full plane by C(-q) = -conj(C(q)) (columns 0 and N/2 as computed, N/2 taken
+ *       as +N/2).  Notes page, "Automatic whole-probe sparse-storage checkpoint"
+ *       (the anti-Hermitian relation and its 257-row intermediate).
+ *   SSB_VARIANT_FULL_PLANE  every entry of the N x N plane corrected on its own,
+ *       index N/2 taken as -N/2 on both axes; the same passage's accepted evaluator.
+ *       It differs from the half plane only on the Nyquist column and row, which
+ *       the library adds to each BF pixel's object as two line terms.
+ *
+ * Errors: SSB_EINVAL (bad handle or variant).
+ */
+enum { SSB_VARIANT_HALF_PLANE = 0, SSB_VARIANT_FULL_PLANE = 1 };
+int ssb_set_variant(ssb_handle* h, int32_t variant);
 
 /*
  * Stage profiling.  When enabled, the library records a pair of HIP events on

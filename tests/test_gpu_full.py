@@ -169,3 +169,22 @@ def test_medium_loss_and_object():
         assert np.sqrt(np.mean(d * d)) <= PHASE_RMS
     finally:
         ssb.ssb_release(h)
+
+
+@pytest.mark.parametrize("b0,b1", [(0, 32), (8896, 8937)])
+def test_full_plane_variant_moments_sampled(full, b0, b1):
+    """The full-plane variant at full size: BF-range moments against the oracle's
+    full-plane definition (Nyquist transfer is nonzero for BF pixels near the disk edge)."""
+    w, counts, h = full
+    og = O.OGeom.from_any(w.geometry)
+    dc = ssb.ssb_query(h)["dc"]
+    params = [-137.0, 16.5, 2.7]
+    ssb.ssb_set_variant(h, ssb.SSB_VARIANT_FULL_PLANE)
+    try:
+        s1, s2 = _moments(h, 512, params, b0, b1)
+    finally:
+        ssb.ssb_set_variant(h, ssb.SSB_VARIANT_HALF_PLANE)
+    r1, r2 = O.bf_moments_full_plane(og, _host(counts, b0, b1), params, dc, list(range(b0, b1)))
+    assert abs(s2 - r2) <= LOSS_RTOL * abs(r2), b0
+    d = s1 - r1
+    assert np.sqrt(np.mean(d * d)) <= 2e-5 * (b1 - b0) and np.max(np.abs(d)) <= 1e-3, b0

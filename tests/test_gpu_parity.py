@@ -391,3 +391,110 @@ def test_error_paths_on_device(small):
     with pytest.raises(ssb.SSBError) as ei:
         ssb.ssb_prepare(w.geometry, dev, w.n_bf - 1)
     assert ei.value.code == ssb._ssb.SSB_ESHAPE
+
+
+# ---------------------------------------------------------------- full-plane variant
+@pytest.fixture
+def full_plane_tiny(tiny):
+    w, counts, p = tiny
+    ssb.ssb_set_variant(p.h, ssb.SSB_VARIANT_FULL_PLANE)
+    yield w, counts, p
+    ssb.ssb_set_variant(p.h, ssb.SSB_VARIANT_HALF_PLANE)
+
+
+def test_full_plane_loss_tiny(full_plane_tiny):
+    w, counts, p = full_plane_tiny
+    g = O.OGeom.from_any(w.geometry)
+    assert ssb.ssb_query(p.h)["variant"] == 1
+    params = np.array([[40.0, 5.0, 0.3], [0.0, 0.0, 0.0], [-73.5, 14.0, 0.47], [120.0, -8.0, 2.9]], np.float32)
+    got = p.loss(params)
+    for k in range(len(params)):
+        ref = O.loss_full_plane(g, counts, params[k])
+        half = O.loss(g, counts, params[k])
+        assert _rel(got[k], ref) <= LOSS_RTOL, (k, got[k], ref)
+        # the two variants differ here by more than the tolerance for some trial
+        if k == 0:
+            assert abs(ref - half) > 0.0
+    # single-trial calls repeat the batch bitwise
+    assert p.loss(params[2:3])[0] == got[2]
+
+
+def test_full_plane_differs_where_pages_say(full_plane_tiny):
+    """Switching the variant changes only the Nyquist-line terms: with the half plane
+    restored, the library returns its half-plane losses again, bitwise."""
+    w, counts, p = full_plane_tiny
+    params = [[-73.5, 14.0, 0.47]]
+    fp = p.loss(params)[0]
+    ssb.ssb_set_variant(p.h, ssb.SSB_VARIANT_HALF_PLANE)
+    hp1 = p.loss(params)[0]
+    ssb.ssb_set_variant(p.h, ssb.SSB_VARIANT_FULL_PLANE)
+    assert p.loss(params)[0] == fp
+    ssb.ssb_set_variant(p.h, ssb.SSB_VARIANT_HALF_PLANE)
+    assert p.loss(params)[0] == hp1
+    g = O.OGeom.from_any(w.geometry)
+    assert _rel(hp1, O.loss(g, counts, params[0])) <= LOSS_RTOL
+    ssb.ssb_set_variant(p.h, ssb.SSB_VARIANT_FULL_PLANE)
+
+
+def test_full_plane_moments_and_object_tiny(full_plane_tiny):
+    w, counts, p = full_plane_tiny
+    g = O.OGeom.from_any(w.geometry)
+    dc = O.dc_value(counts)
+    for params in ([40.0, 5.0, 0.3], [-55.0, 9.0, 1.9]):
+        s1, s2 = p.moments(params, 7, 45)
+        r1, r2 = O.bf_moments_full_plane(g, counts[7:45], params, dc, list(range(7, 45)))
+        assert _rel(s2, r2) <= LOSS_RTOL
+        assert np.max(np.abs(s1 - r1)) <= 1e-4 * 38 ** 0.5
+        phase, psi = p.obj(params)
+        ref_phase, ref_psi = O.object_wave_full_plane(g, counts, params)
+        d = np.angle(np.exp(1j * (phase - ref_phase)))
+        assert np.sqrt(np.mean(d * d)) <= PHASE_RMS
+        assert np.linalg.norm(psi - ref_psi) <= 1e-5 * np.linalg.norm(ref_psi)
+
+
+def test_full_plane_small_equals_half_plane(small):
+    """Hardly any transfer reaches the Nyquist lines at the small workload, where the
+    smooth specimen's spectrum is ~1e-9 of its peak: the variant's loss is the oracle's
+    and equals the half-plane loss to float rounding."""
+    w, counts, p = small
+    g = O.OGeom.from_any(w.geometry)
+    dc = O.dc_value(counts)
+    params = trial_params(w, 3)
+    half = p.loss(params)
+    ssb.ssb_set_variant(p.h, ssb.SSB_VARIANT_FULL_PLANE)
+    try:
+        full = p.loss(params)
+        phase, _ = p.obj(params[0], with_psi=False)
+    finally:
+        ssb.ssb_set_variant(p.h, ssb.SSB_VARIANT_HALF_PLANE)
+    for k in range(3):
+        assert _rel(full[k], O.loss_full_plane(g, counts, params[k], dc)) <= LOSS_RTOL
+        assert abs(full[k] - half[k]) <= 1e-9 * abs(half[k])
+    ref, _ = O.object_wave_full_plane(g, counts, params[0], dc)
+    assert np.sqrt(np.mean(np.angle(np.exp(1j * (phase - ref))) ** 2)) <= PHASE_RMS
+
+
+@pytest.mark.parametrize("n,d,r2", [(64, 16, 20), (256, 24, 36)])   # transfer reaches the Nyquist lines
+def test_full_plane_other_scan_sizes(n, d, r2):
+    w = _custom_workload(n, d, r2)
+    counts = cached_counts(w)
+    og = O.OGeom.from_any(w.geometry)
+    p = Prepared(w.geometry, counts)
+    try:
+        ssb.ssb_set_variant(p.h, ssb.SSB_VARIANT_FULL_PLANE)
+        for params in ([40.0, 5.0, 0.3], [-25.0, 7.0, 2.4]):
+            assert _rel(p.loss([params])[0], O.loss_full_plane(og, counts, params)) <= LOSS_RTOL
+        phase, _ = p.obj([40.0, 5.0, 0.3], with_psi=False)
+        ref, _ = O.object_wave_full_plane(og, counts, [40.0, 5.0, 0.3])
+        assert np.sqrt(np.mean(np.angle(np.exp(1j * (phase - ref))) ** 2)) <= PHASE_RMS
+    finally:
+        p.release()
+
+
+def test_variant_errors(tiny):
+    w, counts, p = tiny
+    for bad in (-1, 2, 7):
+        with pytest.raises(ssb.SSBError) as ei:
+            ssb.ssb_set_variant(p.h, bad)
+        assert ei.value.code == ssb._ssb.SSB_EINVAL
+    assert ssb.ssb_query(p.h)["variant"] == 0
