@@ -175,6 +175,29 @@ def main():
     ms_per_step = total_s * 1e3 / args.steps
     log(f"[bench] loss {loss:.9f}: {ms_per_step:.3f} ms/eval (p50 {np.median(times):.3f}, min {min(times):.3f})")
 
+    # the full-plane variant (every entry of the N x N plane corrected on its own)
+    ssb.ssb_set_variant(h, ssb.SSB_VARIANT_FULL_PLANE)
+    for _ in range(2):
+        ssb.ssb_loss(h, params)
+    fp_steps = max(3, min(args.steps, 10))
+    t1 = time.perf_counter()
+    for _ in range(fp_steps):
+        fp_loss = ssb.ssb_loss(h, params)[0]
+    fp_ms = (time.perf_counter() - t1) * 1e3 / fp_steps
+    fp_phase = torch.empty((n, n), dtype=torch.float32, device=dev)
+    ssb.ssb_object(h, params[0], fp_phase)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(3):
+        ssb.ssb_object(h, params[0], fp_phase)
+    torch.cuda.synchronize()
+    fp_obj_ms = (time.perf_counter() - t1) * 1e3 / 3
+    ssb.ssb_set_variant(h, ssb.SSB_VARIANT_HALF_PLANE)
+    del fp_phase
+    full_plane = {"ms_per_eval": fp_ms, "loss": fp_loss, "object_ms": fp_obj_ms,
+                  "loss_rel_diff_vs_half_plane": abs(fp_loss - loss) / abs(loss)}
+    log(f"[bench] full-plane variant: {fp_ms:.3f} ms/eval, loss {fp_loss:.9f}, object {fp_obj_ms:.3f} ms")
+
     # per-stage device times (HIP events on the library's stream), separate pass
     ssb.ssb_profile(h, 1)
     prof_steps = max(3, min(args.steps, 10))
@@ -367,7 +390,8 @@ def main():
             "object_ms": obj2, "prepare_ms": prep2, "spectrum_gb": info2["spectrum_bytes"] / 1e9,
             "chunk_bf": info2["chunk_bf"],
             "roofline": {"bound": "hbm", "kernel": dom2, "achieved": round(r2[dom2]["gbs"], 1), "peak": PEAK_HBM_GBS,
-                         "unit": "GB/s", "frac": round(r2[dom2]["gbs"] / PEAK_HBM_GBS, 4)},
+                         "unit": "GB/s", "frac": round(r2[dom2]["gbs"] / PEAK_HBM_GBS, 4),
+                         "traffic": measured_traffic(dom2 + "@1024")},
             "stages": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in r2[k].items()}
                        for k in r2},
             # notes page, "128 GB Apple M5 Max size-scaling follow-up": scalar evaluator
@@ -410,6 +434,7 @@ def main():
         "hbm": hbm,
         "cpu_baseline": cpu,
         "detector": detector,
+        "full_plane_variant": full_plane,
         "scan1024": scan1024,
         "oracle_check": oracle_check,
     }
