@@ -90,7 +90,16 @@ template <> struct FftShape<32>  { static constexpr int R = 2, P = 5; };
 template <> struct FftShape<1024> { static constexpr int R = 16, P = 3; };   // radices 16, 8, 8 (below)
 
 // LDS scratch (complex values) one transform's exchanges need.
-template <int N> constexpr int fft_scratch() { return N == 1024 ? N + N / 16 : N; }
+// Exchange address of register r after radix-8 pass p of the 512-point transform
+// in the padded layout p(i) = i + i/8 (one pad slot per 8 values, 576 slots): a lane
+// base plus a constant, so no lane addresses need to stay live.  Writes of pass 0:
+// p(8 j + r) = 9 j + r; writes of pass 1: p(64 (j/8) + j%8 + 8 r) = 72 (j/8) + j%8 + 9 r;
+// reads: p(j + 64 r) = j + j/8 + 72 r.  Unlike the XOR swizzles it leaves some 2-way
+// bank conflicts.
+__device__ __forceinline__ int pad512_write(int p, int j, int r) {
+    return p == 0 ? 9 * j + r : 72 * (j >> 3) + (j & 7) + 9 * r;
+}
+__device__ __forceinline__ int pad512_read(int j, int r) { return j + (j >> 3) + 72 * r; }
 
 // Bijective LDS index maps for the exchange after pass p.  The write and the
 // read of one exchange use the same map, so values are unchanged; the maps only
@@ -114,6 +123,7 @@ struct WaveFFT {
     static constexpr int L = N / R;        // lanes per FFT
     static constexpr int W = 64 / L;       // FFTs per wave
     static constexpr int NT = (P > 1 ? P - 1 : 1);
+    static constexpr int SCRATCH = N;      // LDS values one transform's exchanges use
 
     float2 tw[NT][R - 1];                  // per-lane twiddles of passes 1..P-1
 
@@ -207,6 +217,9 @@ struct WaveFFTT {
     static constexpr int L = N / R;
     static constexpr int W = 64 / L;
     static constexpr int TABLE = N - R;
+    // LDS values one transform's exchanges use: N = 512 takes the padded layout here,
+    // which keeps no lane addresses live across the row pass's loop
+    static constexpr int SCRATCH = N == 512 ? N + N / 8 : N;
 
     __device__ static void fill(float2* tab, int tid, int nthreads) {
         for (int e = tid; e < TABLE; e += nthreads) {
@@ -239,11 +252,19 @@ struct WaveFFTT {
             const int k = j & (ns - 1);
             const int bb = (j - k) * R + k;
             wave_lds_fence();
+            if constexpr (N == 512) {
 #pragma unroll
-            for (int r = 0; r < R; ++r) buf[exch_swizzle<N>(p, bb + r * ns)] = x[r];
-            wave_lds_fence();
+                for (int r = 0; r < R; ++r) buf[pad512_write(p, j, r)] = x[r];
+                wave_lds_fence();
 #pragma unroll
-            for (int r = 0; r < R; ++r) x[r] = buf[exch_swizzle<N>(p, j + r * L)];
+                for (int r = 0; r < R; ++r) x[r] = buf[pad512_read(j, r)];
+            } else {
+#pragma unroll
+                for (int r = 0; r < R; ++r) buf[exch_swizzle<N>(p, bb + r * ns)] = x[r];
+                wave_lds_fence();
+#pragma unroll
+                for (int r = 0; r < R; ++r) x[r] = buf[exch_swizzle<N>(p, j + r * L)];
+            }
             ns *= R;
         }
     }
@@ -296,7 +317,7 @@ __device__ __forceinline__ void dft16(float2 (&x)[16]) {
 }
 
 // LDS index map of the N = 1024 exchanges: one pad slot after every 16 values,
-// p(i) = i + i / 16, so a transform needs N + N/16 slots (fft_scratch).  Every
+// p(i) = i + i / 16, so a transform needs N + N/16 slots (SCRATCH).  Every
 // exchange address is then a per-lane base plus a per-register constant (the
 // instruction's immediate offset), and the stride-16 writes of pass 0 (17 j + r)
 // spread over the banks.  The transform below writes p out per access pattern
@@ -410,6 +431,7 @@ template <int SIGN>
 struct WaveFFTT<1024, SIGN> {
     static constexpr int N = 1024, R = 16, P = 3, L = 64, W = 1;
     static constexpr int TABLE = 7 * 16 + 7 * 128;
+    static constexpr int SCRATCH = N + N / 16;
 
     __device__ static void fill(float2* tab, int tid, int nthreads) {
         for (int e = tid; e < TABLE; e += nthreads) {
@@ -443,6 +465,7 @@ struct WaveFFTT<1024, SIGN> {
 template <int SIGN>
 struct WaveFFT<1024, SIGN> {
     static constexpr int N = 1024, R = 16, P = 3, L = 64, W = 1;
+    static constexpr int SCRATCH = N + N / 16;
     const float2* tab = nullptr;
 
     __device__ __forceinline__ void init(int) { tab = nullptr; }

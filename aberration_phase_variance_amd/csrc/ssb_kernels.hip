@@ -32,7 +32,7 @@ namespace {
 #define SSB_PASS1_THREADS 256 // pass-1 workgroup size
 #endif
 #ifndef SSB_PASS2_MIN_WAVES
-#define SSB_PASS2_MIN_WAVES 1 // pass-2 register budget hint: minimum resident waves per SIMD
+#define SSB_PASS2_MIN_WAVES 6 // pass-2 register budget (N <= 512, half plane): resident waves per SIMD
 #endif
 #ifndef SSB_PASS2_PREFETCH
 #define SSB_PASS2_PREFETCH 0  // pass 2 loads the next BF's column values during the current transform
@@ -196,9 +196,9 @@ template <int N, int MODE>
 __global__ __launch_bounds__(256) void k_cols(const float2* in_m, const float2* in_n, float2* out_m,
                                               float2* out_n, const float2* __restrict__ twt) {
     constexpr int H = N / 2;
-    constexpr int LD = fft_scratch<N>() + kPad;   // a column's slot is also its transform's scratch
     constexpr int SIGN = (MODE == COL_PLAIN_FWD) ? -1 : 1;
     using F = WaveFFT<N, SIGN>;
+    constexpr int LD = F::SCRATCH + kPad;   // a column's slot is also its transform's scratch
     constexpr int kTC = cols_tc<N>();
     __shared__ float2 tile[kTC * LD];
 
@@ -429,8 +429,8 @@ __global__ __launch_bounds__(256) void k_nyq_lines(const float2* __restrict__ gm
                                                    const float2* __restrict__ twt) {
     constexpr int H = N / 2;
     using F = WaveFFT<N, +1>;
-    __shared__ float2 lc[fft_scratch<N>()];
-    __shared__ float2 lr[fft_scratch<N>()];
+    __shared__ float2 lc[F::SCRATCH];
+    __shared__ float2 lr[F::SCRATCH];
     const int bl = blockIdx.x, t = blockIdx.y;
     const int64_t b = bf0 + bl;
     if (!active[b]) return;                       // pass 2 skips inactive BF pixels
@@ -498,7 +498,7 @@ __device__ __forceinline__ void pass1_tile(const float2* __restrict__ gsrc, cons
     constexpr int H = N / 2;
     // column pitch (a column's slot is also its transform's scratch): the 16 lanes of
     // one b64 LDS cycle hit distinct banks
-    constexpr int LD = fft_scratch<N>() + 16 / TC;
+    constexpr int LD = WaveFFT<N, +1>::SCRATCH + 16 / TC;
     constexpr int NT = pass1_threads<N>();
     constexpr int RS = NYQ ? NT : NT / TC;    // rows per sweep
     constexpr int PM = (N + RS - 1) / RS;     // entries per thread
@@ -611,17 +611,29 @@ __global__ __launch_bounds__(pass1_threads<N>()) void k_pass1(const float2* __re
                                                          int64_t bf0, int cap, float2* __restrict__ im,
                                                          float2* __restrict__ in) {
     constexpr int H = N / 2;
-    constexpr int LD = fft_scratch<N>() + 16 / TC;
+    constexpr int LD = WaveFFT<N, +1>::SCRATCH + 16 / TC;
     __shared__ float2 tile[TC * LD];
     __shared__ float2 eu[N];
 
     const int t = blockIdx.y;
-    // Workgroup -> (BF, tile): the H/TC main tiles of a BF, then its Nyquist tile.
-    // (Giving the two tiles that share 128-byte rows ids 8 apart, so that they run
-    // on the same XCD, halves the fetched bytes but measured slower.)
+    // Workgroup -> (BF, tile).  Up to N = 512 BF-major: the H/TC main tiles of a BF,
+    // then its Nyquist tile (the per-trial chi_q table, 1 MB, stays in L2 anyway).
+    // At N = 1024 tile-major: the workgroups running together share one column
+    // tile, so that tile's slice of the 4.2 MB chi_q table stays in L2 instead of
+    // being refetched for every BF pixel (pass 1 4.4 ms against 4.8 ms; BF-major
+    // is the faster order at 512).  (Giving the two tiles that share 128-byte rows
+    // ids 8 apart, so that they run on the same XCD, halves the fetched bytes at 512
+    // but measured slower.)
     constexpr int NTM = H / TC;
-    const int bl = (int)(blockIdx.x / (NTM + 1));
-    const int tix = (int)(blockIdx.x % (NTM + 1));
+    int bl, tix;
+    if constexpr (N >= 1024) {
+        const int cbk = (int)(gridDim.x / (NTM + 1));
+        tix = (int)(blockIdx.x / cbk);
+        bl = (int)(blockIdx.x % cbk);
+    } else {
+        bl = (int)(blockIdx.x / (NTM + 1));
+        tix = (int)(blockIdx.x % (NTM + 1));
+    }
     const int64_t b = bf0 + bl;
     const bool nyq = tix == NTM;
     const int v0 = nyq ? H : tix * TC;
@@ -726,8 +738,14 @@ struct RowPairRaw {
 // FP: the full-plane variant; each BF pixel's object gains (-1)^x A(y) + (-1)^y B(x)
 // from na, nb [t][cap][N] (k_nyq_lines), so the real part varies along a row and
 // every sample takes the general atan2.
+// Register budget: 80 VGPRs (6 waves per SIMD) fit the half-plane row pass up to
+// N = 512 without spills (measured 2.07 ms against 2.19 ms at 82 VGPRs, 5 waves);
+// the 1,024-point and full-plane forms keep the compiler's choice.
 template <int N, bool FP>
-__global__ __launch_bounds__(256, SSB_PASS2_MIN_WAVES) void k_pass2(const float2* __restrict__ im, const float2* __restrict__ in,
+constexpr int pass2_min_waves() { return (N <= 512 && !FP) ? SSB_PASS2_MIN_WAVES : 1; }
+
+template <int N, bool FP>
+__global__ __launch_bounds__(256, (pass2_min_waves<N, FP>())) void k_pass2(const float2* __restrict__ im, const float2* __restrict__ in,
                                                int cap, const uint8_t* __restrict__ active,
                                                const int* __restrict__ vend, int64_t bf0,
                                                int cb, float dcf, float* __restrict__ part_s1,
@@ -739,7 +757,7 @@ __global__ __launch_bounds__(256, SSB_PASS2_MIN_WAVES) void k_pass2(const float2
     __shared__ float2 twt[F::TABLE];
     constexpr int H = N / 2;
     constexpr int R = F::R, L = F::L;
-    __shared__ float2 buf[4 * F::W][fft_scratch<N>()];
+    __shared__ float2 buf[4 * F::W][F::SCRATCH];
     __shared__ double red[4];
 
     const int tid = threadIdx.x;
@@ -951,7 +969,7 @@ __global__ __launch_bounds__(256) void k_g_rows(const uint32_t* __restrict__ cou
     constexpr int H = N / 2;
     using F = WaveFFT<N, -1>;
     constexpr int R = F::R, L = F::L;
-    __shared__ float2 buf[4 * F::W][fft_scratch<N>()];
+    __shared__ float2 buf[4 * F::W][F::SCRATCH];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -1151,7 +1169,7 @@ __global__ __launch_bounds__(256) void k_obj_rows(const float2* __restrict__ pm,
     constexpr int H = N / 2;
     using F = WaveFFT<N, +1>;
     constexpr int R = F::R, L = F::L;
-    __shared__ float2 buf[4 * F::W][fft_scratch<N>()];
+    __shared__ float2 buf[4 * F::W][F::SCRATCH];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int grp = (tid >> 6) * F::W + lane / L;
@@ -1245,7 +1263,7 @@ template <int N>
 __global__ __launch_bounds__(256) void k_obj_nyq_fin(const double2* __restrict__ part, int nseg,
                                                      float2* __restrict__ nab, const float2* __restrict__ twt) {
     using F = WaveFFT<N, +1>;
-    __shared__ float2 l2[2][fft_scratch<N>()];
+    __shared__ float2 l2[2][F::SCRATCH];
     const int tid = threadIdx.x;
     for (int e = tid; e < 2 * N; e += 256) {
         double ax = 0.0, ay = 0.0;
