@@ -76,7 +76,7 @@ def _code(fn, *a):
     return ei.value.code
 
 
-@pytest.mark.parametrize("bad", [dict(scan_n=48), dict(scan_n=1024), dict(det_n=0), dict(dk=0.0),
+@pytest.mark.parametrize("bad", [dict(scan_n=48), dict(scan_n=2048), dict(scan_n=16), dict(det_n=0), dict(dk=0.0),
                                  dict(dk=float("nan")), dict(edge_px=-1.0), dict(alpha_rad=float("inf")),
                                  dict(bf_r2=-1.0), dict(rotation_rad=float("nan"))])
 def test_prepare_rejects_bad_geometry(bad):
@@ -102,6 +102,7 @@ def test_null_handle_calls():
     assert lib.ssb_object(None, p, None, None, None) == ssb._ssb.SSB_EINVAL
     assert lib.ssb_query(None, None) == ssb._ssb.SSB_EINVAL
     assert lib.ssb_set_chunk(None, 64) == ssb._ssb.SSB_EINVAL
+    assert lib.ssb_set_variant(None, 1) == ssb._ssb.SSB_EINVAL
     assert lib.ssb_moments(None, p, 0, 1, None, out, None) == ssb._ssb.SSB_EINVAL
     assert lib.ssb_prepare(None, None, 1, None, None) == ssb._ssb.SSB_EINVAL
     lib.ssb_release(None)          # no-op

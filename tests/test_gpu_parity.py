@@ -380,6 +380,11 @@ def test_error_paths_on_device(small):
     with pytest.raises(ssb.SSBError) as ei:
         p.loss([[float("nan"), 1.0, 0.0]])
     assert ei.value.code == ssb._ssb.SSB_EINVAL
+    with pytest.raises(ssb.SSBError) as ei:          # an empty batch
+        p.loss(np.zeros((0, 3), np.float32))
+    assert ei.value.code == ssb._ssb.SSB_EINVAL
+    # the handle still works after the errors
+    assert _rel(p.loss([[40.0, 5.0, 0.3]])[0], O.loss(O.OGeom.from_any(w.geometry), counts, (40.0, 5.0, 0.3))) <= LOSS_RTOL
     s1 = t.empty((128, 128), dtype=t.float64, device="cuda")
     for b0, b1 in ((-1, 5), (10, 10), (0, w.n_bf + 1)):
         with pytest.raises(ssb.SSBError) as ei:
