@@ -150,3 +150,25 @@ def test_1024_subdisk_loss_and_object(subdisk1024):
     ref_phase, _ = O.object_wave(og, counts, TRUE, dc)
     d = np.angle(np.exp(1j * (phase.cpu().numpy() - ref_phase)))
     assert np.sqrt(np.mean(d * d)) <= PHASE_RMS
+
+
+def test_1024_full_plane_variant_moments(full1024):
+    """The full-plane variant at N = 1024 on the ragged last BF range, against the oracle's
+    full-plane definition; and the variant's batch is bitwise its single-trial calls."""
+    w, counts, h = full1024
+    og = O.OGeom.from_any(w.geometry)
+    dc = ssb.ssb_query(h)["dc"]
+    params = [-137.0, 16.5, 2.7]
+    ssb.ssb_set_variant(h, ssb.SSB_VARIANT_FULL_PLANE)
+    try:
+        s1, s2 = _moments(h, params, 8896, 8937)
+        p = np.array([TRUE, params], np.float32)
+        batch = ssb.ssb_loss(h, p)
+        single = ssb.ssb_loss(h, p[1:2])[0]
+    finally:
+        ssb.ssb_set_variant(h, ssb.SSB_VARIANT_HALF_PLANE)
+    assert single == batch[1]
+    r1, r2 = O.bf_moments_full_plane(og, _host(counts, 8896, 8937), params, dc, list(range(8896, 8937)))
+    assert abs(s2 - r2) <= LOSS_RTOL * abs(r2)
+    d = s1 - r1
+    assert np.sqrt(np.mean(d * d)) <= 2e-5 * 41 and np.max(np.abs(d)) <= 1e-3
