@@ -212,8 +212,14 @@ __global__ __launch_bounds__(256) void k_cols(const float2* in_m, const float2* 
     float2* pout_n = out_n + (int64_t)plane * N;
 
     if (!nyq) {
-        const int c = tid % kTC;
-        for (int u = tid / kTC; u < N; u += 256 / kTC) tile[c * LD + u] = pin_m[tm_index(N, u, v0 + c)];
+        // all of the thread's loads in flight before the LDS stores
+        constexpr int ROWS = 256 / kTC, IT = N / ROWS;
+        const int c = tid % kTC, u0 = tid / kTC;
+        float2 v[IT];
+#pragma unroll
+        for (int k = 0; k < IT; ++k) v[k] = pin_m[tm_index(N, u0 + k * ROWS, v0 + c)];
+#pragma unroll
+        for (int k = 0; k < IT; ++k) tile[c * LD + u0 + k * ROWS] = v[k];
     } else {
         for (int u = tid; u < N; u += 256) tile[u] = pin_n[u];
     }
@@ -888,7 +894,16 @@ __global__ __launch_bounds__(256) void k_accum_s1(const float* __restrict__ part
     if (p >= n2) return;
     double acc = s1run[t * n2 + p];
     const float* src = part + (int64_t)t * gcap * n2 + p;
-    for (int g = 0; g < ng; ++g) acc += (double)src[(int64_t)g * n2];
+    // groups added in order; the loads of 8 groups are issued together
+    int g = 0;
+    for (; g + 8 <= ng; g += 8) {
+        float v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = src[(int64_t)(g + k) * n2];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc += (double)v[k];
+    }
+    for (; g < ng; ++g) acc += (double)src[(int64_t)g * n2];
     s1run[t * n2 + p] = acc;
 }
 
@@ -1148,7 +1163,18 @@ __global__ __launch_bounds__(256) void k_obj_reduce(const double2* __restrict__ 
     const int e = blockIdx.x * 256 + threadIdx.x;
     if (e >= NE) return;
     double ax = 0.0, ay = 0.0;
-    for (int s = 0; s < nseg; ++s) {
+    int s = 0;
+    for (; s + 8 <= nseg; s += 8) {             // segments added in order, 8 loads in flight
+        double2 p[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) p[k] = part[(int64_t)(s + k) * NE + e];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            ax += p[k].x;
+            ay += p[k].y;
+        }
+    }
+    for (; s < nseg; ++s) {
         const double2 p = part[(int64_t)s * NE + e];
         ax += p.x;
         ay += p.y;
