@@ -172,3 +172,24 @@ def test_1024_full_plane_variant_moments(full1024):
     assert abs(s2 - r2) <= LOSS_RTOL * abs(r2)
     d = s1 - r1
     assert np.sqrt(np.mean(d * d)) <= 2e-5 * 41 and np.max(np.abs(d)) <= 1e-3
+
+
+def test_1024_subdisk_full_plane_loss_and_object(subdisk1024):
+    """The full-plane variant's complete loss and object at N = 1024 on the 29-BF sub-disk."""
+    import torch
+    g, counts, hs = subdisk1024
+    og = O.OGeom.from_any(g)
+    dc = O.dc_value(counts)
+    ssb.ssb_set_variant(hs, ssb.SSB_VARIANT_FULL_PLANE)
+    try:
+        got = ssb.ssb_loss(hs, [TRUE])[0]
+        phase = torch.empty((N, N), dtype=torch.float32, device="cuda")
+        ssb.ssb_object(hs, TRUE, phase)
+        torch.cuda.synchronize()
+    finally:
+        ssb.ssb_set_variant(hs, ssb.SSB_VARIANT_HALF_PLANE)
+    ref = O.loss_full_plane(og, counts, TRUE, dc)
+    assert abs(got - ref) <= LOSS_RTOL * abs(ref), (got, ref)
+    ref_phase, _ = O.object_wave_full_plane(og, counts, TRUE, dc)
+    d = np.angle(np.exp(1j * (phase.cpu().numpy() - ref_phase)))
+    assert np.sqrt(np.mean(d * d)) <= PHASE_RMS
