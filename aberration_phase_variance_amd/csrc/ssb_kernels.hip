@@ -497,19 +497,22 @@ template <int N> constexpr int pass1_threads() { return N >= 1024 ? 512 : SSB_PA
 // One pass-1 tile; NYQ selects the Nyquist column at compile time so that every
 // row index, LDS address and load offset of the unrolled entry loops is a
 // compile-time step from the thread's first row.
+// Column pitch of the pass-1 LDS tile (a column's slot is also its transform's
+// scratch): 32/TC past the scratch, so that the correction's stores and loads (TC
+// columns x 32/TC rows per 32 lanes) hit distinct banks.
+template <int N, int TC> constexpr int pass1_ld() { return WaveFFT<N, +1>::SCRATCH + 32 / TC; }
+
 template <int N, int TC, bool NYQ>
 __device__ __forceinline__ void pass1_tile(const float2* __restrict__ gsrc, const float2* __restrict__ chsrc,
                                            const double2 k, const uint4 sr, const TrialConst& m, const GeomDev& geo,
-                                           float2* __restrict__ out, float2* tile, float2* eu, int v0) {
+                                           float2* __restrict__ out, float2* tile, float2* eu, int v0, int csub) {
     constexpr int H = N / 2;
-    // column pitch (a column's slot is also its transform's scratch): the 16 lanes of
-    // one b64 LDS cycle hit distinct banks
-    constexpr int LD = WaveFFT<N, +1>::SCRATCH + 16 / TC;
+    constexpr int LD = pass1_ld<N, TC>();
     constexpr int NT = pass1_threads<N>();
     constexpr int RS = NYQ ? NT : NT / TC;    // rows per sweep
     constexpr int PM = (N + RS - 1) / RS;     // entries per thread
-    constexpr int SSTRIDE = NYQ ? 1 : TC;     // row stride inside the source tile
-    static_assert(NYQ || TC == kTileW, "pass-1 tiles are the layout's tiles");
+    constexpr int SSTRIDE = NYQ ? 1 : kTileW; // row stride inside the source tile
+    static_assert(NYQ || kTileW % TC == 0, "a pass-1 tile is part of one layout tile");
     static_assert(PM <= 16, "two support bits per entry in one 32-bit word");
     using F = WaveFFT<N, +1>;
 
@@ -521,10 +524,11 @@ __device__ __forceinline__ void pass1_tile(const float2* __restrict__ gsrc, cons
     const int lo_p = unpack_lo(sr.y), len_p = unpack_len(sr.y);
 
     // 1. support and loads into registers (all loads in flight together)
-    // gsrc / chsrc: this tile's block (main: [N][TC] tile-major) or the Nyquist column
-    const __amdgpu_buffer_rsrc_t rg = make_rsrc(gsrc, N * (NYQ ? 1 : TC) * 8);
-    const __amdgpu_buffer_rsrc_t rc = make_rsrc(chsrc, N * (NYQ ? 1 : TC) * 8);
-    const int off0 = (ustart * SSTRIDE + c) * 8;
+    // gsrc / chsrc: the layout tile's block (main: [N][kTileW]; this workgroup's
+    // columns start at csub) or the Nyquist column
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(gsrc, N * (NYQ ? 1 : kTileW) * 8);
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(chsrc, N * (NYQ ? 1 : kTileW) * 8);
+    const int off0 = (ustart * SSTRIDE + csub + c) * 8;
     float2 gv[PM], chv[PM];
     unsigned bits = 0;
 #pragma unroll
@@ -595,11 +599,11 @@ __device__ __forceinline__ void pass1_tile(const float2* __restrict__ gsrc, cons
     }
     __syncthreads();
 
-    // 4. store (out: this tile's block of the column-result plane, or the Nyquist column)
+    // 4. store (out: the layout tile's block of the column-result plane, or the Nyquist column)
     if (!NYQ) {
-        float2* om = out + c;
+        float2* om = out + csub + c;
 #pragma unroll 4
-        for (int y = ustart; y < N; y += RS) om[(int64_t)y * TC] = tile[c * LD + y];
+        for (int y = ustart; y < N; y += RS) om[(int64_t)y * kTileW] = tile[c * LD + y];
     } else {
         for (int y = tid; y < N; y += NT) out[y] = tile[y];
     }
@@ -617,7 +621,7 @@ __global__ __launch_bounds__(pass1_threads<N>()) void k_pass1(const float2* __re
                                                          int64_t bf0, int cap, float2* __restrict__ im,
                                                          float2* __restrict__ in) {
     constexpr int H = N / 2;
-    constexpr int LD = WaveFFT<N, +1>::SCRATCH + 16 / TC;
+    constexpr int LD = pass1_ld<N, TC>();
     __shared__ float2 tile[TC * LD];
     __shared__ float2 eu[N];
 
@@ -643,17 +647,21 @@ __global__ __launch_bounds__(pass1_threads<N>()) void k_pass1(const float2* __re
     const int64_t b = bf0 + bl;
     const bool nyq = tix == NTM;
     const int v0 = nyq ? H : tix * TC;
-    if (v0 >= vend[b]) return;                    // all-zero columns (every column of an inactive BF)
+    const int lt = v0 / kTileW;                   // the layout tile holding these columns
+    // layout tiles wholly past the last supported column are all zero (every column
+    // of an inactive BF); they are neither computed nor written, and pass 2 reads
+    // them as zeros.  A layout tile with any supported column is written whole.
+    if ((nyq ? H : lt * kTileW) >= vend[b]) return;
     const double2 k = kb[b];
     const TrialConst m = tc[t];
     if (!nyq) {
         const int v = v0 + (int)threadIdx.x % TC;
-        const int64_t tb = (int64_t)tix * N * TC;        // this tile's block in a plane
+        const int64_t tb = (int64_t)lt * N * kTileW;      // the layout tile's block in a plane
         pass1_tile<N, TC, false>(gm + b * N * H + tb, chm + (int64_t)t * N * H + tb, k, sup[b * (H + 1) + v], m, geo,
-                                 im + ((int64_t)t * cap + bl) * N * H + tb, tile, eu, v0);
+                                 im + ((int64_t)t * cap + bl) * N * H + tb, tile, eu, v0, v0 - lt * kTileW);
     } else {
         pass1_tile<N, TC, true>(gn + b * N, chn + (int64_t)t * N, k, sup[b * (H + 1) + H], m, geo,
-                                in + ((int64_t)t * cap + bl) * N, tile, eu, v0);
+                                in + ((int64_t)t * cap + bl) * N, tile, eu, v0, 0);
     }
 }
 
@@ -1347,7 +1355,10 @@ hipError_t cols_n(const float2* in_m, const float2* in_n, float2* out_m, float2*
     return hipSuccess;
 }
 
-// Column tile of pass 1 and of the object sum: one tile of the tile-major layout.
+// Columns per pass-1 workgroup: one layout tile.  (Half tiles, 4 columns with 256
+// threads, reach 7 waves per SIMD at 71 VGPRs but ran 6.2-6.5 ms against 3.2-3.3 ms
+// at N = 512: both halves pull the tile's whole 64-byte rows, and the E_u table and
+// the twiddles are paid per half.)
 template <int N> constexpr int pass1_tc() { return kTileW; }
 
 template <int N>
@@ -1492,7 +1503,7 @@ hipError_t launch_support(int n, const double2* kb, const uint8_t* active, GeomD
     SSB_DISPATCH_N(n, (support_n<NN>(kb, active, geo, nbf, sup, vend, nsup, st)))
 }
 
-int pass1_tile(int n) { return n >= 512 ? pass1_tc<512>() : pass1_tc<256>(); }
+int pass1_tile(int n) { return kTileW; }     // pass 1 writes whole layout tiles
 
 hipError_t launch_accum(int n, const float* part_s1, const double* part_s2, int gcap, int ng, int n_trials,
                         double* s1run, double* s2run, hipStream_t st) {
@@ -1534,7 +1545,7 @@ template <int N>
 static hipError_t obj_sum_n(const float2* gm, const float2* gn, const double2* kb, const uint4* sup,
                             const int* vend, TrialConst tc, GeomDev geo, int64_t nbf, double2* part, int nseg,
                             hipStream_t st) {
-    constexpr int TC = pass1_tc<N>();
+    constexpr int TC = kTileW;
     const int seglen = (int)((nbf + nseg - 1) / nseg);
     hipLaunchKernelGGL((k_obj_sum<N, TC>), dim3(N / 2 / TC + 1, nseg), dim3(obj_threads<N>()), 0, st, gm, gn, kb, sup,
                        vend, tc, geo, nbf, seglen, part);
