@@ -750,14 +750,16 @@ struct RowPairRaw {
 // BF's column values during the current transform measured slower: the extra
 // registers cost more than it hides.)
 // FP: the full-plane variant; each BF pixel's object gains (-1)^x A(y) + (-1)^y B(x)
-// from na, nb [t][cap][N] (k_nyq_lines), so the real part varies along a row and
-// every sample takes the general atan2.
+// from na, nb [t][cap][N] (k_nyq_lines), so the real part varies along a row: the
+// wave test and the reciprocal of the atan2 fast path are per sample.
 // Register budget: 80 VGPRs (6 waves per SIMD) fit the half-plane row pass up to
 // N = 512 without spills (measured 2.07 ms against 2.19 ms at 82 VGPRs, 5 waves);
 // 128 (4 waves) at N = 1024 (2.85 against 3.26 ms at 136, 3 waves); the
 // full-plane forms keep the compiler's choice.
 template <int N, bool FP>
-constexpr int pass2_min_waves() { return (N <= 512 && !FP) ? SSB_PASS2_MIN_WAVES : (N == 1024 && !FP ? SSB_PASS2_MIN_WAVES_1024 : 1); }
+constexpr int pass2_min_waves() {
+    return FP ? 1 : (N <= 512 ? SSB_PASS2_MIN_WAVES : SSB_PASS2_MIN_WAVES_1024);
+}
 
 template <int N, bool FP>
 __global__ __launch_bounds__(256, (pass2_min_waves<N, FP>())) void k_pass2(const float2* __restrict__ im, const float2* __restrict__ in,
@@ -828,13 +830,36 @@ __global__ __launch_bounds__(256, (pass2_min_waves<N, FP>())) void k_pass2(const
             // rows y0 (even: (-1)^y = +1) and y0 + 1 (odd: -1)
             const float r0 = fmaf(sgn, av0.x, den0), i0 = sgn * av0.y;
             const float r1 = fmaf(sgn, av1.x, den1), i1 = sgn * av1.y;
+            // Re O > 0 and |Im O| <= Re O for every sample of the wave: the [0, 1]
+            // polynomial of Im O / Re O with a reciprocal per sample (bitwise the
+            // general atan2 on those inputs); else the general atan2
+            bool easy = true;
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                const float pa = atan2_f(x[r].x + i0 + bv[r].y, r0 + bv[r].x);
-                const float pb = atan2_f(x[r].y + i1 - bv[r].y, r1 - bv[r].x);
-                s1a[r] += pa;
-                s1b[r] += pb;
-                p2 += pa * pa + pb * pb;
+                const float ra = r0 + bv[r].x, rb = r1 - bv[r].x;
+                x[r].x += i0 + bv[r].y;
+                x[r].y += i1 - bv[r].y;
+                bv[r] = make_float2(ra, rb);
+                easy = easy && ra > 0.f && rb > 0.f && fabsf(x[r].x) <= ra && fabsf(x[r].y) <= rb;
+            }
+            if (__all(easy)) {
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const float pa = atan_unit(x[r].x * __builtin_amdgcn_rcpf(bv[r].x));
+                    const float pb = atan_unit(x[r].y * __builtin_amdgcn_rcpf(bv[r].y));
+                    s1a[r] += pa;
+                    s1b[r] += pb;
+                    p2 += pa * pa + pb * pb;
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const float pa = atan2_f(x[r].x, bv[r].x);
+                    const float pb = atan2_f(x[r].y, bv[r].y);
+                    s1a[r] += pa;
+                    s1b[r] += pb;
+                    p2 += pa * pa + pb * pb;
+                }
             }
         } else {
             // Re O > 0 and |Im O| <= Re O for every sample of the wave: atan2 is the
