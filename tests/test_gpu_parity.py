@@ -193,6 +193,22 @@ def test_loss_small_batch(small):
         assert _rel(got[k], ref) <= LOSS_RTOL, (k, got[k], ref)
 
 
+def test_loss_small_200_trial_batch(small):
+    """The small workload's whole 200-trial batch in one call; every 4th trial (50, spread
+    over the batch) against the oracle, and two of them again as single-trial calls."""
+    w, counts, p = small
+    g = O.OGeom.from_any(w.geometry)
+    dc = O.dc_value(counts)
+    params = trial_params(w)
+    assert params.shape == (200, 3)
+    got = p.loss(params)
+    for k in range(0, 200, 4):
+        ref = O.loss(g, counts, params[k], dc)
+        assert _rel(got[k], ref) <= LOSS_RTOL, (k, got[k], ref)
+    for k in (3, 199):
+        assert p.loss(params[k:k + 1])[0] == got[k]
+
+
 def test_mean_phase_small(small):
     w, counts, p = small
     t = _torch()
