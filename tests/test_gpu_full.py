@@ -188,3 +188,22 @@ def test_full_plane_variant_moments_sampled(full, b0, b1):
     assert abs(s2 - r2) <= LOSS_RTOL * abs(r2), b0
     d = s1 - r1
     assert np.sqrt(np.mean(d * d)) <= 2e-5 * (b1 - b0) and np.max(np.abs(d)) <= 1e-3, b0
+
+
+def test_full_fit_trials_sampled(full):
+    """Eight seeded trials of the full fit's batch (C10 +-200 nm, C12 +-20 nm, phi12 in
+    [0, pi)): moments of a mid-disk BF range against the oracle, and their losses in one
+    batched call equal to single-trial calls."""
+    from synth import trial_params
+    w, counts, h = full
+    og = O.OGeom.from_any(w.geometry)
+    dc = ssb.ssb_query(h)["dc"]
+    trials = trial_params(w, 8)
+    host = _host(counts, 4450, 4493)
+    for k in range(8):
+        s1, s2 = _moments(h, 512, trials[k], 4450, 4493)
+        r1, r2 = O.bf_moments(og, host, trials[k], dc, list(range(4450, 4493)))
+        assert abs(s2 - r2) <= LOSS_RTOL * abs(r2), k
+        assert np.sqrt(np.mean((s1 - r1) ** 2)) <= 2e-5 * 43, k
+    batch = ssb.ssb_loss(h, trials)
+    assert ssb.ssb_loss(h, trials[5:6])[0] == batch[5]
