@@ -294,6 +294,16 @@ def main():
                "sample": f"float64 oracle moments of BF [{b0}, {b1}) ({nb} of {w.n_bf} BF x {n}^2 scan) at the "
                          f"true aberrations, one host thread, {cpu_s:.1f} s",
                "host_cores_available": len(os.sched_getaffinity(0))}
+        # whole evaluations of the oracle at the two smallest workloads (context)
+        from synth import cached_counts
+        whole = {}
+        for wn in ("tiny", "small"):
+            ws = WORKLOADS[wn]
+            cs = cached_counts(ws)
+            t1 = time.perf_counter()
+            O.loss(O.OGeom.from_any(ws.geometry), cs, ws.true_params)
+            whole[wn] = {"s": time.perf_counter() - t1, "samples": ws.n_bf * ws.geometry.scan_n ** 2}
+        cpu["whole_evaluations"] = whole
         s1 = torch.empty((n, n), dtype=torch.float64, device=dev)
         s2 = ssb.ssb_moments(h, params[0], b0, b1, s1)
         s1 = s1.cpu().numpy()
