@@ -4,7 +4,7 @@
 // ssb.h).
 //
 // The detector sum is a streaming integer reduction: every frame is read once,
-// 16 bytes (four pixels) per lane, coalesced across the frame; each workgroup
+// 16 bytes (four pixels) per lane, coalesced across the frame, non-temporal; each workgroup
 // sums a block of frames in 64-bit registers and adds its partials to the output
 // with 64-bit integer atomics, so the result is exact and independent of order.
 // The gather is a tiled transpose: a workgroup reads 64 frames x 64 BF pixels
@@ -56,18 +56,22 @@ __global__ __launch_bounds__(256) void k_detsum4(const uint4* __restrict__ frame
     unsigned long long a0 = 0, a1 = 0, a2 = 0, a3 = 0;
     const uint4* p = frames + f0 * nq + q;
     int64_t f = f0;
-    for (; f + 8 <= f1; f += 8) {
-        uint4 v[8];
+    // 16 frames in flight per lane; non-temporal loads (the frames are read once)
+    // took the sum from 6.45 to 5.85 ms on the full frames
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    constexpr int U = 16;
+    for (; f + U <= f1; f += U) {
+        u32x4 v[U];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] = p[(int64_t)k * nq];
+        for (int k = 0; k < U; ++k) v[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + (int64_t)k * nq));
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
+        for (int k = 0; k < U; ++k) {
             a0 += v[k].x;
             a1 += v[k].y;
             a2 += v[k].z;
             a3 += v[k].w;
         }
-        p += (int64_t)8 * nq;
+        p += (int64_t)U * nq;
     }
     for (; f < f1; ++f, p += nq) {
         const uint4 v = *p;

@@ -149,6 +149,22 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 __device__ __forceinline__ float2 load_or_zero(__amdgpu_buffer_rsrc_t r, int off) {
     return __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
 }
+// The same with the non-temporal cache policy (aux bit 1): for data read once per
+// evaluation (the spectra in pass 1: 3.29 -> 3.22 ms).  Not for the row pass's
+// loads: rows y0 and y0 + 1 of a tile share lines that other waves read too
+// (non-temporal there: pass 2 2.02 -> 2.54 ms).
+__device__ __forceinline__ float2 load_or_zero_nt(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 2));
+}
+// Non-temporal store of one complex value (pass 1's column results, read back only
+// by the next kernel: 3.29 -> 3.14 ms).
+__device__ __forceinline__ void store_nt(float2* p, float2 v) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    f32x2 w;
+    w.x = v.x;
+    w.y = v.y;
+    __builtin_nontemporal_store(w, reinterpret_cast<f32x2*>(p));
+}
 constexpr int kNoLoad = (int)0x80000000;
 
 // (cos, sin) of 2 pi q^T M q
@@ -540,7 +556,7 @@ __device__ __forceinline__ void pass1_tile(const float2* __restrict__ gsrc, cons
         const bool inp = (unsigned)(up - lo_p) < (unsigned)len_p;
         const bool on = (NYQ ? u < N : true) && (inm || inp) && (u != 0 || v != 0);
         const int off = on ? off0 + i * RS * SSTRIDE * 8 : kNoLoad;
-        gv[i] = load_or_zero(rg, off);
+        gv[i] = load_or_zero_nt(rg, off);
         chv[i] = load_or_zero(rc, off);
         bits |= on ? ((inm ? 1u : 0u) | (inp ? 2u : 0u)) << (2 * i) : 0u;
     }
@@ -603,9 +619,9 @@ __device__ __forceinline__ void pass1_tile(const float2* __restrict__ gsrc, cons
     if (!NYQ) {
         float2* om = out + csub + c;
 #pragma unroll 4
-        for (int y = ustart; y < N; y += RS) om[(int64_t)y * kTileW] = tile[c * LD + y];
+        for (int y = ustart; y < N; y += RS) store_nt(om + (int64_t)y * kTileW, tile[c * LD + y]);
     } else {
-        for (int y = tid; y < N; y += NT) out[y] = tile[y];
+        for (int y = tid; y < N; y += NT) store_nt(out + y, tile[y]);
     }
 }
 
