@@ -518,7 +518,7 @@ template <int N> constexpr int pass1_threads() { return N >= 1024 ? 512 : SSB_PA
 // columns x 32/TC rows per 32 lanes) hit distinct banks.
 template <int N, int TC> constexpr int pass1_ld() { return WaveFFT<N, +1>::SCRATCH + 32 / TC; }
 
-template <int N, int TC, bool NYQ>
+template <int N, int TC, bool NYQ, bool STREAM>
 __device__ __forceinline__ void pass1_tile(const float2* __restrict__ gsrc, const float2* __restrict__ chsrc,
                                            const double2 k, const uint4 sr, const TrialConst& m, const GeomDev& geo,
                                            float2* __restrict__ out, float2* tile, float2* eu, int v0, int csub) {
@@ -556,7 +556,7 @@ __device__ __forceinline__ void pass1_tile(const float2* __restrict__ gsrc, cons
         const bool inp = (unsigned)(up - lo_p) < (unsigned)len_p;
         const bool on = (NYQ ? u < N : true) && (inm || inp) && (u != 0 || v != 0);
         const int off = on ? off0 + i * RS * SSTRIDE * 8 : kNoLoad;
-        gv[i] = load_or_zero_nt(rg, off);
+        gv[i] = STREAM ? load_or_zero_nt(rg, off) : load_or_zero(rg, off);
         chv[i] = load_or_zero(rc, off);
         bits |= on ? ((inm ? 1u : 0u) | (inp ? 2u : 0u)) << (2 * i) : 0u;
     }
@@ -619,13 +619,24 @@ __device__ __forceinline__ void pass1_tile(const float2* __restrict__ gsrc, cons
     if (!NYQ) {
         float2* om = out + csub + c;
 #pragma unroll 4
-        for (int y = ustart; y < N; y += RS) store_nt(om + (int64_t)y * kTileW, tile[c * LD + y]);
+        for (int y = ustart; y < N; y += RS) {
+            if constexpr (STREAM) store_nt(om + (int64_t)y * kTileW, tile[c * LD + y]);
+            else om[(int64_t)y * kTileW] = tile[c * LD + y];
+        }
     } else {
-        for (int y = tid; y < N; y += NT) store_nt(out + y, tile[y]);
+        for (int y = tid; y < N; y += NT) {
+            if constexpr (STREAM) store_nt(out + y, tile[y]);
+            else out[y] = tile[y];
+        }
     }
 }
 
-template <int N, int TC>
+// STREAM: non-temporal spectrum loads and column-result stores, for launches whose
+// spectrum tiles are not read again soon: one trial, or a chunk whose spectra
+// exceed the 256 MB MALL.  With many trials the chunk is small (32 BF at 200 trials)
+// and each trial row of the grid re-reads its tiles from the MALL; there the
+// default policy is kept (200-trial batch: 5.30 against 5.55 ms per trial).
+template <int N, int TC, bool STREAM>
 __global__ __launch_bounds__(pass1_threads<N>()) void k_pass1(const float2* __restrict__ gm,
                                                          const float2* __restrict__ gn,
                                                          const float2* __restrict__ chm,
@@ -673,10 +684,10 @@ __global__ __launch_bounds__(pass1_threads<N>()) void k_pass1(const float2* __re
     if (!nyq) {
         const int v = v0 + (int)threadIdx.x % TC;
         const int64_t tb = (int64_t)lt * N * kTileW;      // the layout tile's block in a plane
-        pass1_tile<N, TC, false>(gm + b * N * H + tb, chm + (int64_t)t * N * H + tb, k, sup[b * (H + 1) + v], m, geo,
+        pass1_tile<N, TC, false, STREAM>(gm + b * N * H + tb, chm + (int64_t)t * N * H + tb, k, sup[b * (H + 1) + v], m, geo,
                                  im + ((int64_t)t * cap + bl) * N * H + tb, tile, eu, v0, v0 - lt * kTileW);
     } else {
-        pass1_tile<N, TC, true>(gn + b * N, chn + (int64_t)t * N, k, sup[b * (H + 1) + H], m, geo,
+        pass1_tile<N, TC, true, STREAM>(gn + b * N, chn + (int64_t)t * N, k, sup[b * (H + 1) + H], m, geo,
                                 in + ((int64_t)t * cap + bl) * N, tile, eu, v0, 0);
     }
 }
@@ -1397,8 +1408,14 @@ hipError_t pass1_n(const float2* gm, const float2* gn, const float2* chm, const 
     constexpr int H = N / 2;
     constexpr int TC = pass1_tc<N>();
     // one launch per chunk: (H/TC + 1) tiles per BF in x, trials in y
-    hipLaunchKernelGGL((k_pass1<N, TC>), dim3((unsigned)((int64_t)cb * (H / TC + 1)), n_trials), dim3(pass1_threads<N>()),
-                       0, st, gm, gn, chm, chn, kb, sup, vend, tc, geo, bf0, cap, im, in);
+    const dim3 grid((unsigned)((int64_t)cb * (H / TC + 1)), n_trials);
+    const bool stream = n_trials == 1 || (int64_t)cb * N * (H + 1) * 8 > ((int64_t)192 << 20);
+    if (stream)
+        hipLaunchKernelGGL((k_pass1<N, TC, true>), grid, dim3(pass1_threads<N>()), 0, st, gm, gn, chm, chn, kb, sup,
+                           vend, tc, geo, bf0, cap, im, in);
+    else
+        hipLaunchKernelGGL((k_pass1<N, TC, false>), grid, dim3(pass1_threads<N>()), 0, st, gm, gn, chm, chn, kb, sup,
+                           vend, tc, geo, bf0, cap, im, in);
     return hipGetLastError();
 }
 
