@@ -503,9 +503,10 @@ __global__ __launch_bounds__(256) void k_nyq_lines(const float2* __restrict__ gm
 //      apertures the bracket is already a unit phasor, on an edge ring it is
 //      normalized;
 //   3. one wave-level inverse FFT per column;  4. coalesced store.
-// exp(-i delta) is separable: E_u(u') = exp(-2 pi i u' beta) for all rows is
-// built in LDS per workgroup, E_v(v) = exp(-2 pi i v alpha) per thread (each
-// thread keeps one column).
+// exp(-i delta) = E(u', v) = exp(-2 pi i (u' beta + v alpha)): each thread keeps
+// one column and walks its rows RS apart, so its phasors are two geometric chains
+// (rows below N/2, and rows from N/2 on taken as u - N) advanced by exp(-2 pi i RS
+// beta); the chain starts and the step are reduced in double.
 // 1024-point columns take 512 threads: a thread's share of the tile (N TC / threads
 // entries) stays at 16, the most the per-thread support word holds.
 template <int N> constexpr int pass1_threads() { return N >= 1024 ? 512 : SSB_PASS1_THREADS; }
@@ -513,15 +514,26 @@ template <int N> constexpr int pass1_threads() { return N >= 1024 ? 512 : SSB_PA
 // One pass-1 tile; NYQ selects the Nyquist column at compile time so that every
 // row index, LDS address and load offset of the unrolled entry loops is a
 // compile-time step from the thread's first row.
-// Column pitch of the pass-1 LDS tile (a column's slot is also its transform's
-// scratch): 32/TC past the scratch, so that the correction's stores and loads (TC
-// columns x 32/TC rows per 32 lanes) hit distinct banks.
-template <int N, int TC> constexpr int pass1_ld() { return WaveFFT<N, +1>::SCRATCH + 32 / TC; }
-
+// LDS tile: one slot per column, which is also its transform's scratch.  Where the
+// transform's scratch is exactly N values the slots are packed (pitch N) and row u
+// of column c sits at u ^ 4 (c mod 8): the XOR changes bits 2..4 only, so a column
+// stays a permutation of its own slot, a transform's reads of 64 consecutive rows
+// stay conflict-free, and 32 lanes holding 8 columns x 4 consecutive rows hit 32
+// distinct 8-byte slots (8 columns of 512 values take exactly 32 KB).  Padded
+// transforms (1,024 points) keep the pitch SCRATCH + 32/TC (the same bank spread, no
+// swizzle).  (Five workgroups per CU would fit this LDS but need at most 96 VGPRs:
+// forced there, the kernel spills loaded values to scratch right after their loads,
+// 4.2-4.4 ms against 3.0 ms at the compiler's 127 VGPRs, four workgroups.)
+template <int N> constexpr bool pass1_swz() { return WaveFFT<N, +1>::SCRATCH == N; }
+template <int N, int TC> constexpr int pass1_ld() { return pass1_swz<N>() ? N : WaveFFT<N, +1>::SCRATCH + 32 / TC; }
+template <int N> __device__ __forceinline__ int pass1_row(int c, int u) {
+    if constexpr (pass1_swz<N>()) return u ^ ((c & 7) << 2);
+    else return u;
+}
 template <int N, int TC, bool NYQ, bool STREAM>
 __device__ __forceinline__ void pass1_tile(const float2* __restrict__ gsrc, const float2* __restrict__ chsrc,
                                            const double2 k, const uint4 sr, const TrialConst& m, const GeomDev& geo,
-                                           float2* __restrict__ out, float2* tile, float2* eu, int v0, int csub) {
+                                           float2* __restrict__ out, float2* tile, int v0, int csub) {
     constexpr int H = N / 2;
     constexpr int LD = pass1_ld<N, TC>();
     constexpr int NT = pass1_threads<N>();
@@ -563,30 +575,44 @@ __device__ __forceinline__ void pass1_tile(const float2* __restrict__ gsrc, cons
     // the phase ramps of this BF pixel while the loads are in flight
     double alpha, beta;
     delta_slopes(k.x, k.y, m, geo, alpha, beta);
-    for (int u = tid; u < N; u += NT) eu[u] = phasor_rev_neg((double)(u < H ? u : u - N) * beta);
-    const float2 ev = phasor_rev_neg((double)v * alpha);
-    __syncthreads();                              // E_u complete
+    const double av = (double)v * alpha;
 
     // 2. correction into the LDS tile
     const int flo_m = unpack_lo(sr.z), flen_m = unpack_len(sr.z);
     const int flo_p = unpack_lo(sr.w), flen_p = unpack_len(sr.w);
-    float2* trow = tile + c * LD + ustart;
-    const float2* erow = eu + ustart;
-#pragma unroll
-    for (int i = 0; i < PM; ++i) {
+    static_assert(NYQ || RS % 32 == 0 || !pass1_swz<N>(), "row steps leave the swizzled bits alone");
+    float2* trow = tile + c * LD + pass1_row<N>(c, ustart);
+    auto entry = [&](int i, float2 e) {
         const int u = ustart + i * RS;
-        if (NYQ ? u < N : true) {
-            float2 val = make_float2(0.f, 0.f);
-            const unsigned f = (bits >> (2 * i)) & 3u;
-            if (f) {
-                const int up = (NYQ || RS > H) ? (u < H ? u : u - N) : (i < PM / 2 ? u : u - N);
-                const bool inm = f & 1u, inp = f & 2u;
-                const bool edm = inm && (unsigned)(up - flo_m) >= (unsigned)flen_m;
-                const bool edp = inp && (unsigned)(up - flo_p) >= (unsigned)flen_p;
-                val = correct_entry(gv[i], chv[i], cmul(erow[i * RS], ev), inm, inp, edm, edp, up, v, k.x, k.y,
-                                    geo);
-            }
-            trow[i * RS] = val;
+        float2 val = make_float2(0.f, 0.f);
+        const unsigned f = (bits >> (2 * i)) & 3u;
+        if (f) {
+            const int up = (NYQ || RS > H) ? (u < H ? u : u - N) : (i < PM / 2 ? u : u - N);
+            const bool inm = f & 1u, inp = f & 2u;
+            const bool edm = inm && (unsigned)(up - flo_m) >= (unsigned)flen_m;
+            const bool edp = inp && (unsigned)(up - flo_p) >= (unsigned)flen_p;
+            val = correct_entry(gv[i], chv[i], e, inm, inp, edm, edp, up, v, k.x, k.y, geo);
+        }
+        trow[i * RS] = val;
+    };
+    if constexpr (!NYQ && RS <= H) {
+        // PM/2 rows below N/2, then PM/2 rows from N/2 on; two chains
+        static_assert(PM % 2 == 0 && (PM / 2) * RS == H, "rows split at N/2");
+        float2 ea = phasor_rev_neg(fma((double)ustart, beta, av));
+        float2 eb = phasor_rev_neg(fma((double)(ustart - H), beta, av));
+        const float2 st = phasor_rev_neg((double)RS * beta);
+#pragma unroll
+        for (int i = 0; i < PM / 2; ++i) {
+            entry(i, ea);
+            entry(i + PM / 2, eb);
+            ea = cmul(ea, st);
+            eb = cmul(eb, st);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < PM; ++i) {
+            const int u = ustart + i * RS;
+            if (NYQ ? u < N : true) entry(i, phasor_rev_neg(fma((double)(u < H ? u : u - N), beta, av)));
         }
     }
     __syncthreads();
@@ -604,24 +630,30 @@ __device__ __forceinline__ void pass1_tile(const float2* __restrict__ gsrc, cons
     F fft;
     if constexpr (F::R == 8 || N == 1024) fft.init_products(j);   // sincospi for r = 1, 2, 4, the rest products
     else fft.init(j);
+    // row j + r L of column cc: with L a multiple of 32 the swizzle leaves r L alone
+    auto slot = [&](int cc, int r) {
+        if constexpr (F::L % 32 == 0) return cc * LD + pass1_row<N>(cc, j) + r * F::L;
+        else return cc * LD + pass1_row<N>(cc, j + r * F::L);
+    };
     for (int cc = grp; cc < NCOLS; cc += NG) {
         float2 x[F::R];
 #pragma unroll
-        for (int r = 0; r < F::R; ++r) x[r] = tile[cc * LD + j + r * F::L];
+        for (int r = 0; r < F::R; ++r) x[r] = tile[slot(cc, r)];
         fft.run(x, &tile[cc * LD], j);
         wave_lds_fence();
 #pragma unroll
-        for (int r = 0; r < F::R; ++r) tile[cc * LD + j + r * F::L] = x[r];
+        for (int r = 0; r < F::R; ++r) tile[slot(cc, r)] = x[r];
     }
     __syncthreads();
 
     // 4. store (out: the layout tile's block of the column-result plane, or the Nyquist column)
     if (!NYQ) {
         float2* om = out + csub + c;
+        const float2* tcol = tile + c * LD + pass1_row<N>(c, ustart);
 #pragma unroll 4
         for (int y = ustart; y < N; y += RS) {
-            if constexpr (STREAM) store_nt(om + (int64_t)y * kTileW, tile[c * LD + y]);
-            else om[(int64_t)y * kTileW] = tile[c * LD + y];
+            if constexpr (STREAM) store_nt(om + (int64_t)y * kTileW, tcol[y - ustart]);
+            else om[(int64_t)y * kTileW] = tcol[y - ustart];
         }
     } else {
         for (int y = tid; y < N; y += NT) {
@@ -650,7 +682,6 @@ __global__ __launch_bounds__(pass1_threads<N>()) void k_pass1(const float2* __re
     constexpr int H = N / 2;
     constexpr int LD = pass1_ld<N, TC>();
     __shared__ float2 tile[TC * LD];
-    __shared__ float2 eu[N];
 
     const int t = blockIdx.y;
     // Workgroup -> (BF, tile).  Up to N = 512 BF-major: the H/TC main tiles of a BF,
@@ -685,10 +716,10 @@ __global__ __launch_bounds__(pass1_threads<N>()) void k_pass1(const float2* __re
         const int v = v0 + (int)threadIdx.x % TC;
         const int64_t tb = (int64_t)lt * N * kTileW;      // the layout tile's block in a plane
         pass1_tile<N, TC, false, STREAM>(gm + b * N * H + tb, chm + (int64_t)t * N * H + tb, k, sup[b * (H + 1) + v], m, geo,
-                                 im + ((int64_t)t * cap + bl) * N * H + tb, tile, eu, v0, v0 - lt * kTileW);
+                                 im + ((int64_t)t * cap + bl) * N * H + tb, tile, v0, v0 - lt * kTileW);
     } else {
         pass1_tile<N, TC, true, STREAM>(gn + b * N, chn + (int64_t)t * N, k, sup[b * (H + 1) + H], m, geo,
-                                in + ((int64_t)t * cap + bl) * N, tile, eu, v0, 0);
+                                in + ((int64_t)t * cap + bl) * N, tile, v0, 0);
     }
 }
 
