@@ -724,8 +724,8 @@ __global__ __launch_bounds__(pass1_threads<N>()) void k_pass1(const float2* __re
 }
 
 // Raw column-pass values a row pair needs: lane j gets v = j + r L for r < R/2
-// (direct) and the mirrored w = N - v for r >= R/2, plus the v = 0 and v = N/2
-// entries of both rows.
+// (direct, loaded) and the mirrored w = N - v for r >= R/2 (permuted from other
+// lanes' direct values), plus the v = 0 and v = N/2 entries of both rows.
 template <int N, int R, int L>
 struct RowPairRaw {
     float2 d0[R / 2], d1[R / 2], m0[R / 2], m1[R / 2];
@@ -745,23 +745,14 @@ struct RowPairRaw {
         constexpr int RSTEP = (L / kTileW) * TILE;       // bytes from column v to column v + L
         const int ntile = min((ve + kTileW - 1) / kTileW, H / kTileW);
         const __amdgpu_buffer_rsrc_t rp = make_rsrc(plane, ntile * TILE);
-        // bases: column j, and the lowest mirrored column H - j - (R/2 - 1) L (>= 1).
-        // The empty asm makes them opaque, so the 2 R offsets derived from them are
-        // formed at each call rather than hoisted out of the caller's loop.
+        // base: column j.  The empty asm makes it opaque, so the R offsets derived
+        // from it are formed at each call rather than hoisted out of the caller's loop.
         int od = (int)tm_index(N, y0, j) * 8;
-        int om = (int)tm_index(N, y0, H - j - (R / 2 - 1) * L) * 8;
-        asm volatile("" : "+v"(od), "+v"(om));
+        asm volatile("" : "+v"(od));
 #pragma unroll
         for (int r = 0; r < R / 2; ++r) {
             d0[r] = load_or_zero(rp, od + r * RSTEP);
             d1[r] = load_or_zero(rp, od + r * RSTEP + kTileW * 8);
-        }
-        // mirrored column w = H - j - r L (w = H for j = r = 0 lies past the plane,
-        // reads zero and is replaced by the Nyquist column in assemble)
-#pragma unroll
-        for (int r = 0; r < R / 2; ++r) {
-            m0[r] = load_or_zero(rp, om + (R / 2 - 1 - r) * RSTEP);
-            m1[r] = load_or_zero(rp, om + (R / 2 - 1 - r) * RSTEP + kTileW * 8);
         }
         const float2 zero = make_float2(0.f, 0.f);
         h0 = zero;
@@ -778,10 +769,36 @@ struct RowPairRaw {
         }
     }
 
+    // Mirrored columns w = N/2 - j - r L from the direct values already loaded: for
+    // j > 0, w = (L - j) + (R/2 - 1 - r) L is lane L - j's direct value R/2 - 1 - r
+    // (one cross-lane permute per float, instead of a second load of the same lines:
+    // row pass 2.02-2.07 -> 1.99 ms); for j = 0, w = (R/2 - r) L is the lane's own
+    // (r >= 1; r = 0 is the Nyquist column, replaced in assemble).
+    __device__ __forceinline__ void mirror(int j) {
+        const int lane = (int)threadIdx.x & 63;
+        const int addr = (lane - j + ((L - j) & (L - 1))) * 4;
+#pragma unroll
+        for (int r = 0; r < R / 2; ++r) {
+            const int rs = R / 2 - 1 - r;
+            m0[r].x = __int_as_float(__builtin_amdgcn_ds_bpermute(addr, __float_as_int(d0[rs].x)));
+            m0[r].y = __int_as_float(__builtin_amdgcn_ds_bpermute(addr, __float_as_int(d0[rs].y)));
+            m1[r].x = __int_as_float(__builtin_amdgcn_ds_bpermute(addr, __float_as_int(d1[rs].x)));
+            m1[r].y = __int_as_float(__builtin_amdgcn_ds_bpermute(addr, __float_as_int(d1[rs].y)));
+        }
+        if (j == 0) {
+#pragma unroll
+            for (int r = 1; r < R / 2; ++r) {
+                m0[r] = d0[R / 2 - r];
+                m1[r] = d1[R / 2 - r];
+            }
+        }
+    }
+
     // Z(v) = B0(v) + i B1(v), B_k = -i * (column result of row y_k), extended
     // Hermitian (B(N - v) = conj B(v)) with only real parts kept at v = 0 and N/2.
-    __device__ __forceinline__ void assemble(int j, float2 (&x)[R]) const {
+    __device__ __forceinline__ void assemble(int j, float2 (&x)[R]) {
         constexpr int H = N / 2;
+        mirror(j);
 #pragma unroll
         for (int r = 0; r < R / 2; ++r) {
             float2 a0 = d0[r], a1 = d1[r];
