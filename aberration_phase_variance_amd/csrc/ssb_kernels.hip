@@ -498,7 +498,7 @@ __global__ __launch_bounds__(256) void k_nyq_lines(const float2* __restrict__ gm
 //      entries with nonzero transfer and their exp(i chi_q) (per-trial table) are
 //      loaded into registers through buffer resources, zero-transfer entries get
 //      an out-of-range offset and read as exact zeros without a memory access;
-//      the BF pixel's phase ramps are built while those loads are in flight;
+//      the BF pixel's phase slopes are formed while those loads are in flight;
 //   2. each entry is corrected into the LDS tile: on the flat tops of the
 //      apertures the bracket is already a unit phasor, on an edge ring it is
 //      normalized;
@@ -572,7 +572,7 @@ __device__ __forceinline__ void pass1_tile(const float2* __restrict__ gsrc, cons
         chv[i] = load_or_zero(rc, off);
         bits |= on ? ((inm ? 1u : 0u) | (inp ? 2u : 0u)) << (2 * i) : 0u;
     }
-    // the phase ramps of this BF pixel while the loads are in flight
+    // the phase slopes of this BF pixel while the loads are in flight
     double alpha, beta;
     delta_slopes(k.x, k.y, m, geo, alpha, beta);
     const double av = (double)v * alpha;
@@ -1445,8 +1445,8 @@ hipError_t cols_n(const float2* in_m, const float2* in_n, float2* out_m, float2*
 
 // Columns per pass-1 workgroup: one layout tile.  (Half tiles, 4 columns with 256
 // threads, reach 7 waves per SIMD at 71 VGPRs but ran 6.2-6.5 ms against 3.2-3.3 ms
-// at N = 512: both halves pull the tile's whole 64-byte rows, and the E_u table and
-// the twiddles are paid per half.)
+// at N = 512: both halves pull the tile's whole 64-byte rows, and the row-phase
+// table then built per workgroup and the twiddles were paid per half.)
 template <int N> constexpr int pass1_tc() { return kTileW; }
 
 template <int N>
