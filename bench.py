@@ -173,7 +173,8 @@ def main():
     torch.cuda.synchronize()
     total_s = time.perf_counter() - t_all
     ms_per_step = total_s * 1e3 / args.steps
-    log(f"[bench] loss {loss:.9f}: {ms_per_step:.3f} ms/eval (p50 {np.median(times):.3f}, min {min(times):.3f})")
+    log(f"[bench] loss {loss:.9f}: {ms_per_step:.3f} ms/eval (p50 {np.median(times):.3f}, "
+        f"p95 {np.percentile(times, 95):.3f}, min {min(times):.3f})")
 
     # the full-plane variant (every entry of the N x N plane corrected on its own)
     ssb.ssb_set_variant(h, ssb.SSB_VARIANT_FULL_PLANE)
@@ -431,6 +432,7 @@ def main():
                    "scan_n": n, "det_n": g.det_n, "n_bf": w.n_bf, "trials_per_step": 1},
         "loss": loss,
         "ms_p50": float(np.median(times)),
+        "ms_p95": float(np.percentile(times, 95)),
         "ms_min": float(min(times)),
         "object_ms": object_ms,
         "batch_trials": args.batch,
