@@ -87,6 +87,24 @@ def kernel_source_hash() -> str:
     return hsh.hexdigest()[:16]
 
 
+def plain_stream_gbs(dev) -> float:
+    """HBM rate of a plain elementwise add (2 GiB read + 2 GiB written per call), best of 5."""
+    import torch
+    x = torch.ones(1 << 29, dtype=torch.float32, device=dev)
+    y = torch.empty_like(x)
+    torch.add(x, 1.0, out=y)
+    best = float("inf")
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        torch.add(x, 1.0, out=y)
+        e1.record()
+        e1.synchronize()
+        best = min(best, e0.elapsed_time(e1))
+    del x, y
+    return 2.0 * (1 << 31) / (best * 1e-3) / 1e9
+
+
 def measured_traffic(kernel: str):
     """HBM bytes per launch from the committed counter summary, if it matches these sources."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
@@ -265,6 +283,11 @@ def main():
                      "flops_view": {"achieved_tflops": round(achieved_tf, 3), "peak": PEAK_FP32_TFLOPS,
                                     "frac": round(achieved_tf / PEAK_FP32_TFLOPS, 4)},
                      "kernel_source": kernel_source_hash()})
+    # the practical HBM ceiling on this GPU for context: a plain elementwise add over 2 GiB
+    # (one read and one write stream), timed with events on torch's stream
+    stream_gbs = plain_stream_gbs(dev)
+    roofline.update({"stream_gbs": round(stream_gbs, 1),
+                     "frac_of_stream": round(achieved_gbs / stream_gbs, 4) if roofline["bound"] == "hbm" else None})
     other = "pass2" if dom == "pass1" else "pass1"
     t_other = stage_ms[other] * 1e-3
     other_units = prof[other]["units"] / max(1, prof[other]["launches"])
@@ -402,7 +425,8 @@ def main():
             "chunk_bf": info2["chunk_bf"],
             "roofline": {"bound": "hbm", "kernel": dom2, "achieved": round(r2[dom2]["gbs"], 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(r2[dom2]["gbs"] / PEAK_HBM_GBS, 4),
-                         "traffic": measured_traffic(dom2 + "@1024")},
+                         "traffic": measured_traffic(dom2 + "@1024"),
+                         "frac_of_stream": round(r2[dom2]["gbs"] / stream_gbs, 4)},
             "stages": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in r2[k].items()}
                        for k in r2},
             # notes page, "128 GB Apple M5 Max size-scaling follow-up": scalar evaluator
