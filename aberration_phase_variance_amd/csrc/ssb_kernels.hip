@@ -713,8 +713,8 @@ __global__ __launch_bounds__(pass1_threads<N>()) void k_pass1(const float2* __re
     const double2 k = kb[b];
     const TrialConst m = tc[t];
     if (!nyq) {
-        const int v = v0 + (int)threadIdx.x % TC;
         const int64_t tb = (int64_t)lt * N * kTileW;      // the layout tile's block in a plane
+        const int v = v0 + (int)threadIdx.x % TC;
         pass1_tile<N, TC, false, STREAM>(gm + b * N * H + tb, chm + (int64_t)t * N * H + tb, k, sup[b * (H + 1) + v], m, geo,
                                  im + ((int64_t)t * cap + bl) * N * H + tb, tile, v0, v0 - lt * kTileW);
     } else {
@@ -863,6 +863,26 @@ __global__ __launch_bounds__(256, (pass2_min_waves<N, FP>())) void k_pass2(const
     const int b_lo = g * kGroupBF;
     const int b_hi = min(cb, b_lo + kGroupBF);
 
+    // The group's activity flags and last supported columns, one BF pixel per lane,
+    // read once: inside the loop they come from a ballot mask and lane reads (scalar
+    // values), so each BF pixel's column loads issue at once instead of after a
+    // dependent flag load and its wait.
+    static_assert(kGroupBF <= 64, "one BF pixel of a group per lane");
+    const int gl = lane < b_hi - b_lo ? lane : 0;
+    const bool act_l = lane < b_hi - b_lo && active[bf0 + b_lo + gl];
+    const int ve_l = vend[bf0 + b_lo + gl];
+    const uint64_t amask = __ballot(act_l);
+    auto next_active = [&](int b) {
+        const uint64_t m = b - b_lo < 64 ? amask >> (b - b_lo) : 0;
+        return m ? b + (int)__builtin_ctzll(m) : b_hi;
+    };
+    auto vend_of = [&](int b) { return __builtin_amdgcn_readlane(ve_l, b - b_lo); };
+    auto plane_ptr = [&](int b) { return im + ((int64_t)t * cap + b) * N * H; };
+    auto nyq_ptr = [&](int b) { return in + ((int64_t)t * cap + b) * N; };
+
+    RowPairRaw<N, R, L> cur;
+    int b = next_active(b_lo);
+
     F fft;
     for (int e = tid; e < F::TABLE; e += 256) twt[e] = gtw[e];
     __syncthreads();
@@ -875,18 +895,9 @@ __global__ __launch_bounds__(256, (pass2_min_waves<N, FP>())) void k_pass2(const
     double s2 = 0.0;
     const float sgn = (j & 1) ? -1.f : 1.f;   // (-1)^x for x = j + r L, L even
 
-    auto next_active = [&](int b) {
-        while (b < b_hi && !active[bf0 + b]) ++b;
-        return b;
-    };
-    auto plane_ptr = [&](int b) { return im + ((int64_t)t * cap + b) * N * H; };
-    auto nyq_ptr = [&](int b) { return in + ((int64_t)t * cap + b) * N; };
-
-    RowPairRaw<N, R, L> cur;
-    int b = next_active(b_lo);
     while (b < b_hi) {
         const int bn = next_active(b + 1);
-        cur.load(plane_ptr(b), nyq_ptr(b), y0, j, vend[bf0 + b]);
+        cur.load(plane_ptr(b), nyq_ptr(b), y0, j, vend_of(b));
         float2 x[R];
         cur.assemble(j, x);
         float2 av0, av1, bv[FP ? R : 1];
