@@ -31,6 +31,9 @@ namespace {
 #ifndef SSB_PASS1_THREADS
 #define SSB_PASS1_THREADS 256 // pass-1 workgroup size
 #endif
+#ifndef SSB_ATAN_TERMS
+#define SSB_ATAN_TERMS 8
+#endif
 #ifndef SSB_PASS2_MIN_WAVES_1024
 #define SSB_PASS2_MIN_WAVES_1024 4 // the same at N = 1024 (LDS also allows 4 workgroups per CU)
 #endif
@@ -43,26 +46,6 @@ template <int N> constexpr int cols_tc() { return N >= 1024 ? 8 : 16; }
 constexpr int kPad = 1;       // LDS row padding (complex values)
 
 enum ColMode { COL_PLAIN_FWD = 1, COL_PLAIN_INV = 2 };
-
-// (cos, sin) of 2 pi r for r in [-1/2, 1/2]: quadrant from rint(4 r), then
-// sin(pi f/2) = f S(f^2) and cos(pi f/2) = C(f^2) on f in [-1/2, 1/2] with
-// polynomials fitted here (iteratively reweighted least squares, 4 and 5 terms;
-// max error 1e-7 in float).
-__device__ __forceinline__ float2 cossin_rev(float r) {
-    const float x = 4.0f * r;
-    const float q = rintf(x);
-    const float f = x - q;
-    const float s2 = f * f;
-    const float sn = f * fmaf(fmaf(fmaf(-4.592288751e-03f, s2, 7.967590541e-02f), s2, -6.459629536e-01f), s2,
-                              1.570796251e+00f);
-    const float cs = fmaf(fmaf(fmaf(fmaf(9.036316769e-04f, s2, -2.086007223e-02f), s2, 2.536692023e-01f), s2,
-                               -1.233700514e+00f),
-                          s2, 1.0f);
-    const int qi = (int)q & 3;
-    const float sb = (qi & 1) ? cs : sn;
-    const float cb = (qi & 1) ? sn : cs;
-    return make_float2(((qi + 1) & 2) ? -cb : cb, (qi & 2) ? -sb : sb);
-}
 
 // exp(-2 pi i x) for x in revolutions, reduced in double first.
 __device__ __forceinline__ float2 phasor_rev_neg(double x) {
@@ -181,6 +164,22 @@ __device__ __forceinline__ float2 chi_phasor(double qx, double qy, const TrialCo
 // octant is undone.  atan2(0, 0) = 0; NaN inputs give NaN.
 __device__ __forceinline__ float atan_unit(float t) {
     const float s = t * t;
+#if SSB_ATAN_TERMS == 7
+    float p = 8.250554092e-03f;
+    p = fmaf(p, s, -3.822105378e-02f);
+    p = fmaf(p, s, 8.530547470e-02f);
+    p = fmaf(p, s, -1.356764287e-01f);
+    p = fmaf(p, s, 1.990287155e-01f);
+    p = fmaf(p, s, -3.332884312e-01f);
+#elif SSB_ATAN_TERMS == 8
+    float p = -4.910358693e-03f;
+    p = fmaf(p, s, 2.503707632e-02f);
+    p = fmaf(p, s, -6.061180681e-02f);
+    p = fmaf(p, s, 9.995578229e-02f);
+    p = fmaf(p, s, -1.405041218e-01f);
+    p = fmaf(p, s, 1.997561306e-01f);
+    p = fmaf(p, s, -3.333246410e-01f);
+#else
     float p = 2.903556684e-03f;
     p = fmaf(p, s, -1.628302597e-02f);
     p = fmaf(p, s, 4.303940013e-02f);
@@ -189,10 +188,10 @@ __device__ __forceinline__ float atan_unit(float t) {
     p = fmaf(p, s, -1.420713365e-01f);
     p = fmaf(p, s, 1.999305487e-01f);
     p = fmaf(p, s, -3.333309293e-01f);
+#endif
     p = fmaf(p, s, 1.0f);
     return t * p;
 }
-
 __device__ __forceinline__ float atan2_f(float y, float x) {
     const float ax = fabsf(x), ay = fabsf(y);
     const float mx = fmaxf(ax, ay), mn = fminf(ax, ay);
