@@ -1218,16 +1218,20 @@ __global__ __launch_bounds__(obj_threads<N>()) void k_obj_sum(const float2* __re
         const __amdgpu_buffer_rsrc_t rg =
             nyq ? make_rsrc(gn + b * N, N * 8) : make_rsrc(gm + b * N * H + tb, N * TC * 8);
         float2 gv[PM];
-        unsigned bits = 0;
+        // entry i in the support of either shifted aperture (DC excluded); evaluated
+        // again at the correction instead of kept as flag bits through the loads
+        auto on_of = [&](int i, bool& inm, bool& inp) {
+            const int u = ustart + i * ustep;
+            const int up = u < H ? u : u - N;
+            inm = (unsigned)(up - lo_m) < (unsigned)len_m;
+            inp = (unsigned)(up - lo_p) < (unsigned)len_p;
+            return i < nent && u < N && (inm || inp) && (u != 0 || v != 0);
+        };
 #pragma unroll
         for (int i = 0; i < PM; ++i) {
             const int u = ustart + i * ustep;
-            const int up = u < H ? u : u - N;
-            const bool inm = (unsigned)(up - lo_m) < (unsigned)len_m;
-            const bool inp = (unsigned)(up - lo_p) < (unsigned)len_p;
-            const bool on = i < nent && u < N && (inm || inp) && (u != 0 || v != 0);
-            gv[i] = load_or_zero(rg, on ? (u * sstride + c) * 8 : kNoLoad);
-            bits |= on ? ((inm ? 1u : 0u) | (inp ? 2u : 0u)) << (2 * i) : 0u;
+            bool inm, inp;
+            gv[i] = load_or_zero(rg, on_of(i, inm, inp) ? (u * sstride + c) * 8 : kNoLoad);
         }
         // phase ramps of this BF while its spectrum loads are in flight
         double alpha, beta;
@@ -1237,11 +1241,10 @@ __global__ __launch_bounds__(obj_threads<N>()) void k_obj_sum(const float2* __re
         __syncthreads();                          // row table of this BF complete (double buffered)
 #pragma unroll
         for (int i = 0; i < PM; ++i) {
-            const unsigned f = (bits >> (2 * i)) & 3u;
-            if (f) {
+            bool inm, inp;
+            if (on_of(i, inm, inp)) {
                 const int u = ustart + i * ustep;
                 const int up = u < H ? u : u - N;
-                const bool inm = f & 1u, inp = f & 2u;
                 const bool edm = inm && (unsigned)(up - flo_m) >= (unsigned)flen_m;
                 const bool edp = inp && (unsigned)(up - flo_p) >= (unsigned)flen_p;
                 const float2 cv =
