@@ -350,14 +350,14 @@ __device__ __forceinline__ void dft16(float2 (&x)[16]) {
 
 // Twiddles of the N = 1024 passes.  Pass 1: t[r-1] = exp(SIGN 2 pi i k r / 128),
 // k = j mod 16.  Pass 2: exp(SIGN 2 pi i jv r / 1024) for jv = j (ta) and j + 64 (tb).
-// Either from the table laid out as WaveFFTT<1024>'s, or from six sincospi (r = 1,
-// 2, 4 directly, the other r as products; tb = ta times exp(SIGN i pi r / 8)).
+// Either from the table laid out as WaveFFTT<1024>'s, or computed: r = 1 from the
+// fitted sincos, r = 2 and 4 by squaring, the other r as products; tb = ta times
+// exp(SIGN i pi r / 8).
 template <int SIGN>
 __device__ __forceinline__ void tw1024_products(float2 (&t)[7], int k, float den) {
-    float2 w1, w2, w4;
-    sincospif((float)(SIGN * 2 * k) / den, &w1.y, &w1.x);
-    sincospif((float)(SIGN * 4 * k) / den, &w2.y, &w2.x);
-    sincospif((float)(SIGN * 8 * k) / den, &w4.y, &w4.x);
+    const float2 w1 = cossin_rev((float)(SIGN * k) / den);
+    const float2 w2 = make_float2(fmaf(w1.x, w1.x, -w1.y * w1.y), 2.f * w1.x * w1.y);
+    const float2 w4 = make_float2(fmaf(w2.x, w2.x, -w2.y * w2.y), 2.f * w2.x * w2.y);
     t[0] = w1;
     t[1] = w2;
     t[2] = cmul(w1, w2);
