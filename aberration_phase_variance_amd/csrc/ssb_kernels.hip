@@ -934,7 +934,7 @@ __global__ __launch_bounds__(256, (pass2_min_waves<N, FP>())) void k_pass2(const
                     const float pb = atan_unit(x[r].y * __builtin_amdgcn_rcpf(bv[r].y));
                     s1a[r] += pa;
                     s1b[r] += pb;
-                    p2 += pa * pa + pb * pb;
+                    p2 = fmaf(pb, pb, fmaf(pa, pa, p2));
                 }
             } else {
 #pragma unroll
@@ -943,7 +943,7 @@ __global__ __launch_bounds__(256, (pass2_min_waves<N, FP>())) void k_pass2(const
                     const float pb = atan2_f(x[r].y, bv[r].y);
                     s1a[r] += pa;
                     s1b[r] += pb;
-                    p2 += pa * pa + pb * pb;
+                    p2 = fmaf(pb, pb, fmaf(pa, pa, p2));
                 }
             }
         } else {
@@ -962,7 +962,7 @@ __global__ __launch_bounds__(256, (pass2_min_waves<N, FP>())) void k_pass2(const
                     const float pb = atan_unit(x[r].y * i1);
                     s1a[r] += pa;
                     s1b[r] += pb;
-                    p2 += pa * pa + pb * pb;
+                    p2 = fmaf(pb, pb, fmaf(pa, pa, p2));
                 }
             } else {
 #pragma unroll
@@ -971,7 +971,7 @@ __global__ __launch_bounds__(256, (pass2_min_waves<N, FP>())) void k_pass2(const
                     const float pb = atan2_f(x[r].y, den1);
                     s1a[r] += pa;
                     s1b[r] += pb;
-                    p2 += pa * pa + pb * pb;
+                    p2 = fmaf(pb, pb, fmaf(pa, pa, p2));
                 }
             }
         }
