@@ -31,6 +31,9 @@ METRIC = "ms per phase-variance eval + BF×scan samples/s at 512²×8,937 BF (1 
 PAGES_MS = 222.7
 PEAK_FP32_TFLOPS = 157.3    # MI355X FP32 vector (256 CU x 2.4 GHz, packed)
 PEAK_HBM_GBS = 8000.0
+# vector-instruction issue ceiling: a wave64 VALU instruction occupies a 16-lane SIMD for
+# 4 cycles; 256 CUs x 4 SIMDs at 2.4 GHz
+PEAK_VALU_ISSUE = 256 * 4 * 2.4e9 / 4
 
 
 def algorithmic_work(n: int, info: dict) -> dict:
@@ -105,8 +108,7 @@ def plain_stream_gbs(dev) -> float:
     return 2.0 * (1 << 31) / (best * 1e-3) / 1e9
 
 
-def measured_traffic(kernel: str):
-    """HBM bytes per launch from the committed counter summary, if it matches these sources."""
+def _counter_line(kernel: str):
     path = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
     if not os.path.exists(path):
         return None
@@ -115,8 +117,26 @@ def measured_traffic(kernel: str):
         for line in fh:
             parts = line.split()
             if len(parts) >= 4 and not line.startswith("#") and parts[0] == kernel and parts[1] == want:
-                return float(parts[2]) + float(parts[3])
+                return parts
     return None
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch from the committed counter summary, if it matches these sources."""
+    parts = _counter_line(kernel)
+    return float(parts[2]) + float(parts[3]) if parts else None
+
+
+def issue_view(kernel: str, launch_ms: float):
+    """Vector-instruction issue time of one launch (SQ_INSTS_VALU from the committed counter
+    summary, if it matches these sources) against the measured launch time."""
+    parts = _counter_line(kernel)
+    if not parts or len(parts) < 5:
+        return None
+    insts = float(parts[4])
+    issue_ms = insts / PEAK_VALU_ISSUE * 1e3
+    return {"valu_wave_instructions": insts, "issue_ms": round(issue_ms, 4),
+            "frac": round(issue_ms / launch_ms, 4), "peak_wave_instructions_per_s": PEAK_VALU_ISSUE}
 
 
 def main():
@@ -282,7 +302,8 @@ def main():
                      "algorithmic_flops_per_launch": flops_launch,
                      "flops_view": {"achieved_tflops": round(achieved_tf, 3), "peak": PEAK_FP32_TFLOPS,
                                     "frac": round(achieved_tf / PEAK_FP32_TFLOPS, 4)},
-                     "kernel_source": kernel_source_hash()})
+                     "kernel_source": kernel_source_hash(),
+                     "issue_view": issue_view(dom, stage_ms[dom])})
     # the practical HBM ceiling on this GPU for context: a plain elementwise add over 2 GiB
     # (one read and one write stream), timed with events on torch's stream
     stream_gbs = plain_stream_gbs(dev)
@@ -293,7 +314,8 @@ def main():
     other_units = prof[other]["units"] / max(1, prof[other]["launches"])
     stages_roofline = {other: {"avg_launch_ms": round(stage_ms[other], 4),
                                "achieved_gbs": round(work[other]["bytes"] * other_units / t_other / 1e9, 1),
-                               "achieved_tflops": round(work[other]["flops"] * other_units / t_other / 1e12, 3)}}
+                               "achieved_tflops": round(work[other]["flops"] * other_units / t_other / 1e12, 3),
+                               "issue_view": issue_view(other, stage_ms[other])}}
     g_bytes = info["spectrum_bytes"]
     hbm = {"spectrum_read_gb": g_bytes / 1e9,
            "spectrum_read_frac_of_step": round(g_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
@@ -426,7 +448,8 @@ def main():
             "roofline": {"bound": "hbm", "kernel": dom2, "achieved": round(r2[dom2]["gbs"], 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(r2[dom2]["gbs"] / PEAK_HBM_GBS, 4),
                          "traffic": measured_traffic(dom2 + "@1024"),
-                         "frac_of_stream": round(r2[dom2]["gbs"] / stream_gbs, 4)},
+                         "frac_of_stream": round(r2[dom2]["gbs"] / stream_gbs, 4),
+                         "issue_view": issue_view(dom2 + "@1024", r2[dom2]["avg_launch_ms"])},
             "stages": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in r2[k].items()}
                        for k in r2},
             # notes page, "128 GB Apple M5 Max size-scaling follow-up": scalar evaluator
