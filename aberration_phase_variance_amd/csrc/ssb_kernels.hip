@@ -34,6 +34,9 @@ namespace {
 #ifndef SSB_ATAN_TERMS
 #define SSB_ATAN_TERMS 8
 #endif
+#ifndef SSB_PASS1_MIN_WAVES
+#define SSB_PASS1_MIN_WAVES 5 // pass-1 register budget at N = 512: resident waves per SIMD
+#endif
 #ifndef SSB_PASS2_MIN_WAVES_1024
 #define SSB_PASS2_MIN_WAVES_1024 4 // the same at N = 1024 (LDS also allows 4 workgroups per CU)
 #endif
@@ -126,6 +129,7 @@ __device__ __forceinline__ int unpack_len(unsigned p) { return (int)(p >> 16); }
 // 64-bit load through a buffer resource: an offset at or past the resource's size
 // returns zero without touching memory (predicated loads with no branch).
 typedef int ssb_v2i __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
 }
@@ -268,6 +272,20 @@ __global__ __launch_bounds__(256) void k_cols(const float2* in_m, const float2* 
 
 // exp(i chi_q) = (cos, sin)(2 pi q^T M q) of every half-plane entry, per trial
 // (BF independent): main [t] x tile-major [N/2/8][N][8], nyq [t][N].
+// Pass 1 at N = 512 copies each tile's block of the chi_q table straight into its LDS
+// tile, so the table is stored per layout tile as that tile's LDS image: column c of
+// the tile at c * N, row u at u ^ ((c & 7) << 2) (the tile's XOR swizzle).  Other sizes
+// keep the tile-major [tile][u][8] layout of the spectra.
+template <int N> constexpr bool chi_in_lds() { return N == 512; }
+template <int N> __host__ __device__ __forceinline__ int64_t chi_index(int u, int v) {
+    if constexpr (chi_in_lds<N>()) {
+        const int c = v % kTileW;
+        return (int64_t)(v / kTileW) * N * kTileW + c * N + (u ^ ((c & 7) << 2));
+    } else {
+        return tm_index(N, u, v);
+    }
+}
+
 template <int N>
 __global__ __launch_bounds__(256) void k_chiq(const TrialConst* __restrict__ tc, GeomDev geo,
                                               float2* __restrict__ chm, float2* __restrict__ chn) {
@@ -279,7 +297,7 @@ __global__ __launch_bounds__(256) void k_chiq(const TrialConst* __restrict__ tc,
     const int u = e / (H + 1), v = e % (H + 1);
     const double up = (double)(u < H ? u : u - N);
     const float2 val = chi_phasor(fma(geo.qux, up, geo.qvx * v), fma(geo.quy, up, geo.qvy * v), tc[t]);
-    if (v < H) chm[(int64_t)t * N * H + tm_index(N, u, v)] = val;
+    if (v < H) chm[(int64_t)t * N * H + chi_index<N>(u, v)] = val;
     else chn[(int64_t)t * N + u] = val;
 }
 
@@ -553,10 +571,25 @@ __device__ __forceinline__ void pass1_tile(const float2* __restrict__ gsrc, cons
     // 1. support and loads into registers (all loads in flight together)
     // gsrc / chsrc: the layout tile's block (main: [N][kTileW]; this workgroup's
     // columns start at csub) or the Nyquist column
+    // CL: the tile's chi_q block is stored as the tile's LDS image (chi_index) and is
+    // copied into the LDS tile asynchronously (16 bytes per lane, no registers held),
+    // each entry reading its value back from its own slot at the correction.
+    constexpr bool CL = chi_in_lds<N>() && !NYQ;
+    static_assert(!CL || RS <= H, "the copied block is waited for in the two-chain path");
     const __amdgpu_buffer_rsrc_t rg = make_rsrc(gsrc, N * (NYQ ? 1 : kTileW) * 8);
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(chsrc, N * (NYQ ? 1 : kTileW) * 8);
+    if constexpr (CL) {
+        static_assert(TC == kTileW && LD == N, "the chi_q block is the tile's LDS image");
+        constexpr int WAVE_BYTES = N * kTileW * 8 / (NT / 64);
+        const int lane = tid & 63;
+        const int wb = (tid >> 6) * WAVE_BYTES;
+#pragma unroll
+        for (int k = 0; k < WAVE_BYTES / 1024; ++k)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (lds_ptr_t)((char*)tile + wb + k * 1024), 16,
+                                                     wb + k * 1024 + lane * 16, 0, 0, 0);
+    }
     const int off0 = (ustart * SSTRIDE + csub + c) * 8;
-    float2 gv[PM], chv[PM];
+    float2 gv[PM], chv[CL ? 1 : PM];
     unsigned bits = 0;
 #pragma unroll
     for (int i = 0; i < PM; ++i) {
@@ -568,7 +601,7 @@ __device__ __forceinline__ void pass1_tile(const float2* __restrict__ gsrc, cons
         const bool on = (NYQ ? u < N : true) && (inm || inp) && (u != 0 || v != 0);
         const int off = on ? off0 + i * RS * SSTRIDE * 8 : kNoLoad;
         gv[i] = STREAM ? load_or_zero_nt(rg, off) : load_or_zero(rg, off);
-        chv[i] = load_or_zero(rc, off);
+        if constexpr (!CL) chv[i] = load_or_zero(rc, off);
         bits |= on ? ((inm ? 1u : 0u) | (inp ? 2u : 0u)) << (2 * i) : 0u;
     }
     // the phase slopes of this BF pixel while the loads are in flight
@@ -590,7 +623,10 @@ __device__ __forceinline__ void pass1_tile(const float2* __restrict__ gsrc, cons
             const bool inm = f & 1u, inp = f & 2u;
             const bool edm = inm && (unsigned)(up - flo_m) >= (unsigned)flen_m;
             const bool edp = inp && (unsigned)(up - flo_p) >= (unsigned)flen_p;
-            val = correct_entry(gv[i], chv[i], e, inm, inp, edm, edp, up, v, k.x, k.y, geo);
+            float2 ch;
+            if constexpr (CL) ch = trow[i * RS];
+            else ch = chv[i];
+            val = correct_entry(gv[i], ch, e, inm, inp, edm, edp, up, v, k.x, k.y, geo);
         }
         trow[i * RS] = val;
     };
@@ -600,6 +636,12 @@ __device__ __forceinline__ void pass1_tile(const float2* __restrict__ gsrc, cons
         float2 ea = phasor_rev_neg(fma((double)ustart, beta, av));
         float2 eb = phasor_rev_neg(fma((double)(ustart - H), beta, av));
         const float2 st = phasor_rev_neg((double)RS * beta);
+        if constexpr (CL) {
+            // every wave's copies have landed before any thread reads a slot another
+            // wave filled
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+        }
 #pragma unroll
         for (int i = 0; i < PM / 2; ++i) {
             entry(i, ea);
@@ -667,8 +709,13 @@ __device__ __forceinline__ void pass1_tile(const float2* __restrict__ gsrc, cons
 // exceed the 256 MB MALL.  With many trials the chunk is small (32 BF at 200 trials)
 // and each trial row of the grid re-reads its tiles from the MALL; there the
 // default policy is kept (200-trial batch: 5.30 against 5.55 ms per trial).
+// Register budget: with the chi_q block copied to the LDS (N = 512) the kernel fits
+// the budget of SSB_PASS1_MIN_WAVES waves per SIMD, which the 32 KB tile's LDS also
+// allows (five 32 KB tiles fill the 160 KB of a CU).
+template <int N> constexpr int pass1_min_waves() { return chi_in_lds<N>() ? SSB_PASS1_MIN_WAVES : 1; }
+
 template <int N, int TC, bool STREAM>
-__global__ __launch_bounds__(pass1_threads<N>()) void k_pass1(const float2* __restrict__ gm,
+__global__ __launch_bounds__(pass1_threads<N>(), (pass1_min_waves<N>())) void k_pass1(const float2* __restrict__ gm,
                                                          const float2* __restrict__ gn,
                                                          const float2* __restrict__ chm,
                                                          const float2* __restrict__ chn,
