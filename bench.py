@@ -319,6 +319,13 @@ def main():
     g_bytes = info["spectrum_bytes"]
     hbm = {"spectrum_read_gb": g_bytes / 1e9,
            "spectrum_read_frac_of_step": round(g_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    # the whole evaluation's counted HBM bytes (both passes, committed counters) per step
+    t_pass1, t_pass2 = measured_traffic("pass1"), measured_traffic("pass2")
+    if t_pass1 is not None and t_pass2 is not None:
+        ev_gbs = (t_pass1 + t_pass2) / (ms_per_step * 1e-3) / 1e9
+        hbm.update({"evaluation_counted_gb": round((t_pass1 + t_pass2) / 1e9, 3),
+                    "evaluation_gbs": round(ev_gbs, 1), "evaluation_frac_of_peak": round(ev_gbs / PEAK_HBM_GBS, 4),
+                    "evaluation_frac_of_stream": round(ev_gbs / stream_gbs, 4)})
 
     # oracle on the host: bounded BF sample of the same workload, plus GPU moments of that range
     cpu = None
