@@ -325,3 +325,135 @@ def test_two_pass_half_plane_equals_definition(tiny_counts):
         re = (a[:, 0].real[:, None] + ((-1.0) ** x)[None, :] * a[:, h].real[:, None]) / n
         assert np.max(np.abs(im - ref.imag)) < 1e-12 * np.abs(ref).max()
         assert np.max(np.abs(re - ref.real)) < 1e-12 * np.abs(ref).max()
+
+
+# ------------------------------------------------------------------ loss formula (O12)
+def _variance_pin(loss_fn):
+    """loss_fn(s1, s2, n_bf) against the population variance over BF of a phase stack,
+    averaged over pixels (numpy's var with ddof = 0), and against a two-BF, 2 x 2 example
+    worked by hand: per-pixel variances ((a - b)/2)^2 = 0.01, 0.01, 0, 0.16, mean 0.045."""
+    rng = np.random.Generator(np.random.PCG64(7))
+    ok = True
+    for n_bf, n in ((2, 2), (5, 8), (37, 16)):
+        phi = rng.uniform(-math.pi, math.pi, (n_bf, n, n))
+        ref = float(np.var(phi, axis=0).mean())
+        got = loss_fn(phi.sum(axis=0), float((phi * phi).sum()), n_bf)
+        ok = ok and abs(got - ref) <= 1e-14 * max(1.0, abs(ref))
+    phi = np.array([[[0.1, 0.2], [0.3, 0.4]], [[0.3, 0.0], [0.3, -0.4]]])
+    got = loss_fn(phi.sum(axis=0), float((phi * phi).sum()), 2)
+    return ok and abs(got - 0.045) <= 1e-15
+
+
+def test_loss_from_moments_is_population_variance():
+    assert _variance_pin(O.loss_from_moments)
+
+
+def test_loss_is_variance_of_per_bf_phases(tiny_counts):
+    """The whole loss equals numpy's population variance over the stack of per-BF phase
+    images, each built by its own 2-D inverse DFT (written out as a direct sum here)."""
+    g = _geom("tiny")
+    kx, ky = O.bf_kvectors(g)
+    dc = O.dc_value(tiny_counts)
+    params = (-55.0, 11.0, 1.9)
+    stack = []
+    for b in range(49):
+        t = O.transfer(g, params, kx[b], ky[b])
+        full = O.full_plane(O.corrected_spectrum(O.scan_spectrum(tiny_counts[b]), t, dc))
+        stack.append(np.angle(_direct_dft2(full, +1.0)))
+    ref = float(np.var(np.array(stack), axis=0).mean())
+    assert abs(O.loss(g, tiny_counts, params, dc) - ref) <= 1e-12 * ref
+
+
+def test_variance_pin_catches_planted_mistakes():
+    """Plausible slips in the loss formula each fail the variance pin."""
+    def sample_var(s1, s2, n_bf):              # divides by n_bf - 1
+        n2 = s1.size
+        return (s2 - float(np.sum(s1 * s1)) / n_bf) / ((n_bf - 1) * n2)
+
+    def var_of_mean(s1, s2, n_bf):             # variance of the mean phase image instead
+        m = s1 / n_bf
+        return float(np.var(m))
+
+    def no_pixel_norm(s1, s2, n_bf):           # drops the 1/N^2 of the second term
+        return s2 / (n_bf * s1.size) - float(np.sum((s1 / n_bf) ** 2))
+
+    for bad in (sample_var, var_of_mean, no_pixel_norm):
+        assert not _variance_pin(bad), bad.__name__
+
+
+# ------------------------------------------------------------------ rotation branch of q (O5)
+def _rotation_pin(qfun):
+    """qfun(g) -> (qx, qy) against the scan frequencies rotated counterclockwise by rho
+    written as a complex product: (qx + i qy) = e^{i rho} s (v + i u'), u' signed
+    (fftfreq), v = 0 .. N/2."""
+    ok = True
+    for name, rho in (("tiny", 0.3), ("tiny", -2.1), ("small", 0.3 + math.pi)):
+        g = _geom(name, rotation_rad=rho)
+        n = g.scan_n
+        u = np.arange(n)
+        up = np.where(u < n // 2, u, u - n).astype(np.float64)
+        v = np.arange(n // 2 + 1, dtype=np.float64)
+        z = np.exp(1j * rho) * g.q_step_px * (v[None, :] + 1j * up[:, None])
+        qx, qy = qfun(g)
+        ok = ok and np.max(np.abs(qx - z.real)) < 1e-12 and np.max(np.abs(qy - z.imag)) < 1e-12
+    return ok
+
+
+def test_q_rotation_is_counterclockwise():
+    assert _rotation_pin(O.q_vectors)
+
+
+def test_rotation_pin_catches_planted_mistake():
+    def flipped(g):                            # the sine term of one component with the wrong sign
+        qx, qy = O.q_vectors(dataclasses.replace(g, rotation_rad=0.0))
+        c, s = math.cos(g.rotation_rad), math.sin(g.rotation_rad)
+        return c * qx + s * qy, s * qx + c * qy
+
+    def transposed(g):                         # u and v swapped before rotating
+        qx, qy = O.q_vectors(dataclasses.replace(g, rotation_rad=0.0))
+        c, s = math.cos(g.rotation_rad), math.sin(g.rotation_rad)
+        return c * qy - s * qx, s * qy + c * qx
+
+    assert not _rotation_pin(flipped)
+    assert not _rotation_pin(transposed)
+
+
+def test_transfer_rotation_covariance():
+    """With pure defocus and a round aperture the probe is rotation invariant, so
+    rotating the scan frequencies by rho equals rotating the BF offset by -rho:
+    T_rho(q; k) = T_0(q; Rot(-rho) k) (both shifted apertures move together)."""
+    g0 = _geom("small")
+    rho = 0.7
+    g = dataclasses.replace(g0, rotation_rad=rho)
+    kx, ky = O.bf_kvectors(g0)
+    c, s = math.cos(rho), math.sin(rho)
+    for b in (3, 150, 301):
+        kxr, kyr = c * kx[b] + s * ky[b], -s * kx[b] + c * ky[b]
+        t_rot = O.transfer(g, (-37.0, 0.0, 0.0), kx[b], ky[b])
+        t_ref = O.transfer(g0, (-37.0, 0.0, 0.0), kxr, kyr)
+        assert np.max(np.abs(t_rot - t_ref)) < 1e-12, b
+    # the opposite sense of rotation fails the same check
+    t_bad = O.transfer(dataclasses.replace(g0, rotation_rad=-rho), (-37.0, 0.0, 0.0), kx[150], ky[150])
+    kxr, kyr = c * kx[150] + s * ky[150], -s * kx[150] + c * ky[150]
+    assert np.count_nonzero(np.abs(t_bad - O.transfer(g0, (-37.0, 0.0, 0.0), kxr, kyr)) > 1e-9) > 100
+
+
+def test_conjugate_branch_through_rotation():
+    """L(rho + pi, -theta) = L(rho, theta) with the conjugate branch reached through the
+    geometry's rotation (q -> -q) and negated aberrations (Notes, "Conditional joint
+    rotation check": the 180-degree branch reverses the aberration signs).  At the small
+    workload no Nyquist-line entry has nonzero transfer, so the identity is exact to
+    rounding; per-BF phases are exact negatives."""
+    w = WORKLOADS["small"]
+    counts = cached_counts(w)
+    dc = O.dc_value(counts)
+    ga = _geom("small", rotation_rad=0.3)
+    gb = _geom("small", rotation_rad=0.3 + math.pi)
+    la = O.loss(ga, counts, (40.0, 5.0, 0.3), dc)
+    lb = O.loss(gb, counts, (-40.0, -5.0, 0.3), dc)
+    assert abs(la - lb) <= 1e-12 * la
+    s1a, _ = O.bf_moments(ga, counts[:40], (40.0, 5.0, 0.3), dc, list(range(40)))
+    s1b, _ = O.bf_moments(gb, counts[:40], (-40.0, -5.0, 0.3), dc, list(range(40)))
+    assert np.max(np.abs(s1a + s1b)) < 1e-10
+    # and it is not a tautology: the same aberrations on the rotated branch differ
+    assert abs(O.loss(gb, counts, (40.0, 5.0, 0.3), dc) - la) > 1e-3 * la
