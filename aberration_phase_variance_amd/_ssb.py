@@ -54,6 +54,9 @@ class ssb_info(ctypes.Structure):
         ("columns_read", ctypes.c_int64),
         ("variant", ctypes.c_int32),
         ("pad", ctypes.c_int32),
+        ("workspace_bytes", ctypes.c_int64),
+        ("reserved_trials", ctypes.c_int32),
+        ("pad2", ctypes.c_int32),
     ]
 
 
@@ -110,7 +113,7 @@ class ssb_probe_fit(ctypes.Structure):
     ]
 
 
-EXPORTS = ("ssb_prepare", "ssb_loss", "ssb_moments", "ssb_object", "ssb_spectrum", "ssb_set_chunk",
+EXPORTS = ("ssb_prepare", "ssb_reserve", "ssb_loss", "ssb_moments", "ssb_object", "ssb_spectrum", "ssb_set_chunk",
            "ssb_profile", "ssb_query", "ssb_release", "ssb_last_error", "ssb_nelder_mead", "ssb_fit",
            "ssb_detector_sum", "ssb_fit_probe", "ssb_gather_bf", "ssb_set_variant")
 
@@ -128,6 +131,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     dp, fp = ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_float)
     lib.ssb_prepare.argtypes = [ctypes.POINTER(ssb_geometry), vp, i64, vp, ctypes.POINTER(vp)]
+    lib.ssb_reserve.argtypes = [vp, i32]
     lib.ssb_loss.argtypes = [vp, fp, i32, dp, vp, vp]
     lib.ssb_moments.argtypes = [vp, fp, i64, i64, vp, dp, vp]
     lib.ssb_object.argtypes = [vp, fp, vp, vp, vp]
@@ -168,6 +172,38 @@ def _ptr(x) -> int | None:
     return int(x.data_ptr())
 
 
+def _dev(x, name: str, dtypes: tuple, numel: int, optional: bool = False) -> int | None:
+    """Device address of x after checking it, when it is a tensor: one of the dtypes
+    (names such as "float32"), exactly numel elements, contiguous, on a GPU.  Raw
+    integer addresses are passed through unchecked (the caller vouches for them)."""
+    if x is None:
+        if optional:
+            return None
+        raise ValueError(f"{name}: a device buffer is required")
+    if isinstance(x, int):
+        return x
+    dt = str(x.dtype).replace("torch.", "")
+    if dt not in dtypes:
+        raise ValueError(f"{name}: dtype {dt}, expected one of {', '.join(dtypes)}")
+    if x.numel() != numel:
+        raise ValueError(f"{name}: {x.numel()} elements, expected {numel}")
+    if not x.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if not x.is_cuda:
+        raise ValueError(f"{name}: must be a GPU tensor")
+    return int(x.data_ptr())
+
+
+def _scan_n(handle: int) -> int:
+    info = ssb_info()
+    _check(load_library().ssb_query(handle, ctypes.byref(info)))
+    return info.scan_n
+
+
+_U32 = ("int32", "uint32")
+_C64 = ("float32", "complex64")   # complex64 values as interleaved float32 pairs, or complex64
+
+
 def _stream(s) -> int | None:
     if s is None:
         return None
@@ -194,9 +230,15 @@ def ssb_prepare(geometry, counts, n_bf: int, stream=None) -> int:
     """Returns an opaque handle (int).  counts: device uint32 [n_bf][N][N] (tensor or address)."""
     lib = load_library()
     g = make_geometry(geometry)
+    ptr = _dev(counts, "counts", _U32, int(n_bf) * g.scan_n * g.scan_n)
     h = ctypes.c_void_p()
-    _check(lib.ssb_prepare(ctypes.byref(g), _ptr(counts), int(n_bf), _stream(stream), ctypes.byref(h)))
+    _check(lib.ssb_prepare(ctypes.byref(g), ptr, int(n_bf), _stream(stream), ctypes.byref(h)))
     return h.value
+
+
+def ssb_reserve(handle: int, max_trials: int) -> None:
+    """Size the workspace so that loss calls of up to max_trials trials allocate nothing."""
+    _check(load_library().ssb_reserve(handle, int(max_trials)))
 
 
 def ssb_loss(handle: int, params, mean_phase=None, stream=None) -> np.ndarray:
@@ -204,8 +246,12 @@ def ssb_loss(handle: int, params, mean_phase=None, stream=None) -> np.ndarray:
     lib = load_library()
     p = _params(params)
     out = np.empty(p.shape[0], dtype=np.float64)
+    mp = None
+    if mean_phase is not None:
+        n = _scan_n(handle)
+        mp = _dev(mean_phase, "mean_phase", ("float32",), n * n)
     _check(lib.ssb_loss(handle, p.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), p.shape[0],
-                        out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), _ptr(mean_phase), _stream(stream)))
+                        out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), mp, _stream(stream)))
     return out
 
 
@@ -213,21 +259,30 @@ def ssb_moments(handle: int, params3, bf_begin: int, bf_end: int, s1, stream=Non
     """S1 into device double [N][N] s1; returns S2."""
     lib = load_library()
     p = _params(params3, 1)
+    n = _scan_n(handle)
+    ptr = _dev(s1, "s1", ("float64",), n * n)
     s2 = ctypes.c_double()
     _check(lib.ssb_moments(handle, p.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), int(bf_begin), int(bf_end),
-                           _ptr(s1), ctypes.byref(s2), _stream(stream)))
+                           ptr, ctypes.byref(s2), _stream(stream)))
     return s2.value
 
 
 def ssb_object(handle: int, params3, phase, psi=None, stream=None) -> None:
     lib = load_library()
     p = _params(params3, 1)
-    _check(lib.ssb_object(handle, p.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), _ptr(phase), _ptr(psi),
-                          _stream(stream)))
+    n = _scan_n(handle)
+    ph = _dev(phase, "phase", ("float32",), n * n)
+    ps = None
+    if psi is not None:
+        ps = _dev(psi, "psi", _C64, n * n * (2 if str(getattr(psi, "dtype", "")).endswith("float32") else 1))
+    _check(lib.ssb_object(handle, p.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), ph, ps, _stream(stream)))
 
 
 def ssb_spectrum(handle: int, bf: int, out, stream=None) -> None:
-    _check(load_library().ssb_spectrum(handle, int(bf), _ptr(out), _stream(stream)))
+    """Cached spectrum of BF pixel bf into out: complex64 [N][N/2+1] (or float32 pairs)."""
+    n = _scan_n(handle)
+    ne = n * (n // 2 + 1) * (2 if str(getattr(out, "dtype", "")).endswith("float32") else 1)
+    _check(load_library().ssb_spectrum(handle, int(bf), _dev(out, "out", _C64, ne), _stream(stream)))
 
 
 def ssb_set_chunk(handle: int, chunk_bf: int) -> None:
@@ -313,7 +368,9 @@ def ssb_fit(handle: int, trials, options=None, trace_cap: int = 4096, stream=Non
 
 def ssb_detector_sum(frames, scan_n: int, det_n: int, sums, stream=None) -> None:
     """sums (device uint64 [det_n^2]) = exact sum of the device uint32 frames [scan_n^2][det_n^2]."""
-    _check(load_library().ssb_detector_sum(_ptr(frames), int(scan_n), int(det_n), _ptr(sums), _stream(stream)))
+    f = _dev(frames, "frames", _U32, int(scan_n) ** 2 * int(det_n) ** 2)
+    sp = _dev(sums, "sums", ("int64", "uint64"), int(det_n) ** 2)
+    _check(load_library().ssb_detector_sum(f, int(scan_n), int(det_n), sp, _stream(stream)))
 
 
 def ssb_fit_probe(sums, scan_n: int, det_n: int) -> dict:
@@ -328,4 +385,6 @@ def ssb_fit_probe(sums, scan_n: int, det_n: int) -> dict:
 def ssb_gather_bf(frames, geometry, counts, n_bf: int, stream=None) -> None:
     """counts (device uint32 [n_bf][N][N]) = the BF pixels of the device frames, BF-major."""
     g = make_geometry(geometry)
-    _check(load_library().ssb_gather_bf(_ptr(frames), ctypes.byref(g), _ptr(counts), int(n_bf), _stream(stream)))
+    f = _dev(frames, "frames", _U32, g.scan_n ** 2 * g.det_n ** 2)
+    c = _dev(counts, "counts", _U32, int(n_bf) * g.scan_n ** 2)
+    _check(load_library().ssb_gather_bf(f, ctypes.byref(g), c, int(n_bf), _stream(stream)))

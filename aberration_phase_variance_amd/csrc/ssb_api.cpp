@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -92,6 +93,10 @@ struct ssb_handle {
     // object workspace
     char* ows = nullptr;
     size_t ows_bytes = 0;
+    // trials every loss call up to this many fits without allocating (ssb_reserve)
+    int reserved_trials = 0;
+    // host staging of the per-trial constants (capacity = reserved trials)
+    std::vector<TrialConst> htc;
     // host copy of the active flags, prefix counts for range queries
     std::vector<int64_t> active_prefix;
     // stage profiling
@@ -202,15 +207,15 @@ struct LossPlan {
     size_t total;
 };
 
-LossPlan plan_loss(const ssb_handle* h, int64_t nb, int n_trials) {
+LossPlan plan_loss(const ssb_handle* h, int64_t nb, int n_trials, int variant, int64_t chunk_user) {
     const int64_t n = h->n, hh = h->h;
     const double plane = (double)n * (hh + 1) * sizeof(float2);
     // memory bound on the chunk (intermediate for all trials of the call)
     int64_t budget_cap = (int64_t)(kInterBudget / (plane * n_trials));
     budget_cap = std::max<int64_t>(kGroupBF, (budget_cap / kGroupBF) * kGroupBF);
     int64_t cap = budget_cap;
-    if (h->chunk_user > 0)
-        cap = std::min<int64_t>(cap, ((h->chunk_user + kGroupBF - 1) / kGroupBF) * kGroupBF);
+    if (chunk_user > 0)
+        cap = std::min<int64_t>(cap, ((chunk_user + kGroupBF - 1) / kGroupBF) * kGroupBF);
     const int64_t need = ((nb + kGroupBF - 1) / kGroupBF) * kGroupBF;
     if (cap > need) cap = need;
     LossPlan pl;
@@ -231,12 +236,47 @@ LossPlan plan_loss(const ssb_handle* h, int64_t nb, int n_trials) {
     pl.off_chm = (size_t)align_up<float2>(z, off, (size_t)n_trials * n * hh);
     pl.off_chn = (size_t)align_up<float2>(z, off, (size_t)n_trials * n);
     pl.off_na = pl.off_nb = 0;
-    if (h->variant == SSB_VARIANT_FULL_PLANE) {
+    if (variant == SSB_VARIANT_FULL_PLANE) {
         pl.off_na = (size_t)align_up<float2>(z, off, (size_t)n_trials * cap * n);
         pl.off_nb = (size_t)align_up<float2>(z, off, (size_t)n_trials * cap * n);
     }
     pl.total = off + 256;
     return pl;
+}
+
+LossPlan plan_loss(const ssb_handle* h, int64_t nb, int n_trials) {
+    return plan_loss(h, nb, n_trials, h->variant, h->chunk_user);
+}
+
+// Loss workspace that every call with at most n_trials trials fits, on any BF range, in
+// either variant and under any chunk cap (a cap only shrinks the chunk; the chunk also
+// shrinks as trials grow, so the need is not monotonic in the trial count).
+size_t loss_ws_need(const ssb_handle* h, int n_trials) {
+    size_t need = 0;
+    for (int t = 1; t <= n_trials; ++t)
+        for (int var : {SSB_VARIANT_HALF_PLANE, SSB_VARIANT_FULL_PLANE})
+            need = std::max(need, plan_loss(h, h->n_bf, t, var, 0).total);
+    return need;
+}
+
+// Object workspace layout (both variants' buffers; the half plane leaves the last two unused).
+struct ObjPlan {
+    size_t o_part, o_pm, o_pn, o_npart, o_nab, total;
+};
+ObjPlan plan_object(const ssb_handle* h) {
+    const int n = h->n, hh = h->h;
+    const int nseg = obj_segments(h->n_bf);
+    const size_t ne = (size_t)n * (hh + 1);
+    size_t off = 0;
+    char* z = nullptr;
+    ObjPlan p;
+    p.o_part = (size_t)align_up<double2>(z, off, ne * nseg);
+    p.o_pm = (size_t)align_up<float2>(z, off, (size_t)n * hh);
+    p.o_pn = (size_t)align_up<float2>(z, off, (size_t)n);
+    p.o_npart = (size_t)align_up<double2>(z, off, (size_t)2 * n * nseg);
+    p.o_nab = (size_t)align_up<float2>(z, off, (size_t)2 * n);
+    p.total = off + 256;
+    return p;
 }
 
 int ensure(char** buf, size_t* have, size_t need, const char* what) {
@@ -255,12 +295,27 @@ int ensure(char** buf, size_t* have, size_t need, const char* what) {
     return SSB_OK;
 }
 
+// Workspaces for calls of up to max_trials trials, so that those calls allocate nothing.
+int reserve(ssb_handle* h, int max_trials) {
+    int rc = ensure(&h->ws, &h->ws_bytes, loss_ws_need(h, max_trials), "workspace allocation");
+    if (rc) return rc;
+    if ((rc = ensure(&h->ows, &h->ows_bytes, plan_object(h).total, "object workspace allocation"))) return rc;
+    try {
+        h->htc.reserve((size_t)max_trials);
+    } catch (...) {
+        return fail(SSB_ENOMEM, "host staging of %d trial constants", max_trials);
+    }
+    h->reserved_trials = std::max(h->reserved_trials, max_trials);
+    return SSB_OK;
+}
+
 // Phase moments of n_trials trials over BF [b_begin, b_end): leaves S1 (double
 // [t][N][N]) and S2 (double [t]) in the workspace.
-// htc receives the host copy of the trial constants; it must outlive the
-// stream's use of it (the caller synchronizes before returning).
+// The host copy of the trial constants is staged in the handle (h->htc); it must
+// outlive the stream's use of it (the caller synchronizes before returning).
 int run_moments(ssb_handle* h, const float* params, int n_trials, int64_t b_begin, int64_t b_end,
-                hipStream_t st, std::vector<TrialConst>& htc, LossPlan* out_plan) {
+                hipStream_t st, LossPlan* out_plan) {
+    std::vector<TrialConst>& htc = h->htc;
     const int64_t nb = b_end - b_begin;
     LossPlan pl = plan_loss(h, nb, n_trials);
     int rc = ensure(&h->ws, &h->ws_bytes, pl.total, "workspace allocation");
@@ -278,6 +333,13 @@ int run_moments(ssb_handle* h, const float* params, int n_trials, int64_t b_begi
     float2* nyq_a = fp ? reinterpret_cast<float2*>(h->ws + pl.off_na) : nullptr;
     float2* nyq_b = fp ? reinterpret_cast<float2*>(h->ws + pl.off_nb) : nullptr;
 
+    if ((size_t)n_trials > htc.capacity()) {      // beyond the reservation: the one host allocation
+        try {
+            htc.reserve((size_t)n_trials);
+        } catch (...) {
+            return fail(SSB_ENOMEM, "host staging of %d trial constants", n_trials);
+        }
+    }
     htc.resize(n_trials);
     for (int t = 0; t < n_trials; ++t) htc[t] = trial_const(h, params + 3 * t);
     SSB_HIP(hipMemcpyAsync(tc, htc.data(), sizeof(TrialConst) * n_trials, hipMemcpyHostToDevice, st),
@@ -469,9 +531,8 @@ int ssb_prepare(const ssb_geometry* g, const uint32_t* counts, int64_t n_bf, voi
     unsigned long long tot = 0;
     for (unsigned long long s : sums) tot += s;
     h->dc = (double)tot / (double)n_bf;
-    // size the single-trial workspace now so a plain loss call allocates nothing
-    const LossPlan pl = plan_loss(h, n_bf, 1);
-    int rc = ensure(&h->ws, &h->ws_bytes, pl.total, "workspace allocation");
+    // single-trial loss and object workspaces now, so that those calls allocate nothing
+    int rc = reserve(h, 1);
     if (rc) return cleanup(rc);
     *out = h;
     return SSB_OK;
@@ -487,8 +548,7 @@ int ssb_loss(ssb_handle* h, const float* params, int32_t n_trials, double* losse
     if ((rc = check_params(params, n_trials))) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
     LossPlan pl;
-    std::vector<TrialConst> htc;
-    if ((rc = run_moments(h, params, n_trials, 0, h->n_bf, st, htc, &pl))) {
+    if ((rc = run_moments(h, params, n_trials, 0, h->n_bf, st, &pl))) {
         (void)hipStreamSynchronize(st);
         return rc;
     }
@@ -517,8 +577,7 @@ int ssb_moments(ssb_handle* h, const float* params3, int64_t bf_begin, int64_t b
     if ((rc = check_params(params3, 1))) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
     LossPlan pl;
-    std::vector<TrialConst> htc;
-    if ((rc = run_moments(h, params3, 1, bf_begin, bf_end, st, htc, &pl))) {
+    if ((rc = run_moments(h, params3, 1, bf_begin, bf_end, st, &pl))) {
         (void)hipStreamSynchronize(st);
         return rc;
     }
@@ -536,22 +595,16 @@ int ssb_object(ssb_handle* h, const float* params3, float* phase, float* psi, vo
     if (!params3 || !phase) return fail(SSB_EINVAL, "null argument");
     if ((rc = check_params(params3, 1))) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const int n = h->n, hh = h->h;
+    const int n = h->n;
     const int nseg = obj_segments(h->n_bf);
-    const size_t ne = (size_t)n * (hh + 1);
-    size_t off = 0;
-    char* z = nullptr;
-    const size_t o_part = (size_t)align_up<double2>(z, off, ne * nseg);
-    const size_t o_pm = (size_t)align_up<float2>(z, off, (size_t)n * hh);
-    const size_t o_pn = (size_t)align_up<float2>(z, off, (size_t)n);
+    const ObjPlan op = plan_object(h);            // reserved by ssb_prepare: no allocation here
+    if ((rc = ensure(&h->ows, &h->ows_bytes, op.total, "object workspace allocation"))) return rc;
     const bool fp = h->variant == SSB_VARIANT_FULL_PLANE;
-    const size_t o_npart = fp ? (size_t)align_up<double2>(z, off, (size_t)2 * n * nseg) : 0;
-    const size_t o_nab = fp ? (size_t)align_up<float2>(z, off, (size_t)2 * n) : 0;
-    if ((rc = ensure(&h->ows, &h->ows_bytes, off + 256, "object workspace allocation"))) return rc;
-    double2* part = reinterpret_cast<double2*>(h->ows + o_part);
-    float2* pm = reinterpret_cast<float2*>(h->ows + o_pm);
-    float2* pn = reinterpret_cast<float2*>(h->ows + o_pn);
-    float2* nab = fp ? reinterpret_cast<float2*>(h->ows + o_nab) : nullptr;
+    const size_t o_npart = op.o_npart;
+    double2* part = reinterpret_cast<double2*>(h->ows + op.o_part);
+    float2* pm = reinterpret_cast<float2*>(h->ows + op.o_pm);
+    float2* pn = reinterpret_cast<float2*>(h->ows + op.o_pn);
+    float2* nab = fp ? reinterpret_cast<float2*>(h->ows + op.o_nab) : nullptr;
     const TrialConst tc = trial_const(h, params3);   // kernel argument: no host-staged copy
     {
         StageTimer tm(h, SSB_STAGE_OBJ_SUM, st, h->n_active);
@@ -659,7 +712,18 @@ int ssb_query(const ssb_handle* h, ssb_info* info) {
     info->columns_read = h->columns_read;
     info->variant = h->variant;
     info->pad = 0;
+    info->workspace_bytes = (int64_t)(h->ws_bytes + h->ows_bytes);
+    info->reserved_trials = h->reserved_trials;
+    info->pad2 = 0;
     return SSB_OK;
+}
+
+int ssb_reserve(ssb_handle* h, int32_t max_trials) {
+    g_err.clear();
+    int rc = check_handle(h);
+    if (rc) return rc;
+    if (max_trials < 1 || max_trials > 65535) return fail(SSB_EINVAL, "max_trials must be in [1, 65535]");
+    return reserve(h, max_trials);
 }
 
 void ssb_release(ssb_handle* h) {

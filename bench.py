@@ -7,7 +7,8 @@ already resident in HBM.  Prints one JSON line (rank 0, one GPU).
 Also reported: the object redraw, the per-trial time inside a 200-trial batch,
 the spectrum build (prepare), per-stage device times measured with HIP events on
 the library's stream, the roofline of the dominant kernel, and the float64
-oracle timed on the host on a bounded sample of the same workload.
+oracle timed on the host's cores over whole evaluations (a process pool over BF
+ranges), with its results compared with the library's.
 """
 from __future__ import annotations
 
@@ -146,7 +147,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="full", choices=["tiny", "small", "medium", "full", "full1024"])
     ap.add_argument("--batch", type=int, default=200, help="trials in the batched measurement (0 = skip)")
-    ap.add_argument("--cpu-sample-bf", type=int, default=1024, help="BF pixels in the oracle CPU sample (0 = skip)")
+    ap.add_argument("--cpu-baseline", type=int, default=1,
+                    help="time the float64 oracle on the host's cores (process pool over BF ranges): one whole "
+                         "evaluation and the object of this workload, whole tiny/small/medium evaluations; 0 = skip")
     ap.add_argument("--detector", type=int, default=1,
                     help="also time the detector side on full frames (detector sum, probe fit, BF gather); 0 = skip")
     ap.add_argument("--scan1024", type=int, default=1,
@@ -327,42 +330,66 @@ def main():
                     "evaluation_gbs": round(ev_gbs, 1), "evaluation_frac_of_peak": round(ev_gbs / PEAK_HBM_GBS, 4),
                     "evaluation_frac_of_stream": round(ev_gbs / stream_gbs, 4)})
 
-    # oracle on the host: bounded BF sample of the same workload, plus GPU moments of that range
+    # oracle on the host: whole evaluations with the pooled float64 oracle (every BF pixel,
+    # BF ranges over the host's cores), compared with the library's results
     cpu = None
     oracle_check = None
-    if args.cpu_sample_bf > 0:
+    if args.cpu_baseline:
         from oracle import ssb_oracle as O
+        from oracle.pool import OraclePool
+        from synth import cached_counts
 
-        nb = min(args.cpu_sample_bf, w.n_bf)
-        b0 = max(0, w.n_bf // 2 - nb // 2)
-        b1 = b0 + nb
-        sample = counts[b0:b1].cpu().numpy().view(np.uint32)
         dc = info["dc"]
         og = O.OGeom.from_any(g)
-        log(f"[bench] oracle on BF [{b0}, {b1}) ...")
+        mp = torch.full((n, n), float("nan"), dtype=torch.float32, device=dev)
+        gpu_loss = ssb.ssb_loss(h, params, mp)[0]
+        gpu_phase = torch.full((n, n), float("nan"), dtype=torch.float32, device=dev)
+        ssb.ssb_object(h, params[0], gpu_phase)
+        torch.cuda.synchronize()
         t1 = time.perf_counter()
-        r1, r2 = O.bf_moments(og, sample, params[0], dc, list(range(b0, b1)))
-        cpu_s = time.perf_counter() - t1
-        cpu = {"value": nb * n * n / cpu_s, "unit": "BF×scan samples/s", "cores": 1, "kind": "oracle",
-               "sample": f"float64 oracle moments of BF [{b0}, {b1}) ({nb} of {w.n_bf} BF x {n}^2 scan) at the "
-                         f"true aberrations, one host thread, {cpu_s:.1f} s",
-               "host_cores_available": len(os.sched_getaffinity(0))}
-        # whole evaluations of the oracle at the two smallest workloads (context)
-        from synth import cached_counts
-        whole = {}
-        for wn in ("tiny", "small"):
-            ws = WORKLOADS[wn]
-            cs = cached_counts(ws)
+        pool = OraclePool(lambda b0, b1: counts[b0:b1].cpu().numpy().view(np.uint32), shape=(w.n_bf, n, n))
+        stage_s = time.perf_counter() - t1
+        try:
+            log(f"[bench] oracle: whole {w.name} evaluation on {pool.workers} worker processes ...")
             t1 = time.perf_counter()
-            O.loss(O.OGeom.from_any(ws.geometry), cs, ws.true_params)
-            whole[wn] = {"s": time.perf_counter() - t1, "samples": ws.n_bf * ws.geometry.scan_n ** 2}
-        cpu["whole_evaluations"] = whole
-        s1 = torch.empty((n, n), dtype=torch.float64, device=dev)
-        s2 = ssb.ssb_moments(h, params[0], b0, b1, s1)
-        s1 = s1.cpu().numpy()
-        oracle_check = {"bf_range": [b0, b1], "s2_rel_err": abs(s2 - r2) / abs(r2),
-                        "s1_max_abs_err": float(np.max(np.abs(s1 - r1)))}
-        log(f"[bench] oracle {cpu_s:.1f} s; S2 rel err {oracle_check['s2_rel_err']:.2e}")
+            r1, r2 = pool.moments(og, params[0], dc)
+            eval_s = time.perf_counter() - t1
+            ref_loss = O.loss_from_moments(r1, r2, w.n_bf)
+            t1 = time.perf_counter()
+            ref_phase, _ = pool.object_wave(og, params[0], dc)
+            obj_s = time.perf_counter() - t1
+        finally:
+            pool.close()
+        whole = {}
+        for wn in ("tiny", "small", "medium"):
+            if wn == w.name:
+                continue
+            ws = WORKLOADS[wn]
+            if ws.geometry.scan_n >= 256:
+                cs = make_counts_torch(ws, dev).cpu().numpy().view(np.uint32)
+            else:
+                cs = cached_counts(ws)
+            with OraclePool(cs) as pw:
+                t1 = time.perf_counter()
+                pw.loss(O.OGeom.from_any(ws.geometry), ws.true_params, O.dc_value(cs))
+                whole[wn] = {"s": time.perf_counter() - t1, "samples": ws.n_bf * ws.geometry.scan_n ** 2,
+                             "workers": pw.workers}
+            del cs
+        cpu = {"value": samples / eval_s, "unit": "BF×scan samples/s", "cores": pool.workers, "kind": "oracle",
+               "sample": f"one whole {w.name} evaluation ({w.n_bf} BF x {n}^2 scan, every BF pixel) of the float64 "
+                         f"oracle at the true aberrations: {eval_s:.1f} s on {pool.workers} worker processes "
+                         f"(BF ranges, one NumPy thread each); the object over every BF pixel took {obj_s:.1f} s",
+               "eval_s": eval_s, "ms_per_eval": eval_s * 1e3, "object_s": obj_s, "staging_s": stage_s,
+               "host_cores_available": len(os.sched_getaffinity(0)), "whole_evaluations": whole}
+        d = np.angle(np.exp(1j * (gpu_phase.cpu().numpy() - ref_phase)))
+        dm = mp.cpu().numpy() - r1 / w.n_bf
+        oracle_check = {"bf_range": [0, w.n_bf], "loss_gpu": gpu_loss, "loss_oracle": ref_loss,
+                        "loss_rel_err": abs(gpu_loss - ref_loss) / abs(ref_loss),
+                        "mean_phase_max_abs_err": float(np.max(np.abs(dm))),
+                        "object_phase_rms_rad": float(np.sqrt(np.mean(d * d)))}
+        log(f"[bench] oracle whole evaluation {eval_s:.1f} s, object {obj_s:.1f} s; loss rel err "
+            f"{oracle_check['loss_rel_err']:.2e}, object rms {oracle_check['object_phase_rms_rad']:.2e} rad")
+        del gpu_phase, mp
 
     ssb.ssb_release(h)
     del counts

@@ -53,7 +53,14 @@ enum {
     SSB_EDEVICE = -4   /* a HIP runtime error; the message carries hipGetErrorString */
 };
 
-/* Workload geometry.  Lengths are in detector pixels unless stated otherwise. */
+/* Workload geometry.  Lengths are in detector pixels unless stated otherwise.
+ * The scan sampling enters as q_step_px, the detector pixels one scan-frequency
+ * index spans, 1/(N * scan step * dk); a caller holding the scan step in Angstrom
+ * forms it.  Passing the ratio itself keeps q on an exact lattice when it is dyadic
+ * (e.g. D/N), so every support and flat-top decision of the correction is exact and
+ * reproducible; deriving it from a step in Angstrom would round it and turn the
+ * lattice's exact ties with the aperture edge into near ties.  bf_r2 is a double
+ * because the probe-disk fit (ssb_fit_probe) gives a non-integer radius squared. */
 typedef struct ssb_geometry {
     int32_t scan_n;        /* N: scan side, a power of two in [32, 1024] */
     int32_t det_n;         /* D: detector side, > 0 */
@@ -81,6 +88,9 @@ typedef struct ssb_info {
     int64_t columns_read;    /* column results the row pass reads per trial, all BF (zero columns skipped) */
     int32_t variant;         /* SSB_VARIANT_HALF_PLANE or SSB_VARIANT_FULL_PLANE (ssb_set_variant) */
     int32_t pad;
+    int64_t workspace_bytes; /* device workspace the handle holds (loss + object) */
+    int32_t reserved_trials; /* loss calls with at most this many trials allocate nothing (ssb_reserve) */
+    int32_t pad2;
 } ssb_info;
 
 typedef struct ssb_handle ssb_handle;
@@ -105,18 +115,37 @@ int ssb_prepare(const ssb_geometry* g, const uint32_t* counts, int64_t n_bf,
                 void* stream, ssb_handle** out);
 
 /*
- * ssb_loss: phase-variance loss for n_trials aberration sets.
+ * ssb_loss: phase-variance loss for n_trials aberration sets.  One exact
+ * evaluation covers every BF pixel and every scan pixel (Checkpoints page,
+ * "2026-09-11 full-aperture Apple M5 floor checkpoint": all 8,937 BF terms of the
+ * 512 x 512 scan, no crop or BF reduction), reduced from the phase-sum image and
+ * the squared-phase partials (Notes page, "Standard-only CUDA native 512
+ * calibration"); candidates of a batch share the spectrum fetch and keep their own
+ * correction, transforms and loss (Notes page, "MPS fused candidate-pair
+ * checkpoint").
  *   params      HOST float [n_trials][3] = {C10 nm, C12 nm, phi12 rad}; each value
- *               is taken as given in float32 (the evaluation's exact input).
+ *               is taken as given in float32 (the evaluation's exact input; Notes
+ *               page, "MPS wider exact-simplex checkpoint").
  *   losses      HOST double [n_trials], written on success.
  *   mean_phase  optional DEVICE float [N][N] receiving S1/n_bf of trial 0, or NULL.
  * Each trial's loss is bitwise independent of n_trials, of its position in the
  * batch and of the chunk size.  Synchronizes the stream before returning.
- * Errors: SSB_EINVAL (null handle/params/losses, n_trials < 1, non-finite
- * parameter), SSB_ENOMEM, SSB_EDEVICE.
+ * Allocates nothing when n_trials <= the reserved trial count (1 after
+ * ssb_prepare; see ssb_reserve); a larger batch grows the handle's workspace once.
+ * Errors: SSB_EINVAL (null handle/params/losses, n_trials outside [1, 65535],
+ * non-finite parameter), SSB_ENOMEM, SSB_EDEVICE.
  */
 int ssb_loss(ssb_handle* h, const float* params, int32_t n_trials, double* losses,
              float* mean_phase, void* stream);
+
+/*
+ * ssb_reserve: size the handle's device workspace and host staging for loss calls
+ * of up to max_trials trials (any BF range, either variant, any chunk cap), so
+ * that such calls, and ssb_moments and ssb_object, allocate nothing afterwards.
+ * ssb_prepare reserves one trial.  Reservations only grow.  Errors: SSB_EINVAL
+ * (bad handle, max_trials outside [1, 65535]), SSB_ENOMEM, SSB_EDEVICE.
+ */
+int ssb_reserve(ssb_handle* h, int32_t max_trials);
 
 /*
  * ssb_moments: phase moments of one trial over the BF range [bf_begin, bf_end)
@@ -138,7 +167,8 @@ int ssb_moments(ssb_handle* h, const float* params3, int64_t bf_begin, int64_t b
  *   params3  HOST float[3].
  *   phase    DEVICE float [N][N].
  *   psi      optional DEVICE complex64 [N][N] (interleaved re, im) or NULL.
- * Asynchronous on the stream.  Errors: SSB_EINVAL, SSB_ENOMEM, SSB_EDEVICE.
+ * Asynchronous on the stream; allocates nothing (its workspace is reserved by
+ * ssb_prepare).  Errors: SSB_EINVAL, SSB_EDEVICE.
  */
 int ssb_object(ssb_handle* h, const float* params3, float* phase, float* psi, void* stream);
 

@@ -267,19 +267,32 @@ def mean_phase(g, counts, params3, dc=None):
 
 
 # ---------------------------------------------------------------- O13
-def object_wave(g, counts: np.ndarray, params3, dc: float | None = None):
-    """Phase-of-mean object: psi = ifft2(extension of mean_b C_b); returns (phase, psi)."""
+def corrected_sum(g, counts: np.ndarray, params3, dc: float, bf_list=None) -> np.ndarray:
+    """Sum of the corrected half planes C_b over the listed BF pixels, in increasing BF
+    order (counts[k] holds BF bf_list[k], or every BF in order when bf_list is None)."""
     g = OGeom.from_any(g)
-    if dc is None:
-        dc = dc_value(counts)
     kx_all, ky_all = bf_kvectors(g)
+    if bf_list is None:
+        bf_list = np.arange(kx_all.size)
     qx, qy = q_vectors(g)
     acc = np.zeros((g.scan_n, g.scan_n // 2 + 1), dtype=np.complex128)
-    for b in range(counts.shape[0]):
+    for k, b in enumerate(bf_list):
         t = transfer(g, params3, kx_all[b], ky_all[b], qx, qy)
-        acc += corrected_spectrum(scan_spectrum(counts[b]), t, dc)
-    psi = bf_object(full_plane(acc / counts.shape[0]))
+        acc += corrected_spectrum(scan_spectrum(counts[k]), t, dc)
+    return acc
+
+
+def object_from_sum(acc: np.ndarray, n_bf: int):
+    """Phase-of-mean object from the BF sum of corrected half planes: (phase, psi)."""
+    psi = bf_object(full_plane(acc / n_bf))
     return bf_phase(psi), psi
+
+
+def object_wave(g, counts: np.ndarray, params3, dc: float | None = None):
+    """Phase-of-mean object: psi = ifft2(extension of mean_b C_b); returns (phase, psi)."""
+    if dc is None:
+        dc = dc_value(counts)
+    return object_from_sum(corrected_sum(g, counts, params3, dc), counts.shape[0])
 
 
 # ---------------------------------------------------------------- full-plane variant

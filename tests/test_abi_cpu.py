@@ -107,3 +107,23 @@ def test_null_handle_calls():
     assert lib.ssb_prepare(None, None, 1, None, None) == ssb._ssb.SSB_EINVAL
     lib.ssb_release(None)          # no-op
     assert lib.ssb_last_error() is not None
+
+
+def test_binding_checks_tensors_before_the_call():
+    """Wrong dtype, element count, layout or device is a ValueError raised by the binding
+    before any library call (no GPU needed: CPU tensors fail the device check last)."""
+    import torch
+    g = _geom()
+    with pytest.raises(ValueError, match="dtype"):
+        ssb.ssb_prepare(g, torch.zeros((49, 32, 32), dtype=torch.float32), 49)
+    with pytest.raises(ValueError, match="elements"):
+        ssb.ssb_prepare(g, torch.zeros((48, 32, 32), dtype=torch.int32), 49)
+    with pytest.raises(ValueError, match="contiguous"):
+        ssb.ssb_prepare(g, torch.zeros((49, 32, 32), dtype=torch.int32).transpose(1, 2), 49)
+    with pytest.raises(ValueError, match="GPU"):
+        ssb.ssb_prepare(g, torch.zeros((49, 32, 32), dtype=torch.int32), 49)
+    with pytest.raises(ValueError, match="dtype"):
+        ssb.ssb_detector_sum(0x1000, 2, 2, torch.zeros(4, dtype=torch.float64))
+    with pytest.raises(ValueError, match="elements"):
+        ssb.ssb_gather_bf(0x1000, g, torch.zeros((49, 32, 31), dtype=torch.int32),
+                          49)

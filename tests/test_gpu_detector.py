@@ -31,7 +31,7 @@ def _dev_u32(t, arr):
 
 
 def _sums(t, frames_dev, n, d):
-    s = t.empty(d * d, dtype=t.int64, device="cuda")
+    s = t.full((d * d,), -1, dtype=t.int64, device="cuda")
     ssb.ssb_detector_sum(frames_dev, n, d, s)
     t.cuda.synchronize()
     return s.cpu().numpy().view(np.uint64)
@@ -73,7 +73,7 @@ def test_gather_exact(small_frames):
     geom = dataclasses.replace(g, det_cy=fit["cy"], det_cx=fit["cx"], bf_r2=fit["bf_r2"])
     bi, bj = OD.bf_pixels(sums.reshape(g.det_n, g.det_n), fit["cy"], fit["cx"], fit["bf_r2"])
     ref = OD.gather_bf(frames, g.scan_n, g.det_n, bi, bj)
-    out = t.empty((bi.size, g.scan_n, g.scan_n), dtype=t.int32, device="cuda")
+    out = t.full((bi.size, g.scan_n, g.scan_n), -1, dtype=t.int32, device="cuda")
     ssb.ssb_gather_bf(_dev_u32(t, frames), geom, out, bi.size)
     np.testing.assert_array_equal(out.cpu().numpy().view(np.uint32), ref)
     with pytest.raises(ssb.SSBError) as e:
@@ -93,7 +93,7 @@ def test_automatic_bf_chain(small_frames):
     fit = ssb.ssb_fit_probe(sums, g.scan_n, g.det_n)
     assert fit["n_zero"] == 0
     geom = dataclasses.replace(g, det_cy=fit["det_cy"], det_cx=fit["det_cx"], bf_r2=fit["bf_r2"])
-    counts = t.empty((fit["n_bf"], g.scan_n, g.scan_n), dtype=t.int32, device="cuda")
+    counts = t.full((fit["n_bf"], g.scan_n, g.scan_n), -1, dtype=t.int32, device="cuda")
     ssb.ssb_gather_bf(fdev, geom, counts, fit["n_bf"])
     h = ssb.ssb_prepare(geom, counts, fit["n_bf"])
     try:
@@ -112,7 +112,7 @@ def test_automatic_bf_chain(small_frames):
 
 def test_detector_errors():
     t = _torch()
-    s = t.empty(64, dtype=t.int64, device="cuda")
+    s = t.full((64,), -1, dtype=t.int64, device="cuda")
     host = np.zeros((16, 64), dtype=np.uint32)
     with pytest.raises(ssb.SSBError) as e:
         ssb.ssb_detector_sum(host.ctypes.data, 4, 8, s)

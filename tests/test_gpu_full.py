@@ -1,13 +1,16 @@
 """GPU parity at the full and medium workload sizes, in the launch configuration the
 benchmark times (N = 512, 8,937 BF, default chunking).
 
-The float64 oracle cannot evaluate all 8,937 BF pixels of a 512^2 scan within a
-test's time, so at full size it checks sampled outputs one by one (cached spectra
-of single BF pixels, phase moments of BF ranges including the ragged last group)
-and properties that hold at any size (the loss equals the formula applied to the
-moments of the whole range; moments are additive over a split of the range).  A
-complete N = 512 loss and object check runs on a 317-BF sub-disk of the same counts.
+The complete loss over all 8,937 BF pixels of the 512^2 scan, the mean phase and
+the phase-of-mean object are compared with the float64 oracle run over BF ranges
+in a process pool on the host's cores (the measurement the Checkpoints page's
+"2026-09-11 full-aperture Apple M5 floor checkpoint" insists on: no crop and no BF
+reduction).  Sampled outputs are also checked one by one (cached spectra of single
+BF pixels, phase moments of BF ranges including the ragged last group), with
+properties that hold at any size (the loss equals the formula applied to the
+moments of the whole range; moments are additive over a split of the range).
 Counts come from the seeded device generator; the oracle gets the same bytes.
+Every device output starts as NaN, so a region the library leaves unwritten fails.
 """
 import dataclasses
 import sys
@@ -17,7 +20,8 @@ import pytest
 
 import aberration_phase_variance_amd as ssb
 from oracle import ssb_oracle as O
-from synth import WORKLOADS, make_counts_torch
+from oracle.pool import OraclePool
+from synth import WORKLOADS, make_counts_torch, trial_params
 
 pytestmark = pytest.mark.gpu
 
@@ -50,9 +54,64 @@ def _host(counts, b0, b1):
     return counts[b0:b1].cpu().numpy().view(np.uint32)
 
 
+@pytest.fixture(scope="module")
+def full_pool(full):
+    """The pooled float64 oracle over the full workload's counts (same bytes as the device's)."""
+    w, counts, h = full
+    _say("[full] staging counts for the pooled oracle")
+    with OraclePool(lambda b0, b1: _host(counts, b0, b1), shape=(w.n_bf, 512, 512)) as pool:
+        _say(f"[full] oracle pool of {pool.workers} workers")
+        yield pool
+
+
+def test_full_loss_all_bf(full, full_pool):
+    """The complete exact loss at full size (all 8,937 BF) for the true aberrations and two
+    seeded trials of the full fit's batch, in one batched call, within 1e-5 relative of the
+    oracle; the mean phase of trial 0 within float rounding of the oracle's S1 / n_bf."""
+    import torch
+    w, counts, h = full
+    og = O.OGeom.from_any(w.geometry)
+    dc = ssb.ssb_query(h)["dc"]
+    trials = np.concatenate([np.array([TRUE], np.float32), trial_params(w, 2)])
+    mp = torch.full((512, 512), float("nan"), dtype=torch.float32, device="cuda")
+    got = ssb.ssb_loss(h, trials, mp)
+    mean_phase = mp.cpu().numpy()
+    for k in range(len(trials)):
+        _say(f"[full] oracle over all {w.n_bf} BF, trial {k} {trials[k].tolist()}")
+        s1, s2 = full_pool.moments(og, trials[k], dc)
+        ref = O.loss_from_moments(s1, s2, w.n_bf)
+        _say(f"[full]   gpu {got[k]!r} oracle {ref!r} rel {abs(got[k] - ref) / abs(ref):.2e}")
+        assert abs(got[k] - ref) <= LOSS_RTOL * abs(ref), (k, got[k], ref)
+        if k == 0:
+            d = mean_phase - s1 / w.n_bf
+            assert np.all(np.isfinite(mean_phase))
+            assert np.sqrt(np.mean(d * d)) <= 1e-6 and np.max(np.abs(d)) <= 1e-5
+
+
+def test_full_object_all_bf(full, full_pool):
+    """The phase-of-mean object over all 8,937 BF pixels within 1e-4 rad RMS of the oracle."""
+    import torch
+    w, counts, h = full
+    og = O.OGeom.from_any(w.geometry)
+    dc = ssb.ssb_query(h)["dc"]
+    for params in (TRUE, trial_params(w, 1)[0].tolist()):
+        phase = torch.full((512, 512), float("nan"), dtype=torch.float32, device="cuda")
+        psi = torch.full((512, 512, 2), float("nan"), dtype=torch.float32, device="cuda")
+        ssb.ssb_object(h, params, phase, psi)
+        torch.cuda.synchronize()
+        _say(f"[full] oracle object over all {w.n_bf} BF at {params}")
+        ref_phase, ref_psi = full_pool.object_wave(og, params, dc)
+        d = np.angle(np.exp(1j * (phase.cpu().numpy() - ref_phase)))
+        rms = float(np.sqrt(np.mean(d * d)))
+        p = psi.cpu().numpy()
+        rel = np.linalg.norm(p[..., 0] + 1j * p[..., 1] - ref_psi) / np.linalg.norm(ref_psi)
+        _say(f"[full]   object rms {rms:.2e} rad, psi rel L2 {rel:.2e}")
+        assert rms <= PHASE_RMS and rel <= 1e-5
+
+
 def _moments(h, n, params, b0, b1):
     import torch
-    s1 = torch.empty((n, n), dtype=torch.float64, device="cuda")
+    s1 = torch.full((n, n), float("nan"), dtype=torch.float64, device="cuda")
     s2 = ssb.ssb_moments(h, params, b0, b1, s1)
     return s1.cpu().numpy(), s2
 
@@ -73,7 +132,7 @@ def test_full_spectra_sampled(full):
     w, counts, h = full
     for b in (0, 4468, 8936):
         ref = O.scan_spectrum(_host(counts, b, b + 1)[0])
-        out = torch.empty((512, 257, 2), dtype=torch.float32, device="cuda")
+        out = torch.full((512, 257, 2), float("nan"), dtype=torch.float32, device="cuda")
         ssb.ssb_spectrum(h, b, out)
         o = out.cpu().numpy()
         got = o[..., 0] + 1j * o[..., 1]
@@ -141,7 +200,7 @@ def test_n512_subdisk_loss_and_object(subdisk):
         got = ssb.ssb_loss(hs, [params])[0]
         ref = O.loss(og, counts, params, dc)
         assert abs(got - ref) <= LOSS_RTOL * abs(ref), (params, got, ref)
-    phase = torch.empty((512, 512), dtype=torch.float32, device="cuda")
+    phase = torch.full((512, 512), float("nan"), dtype=torch.float32, device="cuda")
     ssb.ssb_object(hs, TRUE, phase)
     torch.cuda.synchronize()
     ref_phase, _ = O.object_wave(og, counts, TRUE, dc)
@@ -150,6 +209,8 @@ def test_n512_subdisk_loss_and_object(subdisk):
 
 
 def test_medium_loss_and_object():
+    """Medium workload: eight seeded trials of its batch in one call against the pooled
+    oracle, single-trial calls equal to the batch bitwise, and the object."""
     import torch
     w = WORKLOADS["medium"]
     counts = make_counts_torch(w, torch.device("cuda:0"))
@@ -158,10 +219,16 @@ def test_medium_loss_and_object():
         host = counts.cpu().numpy().view(np.uint32)
         og = O.OGeom.from_any(w.geometry)
         dc = O.dc_value(host)
-        got = ssb.ssb_loss(h, [TRUE])[0]
-        ref = O.loss(og, host, TRUE, dc)
-        assert abs(got - ref) <= LOSS_RTOL * abs(ref), (got, ref)
-        phase = torch.empty((256, 256), dtype=torch.float32, device="cuda")
+        trials = np.concatenate([np.array([TRUE], np.float32), trial_params(w, 7)])
+        got = ssb.ssb_loss(h, trials)
+        _say("[medium] pooled oracle, 8 trials")
+        with OraclePool(host) as pool:
+            for k in range(len(trials)):
+                ref = pool.loss(og, trials[k], dc)
+                assert abs(got[k] - ref) <= LOSS_RTOL * abs(ref), (k, got[k], ref)
+        for k in (0, 5):
+            assert ssb.ssb_loss(h, trials[k:k + 1])[0] == got[k]
+        phase = torch.full((256, 256), float("nan"), dtype=torch.float32, device="cuda")
         ssb.ssb_object(h, TRUE, phase)
         torch.cuda.synchronize()
         ref_phase, _ = O.object_wave(og, host, TRUE, dc)

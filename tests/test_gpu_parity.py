@@ -51,8 +51,8 @@ class Prepared:
 
     def obj(self, params, with_psi=True):
         t = self.torch
-        phase = t.empty((self.n, self.n), dtype=t.float32, device="cuda")
-        psi = t.empty((self.n, self.n, 2), dtype=t.float32, device="cuda") if with_psi else None
+        phase = t.full((self.n, self.n), float("nan"), dtype=t.float32, device="cuda")
+        psi = t.full((self.n, self.n, 2), float("nan"), dtype=t.float32, device="cuda") if with_psi else None
         ssb.ssb_object(self.h, params, phase, psi)
         t.cuda.synchronize()
         out_psi = None
@@ -63,13 +63,13 @@ class Prepared:
 
     def moments(self, params, b0, b1):
         t = self.torch
-        s1 = t.empty((self.n, self.n), dtype=t.float64, device="cuda")
+        s1 = t.full((self.n, self.n), float("nan"), dtype=t.float64, device="cuda")
         s2 = ssb.ssb_moments(self.h, params, b0, b1, s1)
         return s1.cpu().numpy(), s2
 
     def spectrum(self, b):
         t = self.torch
-        out = t.empty((self.n, self.n // 2 + 1, 2), dtype=t.float32, device="cuda")
+        out = t.full((self.n, self.n // 2 + 1, 2), float("nan"), dtype=t.float32, device="cuda")
         ssb.ssb_spectrum(self.h, b, out)
         t.cuda.synchronize()
         o = out.cpu().numpy()
@@ -213,7 +213,7 @@ def test_mean_phase_small(small):
     w, counts, p = small
     t = _torch()
     g = O.OGeom.from_any(w.geometry)
-    mp = t.empty((128, 128), dtype=t.float32, device="cuda")
+    mp = t.full((128, 128), float("nan"), dtype=t.float32, device="cuda")
     p.loss([[40.0, 5.0, 0.3]], mp)
     ref = O.mean_phase(g, counts, (40.0, 5.0, 0.3))
     d = mp.cpu().numpy() - ref
@@ -236,6 +236,38 @@ def test_batch_chunk_and_repeat_invariance(small):
     finally:
         ssb.ssb_set_chunk(p.h, 0)
     assert p.loss(a)[0] == single
+
+
+def test_reserved_batch_allocates_nothing(small):
+    """After ssb_reserve(64), loss calls of up to 64 trials, moments and the object leave the
+    handle's workspace as it was (no allocation in the call), and reserve only grows."""
+    w, counts, p = small
+    assert ssb.ssb_query(p.h)["reserved_trials"] >= 1
+    ssb.ssb_reserve(p.h, 64)
+    before = ssb.ssb_query(p.h)
+    assert before["reserved_trials"] == 64 and before["workspace_bytes"] > 0
+    full = p.loss(trial_params(w, 64))
+    part = p.loss(trial_params(w, 17))
+    assert np.array_equal(part, full[:17])
+    p.moments([40.0, 5.0, 0.3], 3, 100)
+    p.obj([40.0, 5.0, 0.3])
+    ssb.ssb_set_variant(p.h, ssb.SSB_VARIANT_FULL_PLANE)
+    try:
+        p.loss(trial_params(w, 64))
+        p.obj([40.0, 5.0, 0.3])
+    finally:
+        ssb.ssb_set_variant(p.h, ssb.SSB_VARIANT_HALF_PLANE)
+    ssb.ssb_set_chunk(p.h, 32)
+    try:
+        p.loss(trial_params(w, 64))
+    finally:
+        ssb.ssb_set_chunk(p.h, 0)
+    ssb.ssb_reserve(p.h, 8)                          # a smaller request keeps the larger reservation
+    after = ssb.ssb_query(p.h)
+    assert after["workspace_bytes"] == before["workspace_bytes"]
+    assert after["reserved_trials"] == 64
+    with pytest.raises(ssb.SSBError):
+        ssb.ssb_reserve(p.h, 0)
 
 
 def test_moments_range_small(small):
@@ -401,13 +433,22 @@ def test_error_paths_on_device(small):
     assert ei.value.code == ssb._ssb.SSB_EINVAL
     # the handle still works after the errors
     assert _rel(p.loss([[40.0, 5.0, 0.3]])[0], O.loss(O.OGeom.from_any(w.geometry), counts, (40.0, 5.0, 0.3))) <= LOSS_RTOL
-    s1 = t.empty((128, 128), dtype=t.float64, device="cuda")
+    s1 = t.full((128, 128), float("nan"), dtype=t.float64, device="cuda")
     for b0, b1 in ((-1, 5), (10, 10), (0, w.n_bf + 1)):
         with pytest.raises(ssb.SSBError) as ei:
             ssb.ssb_moments(p.h, [40.0, 5.0, 0.3], b0, b1, s1)
         assert ei.value.code == ssb._ssb.SSB_ESHAPE
-    with pytest.raises(ssb.SSBError):
-        ssb.ssb_spectrum(p.h, w.n_bf, s1)
+    spec = t.full((128, 65, 2), float("nan"), dtype=t.float32, device="cuda")
+    with pytest.raises(ssb.SSBError) as ei:
+        ssb.ssb_spectrum(p.h, w.n_bf, spec)
+    assert ei.value.code == ssb._ssb.SSB_ESHAPE
+    # the binding checks tensors before the call: dtype, size, contiguity
+    with pytest.raises(ValueError):
+        ssb.ssb_moments(p.h, [40.0, 5.0, 0.3], 0, 5, spec)
+    with pytest.raises(ValueError):
+        ssb.ssb_moments(p.h, [40.0, 5.0, 0.3], 0, 5, s1[:64])
+    with pytest.raises(ValueError):
+        ssb.ssb_object(p.h, [40.0, 5.0, 0.3], t.full((128, 128), 0.0, dtype=t.float32, device="cuda").t())
     dev = t.zeros((w.n_bf - 1, 128, 128), dtype=t.int32, device="cuda")
     with pytest.raises(ssb.SSBError) as ei:
         ssb.ssb_prepare(w.geometry, dev, w.n_bf - 1)

@@ -55,7 +55,7 @@ def _host(counts, b0, b1):
 
 def _moments(h, params, b0, b1):
     import torch
-    s1 = torch.empty((N, N), dtype=torch.float64, device="cuda")
+    s1 = torch.full((N, N), float("nan"), dtype=torch.float64, device="cuda")
     s2 = ssb.ssb_moments(h, params, b0, b1, s1)
     return s1.cpu().numpy(), s2
 
@@ -77,7 +77,7 @@ def test_1024_spectra_sampled(full1024):
     w, counts, h = full1024
     for b in (0, 4468, 8936):
         ref = O.scan_spectrum(_host(counts, b, b + 1)[0])
-        out = torch.empty((N, N // 2 + 1, 2), dtype=torch.float32, device="cuda")
+        out = torch.full((N, N // 2 + 1, 2), float("nan"), dtype=torch.float32, device="cuda")
         ssb.ssb_spectrum(h, b, out)
         o = out.cpu().numpy()
         got = o[..., 0] + 1j * o[..., 1]
@@ -144,7 +144,7 @@ def test_1024_subdisk_loss_and_object(subdisk1024):
         got = ssb.ssb_loss(hs, [params])[0]
         ref = O.loss(og, counts, params, dc)
         assert abs(got - ref) <= LOSS_RTOL * abs(ref), (params, got, ref)
-    phase = torch.empty((N, N), dtype=torch.float32, device="cuda")
+    phase = torch.full((N, N), float("nan"), dtype=torch.float32, device="cuda")
     ssb.ssb_object(hs, TRUE, phase)
     torch.cuda.synchronize()
     ref_phase, _ = O.object_wave(og, counts, TRUE, dc)
@@ -183,7 +183,7 @@ def test_1024_subdisk_full_plane_loss_and_object(subdisk1024):
     ssb.ssb_set_variant(hs, ssb.SSB_VARIANT_FULL_PLANE)
     try:
         got = ssb.ssb_loss(hs, [TRUE])[0]
-        phase = torch.empty((N, N), dtype=torch.float32, device="cuda")
+        phase = torch.full((N, N), float("nan"), dtype=torch.float32, device="cuda")
         ssb.ssb_object(hs, TRUE, phase)
         torch.cuda.synchronize()
     finally:
