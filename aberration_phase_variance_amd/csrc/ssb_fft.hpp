@@ -11,26 +11,15 @@
 
 #include <hip/hip_runtime.h>
 
+#include "ssb_math.hpp"
+
 namespace ssb {
 
-// (cos, sin) of 2 pi r for r in [-1/2, 1/2]: quadrant from rint(4 r), then
-// sin(pi f/2) = f S(f^2) and cos(pi f/2) = C(f^2) on f in [-1/2, 1/2] with
-// polynomials fitted here (iteratively reweighted least squares, 4 and 5 terms;
-// max error 1e-7 in float).
+// (cos, sin) of 2 pi r for r in [-1/2, 1/2] (ssb_math.hpp)
 __device__ __forceinline__ float2 cossin_rev(float r) {
-    const float x = 4.0f * r;
-    const float q = rintf(x);
-    const float f = x - q;
-    const float s2 = f * f;
-    const float sn = f * fmaf(fmaf(fmaf(-4.592288751e-03f, s2, 7.967590541e-02f), s2, -6.459629536e-01f), s2,
-                              1.570796251e+00f);
-    const float cs = fmaf(fmaf(fmaf(fmaf(9.036316769e-04f, s2, -2.086007223e-02f), s2, 2.536692023e-01f), s2,
-                               -1.233700514e+00f),
-                          s2, 1.0f);
-    const int qi = (int)q & 3;
-    const float sb = (qi & 1) ? cs : sn;
-    const float cb = (qi & 1) ? sn : cs;
-    return make_float2(((qi + 1) & 2) ? -cb : cb, (qi & 2) ? -sb : sb);
+    float c, s;
+    cossin_rev_cs(r, c, s);
+    return make_float2(c, s);
 }
 
 __device__ __forceinline__ float2 cadd(float2 a, float2 b) { return make_float2(a.x + b.x, a.y + b.y); }

@@ -31,9 +31,6 @@ namespace {
 #ifndef SSB_PASS1_THREADS
 #define SSB_PASS1_THREADS 256 // pass-1 workgroup size
 #endif
-#ifndef SSB_ATAN_TERMS
-#define SSB_ATAN_TERMS 8
-#endif
 #ifndef SSB_PASS1_MIN_WAVES
 #define SSB_PASS1_MIN_WAVES 5 // pass-1 register budget at N = 512: resident waves per SIMD
 #endif
@@ -161,51 +158,7 @@ __device__ __forceinline__ float2 chi_phasor(double qx, double qy, const TrialCo
     return make_float2(ph.x, -ph.y);
 }
 
-// atan2 in float: octant reduction to t = min/max in [0, 1], atan(t) = t P(t^2)
-// with a degree-8 polynomial in t^2 fitted here (iteratively reweighted least
-// squares on [0, 1] against atan; max relative error 1.4e-8 in exact arithmetic,
-// 3.3e-7 rad absolute in float including the approximate reciprocal), then the
-// octant is undone.  atan2(0, 0) = 0; NaN inputs give NaN.
-__device__ __forceinline__ float atan_unit(float t) {
-    const float s = t * t;
-#if SSB_ATAN_TERMS == 7
-    float p = 8.250554092e-03f;
-    p = fmaf(p, s, -3.822105378e-02f);
-    p = fmaf(p, s, 8.530547470e-02f);
-    p = fmaf(p, s, -1.356764287e-01f);
-    p = fmaf(p, s, 1.990287155e-01f);
-    p = fmaf(p, s, -3.332884312e-01f);
-#elif SSB_ATAN_TERMS == 8
-    float p = -4.910358693e-03f;
-    p = fmaf(p, s, 2.503707632e-02f);
-    p = fmaf(p, s, -6.061180681e-02f);
-    p = fmaf(p, s, 9.995578229e-02f);
-    p = fmaf(p, s, -1.405041218e-01f);
-    p = fmaf(p, s, 1.997561306e-01f);
-    p = fmaf(p, s, -3.333246410e-01f);
-#else
-    float p = 2.903556684e-03f;
-    p = fmaf(p, s, -1.628302597e-02f);
-    p = fmaf(p, s, 4.303940013e-02f);
-    p = fmaf(p, s, -7.533679157e-02f);
-    p = fmaf(p, s, 1.065467894e-01f);
-    p = fmaf(p, s, -1.420713365e-01f);
-    p = fmaf(p, s, 1.999305487e-01f);
-    p = fmaf(p, s, -3.333309293e-01f);
-#endif
-    p = fmaf(p, s, 1.0f);
-    return t * p;
-}
-__device__ __forceinline__ float atan2_f(float y, float x) {
-    const float ax = fabsf(x), ay = fabsf(y);
-    const float mx = fmaxf(ax, ay), mn = fminf(ax, ay);
-    const float t = mx > 0.f ? mn * __builtin_amdgcn_rcpf(mx) : 0.f;
-    float a = atan_unit(t);
-    a = ay > ax ? 1.57079632679489662f - a : a;
-    a = x < 0.f ? 3.14159265358979324f - a : a;
-    a = copysignf(a, y);
-    return (x != x || y != y) ? x + y : a;
-}
+// atan_unit and atan2_f: ssb_math.hpp
 
 // Plain column pass (spectrum builder, object): one workgroup = one plane x one
 // tile of kTC columns (or the Nyquist column).  Coalesced tile load into LDS, one
@@ -640,13 +593,11 @@ __device__ __forceinline__ void pass1_tile(const float2* __restrict__ gsrc, cons
         const float2 st = phasor_rev_neg((double)RS * beta);
         if constexpr (CL) {
             // every wave's copies have landed before any thread reads a slot another
-            // wave filled.  Vector memory operations complete in issue order and the
-            // PM spectrum loads (plus any spill traffic) were issued after the copies,
-            // so waiting until at most PM remain covers the copies and leaves the
-            // spectrum loads in flight; each entry then waits only for its own load
-            // (pass 1 2.96 -> 2.89 ms against a wait for everything here)
-            static_assert(PM == 16, "the wait count below is the number of spectrum loads");
-            asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+            // wave filled.  The compiler tracks the copies to the LDS as outstanding
+            // vector memory operations: before this barrier it waits only until the
+            // operations issued after them (the spectrum loads, any spill) are the
+            // only ones left, so the spectrum loads stay in flight and each entry
+            // waits for its own load (a CPU test checks this in the built assembly)
             __syncthreads();
         }
 #pragma unroll

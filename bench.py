@@ -81,7 +81,7 @@ def kernel_source_hash() -> str:
     import re
     csrc = os.path.join(ROOT, "aberration_phase_variance_amd", "csrc")
     hsh = hashlib.sha256()
-    for name in ("ssb_kernels.hip", "ssb_fft.hpp", "ssb_internal.hpp"):
+    for name in ("ssb_kernels.hip", "ssb_fft.hpp", "ssb_internal.hpp", "ssb_math.hpp"):
         with open(os.path.join(csrc, name)) as fh:
             text = re.sub(r"/\*.*?\*/", "", fh.read(), flags=re.S)
         for line in text.splitlines():
