@@ -113,7 +113,7 @@ class ssb_probe_fit(ctypes.Structure):
     ]
 
 
-EXPORTS = ("ssb_prepare", "ssb_reserve", "ssb_loss", "ssb_moments", "ssb_object", "ssb_spectrum", "ssb_set_chunk",
+EXPORTS = ("ssb_prepare", "ssb_reserve", "ssb_loss", "ssb_loss_noalloc", "ssb_moments", "ssb_object", "ssb_spectrum", "ssb_set_chunk",
            "ssb_profile", "ssb_query", "ssb_release", "ssb_last_error", "ssb_nelder_mead", "ssb_fit",
            "ssb_detector_sum", "ssb_fit_probe", "ssb_gather_bf", "ssb_set_variant")
 
@@ -133,6 +133,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ssb_prepare.argtypes = [ctypes.POINTER(ssb_geometry), vp, i64, vp, ctypes.POINTER(vp)]
     lib.ssb_reserve.argtypes = [vp, i32]
     lib.ssb_loss.argtypes = [vp, fp, i32, dp, vp, vp]
+    lib.ssb_loss_noalloc.argtypes = [vp, fp, i32, dp, vp, vp]
     lib.ssb_moments.argtypes = [vp, fp, i64, i64, vp, dp, vp]
     lib.ssb_object.argtypes = [vp, fp, vp, vp, vp]
     lib.ssb_spectrum.argtypes = [vp, i64, vp, vp]
@@ -252,6 +253,20 @@ def ssb_loss(handle: int, params, mean_phase=None, stream=None) -> np.ndarray:
         mp = _dev(mean_phase, "mean_phase", ("float32",), n * n)
     _check(lib.ssb_loss(handle, p.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), p.shape[0],
                         out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), mp, _stream(stream)))
+    return out
+
+
+def ssb_loss_noalloc(handle: int, params, mean_phase=None, stream=None) -> np.ndarray:
+    """ssb_loss with every per-call buffer in the library's fixed device scratch (no allocation)."""
+    lib = load_library()
+    p = _params(params)
+    out = np.empty(p.shape[0], dtype=np.float64)
+    mp = None
+    if mean_phase is not None:
+        n = _scan_n(handle)
+        mp = _dev(mean_phase, "mean_phase", ("float32",), n * n)
+    _check(lib.ssb_loss_noalloc(handle, p.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), p.shape[0],
+                                out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), mp, _stream(stream)))
     return out
 
 

@@ -97,6 +97,8 @@ struct ssb_handle {
     int reserved_trials = 0;
     // host staging of the per-trial constants (capacity = reserved trials)
     std::vector<TrialConst> htc;
+    // device address of the no-allocation scratch on this handle's device
+    char* scratch = nullptr;
     // host copy of the active flags, prefix counts for range queries
     std::vector<int64_t> active_prefix;
     // stage profiling
@@ -147,9 +149,9 @@ struct StageTimer {
     hipStream_t st;
     int64_t units;
     hipEvent_t a = nullptr, b = nullptr;
-    StageTimer(ssb_handle* h_, int stage_, hipStream_t st_, int64_t units_)
+    StageTimer(ssb_handle* h_, int stage_, hipStream_t st_, int64_t units_, bool allowed = true)
         : h(h_), stage(stage_), st(st_), units(units_) {
-        if (!h->prof_on) return;
+        if (!h->prof_on || !allowed) return;
         a = prof_event(h);
         b = prof_event(h);
         if (a && b) (void)hipEventRecord(a, st);
@@ -310,42 +312,49 @@ int reserve(ssb_handle* h, int max_trials) {
 }
 
 // Phase moments of n_trials trials over BF [b_begin, b_end): leaves S1 (double
-// [t][N][N]) and S2 (double [t]) in the workspace.
-// The host copy of the trial constants is staged in the handle (h->htc); it must
-// outlive the stream's use of it (the caller synchronizes before returning).
-int run_moments(ssb_handle* h, const float* params, int n_trials, int64_t b_begin, int64_t b_end,
-                hipStream_t st, LossPlan* out_plan) {
+// [t][N][N]) and S2 (double [t]) in the workspace ws laid out by pl.
+// staged: the trial constants go through a host copy in the handle (h->htc), which
+// must outlive the stream's use of it (the caller synchronizes before returning);
+// otherwise they are passed to a small kernel by value (no host buffer, nothing
+// allocated, no stage timers).
+int run_moments(ssb_handle* h, char* ws, const LossPlan& pl, const float* params, int n_trials, int64_t b_begin,
+                int64_t b_end, hipStream_t st, bool staged) {
     std::vector<TrialConst>& htc = h->htc;
-    const int64_t nb = b_end - b_begin;
-    LossPlan pl = plan_loss(h, nb, n_trials);
-    int rc = ensure(&h->ws, &h->ws_bytes, pl.total, "workspace allocation");
-    if (rc) return rc;
-    float2* im = reinterpret_cast<float2*>(h->ws + pl.off_im);
-    float2* in = reinterpret_cast<float2*>(h->ws + pl.off_in);
-    float* ps1 = reinterpret_cast<float*>(h->ws + pl.off_ps1);
-    double* ps2 = reinterpret_cast<double*>(h->ws + pl.off_ps2);
-    double* s1 = reinterpret_cast<double*>(h->ws + pl.off_s1);
-    double* s2 = reinterpret_cast<double*>(h->ws + pl.off_s2);
-    TrialConst* tc = reinterpret_cast<TrialConst*>(h->ws + pl.off_tc);
-    float2* chm = reinterpret_cast<float2*>(h->ws + pl.off_chm);
-    float2* chn = reinterpret_cast<float2*>(h->ws + pl.off_chn);
+    float2* im = reinterpret_cast<float2*>(ws + pl.off_im);
+    float2* in = reinterpret_cast<float2*>(ws + pl.off_in);
+    float* ps1 = reinterpret_cast<float*>(ws + pl.off_ps1);
+    double* ps2 = reinterpret_cast<double*>(ws + pl.off_ps2);
+    double* s1 = reinterpret_cast<double*>(ws + pl.off_s1);
+    double* s2 = reinterpret_cast<double*>(ws + pl.off_s2);
+    TrialConst* tc = reinterpret_cast<TrialConst*>(ws + pl.off_tc);
+    float2* chm = reinterpret_cast<float2*>(ws + pl.off_chm);
+    float2* chn = reinterpret_cast<float2*>(ws + pl.off_chn);
     const bool fp = h->variant == SSB_VARIANT_FULL_PLANE;
-    float2* nyq_a = fp ? reinterpret_cast<float2*>(h->ws + pl.off_na) : nullptr;
-    float2* nyq_b = fp ? reinterpret_cast<float2*>(h->ws + pl.off_nb) : nullptr;
+    float2* nyq_a = fp ? reinterpret_cast<float2*>(ws + pl.off_na) : nullptr;
+    float2* nyq_b = fp ? reinterpret_cast<float2*>(ws + pl.off_nb) : nullptr;
 
-    if ((size_t)n_trials > htc.capacity()) {      // beyond the reservation: the one host allocation
-        try {
-            htc.reserve((size_t)n_trials);
-        } catch (...) {
-            return fail(SSB_ENOMEM, "host staging of %d trial constants", n_trials);
+    if (staged) {
+        if ((size_t)n_trials > htc.capacity()) {      // beyond the reservation: the one host allocation
+            try {
+                htc.reserve((size_t)n_trials);
+            } catch (...) {
+                return fail(SSB_ENOMEM, "host staging of %d trial constants", n_trials);
+            }
+        }
+        htc.resize(n_trials);
+        for (int t = 0; t < n_trials; ++t) htc[t] = trial_const(h, params + 3 * t);
+        SSB_HIP(hipMemcpyAsync(tc, htc.data(), sizeof(TrialConst) * n_trials, hipMemcpyHostToDevice, st),
+                "copy trial constants");
+    } else {
+        for (int t0 = 0; t0 < n_trials; t0 += kTrialBlock) {
+            TrialBlock blk;
+            const int cnt = std::min(kTrialBlock, n_trials - t0);
+            for (int k = 0; k < cnt; ++k) blk.t[k] = trial_const(h, params + 3 * (t0 + k));
+            SSB_HIP(launch_set_trials(blk, cnt, tc + t0, st), "trial constants");
         }
     }
-    htc.resize(n_trials);
-    for (int t = 0; t < n_trials; ++t) htc[t] = trial_const(h, params + 3 * t);
-    SSB_HIP(hipMemcpyAsync(tc, htc.data(), sizeof(TrialConst) * n_trials, hipMemcpyHostToDevice, st),
-            "copy trial constants");
     {
-        StageTimer tm(h, SSB_STAGE_REDUCE, st, 0);
+        StageTimer tm(h, SSB_STAGE_REDUCE, st, 0, staged);
         SSB_HIP(launch_fill(s1, (int64_t)n_trials * h->n * h->n, st), "clear S1");
         SSB_HIP(launch_fill(s2, n_trials, st), "clear S2");
         SSB_HIP(launch_chiq(h->n, tc, n_trials, h->geo, chm, chn, st), "phase table launch");
@@ -356,7 +365,7 @@ int run_moments(ssb_handle* h, const float* params, int n_trials, int64_t b_begi
         const int ng = (cb + kGroupBF - 1) / kGroupBF;
         const int64_t units = active_in(h, c0, c0 + cb) * n_trials;
         {
-            StageTimer tm(h, SSB_STAGE_PASS1, st, units);
+            StageTimer tm(h, SSB_STAGE_PASS1, st, units, staged);
             SSB_HIP(launch_pass1(h->n, h->gm, h->gn, chm, chn, h->kb, h->sup, h->vend, tc, n_trials, h->geo, c0, cb,
                                  pl.cap, im, in, st),
                     "pass 1 launch");
@@ -366,17 +375,38 @@ int run_moments(ssb_handle* h, const float* params, int n_trials, int64_t b_begi
                         "Nyquist-line launch");
         }
         {
-            StageTimer tm(h, SSB_STAGE_PASS2, st, units);
+            StageTimer tm(h, SSB_STAGE_PASS2, st, units, staged);
             SSB_HIP(launch_pass2(h->n, im, in, pl.cap, h->active, h->vend, c0, cb, n_trials, h->dc, ps1, ps2,
                                  pl.gcap, h->tw, nyq_a, nyq_b, st),
                     "pass 2 launch");
         }
         {
-            StageTimer tm(h, SSB_STAGE_REDUCE, st, 0);
+            StageTimer tm(h, SSB_STAGE_REDUCE, st, 0, staged);
             SSB_HIP(launch_accum(h->n, ps1, ps2, pl.gcap, ng, n_trials, s1, s2, st), "accumulate launch");
         }
     }
-    if (out_plan) *out_plan = pl;
+    return SSB_OK;
+}
+
+// The loss of n_trials trials over every BF pixel in the workspace ws (layout pl),
+// copied to the host array losses; synchronizes the stream.
+int run_loss(ssb_handle* h, char* ws, const LossPlan& pl, const float* params, int n_trials, double* losses,
+             float* mean_phase, hipStream_t st, bool staged) {
+    int rc = run_moments(h, ws, pl, params, n_trials, 0, h->n_bf, st, staged);
+    if (rc) {
+        (void)hipStreamSynchronize(st);
+        return rc;
+    }
+    double* s1 = reinterpret_cast<double*>(ws + pl.off_s1);
+    double* s2 = reinterpret_cast<double*>(ws + pl.off_s2);
+    double* dl = reinterpret_cast<double*>(ws + pl.off_loss);
+    double* lp = reinterpret_cast<double*>(ws + pl.off_lpart);
+    {
+        StageTimer tm(h, SSB_STAGE_REDUCE, st, 0, staged);
+        SSB_HIP(launch_loss(h->n, s1, s2, n_trials, (double)h->n_bf, lp, dl, mean_phase, st), "loss launch");
+    }
+    SSB_HIP(hipMemcpyAsync(losses, dl, sizeof(double) * n_trials, hipMemcpyDeviceToHost, st), "copy losses");
+    SSB_HIP(hipStreamSynchronize(st), "loss");
     return SSB_OK;
 }
 
@@ -534,6 +564,10 @@ int ssb_prepare(const ssb_geometry* g, const uint32_t* counts, int64_t n_bf, voi
     // single-trial loss and object workspaces now, so that those calls allocate nothing
     int rc = reserve(h, 1);
     if (rc) return cleanup(rc);
+    // the no-allocation scratch's address on this device (looked up once per device)
+    void* sp = nullptr;
+    if ((e = scratch_address(&sp)) != hipSuccess) return cleanup(hip_fail(e, "no-allocation scratch address"));
+    h->scratch = static_cast<char*>(sp);
     *out = h;
     return SSB_OK;
 }
@@ -547,22 +581,38 @@ int ssb_loss(ssb_handle* h, const float* params, int32_t n_trials, double* losse
     if (n_trials < 1 || n_trials > 65535) return fail(SSB_EINVAL, "n_trials must be in [1, 65535]");
     if ((rc = check_params(params, n_trials))) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    LossPlan pl;
-    if ((rc = run_moments(h, params, n_trials, 0, h->n_bf, st, &pl))) {
-        (void)hipStreamSynchronize(st);
-        return rc;
+    const LossPlan pl = plan_loss(h, h->n_bf, n_trials);
+    if ((rc = ensure(&h->ws, &h->ws_bytes, pl.total, "workspace allocation"))) return rc;
+    return run_loss(h, h->ws, pl, params, n_trials, losses, mean_phase, st, true);
+}
+
+int ssb_loss_noalloc(ssb_handle* h, const float* params, int32_t n_trials, double* losses, float* mean_phase,
+                     void* stream) {
+    g_err.clear();
+    int rc = check_handle(h);
+    if (rc) return rc;
+    if (!params || !losses) return fail(SSB_EINVAL, "null params or losses");
+    if (n_trials < 1 || n_trials > 65535) return fail(SSB_EINVAL, "n_trials must be in [1, 65535]");
+    if ((rc = check_params(params, n_trials))) return rc;
+    if (!h->scratch) return fail(SSB_EDEVICE, "no-allocation scratch not found on this handle's device");
+    // the largest chunk (a multiple of the 32-BF group, under the handle's chunk cap)
+    // whose buffers fit the scratch; results do not depend on the chunk
+    const size_t room = scratch_bytes();
+    const int64_t groups = (h->n_bf + kGroupBF - 1) / kGroupBF;
+    int64_t lo = 1, hi = groups;
+    if (h->chunk_user > 0) hi = std::min<int64_t>(hi, (h->chunk_user + kGroupBF - 1) / kGroupBF);
+    if (plan_loss(h, h->n_bf, n_trials, h->variant, kGroupBF).total > room)
+        return fail(SSB_EINVAL,
+                    "%d trials need %zu bytes of scratch even with %d-BF chunks; the no-allocation scratch holds %zu",
+                    (int)n_trials, plan_loss(h, h->n_bf, n_trials, h->variant, kGroupBF).total, kGroupBF, room);
+    while (lo < hi) {
+        const int64_t mid = (lo + hi + 1) / 2;
+        if (plan_loss(h, h->n_bf, n_trials, h->variant, mid * kGroupBF).total <= room) lo = mid;
+        else hi = mid - 1;
     }
-    double* s1 = reinterpret_cast<double*>(h->ws + pl.off_s1);
-    double* s2 = reinterpret_cast<double*>(h->ws + pl.off_s2);
-    double* dl = reinterpret_cast<double*>(h->ws + pl.off_loss);
-    double* lp = reinterpret_cast<double*>(h->ws + pl.off_lpart);
-    {
-        StageTimer tm(h, SSB_STAGE_REDUCE, st, 0);
-        SSB_HIP(launch_loss(h->n, s1, s2, n_trials, (double)h->n_bf, lp, dl, mean_phase, st), "loss launch");
-    }
-    SSB_HIP(hipMemcpyAsync(losses, dl, sizeof(double) * n_trials, hipMemcpyDeviceToHost, st), "copy losses");
-    SSB_HIP(hipStreamSynchronize(st), "loss");
-    return SSB_OK;
+    const LossPlan pl = plan_loss(h, h->n_bf, n_trials, h->variant, lo * kGroupBF);
+    return run_loss(h, h->scratch, pl, params, n_trials, losses, mean_phase, static_cast<hipStream_t>(stream),
+                    false);
 }
 
 int ssb_moments(ssb_handle* h, const float* params3, int64_t bf_begin, int64_t bf_end, double* s1, double* s2,
@@ -576,8 +626,9 @@ int ssb_moments(ssb_handle* h, const float* params3, int64_t bf_begin, int64_t b
                     (long long)h->n_bf);
     if ((rc = check_params(params3, 1))) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    LossPlan pl;
-    if ((rc = run_moments(h, params3, 1, bf_begin, bf_end, st, &pl))) {
+    const LossPlan pl = plan_loss(h, bf_end - bf_begin, 1);
+    if ((rc = ensure(&h->ws, &h->ws_bytes, pl.total, "workspace allocation"))) return rc;
+    if ((rc = run_moments(h, h->ws, pl, params3, 1, bf_begin, bf_end, st, true))) {
         (void)hipStreamSynchronize(st);
         return rc;
     }

@@ -43,6 +43,20 @@ struct GeomDev {
     double hi2;       // (ra + w/2)^2
 };
 
+// Trial constants passed to the device by value (kernel arguments), kTrialBlock at a
+// time: no host staging buffer and no copy engine.
+constexpr int kTrialBlock = 16;
+struct TrialBlock {
+    TrialConst t[kTrialBlock];
+};
+hipError_t launch_set_trials(const TrialBlock& blk, int count, TrialConst* dev, hipStream_t st);
+
+// The no-allocation scratch (ssb_loss_noalloc): a file-scope device array of
+// scratch_bytes() bytes, one per device, kept until the process ends.  scratch_address
+// returns its device address on the current device (looked up once per device).
+size_t scratch_bytes();
+hipError_t scratch_address(void** out);
+
 // Launchers (defined in ssb_kernels.hip).  All return the hipError_t of the
 // launch; grids are chunked internally to keep every dimension in range.
 // FFT twiddle tables (inverse and forward sign, twiddle_count(n) entries each),

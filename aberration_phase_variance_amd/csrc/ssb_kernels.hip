@@ -22,8 +22,36 @@
 #include "ssb_fft.hpp"
 
 #include <algorithm>
+#include <mutex>
+
+// Scratch of the no-allocation loss entry point (for callers that cannot allocate):
+// every chunk buffer of one call lives here.  Each device holds its own copy from
+// the library's load until the process ends.  Host code must use the address
+// hipGetSymbolAddress returns on that device, never this name.
+static __device__ __align__(256) char scratch[(size_t)256 << 20];
 
 namespace ssb {
+
+size_t scratch_bytes() { return sizeof(scratch); }
+
+hipError_t scratch_address(void** out) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = p;
+    }
+    *out = addr[dev];
+    return hipSuccess;
+}
 
 namespace {
 
@@ -1045,6 +1073,11 @@ __global__ __launch_bounds__(256) void k_accum_s2(const double* __restrict__ par
     if (threadIdx.x == 0) s2run[t] = run;
 }
 
+__global__ __launch_bounds__(64) void k_set_trials(TrialBlock blk, int count, TrialConst* __restrict__ out) {
+    const int i = threadIdx.x;
+    if (i < count) out[i] = blk.t[i];
+}
+
 __global__ __launch_bounds__(256) void k_fill(double* p, int64_t count) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i < count) p[i] = 0.0;
@@ -1625,6 +1658,13 @@ hipError_t launch_accum(int n, const float* part_s1, const double* part_s2, int 
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_accum_s2, dim3(n_trials), dim3(256), 0, st, part_s2, gcap, ng, pass2_row_blocks(n), s2run);
+    return hipGetLastError();
+}
+
+hipError_t launch_set_trials(const TrialBlock& blk, int count, TrialConst* dev, hipStream_t st) {
+    if (count <= 0) return hipSuccess;
+    if (count > kTrialBlock) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_set_trials, dim3(1), dim3(64), 0, st, blk, count, dev);
     return hipGetLastError();
 }
 

@@ -139,6 +139,25 @@ int ssb_loss(ssb_handle* h, const float* params, int32_t n_trials, double* losse
              float* mean_phase, void* stream);
 
 /*
+ * ssb_loss_noalloc: ssb_loss for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Same arguments, results and errors as ssb_loss, and the same kernels, but every
+ * per-call buffer lives in a fixed scratch array of 256 MiB that each device holds
+ * from the library's load until the process ends; no hipMalloc, hipFree or other
+ * allocating call is made, on the device or the host (trial constants reach the
+ * device as kernel arguments).  The BF chunk is the largest multiple of 32 pixels
+ * whose buffers fit the scratch (results are bitwise those of ssb_loss, which do not
+ * depend on the chunk); a call whose trials do not fit even with 32-BF chunks is
+ * rejected with SSB_EINVAL (at N = 512 one call takes up to 7 trials, at N = 1024
+ * one).  Every handle on a device shares that device's scratch, which keeps the
+ * last call's contents: calls that overlap on one device race, so issue them on
+ * one stream or serialize them.  Call with the handle's device current.
+ * Synchronizes the stream before returning.
+ */
+int ssb_loss_noalloc(ssb_handle* h, const float* params, int32_t n_trials, double* losses,
+                     float* mean_phase, void* stream);
+
+/*
  * ssb_reserve: size the handle's device workspace and host staging for loss calls
  * of up to max_trials trials (any BF range, either variant, any chunk cap), so
  * that such calls, and ssb_moments and ssb_object, allocate nothing afterwards.
