@@ -55,8 +55,11 @@ int hip_fail(hipError_t e, const char* what) {
 
 constexpr uint64_t kMagic = 0x5353424d49333535ull;   // "SSBMI355"
 constexpr uint64_t kDead = 0xdeadbeefdeadbeefull;
-// Intermediate budget for one chunk (all trials): bounds workspace memory.
-constexpr double kInterBudget = 12.0 * 1024 * 1024 * 1024;
+// Intermediate budget for one chunk (all trials): bounds workspace memory.  Large
+// enough that a 200-trial batch at 512^2 runs in 224-BF chunks (each chunk folds every
+// trial's 2 MB double phase-sum image once, so small chunks cost reduction traffic),
+// small against the 288 GB of one device.
+constexpr double kInterBudget = 48.0 * 1024 * 1024 * 1024;
 
 template <class T>
 T* align_up(char* base, size_t& off, size_t count) {

@@ -62,6 +62,12 @@ namespace {
 #ifndef SSB_PASS1_MIN_WAVES
 #define SSB_PASS1_MIN_WAVES 5 // pass-1 register budget at N = 512: resident waves per SIMD
 #endif
+#ifndef SSB_PASS1_MIN_WAVES_BATCH
+#define SSB_PASS1_MIN_WAVES_BATCH 3 // the same with several trials per workgroup (168 VGPRs; at 4 it spills)
+#endif
+#ifndef SSB_PASS1_TB
+#define SSB_PASS1_TB 8 // trials per pass-1 workgroup in batches
+#endif
 #ifndef SSB_PASS2_MIN_WAVES_1024
 #define SSB_PASS2_MIN_WAVES_1024 4 // the same at N = 1024 (LDS also allows 4 workgroups per CU)
 #endif
@@ -528,10 +534,19 @@ template <int N> __device__ __forceinline__ int pass1_row(int c, int u) {
     if constexpr (pass1_swz<N>()) return u ^ ((c & 7) << 2);
     else return u;
 }
-template <int N, int TC, bool NYQ, bool STREAM>
+// TB trials per workgroup (TB > 1 for batches): the tile's spectrum entries, support
+// flags and BF offset are loaded once and stay in registers while each trial, in turn,
+// brings its own chi_q block, phase chains, correction, transforms and stores (the
+// pages' fused candidates: geometry, aperture weights and the spectrum fetch shared,
+// each candidate with its own correction and transforms).  The arithmetic of each
+// trial is the single-trial path's, so a trial's results do not depend on TB.
+// chsrc / out: trial t0's block; the next trial's is ch_step / out_step values on.
+template <int N, int TC, bool NYQ, bool STREAM, int TB>
 __device__ __forceinline__ void pass1_tile(const float2* __restrict__ gsrc, const float2* __restrict__ chsrc,
-                                           const double2 k, const uint4 sr, const TrialConst& m, const GeomDev& geo,
-                                           float2* __restrict__ out, float2* tile, int v0, int csub) {
+                                           int64_t ch_step, const double2 k, const uint4 sr,
+                                           const TrialConst* __restrict__ tcp, int nt, const GeomDev& geo,
+                                           float2* __restrict__ out, int64_t out_step, float2* tile, int v0,
+                                           int csub) {
     constexpr int H = N / 2;
     constexpr int LD = pass1_ld<N, TC>();
     constexpr int NT = pass1_threads<N>();
@@ -544,9 +559,9 @@ __device__ __forceinline__ void pass1_tile(const float2* __restrict__ gsrc, cons
     const int tid = threadIdx.x;
     const int c = NYQ ? 0 : tid % TC;
     const int v = v0 + c;
-    const int ustart = NYQ ? tid : tid / TC;
-    const int lo_m = unpack_lo(sr.x), len_m = unpack_len(sr.x);
-    const int lo_p = unpack_lo(sr.y), len_p = unpack_len(sr.y);
+    int ustart = NYQ ? tid : tid / TC;
+    int lo_m = unpack_lo(sr.x), len_m = unpack_len(sr.x);
+    int lo_p = unpack_lo(sr.y), len_p = unpack_len(sr.y);
 
     // 1. support and loads into registers (all loads in flight together)
     // gsrc / chsrc: the layout tile's block (main: [N][kTileW]; this workgroup's
@@ -557,18 +572,21 @@ __device__ __forceinline__ void pass1_tile(const float2* __restrict__ gsrc, cons
     constexpr bool CL = chi_in_lds<N>() && !NYQ;
     static_assert(!CL || RS <= H, "the copied block is waited for in the two-chain path");
     const __amdgpu_buffer_rsrc_t rg = make_rsrc(gsrc, N * (NYQ ? 1 : kTileW) * 8);
-    const __amdgpu_buffer_rsrc_t rc = make_rsrc(chsrc, N * (NYQ ? 1 : kTileW) * 8);
-    if constexpr (CL) {
-        static_assert(TC == kTileW && LD == N, "the chi_q block is the tile's LDS image");
-        constexpr int WAVE_BYTES = N * kTileW * 8 / (NT / 64);
-        const int lane = tid & 63;
-        const int wb = (tid >> 6) * WAVE_BYTES;
+    auto copy_chi = [&](const float2* chs) {
+        if constexpr (CL) {
+            static_assert(TC == kTileW && LD == N, "the chi_q block is the tile's LDS image");
+            const __amdgpu_buffer_rsrc_t rc = make_rsrc(chs, N * kTileW * 8);
+            constexpr int WAVE_BYTES = N * kTileW * 8 / (NT / 64);
+            const int lane = tid & 63;
+            const int wb = (tid >> 6) * WAVE_BYTES;
 #pragma unroll
-        for (int k = 0; k < WAVE_BYTES / 1024; ++k)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (lds_ptr_t)((char*)tile + wb + k * 1024), 16,
-                                                     wb + k * 1024 + lane * 16, 0, 0, 0);
-        asm volatile("" ::: "memory");   // the copies stay ahead of every spectrum load
-    }
+            for (int q = 0; q < WAVE_BYTES / 1024; ++q)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (lds_ptr_t)((char*)tile + wb + q * 1024), 16,
+                                                         wb + q * 1024 + lane * 16, 0, 0, 0);
+            asm volatile("" ::: "memory");   // the copies stay ahead of every later load
+        }
+    };
+    copy_chi(chsrc);
     const int off0 = (ustart * SSTRIDE + csub + c) * 8;
     float2 gv[PM], chv[CL ? 1 : PM];
     // entry i in the support of either shifted aperture (DC excluded): evaluated at
@@ -581,111 +599,142 @@ __device__ __forceinline__ void pass1_tile(const float2* __restrict__ gsrc, cons
         inp = (unsigned)(up - lo_p) < (unsigned)len_p;
         return (NYQ ? u < N : true) && (inm || inp) && (u != 0 || v != 0);
     };
+    auto load_chv = [&](const float2* chs) {
+        if constexpr (!CL) {
+            const __amdgpu_buffer_rsrc_t rc = make_rsrc(chs, N * (NYQ ? 1 : kTileW) * 8);
+#pragma unroll
+            for (int i = 0; i < PM; ++i) {
+                bool inm, inp;
+                chv[i] = load_or_zero(rc, flags(i, inm, inp) ? off0 + i * RS * SSTRIDE * 8 : kNoLoad);
+            }
+        }
+    };
 #pragma unroll
     for (int i = 0; i < PM; ++i) {
         bool inm, inp;
         const int off = flags(i, inm, inp) ? off0 + i * RS * SSTRIDE * 8 : kNoLoad;
         gv[i] = STREAM ? load_or_zero_nt(rg, off) : load_or_zero(rg, off);
-        if constexpr (!CL) chv[i] = load_or_zero(rc, off);
     }
-    // the phase slopes of this BF pixel while the loads are in flight
-    double alpha, beta;
-    delta_slopes(k.x, k.y, m, geo, alpha, beta);
-    const double av = (double)v * alpha;
+    load_chv(chsrc);
 
-    // 2. correction into the LDS tile
-    const int flo_m = unpack_lo(sr.z), flen_m = unpack_len(sr.z);
-    const int flo_p = unpack_lo(sr.w), flen_p = unpack_len(sr.w);
+    int flo_m = unpack_lo(sr.z), flen_m = unpack_len(sr.z);
+    int flo_p = unpack_lo(sr.w), flen_p = unpack_len(sr.w);
     static_assert(NYQ || RS % 32 == 0 || !pass1_swz<N>(), "row steps leave the swizzled bits alone");
     float2* trow = tile + c * LD + pass1_row<N>(c, ustart);
-    auto entry = [&](int i, float2 e) {
-        const int u = ustart + i * RS;
-        float2 val = make_float2(0.f, 0.f);
-        bool inm, inp;
-        if (flags(i, inm, inp)) {
-            const int up = (NYQ || RS > H) ? (u < H ? u : u - N) : (i < PM / 2 ? u : u - N);
-            const bool edm = inm && (unsigned)(up - flo_m) >= (unsigned)flen_m;
-            const bool edp = inp && (unsigned)(up - flo_p) >= (unsigned)flen_p;
-            float2 ch;
-            if constexpr (CL) ch = trow[i * RS];
-            else ch = chv[i];
-            val = correct_entry(gv[i], ch, e, inm, inp, edm, edp, up, v, k.x, k.y, geo);
-        }
-        trow[i * RS] = val;
-    };
-    if constexpr (!NYQ && RS <= H) {
-        // PM/2 rows below N/2, then PM/2 rows from N/2 on; two chains
-        static_assert(PM % 2 == 0 && (PM / 2) * RS == H, "rows split at N/2");
-        float2 ea = phasor_rev_neg(fma((double)ustart, beta, av));
-        float2 eb = phasor_rev_neg(fma((double)(ustart - H), beta, av));
-        const float2 st = phasor_rev_neg((double)RS * beta);
-        if constexpr (CL) {
-            // every wave's copies have landed before any thread reads a slot another
-            // wave filled.  The compiler tracks the copies to the LDS as outstanding
-            // vector memory operations: before this barrier it waits only until the
-            // operations issued after them (the spectrum loads, any spill) are the
-            // only ones left, so the spectrum loads stay in flight and each entry
-            // waits for its own load (a CPU test checks this in the built assembly)
-            __syncthreads();
-        }
-#pragma unroll
-        for (int i = 0; i < PM / 2; ++i) {
-            entry(i, ea);
-            entry(i + PM / 2, eb);
-            ea = cmul(ea, st);
-            eb = cmul(eb, st);
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < PM; ++i) {
-            const int u = ustart + i * RS;
-            if (NYQ ? u < N : true) entry(i, phasor_rev_neg(fma((double)(u < H ? u : u - N), beta, av)));
-        }
-    }
-    __syncthreads();
-
-    // 3. column transforms.  The twiddles are computed here rather than loaded
-    // from the shared table: loaded at this point their latency is exposed, loaded
-    // early they hold registers through the correction (both measured slower),
-    // while this arithmetic fills issue slots of waves waiting on memory.  For
-    // radix 8 only r = 1, 2, 4 take a sincospi; r = 3, 5, 6, 7 are their products.
     const int lane = tid & 63;
     const int grp = (tid >> 6) * F::W + lane / F::L;
     const int j = lane % F::L;
     constexpr int NG = (NT / 64) * F::W;
     constexpr int NCOLS = NYQ ? 1 : TC;
-    F fft;
-    if constexpr (F::R == 8 || N == 1024) fft.init_products(j);   // sincospi for r = 1, 2, 4, the rest products
-    else fft.init(j);
     // row j + r L of column cc: with L a multiple of 32 the swizzle leaves r L alone
     auto slot = [&](int cc, int r) {
         if constexpr (F::L % 32 == 0) return cc * LD + pass1_row<N>(cc, j) + r * F::L;
         else return cc * LD + pass1_row<N>(cc, j + r * F::L);
     };
-    for (int cc = grp; cc < NCOLS; cc += NG) {
-        float2 x[F::R];
-#pragma unroll
-        for (int r = 0; r < F::R; ++r) x[r] = tile[slot(cc, r)];
-        fft.run(x, &tile[cc * LD], j);
-        wave_lds_fence();
-#pragma unroll
-        for (int r = 0; r < F::R; ++r) tile[slot(cc, r)] = x[r];
-    }
-    __syncthreads();
 
-    // 4. store (out: the layout tile's block of the column-result plane, or the Nyquist column)
-    if (!NYQ) {
-        float2* om = out + csub + c;
-        const float2* tcol = tile + c * LD + pass1_row<N>(c, ustart);
-#pragma unroll 4
-        for (int y = ustart; y < N; y += RS) {
-            if constexpr (STREAM) store_nt(om + (int64_t)y * kTileW, tcol[y - ustart]);
-            else om[(int64_t)y * kTileW] = tcol[y - ustart];
+    const int ntr = TB == 1 ? 1 : nt;
+    for (int tt = 0; tt < ntr; ++tt) {
+        if constexpr (TB > 1) {
+            // opaque per trial: what derives from the row start and the support intervals
+            // is formed again in each trial instead of held in registers across the
+            // transforms (which would spill)
+            asm volatile("" : "+v"(ustart), "+v"(lo_m), "+v"(len_m), "+v"(lo_p), "+v"(len_p));
+            asm volatile("" : "+v"(flo_m), "+v"(flen_m), "+v"(flo_p), "+v"(flen_p));
         }
-    } else {
-        for (int y = tid; y < N; y += NT) {
-            if constexpr (STREAM) store_nt(out + y, tile[y]);
-            else out[y] = tile[y];
+        if (tt > 0) {
+            // every thread's stores of the previous trial have read the tile before the
+            // next chi_q block lands in it
+            __syncthreads();
+            copy_chi(chsrc + tt * ch_step);
+            load_chv(chsrc + tt * ch_step);
+        }
+        const TrialConst m = tcp[tt];
+        // the phase slopes of this BF pixel while the loads are in flight
+        double alpha, beta;
+        delta_slopes(k.x, k.y, m, geo, alpha, beta);
+        const double av = (double)v * alpha;
+
+        // 2. correction into the LDS tile
+        auto entry = [&](int i, float2 e) {
+            const int u = ustart + i * RS;
+            float2 val = make_float2(0.f, 0.f);
+            bool inm, inp;
+            if (flags(i, inm, inp)) {
+                const int up = (NYQ || RS > H) ? (u < H ? u : u - N) : (i < PM / 2 ? u : u - N);
+                const bool edm = inm && (unsigned)(up - flo_m) >= (unsigned)flen_m;
+                const bool edp = inp && (unsigned)(up - flo_p) >= (unsigned)flen_p;
+                float2 ch;
+                if constexpr (CL) ch = trow[i * RS];
+                else ch = chv[i];
+                val = correct_entry(gv[i], ch, e, inm, inp, edm, edp, up, v, k.x, k.y, geo);
+            }
+            trow[i * RS] = val;
+        };
+        if constexpr (!NYQ && RS <= H) {
+            // PM/2 rows below N/2, then PM/2 rows from N/2 on; two chains
+            static_assert(PM % 2 == 0 && (PM / 2) * RS == H, "rows split at N/2");
+            float2 ea = phasor_rev_neg(fma((double)ustart, beta, av));
+            float2 eb = phasor_rev_neg(fma((double)(ustart - H), beta, av));
+            const float2 st = phasor_rev_neg((double)RS * beta);
+            if constexpr (CL) {
+                // every wave's copies have landed before any thread reads a slot another
+                // wave filled.  The compiler tracks the copies to the LDS as outstanding
+                // vector memory operations: before this barrier it waits only until the
+                // operations issued after them (the spectrum loads, any spill) are the
+                // only ones left, so the spectrum loads stay in flight and each entry
+                // waits for its own load (a CPU test checks this in the built assembly)
+                __syncthreads();
+            }
+#pragma unroll
+            for (int i = 0; i < PM / 2; ++i) {
+                entry(i, ea);
+                entry(i + PM / 2, eb);
+                ea = cmul(ea, st);
+                eb = cmul(eb, st);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < PM; ++i) {
+                const int u = ustart + i * RS;
+                if (NYQ ? u < N : true) entry(i, phasor_rev_neg(fma((double)(u < H ? u : u - N), beta, av)));
+            }
+        }
+        __syncthreads();
+
+        // 3. column transforms.  The twiddles are computed here rather than loaded
+        // from the shared table: loaded at this point their latency is exposed, loaded
+        // early they hold registers through the correction (both measured slower),
+        // while this arithmetic fills issue slots of waves waiting on memory.  For
+        // radix 8 only r = 1, 2, 4 take a sincospi; r = 3, 5, 6, 7 are their products.
+        F fft;
+        if constexpr (F::R == 8 || N == 1024) fft.init_products(j);   // sincospi for r = 1, 2, 4, the rest products
+        else fft.init(j);
+        for (int cc = grp; cc < NCOLS; cc += NG) {
+            float2 x[F::R];
+#pragma unroll
+            for (int r = 0; r < F::R; ++r) x[r] = tile[slot(cc, r)];
+            fft.run(x, &tile[cc * LD], j);
+            wave_lds_fence();
+#pragma unroll
+            for (int r = 0; r < F::R; ++r) tile[slot(cc, r)] = x[r];
+        }
+        __syncthreads();
+
+        // 4. store (out: the layout tile's block of the column-result plane, or the Nyquist column)
+        float2* ot = out + tt * out_step;
+        if (!NYQ) {
+            float2* om = ot + csub + c;
+            const float2* tcol = tile + c * LD + pass1_row<N>(c, ustart);
+#pragma unroll 4
+            for (int y = ustart; y < N; y += RS) {
+                if constexpr (STREAM) store_nt(om + (int64_t)y * kTileW, tcol[y - ustart]);
+                else om[(int64_t)y * kTileW] = tcol[y - ustart];
+            }
+        } else {
+            for (int y = tid; y < N; y += NT) {
+                if constexpr (STREAM) store_nt(ot + y, tile[y]);
+                else ot[y] = tile[y];
+            }
         }
     }
 }
@@ -698,10 +747,14 @@ __device__ __forceinline__ void pass1_tile(const float2* __restrict__ gsrc, cons
 // Register budget: with the chi_q block copied to the LDS (N = 512) the kernel fits
 // the budget of SSB_PASS1_MIN_WAVES waves per SIMD, which the 32 KB tile's LDS also
 // allows (five 32 KB tiles fill the 160 KB of a CU).
-template <int N> constexpr int pass1_min_waves() { return chi_in_lds<N>() ? SSB_PASS1_MIN_WAVES : 1; }
+// With TB > 1 trials per workgroup the spectrum entries stay in registers through the
+// transforms: a 168-VGPR budget (three waves per SIMD; at four the compiler spills).
+template <int N, int TB> constexpr int pass1_min_waves() {
+    return chi_in_lds<N>() ? (TB > 1 ? SSB_PASS1_MIN_WAVES_BATCH : SSB_PASS1_MIN_WAVES) : 1;
+}
 
-template <int N, int TC, bool STREAM>
-__global__ __launch_bounds__(pass1_threads<N>(), (pass1_min_waves<N>())) void k_pass1(const float2* __restrict__ gm,
+template <int N, int TC, bool STREAM, int TB>
+__global__ __launch_bounds__(pass1_threads<N>(), (pass1_min_waves<N, TB>())) void k_pass1(const float2* __restrict__ gm,
                                                          const float2* __restrict__ gn,
                                                          const float2* __restrict__ chm,
                                                          const float2* __restrict__ chn,
@@ -710,12 +763,14 @@ __global__ __launch_bounds__(pass1_threads<N>(), (pass1_min_waves<N>())) void k_
                                                          const int* __restrict__ vend,
                                                          const TrialConst* __restrict__ tc, GeomDev geo,
                                                          int64_t bf0, int cap, float2* __restrict__ im,
-                                                         float2* __restrict__ in) {
+                                                         float2* __restrict__ in, int n_trials) {
     constexpr int H = N / 2;
     constexpr int LD = pass1_ld<N, TC>();
     __shared__ float2 tile[TC * LD];
 
-    const int t = blockIdx.y;
+    // trials [t, t + nt) of this workgroup
+    const int t = blockIdx.y * TB;
+    const int nt = min(TB, n_trials - t);
     // Workgroup -> (BF, tile).  Up to N = 512 BF-major: the H/TC main tiles of a BF,
     // then its Nyquist tile (the per-trial chi_q table, 1 MB, stays in L2 anyway).
     // At N = 1024 tile-major: the workgroups running together share one column
@@ -743,15 +798,17 @@ __global__ __launch_bounds__(pass1_threads<N>(), (pass1_min_waves<N>())) void k_
     // them as zeros.  A layout tile with any supported column is written whole.
     if ((nyq ? H : lt * kTileW) >= vend[b]) return;
     const double2 k = kb[b];
-    const TrialConst m = tc[t];
     if (!nyq) {
         const int64_t tb = (int64_t)lt * N * kTileW;      // the layout tile's block in a plane
         const int v = v0 + (int)threadIdx.x % TC;
-        pass1_tile<N, TC, false, STREAM>(gm + b * N * H + tb, chm + (int64_t)t * N * H + tb, k, sup[b * (H + 1) + v], m, geo,
-                                 im + ((int64_t)t * cap + bl) * N * H + tb, tile, v0, v0 - lt * kTileW);
+        pass1_tile<N, TC, false, STREAM, TB>(gm + b * N * H + tb, chm + (int64_t)t * N * H + tb, (int64_t)N * H, k,
+                                             sup[b * (H + 1) + v], tc + t, nt, geo,
+                                             im + ((int64_t)t * cap + bl) * N * H + tb, (int64_t)cap * N * H, tile,
+                                             v0, v0 - lt * kTileW);
     } else {
-        pass1_tile<N, TC, true, STREAM>(gn + b * N, chn + (int64_t)t * N, k, sup[b * (H + 1) + H], m, geo,
-                                in + ((int64_t)t * cap + bl) * N, tile, v0, 0);
+        pass1_tile<N, TC, true, STREAM, TB>(gn + b * N, chn + (int64_t)t * N, (int64_t)N, k, sup[b * (H + 1) + H],
+                                            tc + t, nt, geo, in + ((int64_t)t * cap + bl) * N, (int64_t)cap * N,
+                                            tile, v0, 0);
     }
 }
 
@@ -1506,15 +1563,26 @@ hipError_t pass1_n(const float2* gm, const float2* gn, const float2* chm, const 
                    int cb, int cap, float2* im, float2* in, hipStream_t st) {
     constexpr int H = N / 2;
     constexpr int TC = pass1_tc<N>();
-    // one launch per chunk: (H/TC + 1) tiles per BF in x, trials in y
-    const dim3 grid((unsigned)((int64_t)cb * (H / TC + 1)), n_trials);
+    // one launch per chunk: (H/TC + 1) tiles per BF in x, groups of TB trials in y
+    constexpr int TB = SSB_PASS1_TB;
+    const dim3 grid1((unsigned)((int64_t)cb * (H / TC + 1)), n_trials);
+    const dim3 gridb((unsigned)((int64_t)cb * (H / TC + 1)), (n_trials + TB - 1) / TB);
     const bool stream = n_trials == 1 || (int64_t)cb * N * (H + 1) * 8 > ((int64_t)192 << 20);
-    if (stream)
-        hipLaunchKernelGGL((k_pass1<N, TC, true>), grid, dim3(pass1_threads<N>()), 0, st, gm, gn, chm, chn, kb, sup,
-                           vend, tc, geo, bf0, cap, im, in);
-    else
-        hipLaunchKernelGGL((k_pass1<N, TC, false>), grid, dim3(pass1_threads<N>()), 0, st, gm, gn, chm, chn, kb, sup,
-                           vend, tc, geo, bf0, cap, im, in);
+    if (n_trials == 1 || TB == 1) {
+        if (stream)
+            hipLaunchKernelGGL((k_pass1<N, TC, true, 1>), grid1, dim3(pass1_threads<N>()), 0, st, gm, gn, chm, chn, kb,
+                               sup, vend, tc, geo, bf0, cap, im, in, n_trials);
+        else
+            hipLaunchKernelGGL((k_pass1<N, TC, false, 1>), grid1, dim3(pass1_threads<N>()), 0, st, gm, gn, chm, chn,
+                               kb, sup, vend, tc, geo, bf0, cap, im, in, n_trials);
+    } else {
+        if (stream)
+            hipLaunchKernelGGL((k_pass1<N, TC, true, TB>), gridb, dim3(pass1_threads<N>()), 0, st, gm, gn, chm, chn,
+                               kb, sup, vend, tc, geo, bf0, cap, im, in, n_trials);
+        else
+            hipLaunchKernelGGL((k_pass1<N, TC, false, TB>), gridb, dim3(pass1_threads<N>()), 0, st, gm, gn, chm, chn,
+                               kb, sup, vend, tc, geo, bf0, cap, im, in, n_trials);
+    }
     return hipGetLastError();
 }
 

@@ -201,7 +201,7 @@ int ssb_spectrum(const ssb_handle* h, int64_t bf, float* out, void* stream);
 /*
  * ssb_set_chunk: cap the BF pixels whose intermediate is resident at once
  * (rounded up to the fixed 32-BF reduction group; also bounded by the library's
- * 12 GiB intermediate budget; 0 restores the budget-only choice).  Results do not
+ * 48 GiB intermediate budget; 0 restores the budget-only choice).  Results do not
  * depend on it (bitwise); it bounds workspace memory.
  */
 int ssb_set_chunk(ssb_handle* h, int64_t chunk_bf);
