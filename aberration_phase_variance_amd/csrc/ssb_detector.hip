@@ -37,6 +37,9 @@ constexpr int kSumFrames = 1024;   // frames per workgroup of the detector sum
 #ifndef SSB_GATHER_BF
 #define SSB_GATHER_BF 64
 #endif
+#ifndef SSB_GATHER_XCD
+#define SSB_GATHER_XCD 1   // BF tiles of one frame block on one XCD (0: a 2-D grid)
+#endif
 constexpr int kTileS = SSB_GATHER_FRAMES;   // gather tile: scan positions ...
 constexpr int kTileB = SSB_GATHER_BF;       // ... x BF pixels
 static_assert(kTileS * kTileB % 256 == 0, "whole tile rows per thread");
@@ -103,8 +106,23 @@ __global__ __launch_bounds__(256) void k_gather(const uint32_t* __restrict__ fra
                                                 uint32_t* __restrict__ out) {
     __shared__ uint32_t t[kTileS][kTileB + 1];
     const int tid = threadIdx.x;
+#if SSB_GATHER_XCD
+    // Workgroup id L -> (frame block x, BF tile y).  Consecutive ids go to the eight
+    // XCDs in turn, so x = 8 (L / 8 / ny) + L % 8 keeps every BF tile of one frame block
+    // on one XCD, dispatched one after another: the 128-byte lines two neighbouring BF
+    // tiles share (a BF run rarely ends on a line boundary) are fetched into that XCD's
+    // L2 once.
+    const int64_t ny = (nbf + kTileB - 1) / kTileB;
+    const int64_t L = blockIdx.x;
+    const int64_t r = L / 8;
+    const int64_t x = (r / ny) * 8 + L % 8, y = r % ny;
+    if (x * kTileS >= nscan) return;
+    const int64_t s0 = x * kTileS;
+    const int64_t b0 = y * kTileB;
+#else
     const int64_t s0 = (int64_t)blockIdx.x * kTileS;
     const int64_t b0 = (int64_t)blockIdx.y * kTileB;
+#endif
     // every load of the thread in flight before the first LDS store
     constexpr int PER = kTileS * kTileB / 256;
     uint32_t v[PER];
@@ -250,7 +268,18 @@ extern "C" int ssb_gather_bf(const uint32_t* frames, const ssb_geometry* g, uint
     const int64_t nscan = (int64_t)g->scan_n * g->scan_n;
     const int64_t np = (int64_t)g->det_n * g->det_n;
     if ((e = hipMemcpyAsync(dpix, pix.data(), pix.size() * sizeof(int), hipMemcpyHostToDevice, st)) == hipSuccess) {
+#if SSB_GATHER_XCD
+        const int64_t nx8 = ((nscan + kTileS - 1) / kTileS + 7) / 8 * 8;
+        const int64_t nblk = nx8 * ((n_bf + kTileB - 1) / kTileB);
+        if (nblk > 0x7fffffff) {
+            (void)hipStreamSynchronize(st);
+            (void)hipFree(dpix);
+            return ssb::set_error(SSB_EINVAL, "gather grid too large");
+        }
+        const dim3 grid((unsigned)nblk);
+#else
         const dim3 grid((unsigned)((nscan + kTileS - 1) / kTileS), (unsigned)((n_bf + kTileB - 1) / kTileB));
+#endif
         hipLaunchKernelGGL(k_gather, grid, dim3(256), 0, st, frames, np, nscan, dpix, n_bf, counts);
         e = hipGetLastError();
     }
