@@ -62,6 +62,9 @@ namespace {
 #ifndef SSB_PASS1_MIN_WAVES
 #define SSB_PASS1_MIN_WAVES 5 // pass-1 register budget at N = 512: resident waves per SIMD
 #endif
+#ifndef SSB_P1_SWZ
+#define SSB_P1_SWZ 1 // pass-1 LDS tile: row u of column c at u ^ ((c mod 8) << SSB_P1_SWZ)
+#endif
 #ifndef SSB_PASS1_MIN_WAVES_BATCH
 #define SSB_PASS1_MIN_WAVES_BATCH 3 // the same with several trials per workgroup (168 VGPRs; at 4 it spills)
 #endif
@@ -261,13 +264,13 @@ __global__ __launch_bounds__(256) void k_cols(const float2* in_m, const float2* 
 // (BF independent): main [t] x tile-major [N/2/8][N][8], nyq [t][N].
 // Pass 1 at N = 512 copies each tile's block of the chi_q table straight into its LDS
 // tile, so the table is stored per layout tile as that tile's LDS image: column c of
-// the tile at c * N, row u at u ^ ((c & 7) << 2) (the tile's XOR swizzle).  Other sizes
+// the tile at c * N, row u at u ^ ((c & 7) << SSB_P1_SWZ) (the tile's XOR swizzle).  Other sizes
 // keep the tile-major [tile][u][8] layout of the spectra.
 template <int N> constexpr bool chi_in_lds() { return N == 512; }
 template <int N> __host__ __device__ __forceinline__ int64_t chi_index(int u, int v) {
     if constexpr (chi_in_lds<N>()) {
         const int c = v % kTileW;
-        return (int64_t)(v / kTileW) * N * kTileW + c * N + (u ^ ((c & 7) << 2));
+        return (int64_t)(v / kTileW) * N * kTileW + c * N + (u ^ ((c & 7) << SSB_P1_SWZ));
     } else {
         return tm_index(N, u, v);
     }
@@ -520,18 +523,22 @@ template <int N> constexpr int pass1_threads() { return N >= 1024 ? 512 : SSB_PA
 // compile-time step from the thread's first row.
 // LDS tile: one slot per column, which is also its transform's scratch.  Where the
 // transform's scratch is exactly N values the slots are packed (pitch N) and row u
-// of column c sits at u ^ 4 (c mod 8): the XOR changes bits 2..4 only, so a column
-// stays a permutation of its own slot, a transform's reads of 64 consecutive rows
-// stay conflict-free, and 32 lanes holding 8 columns x 4 consecutive rows hit 32
-// distinct 8-byte slots (8 columns of 512 values take exactly 32 KB).  Padded
-// transforms (1,024 points) keep the pitch SCRATCH + 32/TC (the same bank spread, no
-// swizzle).  (Five workgroups per CU would fit this LDS but need at most 96 VGPRs:
-// forced there, the kernel spills loaded values to scratch right after their loads,
-// 4.2-4.4 ms against 3.0 ms at the compiler's 127 VGPRs, four workgroups.)
+// of column c sits at u ^ 2 (c mod 8): the XOR changes bits 1..3 only, so a column
+// stays a permutation of its own slot and row steps of 32 leave it alone.  An 8-byte
+// LDS access is served 16 lanes at a time over 32 four-byte banks (the bank-conflict
+// counter shows it: the earlier u ^ 4 (c mod 8), conflict-free for 32 lanes at a time,
+// logged about one conflict cycle per LDS instruction).  16 lanes holding 8 columns x
+// 2 consecutive rows (the correction and the stores) then hit 16 distinct 8-byte
+// slots modulo 16, and 16 consecutive rows of one column (the transform's reads) stay
+// a permutation of an aligned group of 16: pass 1 2.64 -> 2.62 ms.  8 columns of 512
+// values take exactly 32 KB.  Padded transforms (1,024 points) keep the pitch
+// SCRATCH + 32/TC (no swizzle).  (Five workgroups per CU would fit this LDS but need at
+// most 96 VGPRs: forced there, the kernel spills loaded values to scratch right after
+// their loads, 4.2-4.4 ms against 3.0 ms at the compiler's 127 VGPRs, four workgroups.)
 template <int N> constexpr bool pass1_swz() { return WaveFFT<N, +1>::SCRATCH == N; }
 template <int N, int TC> constexpr int pass1_ld() { return pass1_swz<N>() ? N : WaveFFT<N, +1>::SCRATCH + 32 / TC; }
 template <int N> __device__ __forceinline__ int pass1_row(int c, int u) {
-    if constexpr (pass1_swz<N>()) return u ^ ((c & 7) << 2);
+    if constexpr (pass1_swz<N>()) return u ^ ((c & 7) << SSB_P1_SWZ);
     else return u;
 }
 // TB trials per workgroup (TB > 1 for batches): the tile's spectrum entries, support
