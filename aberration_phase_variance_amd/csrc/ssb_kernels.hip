@@ -373,19 +373,21 @@ __device__ __forceinline__ void delta_slopes(double kx, double ky, const TrialCo
 // Inputs: the support flags (inm: A(k - q) has
 // nonzero weight, inp: A(k + q) does; edm/edp: that weight is on the edge ring, not
 // the flat top), the spectrum value g, exp(i chi_q) = ch and e = exp(-i delta).
-// On the flat tops the bracket ((a_- - a_+) cos chi_q, (a_- + a_+) sin chi_q) is
-// already a unit phasor: (+-cos, sin) for one sideband, (0, sign sin) for two (zero
-// when sin chi_q is zero); on an edge ring it is evaluated and normalized.
+// With one sideband the bracket is a positive multiple of (+-cos chi_q, sin chi_q), so
+// its weight cancels in T whether or not it lies on an edge ring.  With two on the flat
+// tops it is (0, sign sin chi_q) (zero when sin chi_q is zero).  Only an entry inside
+// both shifted apertures with at least one weight on its edge ring evaluates the
+// weights and normalizes the bracket.
 __device__ __forceinline__ float2 correct_entry(float2 g, float2 ch, float2 e, bool inm, bool inp, bool edm,
                                                 bool edp, int up, int v, double kx, double ky, const GeomDev& geo) {
     float br, bi;
-    if (edm || edp) {
+    if ((edm || edp) && inm && inp) {
         // keep the rarely needed double-precision distances inside this branch (an
         // empty asm makes the row index opaque, so nothing here is hoisted out of a
         // caller's loop where it would hold registers)
         int upo = up;
         asm volatile("" : "+v"(upo));
-        float am = inm ? 1.f : 0.f, apl = inp ? 1.f : 0.f;
+        float am = 1.f, apl = 1.f;
         if (edm) am = edge_weight(shifted_r2(kx, ky, -1.0, upo, v, geo), geo);
         if (edp) apl = edge_weight(shifted_r2(kx, ky, 1.0, upo, v, geo), geo);
         br = (am - apl) * ch.x;

@@ -143,6 +143,32 @@ def test_aperture_closed_form():
     assert np.allclose(O.aperture(g, 0.6 * r, 0.8 * r), a, atol=1e-14)
 
 
+def test_single_sideband_transfer_ignores_edge_weight(monkeypatch):
+    """T = conj(Gamma)/|Gamma| with one shifted aperture nonzero is a unit phasor whatever
+    that aperture's weight: an edge-ring weight matters only where both sidebands are in."""
+    g = _geom("small")
+    kx, ky = O.bf_kvectors(g)
+    qx, qy = O.q_vectors(g)
+    soft = O.aperture
+    params = (37.0, 8.0, 1.1)
+    ts = {b: O.transfer(g, params, kx[b], ky[b], qx, qy) for b in (0, 70, 200, 316)}
+    monkeypatch.setattr(O, "aperture", lambda gg, x, y: (soft(gg, x, y) > 0).astype(np.float64))
+    n_one = n_two = 0
+    for b, t in ts.items():
+        am = soft(g, kx[b] - qx, ky[b] - qy)
+        ap = soft(g, kx[b] + qx, ky[b] + qy)
+        hard = O.transfer(g, params, kx[b], ky[b], qx, qy)
+        one = ((am > 0) != (ap > 0)) & (((am > 0) & (am < 1)) | ((ap > 0) & (ap < 1)))
+        two = (am > 0) & (ap > 0) & (((am < 1) | (ap < 1)) & (np.abs(am - ap) > 0.05))
+        n_one += int(one.sum())
+        n_two += int(two.sum())
+        assert np.max(np.abs(t[one] - hard[one])) < 1e-12
+        # where both are in and the weights differ, the weights do change T
+        if two.any():
+            assert np.max(np.abs(t[two] - hard[two])) > 1e-3
+    assert n_one > 100 and n_two > 10
+
+
 # ------------------------------------------------------------------ zero aberration (P5)
 def test_zero_aberration_transfer_is_sign_of_sidebands():
     g = _geom("small")
