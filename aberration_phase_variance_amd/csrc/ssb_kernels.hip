@@ -90,6 +90,27 @@ __device__ __forceinline__ float2 phasor_rev_neg(double x) {
     return make_float2(cs.x, -cs.y);
 }
 
+// Phase-ramp chains of a wave that holds 8 consecutive rows x 8 consecutive columns of
+// a tile (row r0 + lane / 8, column v0 + lane % 8): the start exp(-i (u beta + v alpha))
+// of the chain over rows u below N/2 (ea), of the chain over rows u - N (eb) and the step
+// exp(-i rs beta) (st).  The starts factor into a row phasor and a column phasor, so
+// each lane computes one phasor (of one of the 8 rows, one of the 8 columns, the step,
+// or exp(i (N/2) beta)) and gathers the factors it needs from the other lanes, instead
+// of three phasors per lane.  (beta, alpha in revolutions.)
+__device__ __forceinline__ void wave_chain_starts(int lane, int r0, int v0, int rs, int h, double alpha,
+                                                  double beta, float2& ea, float2& eb, float2& st) {
+    const int idx = lane < 8 ? r0 + lane : lane < 16 ? v0 + lane - 8 : lane == 16 ? rs : -h;
+    const float2 ph = phasor_rev_neg((double)idx * (lane >= 8 && lane < 16 ? alpha : beta));
+    auto from = [&](int src) { return make_float2(__shfl(ph.x, src), __shfl(ph.y, src)); };
+    auto uni = [&](int src) {
+        return make_float2(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(ph.x), src)),
+                           __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ph.y), src)));
+    };
+    ea = cmul(from(lane >> 3), from(8 + (lane & 7)));
+    st = uni(16);
+    eb = cmul(ea, uni(17));
+}
+
 // Squared distance |k + sg q(u', v)|^2 (pixels^2) of one shifted aperture center,
 // sg = -1 for A(k - q) and +1 for A(k + q), in double.  Every support and flat-top
 // decision of the correction is taken on this value.
@@ -682,9 +703,9 @@ __device__ __forceinline__ void pass1_tile(const float2* __restrict__ gsrc, cons
         if constexpr (!NYQ && RS <= H) {
             // PM/2 rows below N/2, then PM/2 rows from N/2 on; two chains
             static_assert(PM % 2 == 0 && (PM / 2) * RS == H, "rows split at N/2");
-            float2 ea = phasor_rev_neg(fma((double)ustart, beta, av));
-            float2 eb = phasor_rev_neg(fma((double)(ustart - H), beta, av));
-            const float2 st = phasor_rev_neg((double)RS * beta);
+            float2 ea, eb, st;
+            static_assert(TC == 8 && NT / TC == RS, "a wave is 8 rows x 8 columns of the tile");
+            wave_chain_starts(lane, (tid >> 6) * 8, v0, RS, H, alpha, beta, ea, eb, st);
             if constexpr (CL) {
                 // every wave's copies have landed before any thread reads a slot another
                 // wave filled.  The compiler tracks the copies to the LDS as outstanding
@@ -1247,9 +1268,14 @@ __global__ __launch_bounds__(256) void k_g_rows(const uint32_t* __restrict__ cou
 // thread keeps its tile entries' running sums in registers (float, at most a
 // segment's worth of terms) and loops over the segment's BF pixels in order:
 // support from the per-column intervals, predicated loads, the same correction as
-// pass 1 (exp(-i delta) from a per-BF row table in LDS, double buffered, and a
-// per-thread column phasor; exp(i chi_q) once per entry).  Tiles at or past a BF
-// pixel's last supported column skip it.  Partials per segment in double.
+// pass 1 (exp(-i delta) from two phasor chains per thread, no workgroup barrier in the
+// loop; exp(i chi_q) once per entry).  Tiles at or past a BF pixel's last supported
+// column skip it.  Partials per segment in double.
+// Grid: x = segment, y = column tile.  Workgroups are dispatched x fastest, so every
+// segment of tile 0 goes first: the support, and with it the work, shrinks with the
+// column (tile 0 holds about 26 M of the 503 M support entries at 512^2, the last main
+// tile 1 M), and the lightest items fill the tail (object sum 1.51 -> 1.30 ms against
+// the tile-fastest order).
 // 1024 threads at N = 1024 keep a thread's share of the tile at 8 entries, as at 512.
 template <int N> constexpr int obj_threads() { return N >= 1024 ? 1024 : 512; }
 
@@ -1267,10 +1293,9 @@ __global__ __launch_bounds__(obj_threads<N>()) void k_obj_sum(const float2* __re
     constexpr int PER = (N + RS - 1) / RS;
     constexpr int PERN = (N + NT - 1) / NT;
     constexpr int PM = PER > PERN ? PER : PERN;
-    __shared__ float2 eu[2][N];
 
     const int tid = threadIdx.x;
-    const int tix = blockIdx.x;
+    const int tix = blockIdx.y, seg = blockIdx.x;
     const bool nyq = tix == H / TC;
     const int c = nyq ? 0 : tid % TC;
     const int v0 = nyq ? H : tix * TC;
@@ -1281,7 +1306,7 @@ __global__ __launch_bounds__(obj_threads<N>()) void k_obj_sum(const float2* __re
     static_assert(TC == kTileW, "object tiles are the layout's tiles");
     const int sstride = nyq ? 1 : TC;             // row stride inside the tile block
     const int64_t tb = (int64_t)tix * N * TC;      // this tile's block in a plane
-    const int64_t b_lo = (int64_t)blockIdx.y * seglen;
+    const int64_t b_lo = (int64_t)seg * seglen;
     const int64_t b_hi = min(nbf, b_lo + seglen);
 
     float2 chv[PM], acc[PM];
@@ -1293,14 +1318,31 @@ __global__ __launch_bounds__(obj_threads<N>()) void k_obj_sum(const float2* __re
         acc[i] = make_float2(0.f, 0.f);
     }
 
-    // BF pixels with support in this tile, in order; the next one's column support
-    // and k are fetched while the current one is corrected
-    auto next_bf = [&](int64_t b) {
-        while (b < b_hi && v0 >= vend[b]) ++b;    // no support in this tile (or an inactive BF)
-        return b;
+    // BF pixels with support in this tile, in order, 64 at a time: one last-supported-
+    // column value per lane and a ballot, so stepping to the next one takes no dependent
+    // load (inactive BF pixels have none).  The next one's column support and k are
+    // fetched while the current one is corrected.
+    const int lane = tid & 63;
+    int64_t wbase = b_lo;
+    uint64_t wmask = 0;
+    auto load_window = [&]() {
+        const int64_t bl = wbase + lane;
+        bool has = false;
+        if (bl < b_hi) has = v0 < vend[bl];
+        wmask = __ballot(has);
     };
-    int buf = 0;
-    int64_t b = next_bf(b_lo);
+    auto next_bf = [&]() -> int64_t {
+        while (wmask == 0) {
+            wbase += 64;
+            if (wbase >= b_hi) return b_hi;
+            load_window();
+        }
+        const int64_t bx = wbase + __builtin_ctzll(wmask);
+        wmask &= wmask - 1;
+        return bx;
+    };
+    load_window();
+    int64_t b = next_bf();
     uint4 srn = make_uint4(0, 0, 0, 0);
     double2 kn = make_double2(0.0, 0.0);
     if (b < b_hi) {
@@ -1310,7 +1352,7 @@ __global__ __launch_bounds__(obj_threads<N>()) void k_obj_sum(const float2* __re
     while (b < b_hi) {
         const uint4 sr = srn;
         const double2 k = kn;
-        const int64_t bn = next_bf(b + 1);
+        const int64_t bn = next_bf();
         if (bn < b_hi) {
             srn = sup[bn * (H + 1) + v];
             kn = kb[bn];
@@ -1337,34 +1379,57 @@ __global__ __launch_bounds__(obj_threads<N>()) void k_obj_sum(const float2* __re
             bool inm, inp;
             gv[i] = load_or_zero(rg, on_of(i, inm, inp) ? (u * sstride + c) * 8 : kNoLoad);
         }
-        // phase ramps of this BF while its spectrum loads are in flight
+        // phase ramps exp(-i delta) of this BF while its spectrum loads are in flight: per
+        // thread one chain over its rows below N/2 and one over its rows from N/2 on (steps
+        // of RS rows), as in pass 1; the Nyquist tile's one entry per thread directly
         double alpha, beta;
         delta_slopes(k.x, k.y, m, geo, alpha, beta);
-        for (int u = tid; u < N; u += NT) eu[buf][u] = phasor_rev_neg((double)(u < H ? u : u - N) * beta);
-        const float2 ev = phasor_rev_neg((double)v * alpha);
-        __syncthreads();                          // row table of this BF complete (double buffered)
-#pragma unroll
-        for (int i = 0; i < PM; ++i) {
+        const double av = (double)v * alpha;
+        float2 ea, eb, st;
+        if (!nyq && (PM % 2 == 0 && (PM / 2) * RS == H)) {
+            static_assert(TC == 8, "a wave is 8 rows x 8 columns of the tile");
+            wave_chain_starts(lane, (tid >> 6) * 8, v0, RS, H, alpha, beta, ea, eb, st);
+        } else {
+            ea = phasor_rev_neg(fma((double)(ustart < H ? ustart : ustart - N), beta, av));
+            eb = ea;
+            st = make_float2(1.f, 0.f);
+        }
+        auto entry = [&](int i, float2 e) {
             bool inm, inp;
             if (on_of(i, inm, inp)) {
                 const int u = ustart + i * ustep;
                 const int up = u < H ? u : u - N;
                 const bool edm = inm && (unsigned)(up - flo_m) >= (unsigned)flen_m;
                 const bool edp = inp && (unsigned)(up - flo_p) >= (unsigned)flen_p;
-                const float2 cv =
-                    correct_entry(gv[i], chv[i], cmul(eu[buf][u], ev), inm, inp, edm, edp, up, v, k.x, k.y, geo);
+                const float2 cv = correct_entry(gv[i], chv[i], e, inm, inp, edm, edp, up, v, k.x, k.y, geo);
                 acc[i].x += cv.x;
                 acc[i].y += cv.y;
             }
+        };
+        if constexpr (PM % 2 == 0 && (PM / 2) * RS == H) {
+#pragma unroll
+            for (int i = 0; i < PM / 2; ++i) {
+                entry(i, ea);
+                entry(i + PM / 2, eb);
+                ea = cmul(ea, st);
+                eb = cmul(eb, st);
+            }
+        } else {
+            // small transforms (a thread's rows do not split evenly at N/2): each entry's
+            // phasor directly
+#pragma unroll
+            for (int i = 0; i < PM; ++i) {
+                const int u = ustart + i * ustep;
+                entry(i, phasor_rev_neg(fma((double)(u < H ? u : u - N), beta, av)));
+            }
         }
-        buf ^= 1;
         b = bn;
     }
 #pragma unroll
     for (int i = 0; i < PM; ++i) {
         const int u = ustart + i * ustep;
         if (i < nent && u < N)
-            part[(int64_t)blockIdx.y * NE + (int64_t)u * (H + 1) + v] = make_double2(acc[i].x, acc[i].y);
+            part[(int64_t)seg * NE + (int64_t)u * (H + 1) + v] = make_double2(acc[i].x, acc[i].y);
     }
 }
 
@@ -1776,7 +1841,8 @@ static hipError_t obj_sum_n(const float2* gm, const float2* gn, const double2* k
                             hipStream_t st) {
     constexpr int TC = kTileW;
     const int seglen = (int)((nbf + nseg - 1) / nseg);
-    hipLaunchKernelGGL((k_obj_sum<N, TC>), dim3(N / 2 / TC + 1, nseg), dim3(obj_threads<N>()), 0, st, gm, gn, kb, sup,
+    const dim3 grid(nseg, N / 2 / TC + 1);
+    hipLaunchKernelGGL((k_obj_sum<N, TC>), grid, dim3(obj_threads<N>()), 0, st, gm, gn, kb, sup,
                        vend, tc, geo, nbf, seglen, part);
     return hipGetLastError();
 }
