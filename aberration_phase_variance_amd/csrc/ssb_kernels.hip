@@ -392,34 +392,40 @@ __device__ __forceinline__ void delta_slopes(double kx, double ky, const TrialCo
 // the definition's two shifted probe factors regrouped so that |Gamma| never comes
 // from cancellation, and a(k) > 0 drops out of T.
 // Inputs: the support flags (inm: A(k - q) has
-// nonzero weight, inp: A(k + q) does; edm/edp: that weight is on the edge ring, not
+// nonzero weight, inp: A(k + q) does; edge(edm, edp): that weight is on the edge ring, not
 // the flat top), the spectrum value g, exp(i chi_q) = ch and e = exp(-i delta).
 // With one sideband the bracket is a positive multiple of (+-cos chi_q, sin chi_q), so
 // its weight cancels in T whether or not it lies on an edge ring.  With two on the flat
 // tops it is (0, sign sin chi_q) (zero when sin chi_q is zero).  Only an entry inside
 // both shifted apertures with at least one weight on its edge ring evaluates the
-// weights and normalizes the bracket.
-__device__ __forceinline__ float2 correct_entry(float2 g, float2 ch, float2 e, bool inm, bool inp, bool edm,
-                                                bool edp, int up, int v, double kx, double ky, const GeomDev& geo) {
+// weights and normalizes the bracket, so the edge flags (edge(edm, edp): the weight of
+// A(k - q), A(k + q) is on its edge ring) are asked for only there.
+template <class Edge>
+__device__ __forceinline__ float2 correct_entry(float2 g, float2 ch, float2 e, bool inm, bool inp, Edge edge,
+                                                int up, int v, double kx, double ky, const GeomDev& geo) {
     float br, bi;
-    if ((edm || edp) && inm && inp) {
-        // keep the rarely needed double-precision distances inside this branch (an
-        // empty asm makes the row index opaque, so nothing here is hoisted out of a
-        // caller's loop where it would hold registers)
-        int upo = up;
-        asm volatile("" : "+v"(upo));
-        float am = 1.f, apl = 1.f;
-        if (edm) am = edge_weight(shifted_r2(kx, ky, -1.0, upo, v, geo), geo);
-        if (edp) apl = edge_weight(shifted_r2(kx, ky, 1.0, upo, v, geo), geo);
-        br = (am - apl) * ch.x;
-        bi = (am + apl) * ch.y;
-        const float mag2 = fmaf(br, br, bi * bi);
-        const float inv = mag2 > 0.f ? __builtin_amdgcn_rsqf(mag2) : 0.f;
-        br *= inv;
-        bi *= inv;
-    } else if (inm && inp) {
-        br = 0.f;
-        bi = ch.y > 0.f ? 1.f : (ch.y < 0.f ? -1.f : 0.f);
+    if (inm && inp) {
+        bool edm, edp;
+        edge(edm, edp);
+        if (edm || edp) {
+            // keep the rarely needed double-precision distances inside this branch (an
+            // empty asm makes the row index opaque, so nothing here is hoisted out of a
+            // caller's loop where it would hold registers)
+            int upo = up;
+            asm volatile("" : "+v"(upo));
+            float am = 1.f, apl = 1.f;
+            if (edm) am = edge_weight(shifted_r2(kx, ky, -1.0, upo, v, geo), geo);
+            if (edp) apl = edge_weight(shifted_r2(kx, ky, 1.0, upo, v, geo), geo);
+            br = (am - apl) * ch.x;
+            bi = (am + apl) * ch.y;
+            const float mag2 = fmaf(br, br, bi * bi);
+            const float inv = mag2 > 0.f ? __builtin_amdgcn_rsqf(mag2) : 0.f;
+            br *= inv;
+            bi *= inv;
+        } else {
+            br = 0.f;
+            bi = ch.y > 0.f ? 1.f : (ch.y < 0.f ? -1.f : 0.f);
+        }
     } else {
         br = inm ? ch.x : -ch.x;
         bi = ch.y;
@@ -438,11 +444,13 @@ __device__ float2 correct_direct(float2 g, int up, int v, double kx, double ky, 
     const double rp = shifted_r2(kx, ky, 1.0, up, v, geo);
     const bool inm = rm < geo.hi2, inp = rp < geo.hi2;
     if (!inm && !inp) return make_float2(0.f, 0.f);
-    const bool edm = inm && !(geo.lo2 >= 0.0 && rm <= geo.lo2);
-    const bool edp = inp && !(geo.lo2 >= 0.0 && rp <= geo.lo2);
+    auto edge = [&](bool& edm, bool& edp) {
+        edm = !(geo.lo2 >= 0.0 && rm <= geo.lo2);
+        edp = !(geo.lo2 >= 0.0 && rp <= geo.lo2);
+    };
     const float2 ch = chi_phasor(fma(geo.qux, (double)up, geo.qvx * v), fma(geo.quy, (double)up, geo.qvy * v), m);
     const float2 e = cmul(phasor_rev_neg((double)up * beta), phasor_rev_neg((double)v * alpha));
-    return correct_entry(g, ch, e, inm, inp, edm, edp, up, v, kx, ky, geo);
+    return correct_entry(g, ch, e, inm, inp, edge, up, v, kx, ky, geo);
 }
 
 // Full-plane variant, the Nyquist lines of one BF pixel.  Correcting every entry of
@@ -687,16 +695,21 @@ __device__ __forceinline__ void pass1_tile(const float2* __restrict__ gsrc, cons
         // 2. correction into the LDS tile
         auto entry = [&](int i, float2 e) {
             const int u = ustart + i * RS;
-            float2 val = make_float2(0.f, 0.f);
+            // outside the support the predicated load left gv[i] zero, which is the stored value
+            float2 val = gv[i];
             bool inm, inp;
             if (flags(i, inm, inp)) {
                 const int up = (NYQ || RS > H) ? (u < H ? u : u - N) : (i < PM / 2 ? u : u - N);
-                const bool edm = inm && (unsigned)(up - flo_m) >= (unsigned)flen_m;
-                const bool edp = inp && (unsigned)(up - flo_p) >= (unsigned)flen_p;
+                auto edge = [&](bool& edm, bool& edp) {
+                    int uo = up;   // opaque: the tests stay in the branch that needs them
+                    asm volatile("" : "+v"(uo));
+                    edm = (unsigned)(uo - flo_m) >= (unsigned)flen_m;
+                    edp = (unsigned)(uo - flo_p) >= (unsigned)flen_p;
+                };
                 float2 ch;
                 if constexpr (CL) ch = trow[i * RS];
                 else ch = chv[i];
-                val = correct_entry(gv[i], ch, e, inm, inp, edm, edp, up, v, k.x, k.y, geo);
+                val = correct_entry(gv[i], ch, e, inm, inp, edge, up, v, k.x, k.y, geo);
             }
             trow[i * RS] = val;
         };
@@ -1399,9 +1412,13 @@ __global__ __launch_bounds__(obj_threads<N>()) void k_obj_sum(const float2* __re
             if (on_of(i, inm, inp)) {
                 const int u = ustart + i * ustep;
                 const int up = u < H ? u : u - N;
-                const bool edm = inm && (unsigned)(up - flo_m) >= (unsigned)flen_m;
-                const bool edp = inp && (unsigned)(up - flo_p) >= (unsigned)flen_p;
-                const float2 cv = correct_entry(gv[i], chv[i], e, inm, inp, edm, edp, up, v, k.x, k.y, geo);
+                auto edge = [&](bool& edm, bool& edp) {
+                    int uo = up;   // opaque: the tests stay in the branch that needs them
+                    asm volatile("" : "+v"(uo));
+                    edm = (unsigned)(uo - flo_m) >= (unsigned)flen_m;
+                    edp = (unsigned)(uo - flo_p) >= (unsigned)flen_p;
+                };
+                const float2 cv = correct_entry(gv[i], chv[i], e, inm, inp, edge, up, v, k.x, k.y, geo);
                 acc[i].x += cv.x;
                 acc[i].y += cv.y;
             }
