@@ -1049,8 +1049,8 @@ __global__ __launch_bounds__(256, (pass2_min_waves<N, FP>())) void k_pass2(const
             const float r0 = fmaf(sgn, av0.x, den0), i0 = sgn * av0.y;
             const float r1 = fmaf(sgn, av1.x, den1), i1 = sgn * av1.y;
             // Re O > 0 and |Im O| <= Re O for every sample of the wave: the [0, 1]
-            // polynomial of Im O / Re O with a reciprocal per sample (bitwise the
-            // general atan2 on those inputs); else the general atan2
+            // polynomial of Im O / Re O with a reciprocal per sample (the general
+            // atan2's phase bits on those inputs); else the general atan2
             bool easy = true;
 #pragma unroll
             for (int r = 0; r < R; ++r) {
@@ -1082,8 +1082,9 @@ __global__ __launch_bounds__(256, (pass2_min_waves<N, FP>())) void k_pass2(const
         } else {
             // Re O > 0 and |Im O| <= Re O for every sample of the wave: atan2 is the
             // odd polynomial of Im O / Re O, with one reciprocal per row (the real part
-            // depends on the pixel only through its parity).  Bitwise the same result
-            // as the general atan2 on those inputs.
+            // depends on the pixel only through its parity): the same phase bits as the
+            // general atan2 on those inputs (only the sums may round differently, where the
+            // compiler fuses the polynomial's last multiply into the accumulation).
             bool easy = den0 > 0.f && den1 > 0.f;
 #pragma unroll
             for (int r = 0; r < R; ++r) easy = easy && fabsf(x[r].x) <= den0 && fabsf(x[r].y) <= den1;
