@@ -886,19 +886,14 @@ struct RowPairRaw {
             d0[r] = load_or_zero(rp, od + r * RSTEP);
             d1[r] = load_or_zero(rp, od + r * RSTEP + kTileW * 8);
         }
-        const float2 zero = make_float2(0.f, 0.f);
-        h0 = zero;
-        h1 = zero;
-        if (ve > H) {
-            h0 = nyqc[y0];
-            h1 = nyqc[y0 + 1];
-        }
-        z0 = zero;
-        z1 = zero;
-        if (ve > 0) {
-            z0 = plane[tm_index(N, y0, 0)];
-            z1 = plane[tm_index(N, y0 + 1, 0)];
-        }
+        // the DC column (in the first tile: zero when ve = 0 leaves the resource empty)
+        // and the Nyquist column (a resource of N values only when ve > H; pass 1 did not
+        // write it otherwise), as predicated loads: no branch, no zeroing
+        z0 = load_or_zero(rp, (int)tm_index(N, y0, 0) * 8);
+        z1 = load_or_zero(rp, (int)tm_index(N, y0 + 1, 0) * 8);
+        const __amdgpu_buffer_rsrc_t rn = make_rsrc(nyqc, ve > H ? N * 8 : 0);
+        h0 = load_or_zero(rn, y0 * 8);
+        h1 = load_or_zero(rn, (y0 + 1) * 8);
     }
 
     // Mirrored columns w = N/2 - j - r L from the direct values already loaded: for
