@@ -34,6 +34,19 @@ def _say(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def _check_range(s1, s2, r1, r2, n, what):
+    """Moments of a BF range against the oracle's: S2 and the range's own loss (the formula
+    applied to each side's moments) within LOSS_RTOL, and no pixel of S1 off by more than
+    1e-4 sqrt(n) rad (a phase that crosses the branch cut at +-pi, an error of 2 pi, fails)."""
+    d = s1 - r1
+    lg, lr = O.loss_from_moments(s1, s2, n), O.loss_from_moments(r1, r2, n)
+    rms, mx = float(np.sqrt(np.mean(d * d))), float(np.max(np.abs(d)))
+    _say(f"{what}: S1 error rms {rms:.2e} max {mx:.2e}; loss rel error {abs(lg - lr) / abs(lr):.2e}")
+    assert abs(s2 - r2) <= LOSS_RTOL * abs(r2), what
+    assert abs(lg - lr) <= LOSS_RTOL * abs(lr), what
+    assert mx <= 1e-4 * n ** 0.5, what
+
+
 @pytest.fixture(scope="module")
 def full():
     import torch
@@ -147,9 +160,7 @@ def test_full_moments_sampled(full, b0, b1):
     for params in (TRUE, [-137.0, 16.5, 2.7]):
         s1, s2 = _moments(h, 512, params, b0, b1)
         r1, r2 = O.bf_moments(og, _host(counts, b0, b1), params, dc, list(range(b0, b1)))
-        assert abs(s2 - r2) <= LOSS_RTOL * abs(r2), (b0, params)
-        d = s1 - r1
-        assert np.sqrt(np.mean(d * d)) <= 2e-5 * (b1 - b0) and np.max(np.abs(d)) <= 1e-3, (b0, params)
+        _check_range(s1, s2, r1, r2, b1 - b0, f"BF {b0}..{b1} at {params}")
 
 
 def test_full_loss_is_formula_of_moments(full):
@@ -252,9 +263,7 @@ def test_full_plane_variant_moments_sampled(full, b0, b1):
     finally:
         ssb.ssb_set_variant(h, ssb.SSB_VARIANT_HALF_PLANE)
     r1, r2 = O.bf_moments_full_plane(og, _host(counts, b0, b1), params, dc, list(range(b0, b1)))
-    assert abs(s2 - r2) <= LOSS_RTOL * abs(r2), b0
-    d = s1 - r1
-    assert np.sqrt(np.mean(d * d)) <= 2e-5 * (b1 - b0) and np.max(np.abs(d)) <= 1e-3, b0
+    _check_range(s1, s2, r1, r2, b1 - b0, f"full plane BF {b0}..{b1}")
 
 
 def test_full_fit_trials_sampled(full):
@@ -270,7 +279,6 @@ def test_full_fit_trials_sampled(full):
     for k in range(8):
         s1, s2 = _moments(h, 512, trials[k], 4450, 4493)
         r1, r2 = O.bf_moments(og, host, trials[k], dc, list(range(4450, 4493)))
-        assert abs(s2 - r2) <= LOSS_RTOL * abs(r2), k
-        assert np.sqrt(np.mean((s1 - r1) ** 2)) <= 2e-5 * 43, k
+        _check_range(s1, s2, r1, r2, 43, f"trial {k}")
     batch = ssb.ssb_loss(h, trials)
     assert ssb.ssb_loss(h, trials[5:6])[0] == batch[5]

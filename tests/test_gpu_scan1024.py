@@ -30,6 +30,19 @@ N = 1024
 def _say(msg):
     print(msg, file=sys.stderr, flush=True)
 
+def _check_range(s1, s2, r1, r2, n, what):
+    """Moments of a BF range against the oracle's: S2 and the range's own loss (the formula
+    applied to each side's moments) within LOSS_RTOL, and no pixel of S1 off by more than
+    1e-4 sqrt(n) rad (a phase that crosses the branch cut at +-pi, an error of 2 pi, fails)."""
+    d = s1 - r1
+    lg, lr = O.loss_from_moments(s1, s2, n), O.loss_from_moments(r1, r2, n)
+    rms, mx = float(np.sqrt(np.mean(d * d))), float(np.max(np.abs(d)))
+    _say(f"{what}: S1 error rms {rms:.2e} max {mx:.2e}; loss rel error {abs(lg - lr) / abs(lr):.2e}")
+    assert abs(s2 - r2) <= LOSS_RTOL * abs(r2), what
+    assert abs(lg - lr) <= LOSS_RTOL * abs(lr), what
+    assert mx <= 1e-4 * n ** 0.5, what
+
+
 
 @pytest.fixture(scope="module")
 def full1024():
@@ -96,9 +109,7 @@ def test_1024_moments_sampled(full1024, b0, b1, params):
     _say(f"[scan1024] moments BF {b0}..{b1} at {params}")
     s1, s2 = _moments(h, params, b0, b1)
     r1, r2 = O.bf_moments(og, _host(counts, b0, b1), params, dc, list(range(b0, b1)))
-    assert abs(s2 - r2) <= LOSS_RTOL * abs(r2), (b0, params)
-    d = s1 - r1
-    assert np.sqrt(np.mean(d * d)) <= 2e-5 * (b1 - b0) and np.max(np.abs(d)) <= 1e-3, (b0, params)
+    _check_range(s1, s2, r1, r2, b1 - b0, f"[scan1024] BF {b0}..{b1} at {params}")
 
 
 def test_1024_loss_is_formula_of_moments(full1024):
@@ -169,9 +180,7 @@ def test_1024_full_plane_variant_moments(full1024):
         ssb.ssb_set_variant(h, ssb.SSB_VARIANT_HALF_PLANE)
     assert single == batch[1]
     r1, r2 = O.bf_moments_full_plane(og, _host(counts, 8896, 8937), params, dc, list(range(8896, 8937)))
-    assert abs(s2 - r2) <= LOSS_RTOL * abs(r2)
-    d = s1 - r1
-    assert np.sqrt(np.mean(d * d)) <= 2e-5 * 41 and np.max(np.abs(d)) <= 1e-3
+    _check_range(s1, s2, r1, r2, 41, "[scan1024] full plane BF 8896..8937")
 
 
 def test_1024_subdisk_full_plane_loss_and_object(subdisk1024):
