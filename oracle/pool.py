@@ -20,6 +20,7 @@ from __future__ import annotations
 import multiprocessing as mp
 import os
 import shutil
+import sys
 import tempfile
 
 import numpy as np
@@ -62,6 +63,12 @@ class OraclePool:
 
     def __init__(self, counts, shape=None, workers: int | None = None, chunk_bf: int = 1024,
                  dirpath: str | None = None):
+        # spawned workers re-import the main program by its path: a program read from stdin
+        # has none, and its workers would fail at start-up while the pool respawns them
+        main_file = getattr(sys.modules.get("__main__"), "__file__", None)
+        if main_file is not None and not os.path.exists(main_file):
+            raise RuntimeError(f"OraclePool: the main program ({main_file}) must be a file the "
+                               "worker processes can import")
         if shape is None:
             shape = counts.shape
         self.shape = tuple(int(v) for v in shape)

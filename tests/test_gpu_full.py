@@ -220,8 +220,9 @@ def test_n512_subdisk_loss_and_object(subdisk):
 
 
 def test_medium_loss_and_object():
-    """Medium workload: eight seeded trials of its batch in one call against the pooled
-    oracle, single-trial calls equal to the batch bitwise, and the object."""
+    """Medium workload: its whole 200-trial batch and the true parameters in one call, every
+    trial against the pooled oracle, single-trial calls equal to the batch bitwise, and the
+    object."""
     import torch
     w = WORKLOADS["medium"]
     counts = make_counts_torch(w, torch.device("cuda:0"))
@@ -230,14 +231,20 @@ def test_medium_loss_and_object():
         host = counts.cpu().numpy().view(np.uint32)
         og = O.OGeom.from_any(w.geometry)
         dc = O.dc_value(host)
-        trials = np.concatenate([np.array([TRUE], np.float32), trial_params(w, 7)])
+        trials = np.concatenate([np.array([TRUE], np.float32), trial_params(w)])
+        assert trials.shape == (201, 3)
         got = ssb.ssb_loss(h, trials)
-        _say("[medium] pooled oracle, 8 trials")
+        _say("[medium] pooled oracle, 201 trials")
+        worst = 0.0
         with OraclePool(host) as pool:
             for k in range(len(trials)):
                 ref = pool.loss(og, trials[k], dc)
+                worst = max(worst, abs(got[k] - ref) / abs(ref))
                 assert abs(got[k] - ref) <= LOSS_RTOL * abs(ref), (k, got[k], ref)
-        for k in (0, 5):
+                if k % 50 == 0:
+                    _say(f"[medium]   trial {k}: largest relative difference so far {worst:.2e}")
+        _say(f"[medium] 201 trials: largest relative loss difference {worst:.2e}")
+        for k in (0, 5, 200):
             assert ssb.ssb_loss(h, trials[k:k + 1])[0] == got[k]
         phase = torch.full((256, 256), float("nan"), dtype=torch.float32, device="cuda")
         ssb.ssb_object(h, TRUE, phase)

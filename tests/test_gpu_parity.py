@@ -207,17 +207,23 @@ def test_loss_small_batch(small):
 
 
 def test_loss_small_200_trial_batch(small):
-    """The small workload's whole 200-trial batch in one call; every 4th trial (50, spread
-    over the batch) against the oracle, and two of them again as single-trial calls."""
+    """The small workload's whole 200-trial batch in one call, every trial against the
+    oracle (run over BF ranges in a process pool), and two of them again as single-trial
+    calls."""
+    from oracle.pool import OraclePool
     w, counts, p = small
     g = O.OGeom.from_any(w.geometry)
     dc = O.dc_value(counts)
     params = trial_params(w)
     assert params.shape == (200, 3)
     got = p.loss(params)
-    for k in range(0, 200, 4):
-        ref = O.loss(g, counts, params[k], dc)
-        assert _rel(got[k], ref) <= LOSS_RTOL, (k, got[k], ref)
+    worst = 0.0
+    with OraclePool(counts) as pool:
+        for k in range(200):
+            ref = pool.loss(g, params[k], dc)
+            worst = max(worst, _rel(got[k], ref))
+            assert _rel(got[k], ref) <= LOSS_RTOL, (k, got[k], ref)
+    _say(f"[small] 200 trials: largest relative loss difference {worst:.2e}")
     for k in (3, 199):
         assert p.loss(params[k:k + 1])[0] == got[k]
 
