@@ -316,10 +316,13 @@ int reserve(ssb_handle* h, int max_trials) {
 
 // Phase moments of n_trials trials over BF [b_begin, b_end): leaves S1 (double
 // [t][N][N]) and S2 (double [t]) in the workspace ws laid out by pl.
-// staged: the trial constants go through a host copy in the handle (h->htc), which
-// must outlive the stream's use of it (the caller synchronizes before returning);
-// otherwise they are passed to a small kernel by value (no host buffer, nothing
-// allocated, no stage timers).
+// staged: stage timers run, and batches of more than kTrialBlock trials send their
+// constants through a host copy in the handle (h->htc), which must outlive the
+// stream's use of it (the caller synchronizes before returning).  Otherwise, and for
+// smaller batches in any case, the constants are passed to a small kernel by value (a
+// pageable host-to-device copy of a few hundred bytes held the host for about 50 us
+// per evaluation; nothing allocated).  The first chunk's accumulation writes S1 and S2
+// outright, so they need no clearing launch.
 int run_moments(ssb_handle* h, char* ws, const LossPlan& pl, const float* params, int n_trials, int64_t b_begin,
                 int64_t b_end, hipStream_t st, bool staged) {
     std::vector<TrialConst>& htc = h->htc;
@@ -336,7 +339,7 @@ int run_moments(ssb_handle* h, char* ws, const LossPlan& pl, const float* params
     float2* nyq_a = fp ? reinterpret_cast<float2*>(ws + pl.off_na) : nullptr;
     float2* nyq_b = fp ? reinterpret_cast<float2*>(ws + pl.off_nb) : nullptr;
 
-    if (staged) {
+    if (staged && n_trials > kTrialBlock) {
         if ((size_t)n_trials > htc.capacity()) {      // beyond the reservation: the one host allocation
             try {
                 htc.reserve((size_t)n_trials);
@@ -358,8 +361,10 @@ int run_moments(ssb_handle* h, char* ws, const LossPlan& pl, const float* params
     }
     {
         StageTimer tm(h, SSB_STAGE_REDUCE, st, 0, staged);
-        SSB_HIP(launch_fill(s1, (int64_t)n_trials * h->n * h->n, st), "clear S1");
-        SSB_HIP(launch_fill(s2, n_trials, st), "clear S2");
+        if (b_begin >= b_end) {                       // no chunk below writes the sums
+            SSB_HIP(launch_fill(s1, (int64_t)n_trials * h->n * h->n, st), "clear S1");
+            SSB_HIP(launch_fill(s2, n_trials, st), "clear S2");
+        }
         SSB_HIP(launch_chiq(h->n, tc, n_trials, h->geo, chm, chn, st), "phase table launch");
     }
 
@@ -385,7 +390,8 @@ int run_moments(ssb_handle* h, char* ws, const LossPlan& pl, const float* params
         }
         {
             StageTimer tm(h, SSB_STAGE_REDUCE, st, 0, staged);
-            SSB_HIP(launch_accum(h->n, ps1, ps2, pl.gcap, ng, n_trials, s1, s2, st), "accumulate launch");
+            SSB_HIP(launch_accum(h->n, ps1, ps2, pl.gcap, ng, n_trials, s1, s2, c0 == b_begin, st),
+                    "accumulate launch");
         }
     }
     return SSB_OK;

@@ -96,7 +96,7 @@ hipError_t launch_support(int n, const double2* kb, const uint8_t* active, GeomD
 int pass1_tile(int n);
 int pass2_row_blocks(int n);
 hipError_t launch_accum(int n, const float* part_s1, const double* part_s2, int gcap, int ng,
-                        int n_trials, double* s1run, double* s2run, hipStream_t st);
+                        int n_trials, double* s1run, double* s2run, bool first, hipStream_t st);
 hipError_t launch_fill(double* p, int64_t count, hipStream_t st);
 int loss_blocks();
 hipError_t launch_loss(int n, const double* s1run, const double* s2run, int n_trials, double n_bf,

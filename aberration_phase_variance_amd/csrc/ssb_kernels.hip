@@ -1122,12 +1122,13 @@ __global__ __launch_bounds__(256, (pass2_min_waves<N, FP>())) void k_pass2(const
 }
 
 // S1run[t][p] += sum over groups g (in order) of part_s1[t][g][p], in double.
+// first: the range's first chunk, whose sums start from zero (no clearing launch)
 __global__ __launch_bounds__(256) void k_accum_s1(const float* __restrict__ part, int gcap, int ng,
-                                                  int64_t n2, double* __restrict__ s1run) {
+                                                  int64_t n2, double* __restrict__ s1run, int first) {
     const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int t = blockIdx.y;
     if (p >= n2) return;
-    double acc = s1run[t * n2 + p];
+    double acc = first ? 0.0 : s1run[t * n2 + p];
     const float* src = part + (int64_t)t * gcap * n2 + p;
     // groups added in order; the loads of 8 groups are issued together
     int g = 0;
@@ -1146,11 +1147,11 @@ __global__ __launch_bounds__(256) void k_accum_s1(const float* __restrict__ part
 // thread per group forms its group's sum; one thread then adds the group sums in
 // group order.  Independent of how groups are chunked.
 __global__ __launch_bounds__(256) void k_accum_s2(const double* __restrict__ part, int gcap, int ng, int rb,
-                                                  double* __restrict__ s2run) {
+                                                  double* __restrict__ s2run, int first) {
     __shared__ double gs[256];
     const int t = blockIdx.x;
     double run = 0.0;
-    if (threadIdx.x == 0) run = s2run[t];
+    if (threadIdx.x == 0 && !first) run = s2run[t];
     for (int g0 = 0; g0 < ng; g0 += 256) {
         const int g = g0 + threadIdx.x;
         double v = 0.0;
@@ -1806,13 +1807,14 @@ hipError_t launch_support(int n, const double2* kb, const uint8_t* active, GeomD
 int pass1_tile(int n) { return kTileW; }     // pass 1 writes whole layout tiles
 
 hipError_t launch_accum(int n, const float* part_s1, const double* part_s2, int gcap, int ng, int n_trials,
-                        double* s1run, double* s2run, hipStream_t st) {
+                        double* s1run, double* s2run, bool first, hipStream_t st) {
     const int64_t n2 = (int64_t)n * n;
     hipLaunchKernelGGL(k_accum_s1, dim3((unsigned)((n2 + 255) / 256), n_trials), dim3(256), 0, st, part_s1, gcap,
-                       ng, n2, s1run);
+                       ng, n2, s1run, (int)first);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_accum_s2, dim3(n_trials), dim3(256), 0, st, part_s2, gcap, ng, pass2_row_blocks(n), s2run);
+    hipLaunchKernelGGL(k_accum_s2, dim3(n_trials), dim3(256), 0, st, part_s2, gcap, ng, pass2_row_blocks(n), s2run,
+                       (int)first);
     return hipGetLastError();
 }
 
