@@ -75,7 +75,7 @@ namespace {
 #define SSB_PASS2_MIN_WAVES_1024 4 // the same at N = 1024 (LDS also allows 4 workgroups per CU)
 #endif
 #ifndef SSB_PASS2_MIN_WAVES
-#define SSB_PASS2_MIN_WAVES 6 // pass-2 register budget (N <= 512, half plane): resident waves per SIMD
+#define SSB_PASS2_MIN_WAVES 7 // pass-2 register budget (N <= 512, half plane): resident waves per SIMD
 #endif
 
 // columns per column-pass tile (LDS: kTC x (N + 1) complex values)
@@ -954,8 +954,10 @@ struct RowPairRaw {
 // FP: the full-plane variant; each BF pixel's object gains (-1)^x A(y) + (-1)^y B(x)
 // from na, nb [t][cap][N] (k_nyq_lines), so the real part varies along a row: the
 // wave test and the reciprocal of the atan2 fast path are per sample.
-// Register budget: 80 VGPRs (6 waves per SIMD) fit the half-plane row pass up to
-// N = 512 without spills (measured 2.07 ms against 2.19 ms at 82 VGPRs, 5 waves);
+// Register budget: 72 VGPRs (7 waves per SIMD, which is also what the LDS allows: seven
+// 22.5 KB workgroups per CU) fit the half-plane row pass up to N = 512 without spills
+// (1.908 -> 1.880 ms against 78 VGPRs and 6 waves; earlier 2.07 against 2.19 ms for 6
+// against 5 waves);
 // 128 (4 waves) at N = 1024 (2.85 against 3.26 ms at 136, 3 waves); the
 // full-plane forms keep the compiler's choice.
 template <int N, bool FP>
