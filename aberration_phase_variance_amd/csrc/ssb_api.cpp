@@ -100,6 +100,10 @@ struct ssb_handle {
     int reserved_trials = 0;
     // host staging of the per-trial constants (capacity = reserved trials)
     std::vector<TrialConst> htc;
+    // pinned host landing area for the losses of up to hres_cap trials (the copy back
+    // then needs no staging through a pageable buffer)
+    double* hres = nullptr;
+    int hres_cap = 0;
     // device address of the no-allocation scratch on this handle's device
     char* scratch = nullptr;
     // host copy of the active flags, prefix counts for range queries
@@ -310,6 +314,15 @@ int reserve(ssb_handle* h, int max_trials) {
     } catch (...) {
         return fail(SSB_ENOMEM, "host staging of %d trial constants", max_trials);
     }
+    const int cap = std::max(max_trials, kTrialBlock);
+    if (cap > h->hres_cap) {
+        double* p = nullptr;
+        if (hipHostMalloc(reinterpret_cast<void**>(&p), sizeof(double) * cap, hipHostMallocDefault) != hipSuccess)
+            return fail(SSB_ENOMEM, "pinned host buffer for %d losses", cap);
+        if (h->hres) (void)hipHostFree(h->hres);
+        h->hres = p;
+        h->hres_cap = cap;
+    }
     h->reserved_trials = std::max(h->reserved_trials, max_trials);
     return SSB_OK;
 }
@@ -319,10 +332,10 @@ int reserve(ssb_handle* h, int max_trials) {
 // staged: stage timers run, and batches of more than kTrialBlock trials send their
 // constants through a host copy in the handle (h->htc), which must outlive the
 // stream's use of it (the caller synchronizes before returning).  Otherwise, and for
-// smaller batches in any case, the constants are passed to a small kernel by value (a
-// pageable host-to-device copy of a few hundred bytes held the host for about 50 us
-// per evaluation; nothing allocated).  The first chunk's accumulation writes S1 and S2
-// outright, so they need no clearing launch.
+// smaller batches in any case, the constants are passed to a small kernel by value (one
+// launch instead of a staged pageable copy; nothing allocated).  The first chunk's
+// accumulation writes S1 and S2 outright, so they need no clearing launch (with the
+// previous change, about 0.015 ms per evaluation).
 int run_moments(ssb_handle* h, char* ws, const LossPlan& pl, const float* params, int n_trials, int64_t b_begin,
                 int64_t b_end, hipStream_t st, bool staged) {
     std::vector<TrialConst>& htc = h->htc;
@@ -414,8 +427,14 @@ int run_loss(ssb_handle* h, char* ws, const LossPlan& pl, const float* params, i
         StageTimer tm(h, SSB_STAGE_REDUCE, st, 0, staged);
         SSB_HIP(launch_loss(h->n, s1, s2, n_trials, (double)h->n_bf, lp, dl, mean_phase, st), "loss launch");
     }
-    SSB_HIP(hipMemcpyAsync(losses, dl, sizeof(double) * n_trials, hipMemcpyDeviceToHost, st), "copy losses");
-    SSB_HIP(hipStreamSynchronize(st), "loss");
+    if (n_trials <= h->hres_cap) {
+        SSB_HIP(hipMemcpyAsync(h->hres, dl, sizeof(double) * n_trials, hipMemcpyDeviceToHost, st), "copy losses");
+        SSB_HIP(hipStreamSynchronize(st), "loss");
+        std::memcpy(losses, h->hres, sizeof(double) * n_trials);
+    } else {
+        SSB_HIP(hipMemcpyAsync(losses, dl, sizeof(double) * n_trials, hipMemcpyDeviceToHost, st), "copy losses");
+        SSB_HIP(hipStreamSynchronize(st), "loss");
+    }
     return SSB_OK;
 }
 
@@ -799,6 +818,7 @@ void ssb_release(ssb_handle* h) {
     (void)hipFree(h->tw);
     (void)hipFree(h->ws);
     (void)hipFree(h->ows);
+    if (h->hres) (void)hipHostFree(h->hres);
     for (auto& r : h->prof_pending) {
         (void)hipEventSynchronize(r.b);
         (void)hipEventDestroy(r.a);

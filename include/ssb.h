@@ -158,9 +158,10 @@ int ssb_loss_noalloc(ssb_handle* h, const float* params, int32_t n_trials, doubl
                      float* mean_phase, void* stream);
 
 /*
- * ssb_reserve: size the handle's device workspace and host staging for loss calls
- * of up to max_trials trials (any BF range, either variant, any chunk cap), so
- * that such calls, and ssb_moments and ssb_object, allocate nothing afterwards.
+ * ssb_reserve: size the handle's device workspace, host staging and pinned host
+ * landing area for the losses (at least 16 trials) for loss calls of up to max_trials
+ * trials (any BF range, either variant, any chunk cap), so that such calls, and
+ * ssb_moments and ssb_object, allocate nothing afterwards.
  * ssb_prepare reserves one trial.  Reservations only grow.  Errors: SSB_EINVAL
  * (bad handle, max_trials outside [1, 65535]), SSB_ENOMEM, SSB_EDEVICE.
  */
