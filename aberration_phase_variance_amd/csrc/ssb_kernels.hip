@@ -778,11 +778,13 @@ __device__ __forceinline__ void pass1_tile(const float2* __restrict__ gsrc, cons
 
         // 4. store (out: the layout tile's block of the column-result plane, or the Nyquist column)
         float2* ot = out + tt * out_step;
-        if constexpr (!NYQ && TC == 8 && pass1_swz<N>()) {
+        if constexpr (!NYQ && TC == 8) {
             // 16 bytes per lane: lane (row y, column pair cp) stores columns 2cp and 2cp + 1
             // of row y.  Half the store instructions of one column per lane: the vector-memory
             // address path (its queue is full about a sixth of the time in this kernel), not
-            // the bytes, is what the instruction count costs (pass 1 2.53 -> 2.41 ms)
+            // the bytes, is what the instruction count costs (pass 1 2.53 -> 2.41 ms; at
+            // 1024^2, where the padded tile leaves some 2-way bank conflicts in these reads,
+            // 11.47 -> 10.97 ms)
             constexpr int RS2 = NT / 4;
             const int cp = tid & 3, c0 = 2 * cp, c1 = 2 * cp + 1;
             float2* om = ot + csub + c0;
