@@ -191,6 +191,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 __device__ __forceinline__ float2 load_or_zero(__amdgpu_buffer_rsrc_t r, int off) {
     return __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
 }
+// 16 bytes (two complex values) or zeros, like load_or_zero.
+__device__ __forceinline__ float4 load4_or_zero(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
 // The same with the non-temporal cache policy (aux bit 1): for data read once per
 // evaluation (the spectra in pass 1: 3.29 -> 3.22 ms).  Not for the row pass's
 // loads: rows y0 and y0 + 1 of a tile share lines that other waves read too
@@ -776,37 +780,59 @@ __device__ __forceinline__ void pass1_tile(const float2* __restrict__ gsrc, cons
         }
         __syncthreads();
 
-        // 4. store (out: the layout tile's block of the column-result plane, or the Nyquist column)
+        // 4. store, in the row pass's form (out: the layout tile's block of the column-result
+        // plane, or the Nyquist column).  The row pass transforms rows y0 = 2p and y0 + 1
+        // together as Z(v) = B0(v) + i B1(v), B_k = -i C(y_k, v) (C: the column results),
+        // extended Hermitian; both Z(v) = (C0.y + C1.x, C1.y - C0.x) and
+        // Z(N - v) = (C0.y - C1.x, C0.x + C1.y) come from the same two values, so they are
+        // formed here, where vector issue has room, and stored as one 16-byte unit
+        // [Z(v), Z(N - v)] per row pair and column (the pair's two 64-byte rows hold its
+        // 8 columns' units).  At v = 0 the unit is [(C0.y, C1.y), (C0.x, C1.x)]: the
+        // transform takes only the imaginary parts there, and the real parts are the
+        // object's real part along the two rows.  The Nyquist column's unit per row pair is
+        // [(C0.y, C1.y), (C0.x, C1.x)] in the same way.  Bitwise the sums the row pass formed
+        // itself; the row pass loses its assembly arithmetic, half its cross-lane permutes
+        // and two of its loads per BF pixel (pass 2 1.88-1.92 -> 1.73-1.77 ms, pass 1
+        // 2.40 -> 2.45 ms, 4.44-4.55 -> 4.33 ms per evaluation in one run).
         float2* ot = out + tt * out_step;
         if constexpr (!NYQ && TC == 8) {
-            // 16 bytes per lane: lane (row y, column pair cp) stores columns 2cp and 2cp + 1
-            // of row y.  Half the store instructions of one column per lane: the vector-memory
-            // address path (its queue is full about a sixth of the time in this kernel), not
-            // the bytes, is what the instruction count costs (pass 1 2.53 -> 2.41 ms; at
-            // 1024^2, where the padded tile leaves some 2-way bank conflicts in these reads,
-            // 11.47 -> 10.97 ms)
-            constexpr int RS2 = NT / 4;
-            const int cp = tid & 3, c0 = 2 * cp, c1 = 2 * cp + 1;
-            float2* om = ot + csub + c0;
-#pragma unroll 4
-            for (int y = tid >> 2; y < N; y += RS2) {
-                const float2 a = tile[c0 * LD + pass1_row<N>(c0, y)];
-                const float2 b = tile[c1 * LD + pass1_row<N>(c1, y)];
-                if constexpr (STREAM) store2_nt(om + (int64_t)y * kTileW, a, b);
-                else store2(om + (int64_t)y * kTileW, a, b);
-            }
+            // unit q = (p, c) = (q / 8, q % 8): 16 bytes per lane, 8 lanes per 128-byte row
+            // pair, at 2 q values into the tile's block; rows 2p and 2p + 1 of a column are
+            // adjacent LDS slots (the swizzle leaves bit 0 alone, and steps of NT / 4 rows
+            // leave it as it is).  The DC form only in the first tile (a uniform branch).
+            constexpr int UNITS = (N / 2) * TC;
+            constexpr int KU = (UNITS + NT - 1) / NT;
+            static_assert(UNITS % NT == 0 || KU == 1, "whole sweeps, or one partial sweep");
+            static_assert((NT / 4) % 16 == 0 || !pass1_swz<N>(), "row steps leave the swizzled bits alone");
+            const int cc = tid & 7;
+            const float2* src = tile + cc * LD + pass1_row<N>(cc, 2 * (tid >> 3));
+            float2* dst = ot + csub + 2 * tid;
+            auto sweep = [&](auto dcv) {
+                constexpr bool DC = decltype(dcv)::value;
+#pragma unroll
+                for (int k = 0; k < KU; ++k) {
+                    if (UNITS % NT != 0 && tid + k * NT >= UNITS) break;
+                    const float2 c0 = src[k * (NT / 4)], c1 = src[k * (NT / 4) + 1];
+                    float2 zs = make_float2(c0.y + c1.x, c1.y - c0.x);
+                    float2 zm = make_float2(c0.y - c1.x, c0.x + c1.y);
+                    if (DC && cc == 0) {
+                        zs = make_float2(c0.y, c1.y);
+                        zm = make_float2(c0.x, c1.x);
+                    }
+                    if constexpr (STREAM) store2_nt(dst + 2 * k * NT, zs, zm);
+                    else store2(dst + 2 * k * NT, zs, zm);
+                }
+            };
+            if (v0 == 0) sweep(std::true_type{});
+            else sweep(std::false_type{});
         } else if (!NYQ) {
-            float2* om = ot + csub + c;
-            const float2* tcol = tile + c * LD + pass1_row<N>(c, ustart);
-#pragma unroll 4
-            for (int y = ustart; y < N; y += RS) {
-                if constexpr (STREAM) store_nt(om + (int64_t)y * kTileW, tcol[y - ustart]);
-                else om[(int64_t)y * kTileW] = tcol[y - ustart];
-            }
+            static_assert(NYQ || TC == 8, "main tiles are whole layout tiles");
         } else {
-            for (int y = tid; y < N; y += NT) {
-                if constexpr (STREAM) store_nt(ot + y, tile[y]);
-                else ot[y] = tile[y];
+            for (int pr = tid; pr < N / 2; pr += NT) {
+                const float2 c0 = tile[2 * pr], c1 = tile[2 * pr + 1];
+                const float2 zs = make_float2(c0.y, c1.y), zm = make_float2(c0.x, c1.x);
+                if constexpr (STREAM) store2_nt(ot + 2 * pr, zs, zm);
+                else store2(ot + 2 * pr, zs, zm);
             }
         }
     }
@@ -888,6 +914,8 @@ __global__ __launch_bounds__(pass1_threads<N>(), (pass1_min_waves<N, TB>())) voi
 // Raw column-pass values a row pair needs: lane j gets v = j + r L for r < R/2
 // (direct, loaded) and the mirrored w = N - v for r >= R/2 (permuted from other
 // lanes' direct values), plus the v = 0 and v = N/2 entries of both rows.
+// (The object's row transform reads its column results in this raw form; the row pass
+// reads pass 1's row-pair form, RowPairUnits below.)
 template <int N, int R, int L>
 struct RowPairRaw {
     float2 d0[R / 2], d1[R / 2], m0[R / 2], m1[R / 2];
@@ -976,6 +1004,59 @@ struct RowPairRaw {
     }
 };
 
+// The row pass's inputs in pass 1's row-pair form: per row pair and column v a 16-byte
+// unit [Z(v), Z(N - v)] (Z as in RowPairRaw::assemble, formed by pass 1), at v = 0
+// [Z(0), (Re C(y0, 0), Re C(y0 + 1, 0))], and per row pair of the Nyquist column
+// [Z(N/2), (Re C(y0, N/2), Re C(y0 + 1, N/2))].  Lane j loads its direct units; its
+// mirrored values Z(N - w) come from lane L - j's units (for j = 0 from its own, and
+// the Nyquist unit at v = N/2).  Bitwise the values RowPairRaw assembles.
+template <int N, int R, int L>
+struct RowPairUnits {
+    float4 u[R / 2];
+    float2 m[R / 2];
+    float4 hn;        // the Nyquist unit
+    float2 zr;        // real parts of the DC column on rows y0, y0 + 1
+
+    __device__ __forceinline__ void load(const float2* plane, const float2* nyqc, int y0, int j, int ve) {
+        constexpr int H = N / 2;
+        static_assert(L % kTileW == 0, "a lane group spans whole tiles");
+        constexpr int TILE = N * kTileW * 8;
+        constexpr int RSTEP = (L / kTileW) * TILE;
+        const int ntile = min((ve + kTileW - 1) / kTileW, H / kTileW);
+        const __amdgpu_buffer_rsrc_t rp = make_rsrc(plane, ntile * TILE);
+        // unit (y0 / 2, j): the pair's 128 bytes at row y0 of the layout tile, 16 bytes
+        // per column
+        int od = (int)tm_index(N, y0, j) * 8 + (j % kTileW) * 8;
+        asm volatile("" : "+v"(od));
+#pragma unroll
+        for (int r = 0; r < R / 2; ++r) u[r] = load4_or_zero(rp, od + r * RSTEP);
+        zr = load_or_zero(rp, y0 * (kTileW * 8) + 8);
+        const __amdgpu_buffer_rsrc_t rn = make_rsrc(nyqc, ve > H ? N * 8 : 0);
+        hn = load4_or_zero(rn, y0 * 8);
+    }
+
+    __device__ __forceinline__ void assemble(int j, float2 (&x)[R]) {
+        const int lane = (int)threadIdx.x & 63;
+        const int addr = (lane - j + ((L - j) & (L - 1))) * 4;
+#pragma unroll
+        for (int r = 0; r < R / 2; ++r) {
+            const int rs = R / 2 - 1 - r;
+            m[r].x = __int_as_float(__builtin_amdgcn_ds_bpermute(addr, __float_as_int(u[rs].z)));
+            m[r].y = __int_as_float(__builtin_amdgcn_ds_bpermute(addr, __float_as_int(u[rs].w)));
+        }
+#pragma unroll
+        for (int r = 0; r < R / 2; ++r) {
+            x[r] = make_float2(u[r].x, u[r].y);
+            if (r == 0) x[R / 2] = j == 0 ? make_float2(hn.x, hn.y) : m[0];
+            else x[r + R / 2] = j == 0 ? make_float2(u[R / 2 - r].z, u[R / 2 - r].w) : m[r];
+        }
+    }
+    __device__ __forceinline__ float dc_re0() const { return zr.x; }
+    __device__ __forceinline__ float dc_re1() const { return zr.y; }
+    __device__ __forceinline__ float ny_re0() const { return hn.z; }
+    __device__ __forceinline__ float ny_re1() const { return hn.w; }
+};
+
 // Pass 2: one workgroup = 4*W row pairs x one 32-BF group x one trial.  Loops
 // over the group's BF pixels in order, accumulating per-pixel phase sums in
 // registers (float) and the squared phase (double per lane).  (Loading the next
@@ -1039,7 +1120,7 @@ __global__ __launch_bounds__(256, (pass2_min_waves<N, FP>())) void k_pass2(const
     auto plane_ptr = [&](int b) { return im + ((int64_t)t * cap + b) * N * H; };
     auto nyq_ptr = [&](int b) { return in + ((int64_t)t * cap + b) * N; };
 
-    RowPairRaw<N, R, L> cur;
+    RowPairUnits<N, R, L> cur;
     int b = next_active(b_lo);
 
     F fft;
@@ -1068,8 +1149,8 @@ __global__ __launch_bounds__(256, (pass2_min_waves<N, FP>())) void k_pass2(const
             for (int r = 0; r < R; ++r) bv[r] = nb[o + j + r * L];
         }
         fft.run(x, buf[grp], j, twt);
-        const float den0 = dcf + cur.z0.x + sgn * cur.h0.x;
-        const float den1 = dcf + cur.z1.x + sgn * cur.h1.x;
+        const float den0 = dcf + cur.dc_re0() + sgn * cur.ny_re0();
+        const float den1 = dcf + cur.dc_re1() + sgn * cur.ny_re1();
         float p2 = 0.f;
         if constexpr (FP) {
             // rows y0 (even: (-1)^y = +1) and y0 + 1 (odd: -1)
