@@ -1193,10 +1193,20 @@ __global__ __launch_bounds__(256, (pass2_min_waves<N, FP>())) void k_pass2(const
             // depends on the pixel only through its parity): the same phase bits as the
             // general atan2 on those inputs (only the sums may round differently, where the
             // compiler fuses the polynomial's last multiply into the accumulation).
-            bool easy = den0 > 0.f && den1 > 0.f;
+            // The test takes each row's largest |Im O| (three-input maxima) against its real
+            // part, and the four tests' lane masks are combined in scalar registers: six
+            // vector instructions fewer per BF pixel than a compare per sample (a NaN sample
+            // makes the sums NaN on either path).
+            float ma = fabsf(x[0].x), mb = fabsf(x[0].y);
 #pragma unroll
-            for (int r = 0; r < R; ++r) easy = easy && fabsf(x[r].x) <= den0 && fabsf(x[r].y) <= den1;
-            if (__all(easy)) {
+            for (int r = 1; r < R; ++r) {
+                ma = fmaxf(ma, fabsf(x[r].x));
+                mb = fmaxf(mb, fabsf(x[r].y));
+            }
+            // LLVM predicates 2: ordered >, 5: ordered <=
+            const uint64_t easy_m = __builtin_amdgcn_fcmpf(den0, 0.f, 2) & __builtin_amdgcn_fcmpf(den1, 0.f, 2) &
+                                    __builtin_amdgcn_fcmpf(ma, den0, 5) & __builtin_amdgcn_fcmpf(mb, den1, 5);
+            if (easy_m == __builtin_amdgcn_read_exec()) {
                 const float i0 = __builtin_amdgcn_rcpf(den0), i1 = __builtin_amdgcn_rcpf(den1);
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
