@@ -279,7 +279,7 @@ ObjPlan plan_object(const ssb_handle* h) {
     size_t off = 0;
     char* z = nullptr;
     ObjPlan p;
-    p.o_part = (size_t)align_up<double2>(z, off, ne * nseg);
+    p.o_part = (size_t)align_up<float2>(z, off, ne * nseg);
     p.o_pm = (size_t)align_up<float2>(z, off, (size_t)n * hh);
     p.o_pn = (size_t)align_up<float2>(z, off, (size_t)n);
     p.o_npart = (size_t)align_up<double2>(z, off, (size_t)2 * n * nseg);
@@ -680,7 +680,7 @@ int ssb_object(ssb_handle* h, const float* params3, float* phase, float* psi, vo
     if ((rc = ensure(&h->ows, &h->ows_bytes, op.total, "object workspace allocation"))) return rc;
     const bool fp = h->variant == SSB_VARIANT_FULL_PLANE;
     const size_t o_npart = op.o_npart;
-    double2* part = reinterpret_cast<double2*>(h->ows + op.o_part);
+    float2* part = reinterpret_cast<float2*>(h->ows + op.o_part);
     float2* pm = reinterpret_cast<float2*>(h->ows + op.o_pm);
     float2* pn = reinterpret_cast<float2*>(h->ows + op.o_pn);
     float2* nab = fp ? reinterpret_cast<float2*>(h->ows + op.o_nab) : nullptr;

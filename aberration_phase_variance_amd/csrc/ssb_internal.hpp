@@ -104,9 +104,9 @@ hipError_t launch_loss(int n, const double* s1run, const double* s2run, int n_tr
 // Object: sum of corrected spectra over all BF, then one 2-D inverse transform.
 int obj_segments(int64_t nbf);
 hipError_t launch_obj_sum(int n, const float2* gm, const float2* gn, const double2* kb, const uint4* sup,
-                          const int* vend, TrialConst tc, GeomDev geo, int64_t nbf, double2* part, int nseg,
+                          const int* vend, TrialConst tc, GeomDev geo, int64_t nbf, float2* part, int nseg,
                           hipStream_t st);
-hipError_t launch_obj_reduce(int n, const double2* part, int nseg, float2* pm, float2* pn,
+hipError_t launch_obj_reduce(int n, const float2* part, int nseg, float2* pm, float2* pn,
                              hipStream_t st);
 hipError_t launch_obj_cols(int n, float2* pm, float2* pn, const float2* tw_inv, hipStream_t st);
 hipError_t launch_obj_rows(int n, const float2* pm, const float2* pn, double dcsum, double scale, float* phase,

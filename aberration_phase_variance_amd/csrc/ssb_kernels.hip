@@ -1438,7 +1438,8 @@ __global__ __launch_bounds__(256) void k_g_rows(const uint32_t* __restrict__ cou
 // support from the per-column intervals, predicated loads, the same correction as
 // pass 1 (exp(-i delta) from two phasor chains per thread, no workgroup barrier in the
 // loop; exp(i chi_q) once per entry).  Tiles at or past a BF pixel's last supported
-// column skip it.  Partials per segment in double.
+// column skip it.  Partials per segment: the float sums themselves (added in double
+// by k_obj_reduce, so storing them as float loses nothing and halves their traffic).
 // Grid: x = segment, y = column tile.  Workgroups are dispatched x fastest, so every
 // segment of tile 0 goes first: the support, and with it the work, shrinks with the
 // column (tile 0 holds about 26 M of the 503 M support entries at 512^2, the last main
@@ -1456,7 +1457,7 @@ template <int N, int TC>
 __device__ __forceinline__ void obj_tile_pair(const float2* __restrict__ gm, const double2* __restrict__ kb,
                                               const uint4* __restrict__ sup, const int* __restrict__ vend,
                                               const TrialConst& m, const GeomDev& geo, int64_t nbf, int seglen,
-                                              double2* __restrict__ part, int tix, int seg) {
+                                              float2* __restrict__ part, int tix, int seg) {
     constexpr int H = N / 2;
     constexpr int NE = N * (H + 1);
     constexpr int NT = obj_threads<N>();
@@ -1574,9 +1575,9 @@ __device__ __forceinline__ void obj_tile_pair(const float2* __restrict__ gm, con
 #pragma unroll
     for (int k = 0; k < PK; ++k) {
         const int u = rr + k * RQ;
-        double2* o = part + (int64_t)seg * NE + (int64_t)u * (H + 1) + vA;
-        o[0] = make_double2(acc[2 * k].x, acc[2 * k].y);
-        o[1] = make_double2(acc[2 * k + 1].x, acc[2 * k + 1].y);
+        float2* o = part + (int64_t)seg * NE + (int64_t)u * (H + 1) + vA;
+        o[0] = acc[2 * k];
+        o[1] = acc[2 * k + 1];
     }
 }
 
@@ -1586,7 +1587,7 @@ __global__ __launch_bounds__(obj_threads<N>()) void k_obj_sum(const float2* __re
                                                          const double2* __restrict__ kb,
                                                          const uint4* __restrict__ sup,
                                                          const int* __restrict__ vend, TrialConst m, GeomDev geo,
-                                                         int64_t nbf, int seglen, double2* __restrict__ part) {
+                                                         int64_t nbf, int seglen, float2* __restrict__ part) {
     constexpr int H = N / 2;
     constexpr int NE = N * (H + 1);
     constexpr int NT = obj_threads<N>();
@@ -1742,12 +1743,12 @@ __global__ __launch_bounds__(obj_threads<N>()) void k_obj_sum(const float2* __re
     for (int i = 0; i < PM; ++i) {
         const int u = ustart + i * ustep;
         if (i < nent && u < N)
-            part[(int64_t)seg * NE + (int64_t)u * (H + 1) + v] = make_double2(acc[i].x, acc[i].y);
+            part[(int64_t)seg * NE + (int64_t)u * (H + 1) + v] = acc[i];
     }
 }
 
 template <int N>
-__global__ __launch_bounds__(256) void k_obj_reduce(const double2* __restrict__ part, int nseg,
+__global__ __launch_bounds__(256) void k_obj_reduce(const float2* __restrict__ part, int nseg,
                                                     float2* __restrict__ pm, float2* __restrict__ pn) {
     constexpr int H = N / 2;
     constexpr int NE = N * (H + 1);
@@ -1756,7 +1757,7 @@ __global__ __launch_bounds__(256) void k_obj_reduce(const double2* __restrict__ 
     double ax = 0.0, ay = 0.0;
     int s = 0;
     for (; s + 8 <= nseg; s += 8) {             // segments added in order, 8 loads in flight
-        double2 p[8];
+        float2 p[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) p[k] = part[(int64_t)(s + k) * NE + e];
 #pragma unroll
@@ -1766,7 +1767,7 @@ __global__ __launch_bounds__(256) void k_obj_reduce(const double2* __restrict__ 
         }
     }
     for (; s < nseg; ++s) {
-        const double2 p = part[(int64_t)s * NE + e];
+        const float2 p = part[(int64_t)s * NE + e];
         ax += p.x;
         ay += p.y;
     }
@@ -2151,7 +2152,7 @@ int obj_segments(int64_t nbf) {
 
 template <int N>
 static hipError_t obj_sum_n(const float2* gm, const float2* gn, const double2* kb, const uint4* sup,
-                            const int* vend, TrialConst tc, GeomDev geo, int64_t nbf, double2* part, int nseg,
+                            const int* vend, TrialConst tc, GeomDev geo, int64_t nbf, float2* part, int nseg,
                             hipStream_t st) {
     constexpr int TC = kTileW;
     const int seglen = (int)((nbf + nseg - 1) / nseg);
@@ -2162,19 +2163,19 @@ static hipError_t obj_sum_n(const float2* gm, const float2* gn, const double2* k
 }
 
 hipError_t launch_obj_sum(int n, const float2* gm, const float2* gn, const double2* kb, const uint4* sup,
-                          const int* vend, TrialConst tc, GeomDev geo, int64_t nbf, double2* part, int nseg,
+                          const int* vend, TrialConst tc, GeomDev geo, int64_t nbf, float2* part, int nseg,
                           hipStream_t st) {
     SSB_DISPATCH_N(n, (obj_sum_n<NN>(gm, gn, kb, sup, vend, tc, geo, nbf, part, nseg, st)))
 }
 
 template <int N>
-static hipError_t obj_reduce_n(const double2* part, int nseg, float2* pm, float2* pn, hipStream_t st) {
+static hipError_t obj_reduce_n(const float2* part, int nseg, float2* pm, float2* pn, hipStream_t st) {
     constexpr int NE = N * (N / 2 + 1);
     hipLaunchKernelGGL(k_obj_reduce<N>, dim3((NE + 255) / 256), dim3(256), 0, st, part, nseg, pm, pn);
     return hipGetLastError();
 }
 
-hipError_t launch_obj_reduce(int n, const double2* part, int nseg, float2* pm, float2* pn, hipStream_t st) {
+hipError_t launch_obj_reduce(int n, const float2* part, int nseg, float2* pm, float2* pn, hipStream_t st) {
     SSB_DISPATCH_N(n, (obj_reduce_n<NN>(part, nseg, pm, pn, st)))
 }
 
