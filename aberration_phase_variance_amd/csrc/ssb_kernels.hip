@@ -1466,7 +1466,7 @@ __device__ __forceinline__ void obj_tile_pair(const float2* __restrict__ gm, con
     static_assert(TC == 8 && PK % 2 == 0 && (PK / 2) * RQ == H && RQ % 16 == 0, "two chains split at N/2");
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int cA = 2 * (tid & 3), cB = cA + 1;
+    const int cA = 2 * (tid & 3);
     const int rr = tid >> 2;
     const int v0 = tix * TC, vA = v0 + cA, vB = vA + 1;
     const int64_t tb = (int64_t)tix * N * TC;
