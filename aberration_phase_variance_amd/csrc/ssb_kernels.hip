@@ -811,9 +811,9 @@ __device__ __forceinline__ void pass1_tile(const float2* __restrict__ gsrc, cons
         // transform takes only the imaginary parts there, and the real parts are the
         // object's real part along the two rows.  The Nyquist column's unit per row pair is
         // [(C0.y, C1.y), (C0.x, C1.x)] in the same way.  Bitwise the sums the row pass formed
-        // itself; the row pass loses its assembly arithmetic, half its cross-lane permutes
-        // and two of its loads per BF pixel (pass 2 1.88-1.92 -> 1.73-1.77 ms, pass 1
-        // 2.40 -> 2.45 ms, 4.44-4.55 -> 4.33 ms per evaluation in one run).
+        // itself; the row pass loses its assembly arithmetic, its cross-lane permutes and two
+        // of its loads per BF pixel (pass 2 1.88-1.92 -> 1.73-1.77 ms with half the permutes
+        // left, pass 1 2.40 -> 2.45 ms, 4.44-4.55 -> 4.33 ms per evaluation in one run).
         float2* ot = out + tt * out_step;
         if constexpr (!NYQ && TC == 8) {
             // unit q = (p, c) = (q / 8, q % 8): 16 bytes per lane, 8 lanes per 128-byte row
@@ -1027,13 +1027,17 @@ struct RowPairRaw {
 // The row pass's inputs in pass 1's row-pair form: per row pair and column v a 16-byte
 // unit [Z(v), Z(N - v)] (Z as in RowPairRaw::assemble, formed by pass 1), at v = 0
 // [Z(0), (Re C(y0, 0), Re C(y0 + 1, 0))], and per row pair of the Nyquist column
-// [Z(N/2), (Re C(y0, N/2), Re C(y0 + 1, N/2))].  Lane j loads its direct units; its
-// mirrored values Z(N - w) come from lane L - j's units (for j = 0 from its own, and
-// the Nyquist unit at v = N/2).  Bitwise the values RowPairRaw assembles.
+// [Z(N/2), (Re C(y0, N/2), Re C(y0 + 1, N/2))].  Lane j loads the Z(v) halves of its direct
+// units (v = j + r L) and the Z(N - w) halves of the units at its mirrored columns
+// w = N/2 - j - r L, which give x[r + R/2] = Z(v + N/2) directly; for j = 0 and r = 0 that
+// is the Nyquist unit (the offset of column N/2 lies past the plane's resource and loads
+// zero; the Nyquist unit's value is selected instead).  Bitwise the values RowPairRaw
+// assembles.  (Taking the mirrored halves from lane L - j's own 16-byte loads with cross-lane
+// permutes instead: pass 2 1.724-1.734 against 1.709-1.722 ms, in a 200-trial batch 1.774
+// against 1.727 ms per trial.)
 template <int N, int R, int L>
 struct RowPairUnits {
-    float4 u[R / 2];
-    float2 m[R / 2];
+    float2 s[R / 2], d[R / 2];
     float4 hn;        // the Nyquist unit
     float2 zr;        // real parts of the DC column on rows y0, y0 + 1
 
@@ -1044,31 +1048,25 @@ struct RowPairUnits {
         constexpr int RSTEP = (L / kTileW) * TILE;
         const int ntile = min((ve + kTileW - 1) / kTileW, H / kTileW);
         const __amdgpu_buffer_rsrc_t rp = make_rsrc(plane, ntile * TILE);
-        // unit (y0 / 2, j): the pair's 128 bytes at row y0 of the layout tile, 16 bytes
-        // per column
         int od = (int)tm_index(N, y0, j) * 8 + (j % kTileW) * 8;
-        asm volatile("" : "+v"(od));
+        const int w0 = H - j;
+        int om = (int)tm_index(N, y0, w0) * 8 + (w0 % kTileW) * 8 + 8;
+        asm volatile("" : "+v"(od), "+v"(om));
 #pragma unroll
-        for (int r = 0; r < R / 2; ++r) u[r] = load4_or_zero(rp, od + r * RSTEP);
+        for (int r = 0; r < R / 2; ++r) {
+            s[r] = load_or_zero(rp, od + r * RSTEP);
+            d[r] = load_or_zero(rp, om - r * RSTEP);
+        }
         zr = load_or_zero(rp, y0 * (kTileW * 8) + 8);
         const __amdgpu_buffer_rsrc_t rn = make_rsrc(nyqc, ve > H ? N * 8 : 0);
         hn = load4_or_zero(rn, y0 * 8);
     }
 
     __device__ __forceinline__ void assemble(int j, float2 (&x)[R]) {
-        const int lane = (int)threadIdx.x & 63;
-        const int addr = (lane - j + ((L - j) & (L - 1))) * 4;
 #pragma unroll
         for (int r = 0; r < R / 2; ++r) {
-            const int rs = R / 2 - 1 - r;
-            m[r].x = __int_as_float(__builtin_amdgcn_ds_bpermute(addr, __float_as_int(u[rs].z)));
-            m[r].y = __int_as_float(__builtin_amdgcn_ds_bpermute(addr, __float_as_int(u[rs].w)));
-        }
-#pragma unroll
-        for (int r = 0; r < R / 2; ++r) {
-            x[r] = make_float2(u[r].x, u[r].y);
-            if (r == 0) x[R / 2] = j == 0 ? make_float2(hn.x, hn.y) : m[0];
-            else x[r + R / 2] = j == 0 ? make_float2(u[R / 2 - r].z, u[R / 2 - r].w) : m[r];
+            x[r] = s[r];
+            x[r + R / 2] = (r == 0 && j == 0) ? make_float2(hn.x, hn.y) : d[r];
         }
     }
     __device__ __forceinline__ float dc_re0() const { return zr.x; }
