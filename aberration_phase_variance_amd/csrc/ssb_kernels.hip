@@ -1088,10 +1088,11 @@ struct RowPairUnits {
 // (1.908 -> 1.880 ms against 78 VGPRs and 6 waves; earlier 2.07 against 2.19 ms for 6
 // against 5 waves);
 // 128 (4 waves) at N = 1024 (2.85 against 3.26 ms at 136, 3 waves); the
-// full-plane forms keep the compiler's choice.
+// full-plane form 96 up to N = 512 (5 waves, 44 bytes of spills; 2.31-2.32 -> 2.24 ms against the
+// compiler's 124 VGPRs and 4 waves) and the compiler's choice at N = 1024.
 template <int N, bool FP>
 constexpr int pass2_min_waves() {
-    return FP ? 1 : (N <= 512 ? SSB_PASS2_MIN_WAVES : SSB_PASS2_MIN_WAVES_1024);
+    return FP ? (N <= 512 ? 5 : 1) : (N <= 512 ? SSB_PASS2_MIN_WAVES : SSB_PASS2_MIN_WAVES_1024);
 }
 
 template <int N, bool FP>
