@@ -113,7 +113,8 @@ class ssb_probe_fit(ctypes.Structure):
     ]
 
 
-EXPORTS = ("ssb_prepare", "ssb_reserve", "ssb_loss", "ssb_loss_noalloc", "ssb_moments", "ssb_object", "ssb_spectrum", "ssb_set_chunk",
+EXPORTS = ("ssb_prepare", "ssb_reserve", "ssb_loss", "ssb_loss_noalloc", "ssb_moments", "ssb_object",
+           "ssb_loss_object", "ssb_spectrum", "ssb_set_chunk",
            "ssb_profile", "ssb_query", "ssb_release", "ssb_last_error", "ssb_nelder_mead", "ssb_fit",
            "ssb_detector_sum", "ssb_fit_probe", "ssb_gather_bf", "ssb_set_variant")
 
@@ -136,6 +137,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ssb_loss_noalloc.argtypes = [vp, fp, i32, dp, vp, vp]
     lib.ssb_moments.argtypes = [vp, fp, i64, i64, vp, dp, vp]
     lib.ssb_object.argtypes = [vp, fp, vp, vp, vp]
+    lib.ssb_loss_object.argtypes = [vp, fp, dp, vp, vp, vp]
     lib.ssb_spectrum.argtypes = [vp, i64, vp, vp]
     lib.ssb_set_chunk.argtypes = [vp, i64]
     lib.ssb_set_variant.argtypes = [vp, i32]
@@ -291,6 +293,22 @@ def ssb_object(handle: int, params3, phase, psi=None, stream=None) -> None:
     if psi is not None:
         ps = _dev(psi, "psi", _C64, n * n * (2 if str(getattr(psi, "dtype", "")).endswith("float32") else 1))
     _check(lib.ssb_object(handle, p.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), ph, ps, _stream(stream)))
+
+
+def ssb_loss_object(handle: int, params3, phase, psi=None, stream=None) -> float:
+    """One trial's loss (returned) and its phase-of-mean object into device float [N][N] phase
+    (and complex64 [N][N] psi when given), from one pass over the spectra."""
+    lib = load_library()
+    p = _params(params3, 1)
+    n = _scan_n(handle)
+    ph = _dev(phase, "phase", ("float32",), n * n)
+    ps = None
+    if psi is not None:
+        ps = _dev(psi, "psi", _C64, n * n * (2 if str(getattr(psi, "dtype", "")).endswith("float32") else 1))
+    loss = ctypes.c_double()
+    _check(lib.ssb_loss_object(handle, p.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), ctypes.byref(loss), ph, ps,
+                               _stream(stream)))
+    return loss.value
 
 
 def ssb_spectrum(handle: int, bf: int, out, stream=None) -> None:

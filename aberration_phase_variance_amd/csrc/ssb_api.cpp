@@ -208,15 +208,23 @@ TrialConst trial_const(const ssb_handle* h, const float* p) {
     return t;
 }
 
+// Whether the row pass forms the object sums itself (ssb_loss_object): half plane, scan
+// sizes up to 512 (at 1,024 the sums would not fit the row pass's registers).
+bool fused_object(const ssb_handle* h, int variant) {
+    return variant == SSB_VARIANT_HALF_PLANE && pass2_obj_sizes(h->n);
+}
+
 struct LossPlan {
     int cap;       // BF capacity of one chunk (multiple of kGroupBF)
     int gcap;      // groups per chunk
     size_t off_im, off_in, off_ps1, off_ps2, off_s1, off_s2, off_loss, off_lpart, off_tc, off_chm, off_chn;
     size_t off_na, off_nb;   // full-plane variant only (else 0)
+    size_t off_po, off_oacc; // object sums of the row pass (fused loss and object; else 0)
     size_t total;
 };
 
-LossPlan plan_loss(const ssb_handle* h, int64_t nb, int n_trials, int variant, int64_t chunk_user) {
+LossPlan plan_loss(const ssb_handle* h, int64_t nb, int n_trials, int variant, int64_t chunk_user,
+                   bool obj = false) {
     const int64_t n = h->n, hh = h->h;
     const double plane = (double)n * (hh + 1) * sizeof(float2);
     // memory bound on the chunk (intermediate for all trials of the call)
@@ -249,6 +257,11 @@ LossPlan plan_loss(const ssb_handle* h, int64_t nb, int n_trials, int variant, i
         pl.off_na = (size_t)align_up<float2>(z, off, (size_t)n_trials * cap * n);
         pl.off_nb = (size_t)align_up<float2>(z, off, (size_t)n_trials * cap * n);
     }
+    pl.off_po = pl.off_oacc = 0;
+    if (obj) {
+        pl.off_po = (size_t)align_up<float>(z, off, (size_t)n_trials * pl.gcap * obj_sum_count(h->n));
+        pl.off_oacc = (size_t)align_up<double>(z, off, (size_t)n_trials * obj_sum_count(h->n));
+    }
     pl.total = off + 256;
     return pl;
 }
@@ -265,6 +278,9 @@ size_t loss_ws_need(const ssb_handle* h, int n_trials) {
     for (int t = 1; t <= n_trials; ++t)
         for (int var : {SSB_VARIANT_HALF_PLANE, SSB_VARIANT_FULL_PLANE})
             need = std::max(need, plan_loss(h, h->n_bf, t, var, 0).total);
+    // the fused loss and object (one trial, half plane)
+    if (fused_object(h, SSB_VARIANT_HALF_PLANE))
+        need = std::max(need, plan_loss(h, h->n_bf, 1, SSB_VARIANT_HALF_PLANE, 0, true).total);
     return need;
 }
 
@@ -336,8 +352,10 @@ int reserve(ssb_handle* h, int max_trials) {
 // launch instead of a staged pageable copy; nothing allocated).  The first chunk's
 // accumulation writes S1 and S2 outright, so they need no clearing launch (with the
 // previous change, about 0.015 ms per evaluation).
+// obj: the row pass also leaves the object sums of every chunk, accumulated in
+// ws + pl.off_oacc (the plan must have them).
 int run_moments(ssb_handle* h, char* ws, const LossPlan& pl, const float* params, int n_trials, int64_t b_begin,
-                int64_t b_end, hipStream_t st, bool staged) {
+                int64_t b_end, hipStream_t st, bool staged, bool obj = false) {
     std::vector<TrialConst>& htc = h->htc;
     float2* im = reinterpret_cast<float2*>(ws + pl.off_im);
     float2* in = reinterpret_cast<float2*>(ws + pl.off_in);
@@ -351,6 +369,8 @@ int run_moments(ssb_handle* h, char* ws, const LossPlan& pl, const float* params
     const bool fp = h->variant == SSB_VARIANT_FULL_PLANE;
     float2* nyq_a = fp ? reinterpret_cast<float2*>(ws + pl.off_na) : nullptr;
     float2* nyq_b = fp ? reinterpret_cast<float2*>(ws + pl.off_nb) : nullptr;
+    float* po = obj ? reinterpret_cast<float*>(ws + pl.off_po) : nullptr;
+    double* oacc = obj ? reinterpret_cast<double*>(ws + pl.off_oacc) : nullptr;
 
     if (staged && n_trials > kTrialBlock) {
         if ((size_t)n_trials > htc.capacity()) {      // beyond the reservation: the one host allocation
@@ -377,6 +397,7 @@ int run_moments(ssb_handle* h, char* ws, const LossPlan& pl, const float* params
         if (b_begin >= b_end) {                       // no chunk below writes the sums
             SSB_HIP(launch_fill(s1, (int64_t)n_trials * h->n * h->n, st), "clear S1");
             SSB_HIP(launch_fill(s2, n_trials, st), "clear S2");
+            if (obj) SSB_HIP(launch_fill(oacc, (int64_t)n_trials * obj_sum_count(h->n), st), "clear object sums");
         }
         SSB_HIP(launch_chiq(h->n, tc, n_trials, h->geo, chm, chn, st), "phase table launch");
     }
@@ -398,13 +419,16 @@ int run_moments(ssb_handle* h, char* ws, const LossPlan& pl, const float* params
         {
             StageTimer tm(h, SSB_STAGE_PASS2, st, units, staged);
             SSB_HIP(launch_pass2(h->n, im, in, pl.cap, h->active, h->vend, c0, cb, n_trials, h->dc, ps1, ps2,
-                                 pl.gcap, h->tw, nyq_a, nyq_b, st),
+                                 pl.gcap, h->tw, nyq_a, nyq_b, po, st),
                     "pass 2 launch");
         }
         {
             StageTimer tm(h, SSB_STAGE_REDUCE, st, 0, staged);
             SSB_HIP(launch_accum(h->n, ps1, ps2, pl.gcap, ng, n_trials, s1, s2, c0 == b_begin, st),
                     "accumulate launch");
+            if (obj)
+                SSB_HIP(launch_accum_obj(h->n, po, pl.gcap, ng, n_trials, oacc, c0 == b_begin, st),
+                        "object-sum accumulate launch");
         }
     }
     return SSB_OK;
@@ -412,9 +436,12 @@ int run_moments(ssb_handle* h, char* ws, const LossPlan& pl, const float* params
 
 // The loss of n_trials trials over every BF pixel in the workspace ws (layout pl),
 // copied to the host array losses; synchronizes the stream.
+// With obj (one trial, a plan that has the object sums) the object's phase (and psi when
+// not null) is written as well, from the row pass's object sums.
 int run_loss(ssb_handle* h, char* ws, const LossPlan& pl, const float* params, int n_trials, double* losses,
-             float* mean_phase, hipStream_t st, bool staged) {
-    int rc = run_moments(h, ws, pl, params, n_trials, 0, h->n_bf, st, staged);
+             float* mean_phase, hipStream_t st, bool staged, bool obj = false, float* phase = nullptr,
+             float* psi = nullptr) {
+    int rc = run_moments(h, ws, pl, params, n_trials, 0, h->n_bf, st, staged, obj);
     if (rc) {
         (void)hipStreamSynchronize(st);
         return rc;
@@ -426,6 +453,16 @@ int run_loss(ssb_handle* h, char* ws, const LossPlan& pl, const float* params, i
     {
         StageTimer tm(h, SSB_STAGE_REDUCE, st, 0, staged);
         SSB_HIP(launch_loss(h->n, s1, s2, n_trials, (double)h->n_bf, lp, dl, mean_phase, st), "loss launch");
+    }
+    if (obj) {
+        StageTimer tm(h, SSB_STAGE_OBJ_FFT, st, 0, staged);
+        const int n = h->n;
+        // the inactive BF pixels add their DC term only
+        const double re_extra = h->dc * (double)(h->n_bf - h->n_active);
+        const double scale = 1.0 / ((double)h->n_bf * (double)n * (double)n);
+        SSB_HIP(launch_obj_from_sums(n, reinterpret_cast<double*>(ws + pl.off_oacc), re_extra, scale, phase,
+                                     reinterpret_cast<float2*>(psi), st),
+                "object from sums");
     }
     if (n_trials <= h->hres_cap) {
         SSB_HIP(hipMemcpyAsync(h->hres, dl, sizeof(double) * n_trials, hipMemcpyDeviceToHost, st), "copy losses");
@@ -704,6 +741,25 @@ int ssb_object(ssb_handle* h, const float* params3, float* phase, float* psi, vo
                 "object rows");
     }
     return SSB_OK;
+}
+
+int ssb_loss_object(ssb_handle* h, const float* params3, double* loss, float* phase, float* psi, void* stream) {
+    g_err.clear();
+    int rc = check_handle(h);
+    if (rc) return rc;
+    if (!params3 || !loss || !phase) return fail(SSB_EINVAL, "null argument");
+    if ((rc = check_params(params3, 1))) return rc;
+    if (!fused_object(h, h->variant)) {
+        // full-plane variant, 1,024-point scans: the loss, then the object's own pass
+        if ((rc = ssb_loss(h, params3, 1, loss, nullptr, stream))) return rc;
+        if ((rc = ssb_object(h, params3, phase, psi, stream))) return rc;
+        SSB_HIP(hipStreamSynchronize(static_cast<hipStream_t>(stream)), "object");
+        return SSB_OK;
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const LossPlan pl = plan_loss(h, h->n_bf, 1, h->variant, h->chunk_user, true);
+    if ((rc = ensure(&h->ws, &h->ws_bytes, pl.total, "workspace allocation"))) return rc;
+    return run_loss(h, h->ws, pl, params3, 1, loss, nullptr, st, true, true, phase, psi);
 }
 
 int ssb_spectrum(const ssb_handle* h, int64_t bf, float* out, void* stream) {

@@ -1090,19 +1090,27 @@ struct RowPairUnits {
 // 128 (4 waves) at N = 1024 (2.85 against 3.26 ms at 136, 3 waves); the
 // full-plane form 96 up to N = 512 (5 waves, 44 bytes of spills; 2.31-2.32 -> 2.24 ms against the
 // compiler's 124 VGPRs and 4 waves) and the compiler's choice at N = 1024.
-template <int N, bool FP>
+// OBJ: the row pass also sums each pixel's object O_b over the group's BF pixels (the
+// object's 16 sums per lane take the budget of five waves per SIMD: 94 VGPRs)
+template <int N, bool FP, bool OBJ = false>
 constexpr int pass2_min_waves() {
-    return FP ? (N <= 512 ? 5 : 1) : (N <= 512 ? SSB_PASS2_MIN_WAVES : SSB_PASS2_MIN_WAVES_1024);
+    return OBJ ? 5 : FP ? (N <= 512 ? 5 : 1) : (N <= 512 ? SSB_PASS2_MIN_WAVES : SSB_PASS2_MIN_WAVES_1024);
 }
 
-template <int N, bool FP>
-__global__ __launch_bounds__(256, (pass2_min_waves<N, FP>())) void k_pass2(const float2* __restrict__ im, const float2* __restrict__ in,
+// part_obj (OBJ only): per trial and group, N * N sums of Im O_b over the group's active BF
+// pixels (row-major, like part_s1), then 2 N sums of Re O_b per row and column parity (Re O_b
+// depends on the column only through its parity: the DC term, the v = 0 column's real part
+// along the row, and the Nyquist column's, with sign (-1)^x)
+template <int N, bool FP, bool OBJ = false>
+__global__ __launch_bounds__(256, (pass2_min_waves<N, FP, OBJ>())) void k_pass2(const float2* __restrict__ im, const float2* __restrict__ in,
                                                int cap, const uint8_t* __restrict__ active,
                                                const int* __restrict__ vend, int64_t bf0,
                                                int cb, float dcf, float* __restrict__ part_s1,
                                                double* __restrict__ part_s2, int gcap,
                                                const float2* __restrict__ gtw,
-                                               const float2* __restrict__ na, const float2* __restrict__ nb) {
+                                               const float2* __restrict__ na, const float2* __restrict__ nb,
+                                               float* __restrict__ part_obj) {
+    static_assert(!(OBJ && FP), "object sums in the half-plane row pass only");
     // FFT twiddles from an LDS copy of the table (not registers: 4 waves per SIMD)
     using F = WaveFFTT<N, +1>;
     __shared__ float2 twt[F::TABLE];
@@ -1153,6 +1161,9 @@ __global__ __launch_bounds__(256, (pass2_min_waves<N, FP>())) void k_pass2(const
     }
     double s2 = 0.0;
     const float sgn = (j & 1) ? -1.f : 1.f;   // (-1)^x for x = j + r L, L even
+    float oa[OBJ ? R : 1], ob[OBJ ? R : 1], rea = 0.f, reb = 0.f;
+#pragma unroll
+    for (int r = 0; r < (OBJ ? R : 1); ++r) oa[r] = ob[r] = 0.f;
 
     while (b < b_hi) {
         const int bn = next_active(b + 1);
@@ -1225,12 +1236,26 @@ __global__ __launch_bounds__(256, (pass2_min_waves<N, FP>())) void k_pass2(const
             // LLVM predicates 2: ordered >, 5: ordered <=
             const uint64_t easy_m = __builtin_amdgcn_fcmpf(den0, 0.f, 2) & __builtin_amdgcn_fcmpf(den1, 0.f, 2) &
                                     __builtin_amdgcn_fcmpf(ma, den0, 5) & __builtin_amdgcn_fcmpf(mb, den1, 5);
+            if constexpr (OBJ) {
+                // O_b on rows y0 and y0 + 1: real parts den0, den1; imaginary parts x[r]
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    oa[r] += x[r].x;
+                    ob[r] += x[r].y;
+                }
+                rea += den0;
+                reb += den1;
+            }
             if (easy_m == __builtin_amdgcn_read_exec()) {
                 const float i0 = __builtin_amdgcn_rcpf(den0), i1 = __builtin_amdgcn_rcpf(den1);
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
-                    const float pa = atan_unit(x[r].x * i0);
-                    const float pb = atan_unit(x[r].y * i1);
+                    float pa = atan_unit(x[r].x * i0);
+                    float pb = atan_unit(x[r].y * i1);
+                    // each phase rounded on its own before it is summed: the polynomial's
+                    // last multiply is never fused into the sums, in any variant of this
+                    // kernel, so the object-summing variant gives the same moments bitwise
+                    asm("" : "+v"(pa), "+v"(pb));
                     s1a[r] += pa;
                     s1b[r] += pb;
                     p2 = fmaf(pb, pb, fmaf(pa, pa, p2));
@@ -1238,8 +1263,9 @@ __global__ __launch_bounds__(256, (pass2_min_waves<N, FP>())) void k_pass2(const
             } else {
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
-                    const float pa = atan2_f(x[r].x, den0);
-                    const float pb = atan2_f(x[r].y, den1);
+                    float pa = atan2_f(x[r].x, den0);
+                    float pb = atan2_f(x[r].y, den1);
+                    asm("" : "+v"(pa), "+v"(pb));
                     s1a[r] += pa;
                     s1b[r] += pb;
                     p2 = fmaf(pb, pb, fmaf(pa, pa, p2));
@@ -1255,6 +1281,19 @@ __global__ __launch_bounds__(256, (pass2_min_waves<N, FP>())) void k_pass2(const
     for (int r = 0; r < R; ++r) {
         o[j + r * L] = s1a[r];
         o[N + j + r * L] = s1b[r];
+    }
+    if constexpr (OBJ) {
+        float* po = part_obj + ((int64_t)t * gcap + g) * ((int64_t)N * N + 2 * N);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            po[(int64_t)y0 * N + j + r * L] = oa[r];
+            po[(int64_t)(y0 + 1) * N + j + r * L] = ob[r];
+        }
+        // Re sums per row and column parity: lanes 0 (even columns) and 1 (odd)
+        if (j < 2) {
+            po[(int64_t)N * N + 2 * y0 + j] = rea;
+            po[(int64_t)N * N + 2 * (y0 + 1) + j] = reb;
+        }
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) s2 += __shfl_xor(s2, off);
@@ -1320,6 +1359,23 @@ __global__ __launch_bounds__(256) void k_accum_s2(const double* __restrict__ par
         __syncthreads();
     }
     if (threadIdx.x == 0) s2run[t] = run;
+}
+
+// The object redraw from the row pass's sums (one trial): per pixel (y, x), the object
+// summed over every BF pixel is Re = acc[N^2 + 2 y + x mod 2] + re_extra (the inactive BF
+// pixels contribute their DC term only) and Im = acc[y N + x]; its phase is the phase of
+// the mean object.
+__global__ __launch_bounds__(256) void k_obj_from_sums(const double* __restrict__ acc, int n, double re_extra,
+                                                        double scale, float* __restrict__ phase,
+                                                        float2* __restrict__ psi) {
+    const int64_t n2 = (int64_t)n * n;
+    const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (p >= n2) return;
+    const int y = (int)(p / n), x = (int)(p - (int64_t)y * n);
+    const double re = acc[n2 + 2 * y + (x & 1)] + re_extra;
+    const double imv = acc[p];
+    phase[p] = (float)atan2(imv, re);
+    if (psi) psi[p] = make_float2((float)(re * scale), (float)(imv * scale));
 }
 
 __global__ __launch_bounds__(64) void k_set_trials(TrialBlock blk, int count, TrialConst* __restrict__ out) {
@@ -2063,24 +2119,33 @@ int pass2_row_blocks(int n) {
 template <int N>
 static hipError_t pass2_n(const float2* im, const float2* in, int cap, const uint8_t* active, const int* vend,
                           int64_t bf0, int cb, int n_trials, double dc, float* part_s1, double* part_s2, int gcap,
-                          const float2* tw, const float2* na, const float2* nb, hipStream_t st) {
+                          const float2* tw, const float2* na, const float2* nb, float* part_obj, hipStream_t st) {
     const int ng = (cb + kGroupBF - 1) / kGroupBF;
     const dim3 grid(row_blocks<N>(), ng, n_trials);
-    if (na)
+    if (part_obj) {
+        if constexpr (pass2_obj_sizes(N)) {
+            if (na) return hipErrorInvalidValue;
+            hipLaunchKernelGGL((k_pass2<N, false, true>), grid, dim3(256), 0, st, im, in, cap, active, vend, bf0, cb,
+                               (float)dc, part_s1, part_s2, gcap, tw, na, nb, part_obj);
+        } else {
+            return hipErrorInvalidValue;
+        }
+    } else if (na) {
         hipLaunchKernelGGL((k_pass2<N, true>), grid, dim3(256), 0, st, im, in, cap, active, vend, bf0, cb, (float)dc,
-                           part_s1, part_s2, gcap, tw, na, nb);
-    else
+                           part_s1, part_s2, gcap, tw, na, nb, part_obj);
+    } else {
         hipLaunchKernelGGL((k_pass2<N, false>), grid, dim3(256), 0, st, im, in, cap, active, vend, bf0, cb,
-                           (float)dc, part_s1, part_s2, gcap, tw, na, nb);
+                           (float)dc, part_s1, part_s2, gcap, tw, na, nb, part_obj);
+    }
     return hipGetLastError();
 }
 
 hipError_t launch_pass2(int n, const float2* im, const float2* in, int cap, const uint8_t* active,
                         const int* vend, int64_t bf0, int cb, int n_trials, double dc, float* part_s1,
                         double* part_s2, int gcap, const float2* tw_inv, const float2* na, const float2* nb,
-                        hipStream_t st) {
+                        float* part_obj, hipStream_t st) {
     SSB_DISPATCH_N(n, (pass2_n<NN>(im, in, cap, active, vend, bf0, cb, n_trials, dc, part_s1, part_s2, gcap, tw_inv,
-                                   na, nb, st)))
+                                   na, nb, part_obj, st)))
 }
 
 template <int N>
@@ -2114,6 +2179,22 @@ hipError_t launch_accum(int n, const float* part_s1, const double* part_s2, int 
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_accum_s2, dim3(n_trials), dim3(256), 0, st, part_s2, gcap, ng, pass2_row_blocks(n), s2run,
                        (int)first);
+    return hipGetLastError();
+}
+
+hipError_t launch_accum_obj(int n, const float* part_obj, int gcap, int ng, int n_trials, double* acc, bool first,
+                            hipStream_t st) {
+    const int64_t n2 = obj_sum_count(n);
+    hipLaunchKernelGGL(k_accum_s1, dim3((unsigned)((n2 + 255) / 256), n_trials), dim3(256), 0, st, part_obj, gcap,
+                       ng, n2, acc, (int)first);
+    return hipGetLastError();
+}
+
+hipError_t launch_obj_from_sums(int n, const double* acc, double re_extra, double scale, float* phase, float2* psi,
+                                hipStream_t st) {
+    const int64_t n2 = (int64_t)n * n;
+    hipLaunchKernelGGL(k_obj_from_sums, dim3((unsigned)((n2 + 255) / 256)), dim3(256), 0, st, acc, n, re_extra, scale,
+                       phase, psi);
     return hipGetLastError();
 }
 

@@ -4,7 +4,8 @@ One step = one exact phase-variance loss evaluation (one trial) of the full
 workload: 512 x 512 scan x 8,937 BF pixels, from cached complex64 spectra
 already resident in HBM.  Prints one JSON line (rank 0, one GPU).
 
-Also reported: the object redraw, the per-trial time inside a 200-trial batch,
+Also reported: the object redraw, the loss and object from one call, the per-trial
+time inside a 200-trial batch,
 the spectrum build (prepare), per-stage device times measured with HIP events on
 the library's stream, the roofline of the dominant kernel, and the float64
 oracle timed on the host's cores over whole evaluations (a process pool over BF
@@ -261,6 +262,14 @@ def main():
     torch.cuda.synchronize()
     object_ms = (time.perf_counter() - t1) * 1e3 / n_obj
     log(f"[bench] object {object_ms:.3f} ms")
+
+    # loss and object from one pass (ssb_loss_object), host clock, synchronizing call
+    lo_loss = ssb.ssb_loss_object(h, params[0], phase)
+    t1 = time.perf_counter()
+    for _ in range(n_obj):
+        lo_loss = ssb.ssb_loss_object(h, params[0], phase)
+    loss_object_ms = (time.perf_counter() - t1) * 1e3 / n_obj
+    log(f"[bench] loss and object in one call {loss_object_ms:.3f} ms (loss bitwise ssb_loss's: {lo_loss == loss})")
 
     batch_ms_per_trial = None
     fit = None
@@ -524,6 +533,8 @@ def main():
         "ms_p95": float(np.percentile(times, 95)),
         "ms_min": float(min(times)),
         "object_ms": object_ms,
+        "loss_object_ms": loss_object_ms,
+        "loss_object_same_loss": bool(lo_loss == loss),
         "batch_trials": args.batch,
         "batch_ms_per_trial": batch_ms_per_trial,
         "fit": fit,

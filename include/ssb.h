@@ -193,6 +193,27 @@ int ssb_moments(ssb_handle* h, const float* params3, int64_t bf_begin, int64_t b
 int ssb_object(ssb_handle* h, const float* params3, float* phase, float* psi, void* stream);
 
 /*
+ * ssb_loss_object: one trial's loss and its phase-of-mean object from one pass over
+ * the cached spectra (the loss of ssb_loss and the object of ssb_object, Notes page,
+ * "Standard-only CUDA native 512 calibration").  The object transform is linear, so
+ * the mean object equals the mean of the per-BF objects O_b that the loss already
+ * forms before taking their phases: the row pass also sums O_b over each 32-BF group,
+ * and the sums are added in double in group order.  The loss is bitwise that of
+ * ssb_loss; phase and psi agree with ssb_object to float rounding (the two sum in
+ * different orders).  For the full-plane variant and 1,024-point scans the call runs
+ * ssb_loss and then ssb_object.
+ *   params3  HOST float[3].
+ *   loss     HOST double, written on success.
+ *   phase    DEVICE float [N][N].
+ *   psi      optional DEVICE complex64 [N][N] (interleaved re, im) or NULL.
+ * Synchronizes the stream before returning.  Allocates nothing (ssb_prepare reserves
+ * its buffers).  Errors: SSB_EINVAL (null handle/params/loss/phase, non-finite
+ * parameter), SSB_ENOMEM, SSB_EDEVICE.
+ */
+int ssb_loss_object(ssb_handle* h, const float* params3, double* loss, float* phase, float* psi,
+                    void* stream);
+
+/*
  * ssb_spectrum: copy the cached spectrum of BF pixel bf as complex64
  * [N][N/2 + 1] (interleaved re, im, logical half-plane order) into the DEVICE
  * buffer out.  Asynchronous.  Errors: SSB_EINVAL, SSB_ESHAPE, SSB_EDEVICE.

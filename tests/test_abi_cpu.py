@@ -100,6 +100,7 @@ def test_null_handle_calls():
     out = (ctypes.c_double * 1)()
     assert lib.ssb_loss(None, p, 1, out, None, None) == ssb._ssb.SSB_EINVAL
     assert lib.ssb_object(None, p, None, None, None) == ssb._ssb.SSB_EINVAL
+    assert lib.ssb_loss_object(None, p, out, None, None, None) == ssb._ssb.SSB_EINVAL
     assert lib.ssb_query(None, None) == ssb._ssb.SSB_EINVAL
     assert lib.ssb_set_chunk(None, 64) == ssb._ssb.SSB_EINVAL
     assert lib.ssb_set_variant(None, 1) == ssb._ssb.SSB_EINVAL

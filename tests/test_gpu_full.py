@@ -102,7 +102,8 @@ def test_full_loss_all_bf(full, full_pool):
 
 
 def test_full_object_all_bf(full, full_pool):
-    """The phase-of-mean object over all 8,937 BF pixels within 1e-4 rad RMS of the oracle."""
+    """The phase-of-mean object over all 8,937 BF pixels within 1e-4 rad RMS of the oracle,
+    from ssb_object and from the fused ssb_loss_object."""
     import torch
     w, counts, h = full
     og = O.OGeom.from_any(w.geometry)
@@ -120,6 +121,17 @@ def test_full_object_all_bf(full, full_pool):
         rel = np.linalg.norm(p[..., 0] + 1j * p[..., 1] - ref_psi) / np.linalg.norm(ref_psi)
         _say(f"[full]   object rms {rms:.2e} rad, psi rel L2 {rel:.2e}")
         assert rms <= PHASE_RMS and rel <= 1e-5
+        # the fused loss and object: the loss bitwise ssb_loss's, the object the oracle's
+        phase.fill_(float("nan"))
+        psi.fill_(float("nan"))
+        loss = ssb.ssb_loss_object(h, params, phase, psi)
+        assert loss == ssb.ssb_loss(h, [params])[0]
+        d2 = np.angle(np.exp(1j * (phase.cpu().numpy() - ref_phase)))
+        rms2 = float(np.sqrt(np.mean(d2 * d2)))
+        p2 = psi.cpu().numpy()
+        rel2 = np.linalg.norm(p2[..., 0] + 1j * p2[..., 1] - ref_psi) / np.linalg.norm(ref_psi)
+        _say(f"[full]   fused loss and object: object rms {rms2:.2e} rad, psi rel L2 {rel2:.2e}")
+        assert rms2 <= PHASE_RMS and rel2 <= 1e-5
 
 
 def _moments(h, n, params, b0, b1):

@@ -74,6 +74,18 @@ class Prepared:
             out_psi = p[..., 0] + 1j * p[..., 1]
         return phase.cpu().numpy(), out_psi
 
+    def loss_obj(self, params, with_psi=True):
+        """ssb_loss_object on NaN-filled outputs: (loss, phase, psi or None)."""
+        t = self.torch
+        phase = t.full((self.n, self.n), float("nan"), dtype=t.float32, device="cuda")
+        psi = t.full((self.n, self.n, 2), float("nan"), dtype=t.float32, device="cuda") if with_psi else None
+        loss = ssb.ssb_loss_object(self.h, params, phase, psi)
+        out_psi = None
+        if psi is not None:
+            q = psi.cpu().numpy()
+            out_psi = q[..., 0] + 1j * q[..., 1]
+        return loss, phase.cpu().numpy(), out_psi
+
     def moments(self, params, b0, b1):
         t = self.torch
         s1 = t.full((self.n, self.n), float("nan"), dtype=t.float64, device="cuda")
@@ -313,6 +325,50 @@ def test_object_vs_oracle(fx, request):
         assert np.linalg.norm(psi - ref_psi) <= 1e-5 * np.linalg.norm(ref_psi)
 
 
+def _wrapped(a, b):
+    return np.angle(np.exp(1j * (a - b)))
+
+
+def check_loss_object(p, params, ref_phase=None, ref_psi=None, what=""):
+    """ssb_loss_object against ssb_loss (bitwise), ssb_object (float rounding: at most
+    1e-5 rad, psi within 1e-6 relative L2) and, when given, the oracle's object."""
+    loss, phase, psi = p.loss_obj(params)
+    assert loss == p.loss([params])[0], what
+    ph2, psi2 = p.obj(params)
+    d = _wrapped(phase, ph2)
+    _say(f"[loss+object] {what} {params}: phase vs ssb_object max {np.max(np.abs(d)):.2e} rad")
+    assert np.max(np.abs(d)) <= 1e-5, what
+    assert np.linalg.norm(psi - psi2) <= 1e-6 * np.linalg.norm(psi2), what
+    if ref_phase is not None:
+        assert np.sqrt(np.mean(_wrapped(phase, ref_phase) ** 2)) <= PHASE_RMS, what
+    if ref_psi is not None:
+        assert np.linalg.norm(psi - ref_psi) <= 1e-5 * np.linalg.norm(ref_psi), what
+
+
+@pytest.mark.parametrize("fx", ["tiny", "small"])
+def test_loss_object_vs_oracle(fx, request):
+    """The fused call: the loss of ssb_loss and the object of ssb_object from one pass."""
+    w, counts, p = request.getfixturevalue(fx)
+    g = O.OGeom.from_any(w.geometry)
+    for params in ([40.0, 5.0, 0.3], [-55.0, 9.0, 1.9], [0.0, 0.0, 0.0]):
+        ref_phase, ref_psi = O.object_wave(g, counts, params)
+        check_loss_object(p, params, ref_phase, ref_psi, fx)
+        assert _rel(p.loss_obj(params, with_psi=False)[0], O.loss(g, counts, params)) <= LOSS_RTOL
+
+
+def test_loss_object_chunked(small):
+    """Chunks smaller than the BF set: the object sums carry over from chunk to chunk."""
+    w, counts, p = small
+    g = O.OGeom.from_any(w.geometry)
+    params = [-30.0, 6.0, 0.7]
+    ref_phase, ref_psi = O.object_wave(g, counts, params)
+    ssb.ssb_set_chunk(p.h, 64)
+    try:
+        check_loss_object(p, params, ref_phase, ref_psi, "small, 64-BF chunks")
+    finally:
+        ssb.ssb_set_chunk(p.h, 0)
+
+
 # ---------------------------------------------------------------- edge cases
 @pytest.mark.parametrize("fx", ["tiny", "small"])
 def test_zero_aberration(fx, request):
@@ -387,8 +443,10 @@ def test_inactive_bf_pixels():
         for params in ([40.0, 5.0, 0.3], [10.0, -3.0, 1.0]):
             assert _rel(p.loss([params])[0], O.loss(og, counts, params)) <= LOSS_RTOL
             phase, _ = p.obj(params, with_psi=False)
-            ref, _ = O.object_wave(og, counts, params)
+            ref, ref_psi = O.object_wave(og, counts, params)
             assert np.sqrt(np.mean(np.angle(np.exp(1j * (phase - ref))) ** 2)) <= PHASE_RMS
+            # the fused call adds the inactive pixels' DC terms itself
+            check_loss_object(p, params, ref, ref_psi, "inactive BF pixels")
     finally:
         p.release()
 
@@ -435,8 +493,9 @@ def test_other_scan_sizes(n, d, r2):
         for params in ([40.0, 5.0, 0.3], [-25.0, 7.0, 2.4]):
             assert _rel(p.loss([params])[0], O.loss(og, counts, params)) <= LOSS_RTOL
         phase, _ = p.obj([40.0, 5.0, 0.3], with_psi=False)
-        ref, _ = O.object_wave(og, counts, [40.0, 5.0, 0.3])
+        ref, ref_psi = O.object_wave(og, counts, [40.0, 5.0, 0.3])
         assert np.sqrt(np.mean(np.angle(np.exp(1j * (phase - ref))) ** 2)) <= PHASE_RMS
+        check_loss_object(p, [40.0, 5.0, 0.3], ref, ref_psi, f"N = {n}")
     finally:
         p.release()
 
@@ -531,6 +590,11 @@ def test_full_plane_moments_and_object_tiny(full_plane_tiny):
         d = np.angle(np.exp(1j * (phase - ref_phase)))
         assert np.sqrt(np.mean(d * d)) <= PHASE_RMS
         assert np.linalg.norm(psi - ref_psi) <= 1e-5 * np.linalg.norm(ref_psi)
+        # the fused call runs ssb_loss and then ssb_object in this variant: bitwise theirs
+        loss, phase2, psi2 = p.loss_obj(params)
+        assert loss == p.loss([params])[0]
+        np.testing.assert_array_equal(phase2, phase)
+        np.testing.assert_array_equal(psi2, psi)
 
 
 def test_full_plane_small_equals_half_plane(small):

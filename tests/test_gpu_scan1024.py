@@ -161,6 +161,10 @@ def test_1024_subdisk_loss_and_object(subdisk1024):
     ref_phase, _ = O.object_wave(og, counts, TRUE, dc)
     d = np.angle(np.exp(1j * (phase.cpu().numpy() - ref_phase)))
     assert np.sqrt(np.mean(d * d)) <= PHASE_RMS
+    # ssb_loss_object at N = 1024 runs ssb_loss and then ssb_object: bitwise theirs
+    phase2 = torch.full((N, N), float("nan"), dtype=torch.float32, device="cuda")
+    assert ssb.ssb_loss_object(hs, TRUE, phase2) == ssb.ssb_loss(hs, [TRUE])[0]
+    assert torch.equal(phase2, phase)
 
 
 def test_1024_full_plane_variant_moments(full1024):
