@@ -161,8 +161,8 @@ int ssb_loss_noalloc(ssb_handle* h, const float* params, int32_t n_trials, doubl
  * ssb_reserve: size the handle's device workspace, host staging and pinned host
  * landing area for the losses (at least 16 trials) for loss calls of up to max_trials
  * trials (any BF range, either variant, any chunk cap), so that such calls, and
- * ssb_moments and ssb_object, allocate nothing afterwards.
- * ssb_prepare reserves one trial.  Reservations only grow.  Errors: SSB_EINVAL
+ * ssb_moments, ssb_object and ssb_loss_object, allocate nothing afterwards.
+ * ssb_prepare reserves one trial (and the object sums ssb_loss_object uses).  Reservations only grow.  Errors: SSB_EINVAL
  * (bad handle, max_trials outside [1, 65535]), SSB_ENOMEM, SSB_EDEVICE.
  */
 int ssb_reserve(ssb_handle* h, int32_t max_trials);
