@@ -208,11 +208,9 @@ TrialConst trial_const(const ssb_handle* h, const float* p) {
     return t;
 }
 
-// Whether the row pass forms the object sums itself (ssb_loss_object): half plane, scan
-// sizes up to 512 (at 1,024 the sums would not fit the row pass's registers).
-bool fused_object(const ssb_handle* h, int variant) {
-    return variant == SSB_VARIANT_HALF_PLANE && pass2_obj_sizes(h->n);
-}
+// Whether the row pass forms the object sums itself (ssb_loss_object): scan sizes up to
+// 512 (at 1,024 the sums would not fit the row pass's registers).
+bool fused_object(const ssb_handle* h) { return pass2_obj_sizes(h->n); }
 
 struct LossPlan {
     int cap;       // BF capacity of one chunk (multiple of kGroupBF)
@@ -259,8 +257,9 @@ LossPlan plan_loss(const ssb_handle* h, int64_t nb, int n_trials, int variant, i
     }
     pl.off_po = pl.off_oacc = 0;
     if (obj) {
-        pl.off_po = (size_t)align_up<float>(z, off, (size_t)n_trials * pl.gcap * obj_sum_count(h->n));
-        pl.off_oacc = (size_t)align_up<double>(z, off, (size_t)n_trials * obj_sum_count(h->n));
+        const int64_t no = obj_sum_count(h->n, variant == SSB_VARIANT_FULL_PLANE);
+        pl.off_po = (size_t)align_up<float>(z, off, (size_t)n_trials * pl.gcap * no);
+        pl.off_oacc = (size_t)align_up<double>(z, off, (size_t)n_trials * no);
     }
     pl.total = off + 256;
     return pl;
@@ -278,9 +277,10 @@ size_t loss_ws_need(const ssb_handle* h, int n_trials) {
     for (int t = 1; t <= n_trials; ++t)
         for (int var : {SSB_VARIANT_HALF_PLANE, SSB_VARIANT_FULL_PLANE})
             need = std::max(need, plan_loss(h, h->n_bf, t, var, 0).total);
-    // the fused loss and object (one trial, half plane)
-    if (fused_object(h, SSB_VARIANT_HALF_PLANE))
-        need = std::max(need, plan_loss(h, h->n_bf, 1, SSB_VARIANT_HALF_PLANE, 0, true).total);
+    // the fused loss and object (one trial)
+    if (fused_object(h))
+        for (int var : {SSB_VARIANT_HALF_PLANE, SSB_VARIANT_FULL_PLANE})
+            need = std::max(need, plan_loss(h, h->n_bf, 1, var, 0, true).total);
     return need;
 }
 
@@ -397,7 +397,7 @@ int run_moments(ssb_handle* h, char* ws, const LossPlan& pl, const float* params
         if (b_begin >= b_end) {                       // no chunk below writes the sums
             SSB_HIP(launch_fill(s1, (int64_t)n_trials * h->n * h->n, st), "clear S1");
             SSB_HIP(launch_fill(s2, n_trials, st), "clear S2");
-            if (obj) SSB_HIP(launch_fill(oacc, (int64_t)n_trials * obj_sum_count(h->n), st), "clear object sums");
+            if (obj) SSB_HIP(launch_fill(oacc, (int64_t)n_trials * obj_sum_count(h->n, fp), st), "clear object sums");
         }
         SSB_HIP(launch_chiq(h->n, tc, n_trials, h->geo, chm, chn, st), "phase table launch");
     }
@@ -427,7 +427,7 @@ int run_moments(ssb_handle* h, char* ws, const LossPlan& pl, const float* params
             SSB_HIP(launch_accum(h->n, ps1, ps2, pl.gcap, ng, n_trials, s1, s2, c0 == b_begin, st),
                     "accumulate launch");
             if (obj)
-                SSB_HIP(launch_accum_obj(h->n, po, pl.gcap, ng, n_trials, oacc, c0 == b_begin, st),
+                SSB_HIP(launch_accum_obj(h->n, fp, po, pl.gcap, ng, n_trials, oacc, c0 == b_begin, st),
                         "object-sum accumulate launch");
         }
     }
@@ -460,7 +460,8 @@ int run_loss(ssb_handle* h, char* ws, const LossPlan& pl, const float* params, i
         // the inactive BF pixels add their DC term only
         const double re_extra = h->dc * (double)(h->n_bf - h->n_active);
         const double scale = 1.0 / ((double)h->n_bf * (double)n * (double)n);
-        SSB_HIP(launch_obj_from_sums(n, reinterpret_cast<double*>(ws + pl.off_oacc), re_extra, scale, phase,
+        SSB_HIP(launch_obj_from_sums(n, h->variant == SSB_VARIANT_FULL_PLANE,
+                                     reinterpret_cast<double*>(ws + pl.off_oacc), re_extra, scale, phase,
                                      reinterpret_cast<float2*>(psi), st),
                 "object from sums");
     }
@@ -749,8 +750,8 @@ int ssb_loss_object(ssb_handle* h, const float* params3, double* loss, float* ph
     if (rc) return rc;
     if (!params3 || !loss || !phase) return fail(SSB_EINVAL, "null argument");
     if ((rc = check_params(params3, 1))) return rc;
-    if (!fused_object(h, h->variant)) {
-        // full-plane variant, 1,024-point scans: the loss, then the object's own pass
+    if (!fused_object(h)) {
+        // 1,024-point scans: the loss, then the object's own pass
         if ((rc = ssb_loss(h, params3, 1, loss, nullptr, stream))) return rc;
         if ((rc = ssb_object(h, params3, phase, psi, stream))) return rc;
         SSB_HIP(hipStreamSynchronize(static_cast<hipStream_t>(stream)), "object");

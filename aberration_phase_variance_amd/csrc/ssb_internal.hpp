@@ -77,23 +77,23 @@ hipError_t launch_pass1(int n, const float2* gm, const float2* gn, const float2*
                         const double2* kb, const uint4* sup, const int* vend, const TrialConst* tc, int n_trials,
                         GeomDev geo, int64_t bf0, int cb, int cap, float2* im, float2* in, hipStream_t st);
 // Pass 2: row transforms, atan2 and moments, one partial per 32-BF group.  With part_obj
-// (half plane, scan sizes where pass2_obj_sizes holds) it also writes each group's object
-// sums: [t][g] blocks of obj_sum_count(n) floats (N * N sums of Im O_b, then 2 N sums of
-// Re O_b per row and column parity).
+// (scan sizes where pass2_obj_sizes holds) it also writes each group's object sums:
+// [t][g] blocks of obj_sum_count(n, fp) floats (N * N sums of Im O_b, then the sums of
+// Re O_b: 2 N per row and column parity for the half plane, N * N for the full plane).
 constexpr bool pass2_obj_sizes(int n) { return n <= 512; }
-constexpr int64_t obj_sum_count(int n) { return (int64_t)n * n + 2 * n; }
+constexpr int64_t obj_sum_count(int n, bool fp) { return (int64_t)n * n + (fp ? (int64_t)n * n : 2 * n); }
 hipError_t launch_pass2(int n, const float2* im, const float2* in, int cap, const uint8_t* active,
                         const int* vend, int64_t bf0, int cb, int n_trials, double dc, float* part_s1,
                         double* part_s2, int gcap, const float2* tw_inv, const float2* na, const float2* nb,
                         float* part_obj, hipStream_t st);
-// acc[t][i] (+)= sum over groups g < ng, in order, of part_obj[t][g][i] (double), i < obj_sum_count(n)
-hipError_t launch_accum_obj(int n, const float* part_obj, int gcap, int ng, int n_trials, double* acc, bool first,
-                            hipStream_t st);
+// acc[t][i] (+)= sum over groups g < ng, in order, of part_obj[t][g][i] (double), i < obj_sum_count(n, fp)
+hipError_t launch_accum_obj(int n, bool fp, const float* part_obj, int gcap, int ng, int n_trials, double* acc,
+                            bool first, hipStream_t st);
 // Phase (and psi, when not null) of the object summed over all BF pixels from one trial's
-// accumulated row-pass sums: Re = acc's parity sum + re_extra, Im = acc's pixel sum;
+// accumulated row-pass sums: Re = acc's Re sum + re_extra, Im = acc's pixel sum;
 // psi = (Re, Im) * scale.
-hipError_t launch_obj_from_sums(int n, const double* acc, double re_extra, double scale, float* phase, float2* psi,
-                                hipStream_t st);
+hipError_t launch_obj_from_sums(int n, bool fp, const double* acc, double re_extra, double scale, float* phase,
+                                float2* psi, hipStream_t st);
 // Full-plane variant: the Nyquist-line terms A, B ([t][cap][N] each) of the chunk's
 // BF pixels (pass 2 adds them when na is not null).
 hipError_t launch_nyq_lines(int n, const float2* gm, const float2* gn, const double2* kb, const uint8_t* active,

@@ -74,6 +74,9 @@ namespace {
 #ifndef SSB_PASS2_MIN_WAVES_1024
 #define SSB_PASS2_MIN_WAVES_1024 4 // the same at N = 1024 (LDS also allows 4 workgroups per CU)
 #endif
+#ifndef SSB_PASS2_OBJ_FP_WAVES
+#define SSB_PASS2_OBJ_FP_WAVES 4 // full-plane row pass with the object sums: resident waves per SIMD
+#endif
 #ifndef SSB_PASS2_MIN_WAVES
 #define SSB_PASS2_MIN_WAVES 7 // pass-2 register budget (N <= 512, half plane): resident waves per SIMD
 #endif
@@ -1091,16 +1094,19 @@ struct RowPairUnits {
 // full-plane form 96 up to N = 512 (5 waves, 44 bytes of spills; 2.31-2.32 -> 2.24 ms against the
 // compiler's 124 VGPRs and 4 waves) and the compiler's choice at N = 1024.
 // OBJ: the row pass also sums each pixel's object O_b over the group's BF pixels (the
-// object's 16 sums per lane take the budget of five waves per SIMD: 94 VGPRs)
+// half plane's 18 sums per lane take the budget of five waves per SIMD, 94 VGPRs; the full
+// plane's 32 that of SSB_PASS2_OBJ_FP_WAVES)
 template <int N, bool FP, bool OBJ = false>
 constexpr int pass2_min_waves() {
-    return OBJ ? 5 : FP ? (N <= 512 ? 5 : 1) : (N <= 512 ? SSB_PASS2_MIN_WAVES : SSB_PASS2_MIN_WAVES_1024);
+    return OBJ ? (FP ? SSB_PASS2_OBJ_FP_WAVES : 5)
+               : FP ? (N <= 512 ? 5 : 1) : (N <= 512 ? SSB_PASS2_MIN_WAVES : SSB_PASS2_MIN_WAVES_1024);
 }
 
 // part_obj (OBJ only): per trial and group, N * N sums of Im O_b over the group's active BF
-// pixels (row-major, like part_s1), then 2 N sums of Re O_b per row and column parity (Re O_b
-// depends on the column only through its parity: the DC term, the v = 0 column's real part
-// along the row, and the Nyquist column's, with sign (-1)^x)
+// pixels (row-major, like part_s1), then for the half plane 2 N sums of Re O_b per row and
+// column parity (there Re O_b depends on the column only through its parity: the DC term,
+// the v = 0 column's real part along the row, and the Nyquist column's, with sign (-1)^x),
+// for the full plane N * N sums of Re O_b per pixel
 template <int N, bool FP, bool OBJ = false>
 __global__ __launch_bounds__(256, (pass2_min_waves<N, FP, OBJ>())) void k_pass2(const float2* __restrict__ im, const float2* __restrict__ in,
                                                int cap, const uint8_t* __restrict__ active,
@@ -1110,7 +1116,6 @@ __global__ __launch_bounds__(256, (pass2_min_waves<N, FP, OBJ>())) void k_pass2(
                                                const float2* __restrict__ gtw,
                                                const float2* __restrict__ na, const float2* __restrict__ nb,
                                                float* __restrict__ part_obj) {
-    static_assert(!(OBJ && FP), "object sums in the half-plane row pass only");
     // FFT twiddles from an LDS copy of the table (not registers: 4 waves per SIMD)
     using F = WaveFFTT<N, +1>;
     __shared__ float2 twt[F::TABLE];
@@ -1162,8 +1167,11 @@ __global__ __launch_bounds__(256, (pass2_min_waves<N, FP, OBJ>())) void k_pass2(
     double s2 = 0.0;
     const float sgn = (j & 1) ? -1.f : 1.f;   // (-1)^x for x = j + r L, L even
     float oa[OBJ ? R : 1], ob[OBJ ? R : 1], rea = 0.f, reb = 0.f;
+    float qa[OBJ && FP ? R : 1], qb[OBJ && FP ? R : 1];
 #pragma unroll
     for (int r = 0; r < (OBJ ? R : 1); ++r) oa[r] = ob[r] = 0.f;
+#pragma unroll
+    for (int r = 0; r < (OBJ && FP ? R : 1); ++r) qa[r] = qb[r] = 0.f;
 
     while (b < b_hi) {
         const int bn = next_active(b + 1);
@@ -1198,11 +1206,22 @@ __global__ __launch_bounds__(256, (pass2_min_waves<N, FP, OBJ>())) void k_pass2(
                 bv[r] = make_float2(ra, rb);
                 easy = easy && ra > 0.f && rb > 0.f && fabsf(x[r].x) <= ra && fabsf(x[r].y) <= rb;
             }
+            if constexpr (OBJ) {
+                // O_b on rows y0 and y0 + 1: real parts bv[r], imaginary parts x[r]
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    oa[r] += x[r].x;
+                    ob[r] += x[r].y;
+                    qa[r] += bv[r].x;
+                    qb[r] += bv[r].y;
+                }
+            }
             if (__all(easy)) {
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
-                    const float pa = atan_unit(x[r].x * __builtin_amdgcn_rcpf(bv[r].x));
-                    const float pb = atan_unit(x[r].y * __builtin_amdgcn_rcpf(bv[r].y));
+                    float pa = atan_unit(x[r].x * __builtin_amdgcn_rcpf(bv[r].x));
+                    float pb = atan_unit(x[r].y * __builtin_amdgcn_rcpf(bv[r].y));
+                    asm("" : "+v"(pa), "+v"(pb));   // each phase rounded before it is summed
                     s1a[r] += pa;
                     s1b[r] += pb;
                     p2 = fmaf(pb, pb, fmaf(pa, pa, p2));
@@ -1210,8 +1229,9 @@ __global__ __launch_bounds__(256, (pass2_min_waves<N, FP, OBJ>())) void k_pass2(
             } else {
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
-                    const float pa = atan2_f(x[r].x, bv[r].x);
-                    const float pb = atan2_f(x[r].y, bv[r].y);
+                    float pa = atan2_f(x[r].x, bv[r].x);
+                    float pb = atan2_f(x[r].y, bv[r].y);
+                    asm("" : "+v"(pa), "+v"(pb));
                     s1a[r] += pa;
                     s1b[r] += pb;
                     p2 = fmaf(pb, pb, fmaf(pa, pa, p2));
@@ -1283,14 +1303,20 @@ __global__ __launch_bounds__(256, (pass2_min_waves<N, FP, OBJ>())) void k_pass2(
         o[N + j + r * L] = s1b[r];
     }
     if constexpr (OBJ) {
-        float* po = part_obj + ((int64_t)t * gcap + g) * ((int64_t)N * N + 2 * N);
+        float* po = part_obj + ((int64_t)t * gcap + g) * obj_sum_count(N, FP);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             po[(int64_t)y0 * N + j + r * L] = oa[r];
             po[(int64_t)(y0 + 1) * N + j + r * L] = ob[r];
         }
-        // Re sums per row and column parity: lanes 0 (even columns) and 1 (odd)
-        if (j < 2) {
+        if constexpr (FP) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                po[(int64_t)N * N + (int64_t)y0 * N + j + r * L] = qa[r];
+                po[(int64_t)N * N + (int64_t)(y0 + 1) * N + j + r * L] = qb[r];
+            }
+        } else if (j < 2) {
+            // Re sums per row and column parity: lanes 0 (even columns) and 1 (odd)
             po[(int64_t)N * N + 2 * y0 + j] = rea;
             po[(int64_t)N * N + 2 * (y0 + 1) + j] = reb;
         }
@@ -1362,17 +1388,17 @@ __global__ __launch_bounds__(256) void k_accum_s2(const double* __restrict__ par
 }
 
 // The object redraw from the row pass's sums (one trial): per pixel (y, x), the object
-// summed over every BF pixel is Re = acc[N^2 + 2 y + x mod 2] + re_extra (the inactive BF
-// pixels contribute their DC term only) and Im = acc[y N + x]; its phase is the phase of
-// the mean object.
-__global__ __launch_bounds__(256) void k_obj_from_sums(const double* __restrict__ acc, int n, double re_extra,
-                                                        double scale, float* __restrict__ phase,
+// summed over every BF pixel is Re = acc[N^2 + 2 y + x mod 2] (half plane) or
+// acc[N^2 + y N + x] (full plane), plus re_extra (the inactive BF pixels contribute their
+// DC term only), and Im = acc[y N + x]; its phase is the phase of the mean object.
+__global__ __launch_bounds__(256) void k_obj_from_sums(const double* __restrict__ acc, int n, int fp,
+                                                        double re_extra, double scale, float* __restrict__ phase,
                                                         float2* __restrict__ psi) {
     const int64_t n2 = (int64_t)n * n;
     const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (p >= n2) return;
     const int y = (int)(p / n), x = (int)(p - (int64_t)y * n);
-    const double re = acc[n2 + 2 * y + (x & 1)] + re_extra;
+    const double re = (fp ? acc[n2 + p] : acc[n2 + 2 * y + (x & 1)]) + re_extra;
     const double imv = acc[p];
     phase[p] = (float)atan2(imv, re);
     if (psi) psi[p] = make_float2((float)(re * scale), (float)(imv * scale));
@@ -2124,9 +2150,12 @@ static hipError_t pass2_n(const float2* im, const float2* in, int cap, const uin
     const dim3 grid(row_blocks<N>(), ng, n_trials);
     if (part_obj) {
         if constexpr (pass2_obj_sizes(N)) {
-            if (na) return hipErrorInvalidValue;
-            hipLaunchKernelGGL((k_pass2<N, false, true>), grid, dim3(256), 0, st, im, in, cap, active, vend, bf0, cb,
-                               (float)dc, part_s1, part_s2, gcap, tw, na, nb, part_obj);
+            if (na)
+                hipLaunchKernelGGL((k_pass2<N, true, true>), grid, dim3(256), 0, st, im, in, cap, active, vend, bf0,
+                                   cb, (float)dc, part_s1, part_s2, gcap, tw, na, nb, part_obj);
+            else
+                hipLaunchKernelGGL((k_pass2<N, false, true>), grid, dim3(256), 0, st, im, in, cap, active, vend, bf0,
+                                   cb, (float)dc, part_s1, part_s2, gcap, tw, na, nb, part_obj);
         } else {
             return hipErrorInvalidValue;
         }
@@ -2182,19 +2211,19 @@ hipError_t launch_accum(int n, const float* part_s1, const double* part_s2, int 
     return hipGetLastError();
 }
 
-hipError_t launch_accum_obj(int n, const float* part_obj, int gcap, int ng, int n_trials, double* acc, bool first,
-                            hipStream_t st) {
-    const int64_t n2 = obj_sum_count(n);
+hipError_t launch_accum_obj(int n, bool fp, const float* part_obj, int gcap, int ng, int n_trials, double* acc,
+                            bool first, hipStream_t st) {
+    const int64_t n2 = obj_sum_count(n, fp);
     hipLaunchKernelGGL(k_accum_s1, dim3((unsigned)((n2 + 255) / 256), n_trials), dim3(256), 0, st, part_obj, gcap,
                        ng, n2, acc, (int)first);
     return hipGetLastError();
 }
 
-hipError_t launch_obj_from_sums(int n, const double* acc, double re_extra, double scale, float* phase, float2* psi,
-                                hipStream_t st) {
+hipError_t launch_obj_from_sums(int n, bool fp, const double* acc, double re_extra, double scale, float* phase,
+                                float2* psi, hipStream_t st) {
     const int64_t n2 = (int64_t)n * n;
-    hipLaunchKernelGGL(k_obj_from_sums, dim3((unsigned)((n2 + 255) / 256)), dim3(256), 0, st, acc, n, re_extra, scale,
-                       phase, psi);
+    hipLaunchKernelGGL(k_obj_from_sums, dim3((unsigned)((n2 + 255) / 256)), dim3(256), 0, st, acc, n, (int)fp,
+                       re_extra, scale, phase, psi);
     return hipGetLastError();
 }
 

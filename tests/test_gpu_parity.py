@@ -590,11 +590,8 @@ def test_full_plane_moments_and_object_tiny(full_plane_tiny):
         d = np.angle(np.exp(1j * (phase - ref_phase)))
         assert np.sqrt(np.mean(d * d)) <= PHASE_RMS
         assert np.linalg.norm(psi - ref_psi) <= 1e-5 * np.linalg.norm(ref_psi)
-        # the fused call runs ssb_loss and then ssb_object in this variant: bitwise theirs
-        loss, phase2, psi2 = p.loss_obj(params)
-        assert loss == p.loss([params])[0]
-        np.testing.assert_array_equal(phase2, phase)
-        np.testing.assert_array_equal(psi2, psi)
+        # the fused call in this variant: the full-plane row pass sums Re and Im of O_b per pixel
+        check_loss_object(p, params, ref_phase, ref_psi, "full plane, tiny")
 
 
 def test_full_plane_small_equals_half_plane(small):
@@ -615,8 +612,13 @@ def test_full_plane_small_equals_half_plane(small):
     for k in range(3):
         assert _rel(full[k], O.loss_full_plane(g, counts, params[k], dc)) <= LOSS_RTOL
         assert abs(full[k] - half[k]) <= 1e-9 * abs(half[k])
-    ref, _ = O.object_wave_full_plane(g, counts, params[0], dc)
+    ref, ref_psi = O.object_wave_full_plane(g, counts, params[0], dc)
     assert np.sqrt(np.mean(np.angle(np.exp(1j * (phase - ref))) ** 2)) <= PHASE_RMS
+    ssb.ssb_set_variant(p.h, ssb.SSB_VARIANT_FULL_PLANE)
+    try:
+        check_loss_object(p, params[0].tolist(), ref, ref_psi, "full plane, small")
+    finally:
+        ssb.ssb_set_variant(p.h, ssb.SSB_VARIANT_HALF_PLANE)
 
 
 @pytest.mark.parametrize("n,d,r2", [(64, 16, 20), (256, 24, 36)])   # transfer reaches the Nyquist lines
@@ -630,8 +632,9 @@ def test_full_plane_other_scan_sizes(n, d, r2):
         for params in ([40.0, 5.0, 0.3], [-25.0, 7.0, 2.4]):
             assert _rel(p.loss([params])[0], O.loss_full_plane(og, counts, params)) <= LOSS_RTOL
         phase, _ = p.obj([40.0, 5.0, 0.3], with_psi=False)
-        ref, _ = O.object_wave_full_plane(og, counts, [40.0, 5.0, 0.3])
+        ref, ref_psi = O.object_wave_full_plane(og, counts, [40.0, 5.0, 0.3])
         assert np.sqrt(np.mean(np.angle(np.exp(1j * (phase - ref))) ** 2)) <= PHASE_RMS
+        check_loss_object(p, [40.0, 5.0, 0.3], ref, ref_psi, f"full plane, N = {n}")
     finally:
         p.release()
 
