@@ -235,11 +235,18 @@ def main():
         ssb.ssb_object(h, params[0], fp_phase)
     torch.cuda.synchronize()
     fp_obj_ms = (time.perf_counter() - t1) * 1e3 / 3
+    ssb.ssb_loss_object(h, params[0], fp_phase)
+    t1 = time.perf_counter()
+    for _ in range(3):
+        fp_lo = ssb.ssb_loss_object(h, params[0], fp_phase)
+    fp_lo_ms = (time.perf_counter() - t1) * 1e3 / 3
     ssb.ssb_set_variant(h, ssb.SSB_VARIANT_HALF_PLANE)
     del fp_phase
-    full_plane = {"ms_per_eval": fp_ms, "loss": fp_loss, "object_ms": fp_obj_ms,
+    full_plane = {"ms_per_eval": fp_ms, "loss": fp_loss, "object_ms": fp_obj_ms, "loss_object_ms": fp_lo_ms,
+                  "loss_object_same_loss": bool(fp_lo == fp_loss),
                   "loss_rel_diff_vs_half_plane": abs(fp_loss - loss) / abs(loss)}
-    log(f"[bench] full-plane variant: {fp_ms:.3f} ms/eval, loss {fp_loss:.9f}, object {fp_obj_ms:.3f} ms")
+    log(f"[bench] full-plane variant: {fp_ms:.3f} ms/eval, loss {fp_loss:.9f}, object {fp_obj_ms:.3f} ms, "
+        f"loss and object in one call {fp_lo_ms:.3f} ms")
 
     # per-stage device times (HIP events on the library's stream), separate pass
     ssb.ssb_profile(h, 1)
