@@ -208,9 +208,12 @@ TrialConst trial_const(const ssb_handle* h, const float* p) {
     return t;
 }
 
-// Whether the row pass forms the object sums itself (ssb_loss_object): scan sizes up to
-// 512 (at 1,024 the sums would not fit the row pass's registers).
-bool fused_object(const ssb_handle* h) { return pass2_obj_sizes(h->n); }
+// Whether the row pass forms the object sums itself (ssb_loss_object): every scan size in
+// the half plane, up to 512 in the full plane (at 1,024 the full plane's sums would not fit
+// the row pass's registers).
+bool fused_object(const ssb_handle* h, int variant) {
+    return pass2_obj_sizes(h->n, variant == SSB_VARIANT_FULL_PLANE);
+}
 
 struct LossPlan {
     int cap;       // BF capacity of one chunk (multiple of kGroupBF)
@@ -278,9 +281,8 @@ size_t loss_ws_need(const ssb_handle* h, int n_trials) {
         for (int var : {SSB_VARIANT_HALF_PLANE, SSB_VARIANT_FULL_PLANE})
             need = std::max(need, plan_loss(h, h->n_bf, t, var, 0).total);
     // the fused loss and object (one trial)
-    if (fused_object(h))
-        for (int var : {SSB_VARIANT_HALF_PLANE, SSB_VARIANT_FULL_PLANE})
-            need = std::max(need, plan_loss(h, h->n_bf, 1, var, 0, true).total);
+    for (int var : {SSB_VARIANT_HALF_PLANE, SSB_VARIANT_FULL_PLANE})
+        if (fused_object(h, var)) need = std::max(need, plan_loss(h, h->n_bf, 1, var, 0, true).total);
     return need;
 }
 
@@ -750,8 +752,8 @@ int ssb_loss_object(ssb_handle* h, const float* params3, double* loss, float* ph
     if (rc) return rc;
     if (!params3 || !loss || !phase) return fail(SSB_EINVAL, "null argument");
     if ((rc = check_params(params3, 1))) return rc;
-    if (!fused_object(h)) {
-        // 1,024-point scans: the loss, then the object's own pass
+    if (!fused_object(h, h->variant)) {
+        // the full plane at 1,024 points: the loss, then the object's own pass
         if ((rc = ssb_loss(h, params3, 1, loss, nullptr, stream))) return rc;
         if ((rc = ssb_object(h, params3, phase, psi, stream))) return rc;
         SSB_HIP(hipStreamSynchronize(static_cast<hipStream_t>(stream)), "object");

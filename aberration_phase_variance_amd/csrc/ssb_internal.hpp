@@ -77,10 +77,11 @@ hipError_t launch_pass1(int n, const float2* gm, const float2* gn, const float2*
                         const double2* kb, const uint4* sup, const int* vend, const TrialConst* tc, int n_trials,
                         GeomDev geo, int64_t bf0, int cb, int cap, float2* im, float2* in, hipStream_t st);
 // Pass 2: row transforms, atan2 and moments, one partial per 32-BF group.  With part_obj
-// (scan sizes where pass2_obj_sizes holds) it also writes each group's object sums:
+// (scan sizes and variants where pass2_obj_sizes holds; at 1,024 points the full plane's
+// sums would not fit the row pass's registers) it also writes each group's object sums:
 // [t][g] blocks of obj_sum_count(n, fp) floats (N * N sums of Im O_b, then the sums of
 // Re O_b: 2 N per row and column parity for the half plane, N * N for the full plane).
-constexpr bool pass2_obj_sizes(int n) { return n <= 512; }
+constexpr bool pass2_obj_sizes(int n, bool fp) { return fp ? n <= 512 : n <= 1024; }
 constexpr int64_t obj_sum_count(int n, bool fp) { return (int64_t)n * n + (fp ? (int64_t)n * n : 2 * n); }
 hipError_t launch_pass2(int n, const float2* im, const float2* in, int cap, const uint8_t* active,
                         const int* vend, int64_t bf0, int cb, int n_trials, double dc, float* part_s1,

@@ -1094,11 +1094,11 @@ struct RowPairUnits {
 // full-plane form 96 up to N = 512 (5 waves, 44 bytes of spills; 2.31-2.32 -> 2.24 ms against the
 // compiler's 124 VGPRs and 4 waves) and the compiler's choice at N = 1024.
 // OBJ: the row pass also sums each pixel's object O_b over the group's BF pixels (the
-// half plane's 18 sums per lane take the budget of five waves per SIMD, 94 VGPRs; the full
-// plane's 32 that of SSB_PASS2_OBJ_FP_WAVES)
+// half plane's 18 sums per lane take the budget of five waves per SIMD, 94 VGPRs, or at
+// 1,024 points of three, 161 VGPRs; the full plane's 32 that of SSB_PASS2_OBJ_FP_WAVES)
 template <int N, bool FP, bool OBJ = false>
 constexpr int pass2_min_waves() {
-    return OBJ ? (FP ? SSB_PASS2_OBJ_FP_WAVES : 5)
+    return OBJ ? (FP ? SSB_PASS2_OBJ_FP_WAVES : (N <= 512 ? 5 : 3))
                : FP ? (N <= 512 ? 5 : 1) : (N <= 512 ? SSB_PASS2_MIN_WAVES : SSB_PASS2_MIN_WAVES_1024);
 }
 
@@ -2149,15 +2149,18 @@ static hipError_t pass2_n(const float2* im, const float2* in, int cap, const uin
     const int ng = (cb + kGroupBF - 1) / kGroupBF;
     const dim3 grid(row_blocks<N>(), ng, n_trials);
     if (part_obj) {
-        if constexpr (pass2_obj_sizes(N)) {
-            if (na)
+        if (na) {
+            if constexpr (pass2_obj_sizes(N, true))
                 hipLaunchKernelGGL((k_pass2<N, true, true>), grid, dim3(256), 0, st, im, in, cap, active, vend, bf0,
                                    cb, (float)dc, part_s1, part_s2, gcap, tw, na, nb, part_obj);
             else
+                return hipErrorInvalidValue;
+        } else {
+            if constexpr (pass2_obj_sizes(N, false))
                 hipLaunchKernelGGL((k_pass2<N, false, true>), grid, dim3(256), 0, st, im, in, cap, active, vend, bf0,
                                    cb, (float)dc, part_s1, part_s2, gcap, tw, na, nb, part_obj);
-        } else {
-            return hipErrorInvalidValue;
+            else
+                return hipErrorInvalidValue;
         }
     } else if (na) {
         hipLaunchKernelGGL((k_pass2<N, true>), grid, dim3(256), 0, st, im, in, cap, active, vend, bf0, cb, (float)dc,

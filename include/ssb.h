@@ -200,8 +200,8 @@ int ssb_object(ssb_handle* h, const float* params3, float* phase, float* psi, vo
  * forms before taking their phases: the row pass also sums O_b over each 32-BF group,
  * and the sums are added in double in group order.  The loss is bitwise that of
  * ssb_loss; phase and psi agree with ssb_object to float rounding (the two sum in
- * different orders).  Either variant; for 1,024-point scans the call runs ssb_loss and
- * then ssb_object.
+ * different orders).  Either variant; only the full-plane variant of 1,024-point scans
+ * runs ssb_loss and then ssb_object (the returned results are those two calls').
  *   params3  HOST float[3].
  *   loss     HOST double, written on success.
  *   phase    DEVICE float [N][N].
