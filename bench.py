@@ -492,6 +492,11 @@ def main():
             ssb.ssb_object(h2, p2[0], phase2)
         torch.cuda.synchronize()
         obj2 = (time.perf_counter() - t1) * 1e3 / 3
+        ssb.ssb_loss_object(h2, p2[0], phase2)
+        t1 = time.perf_counter()
+        for _ in range(3):
+            ssb.ssb_loss_object(h2, p2[0], phase2)
+        lo2 = (time.perf_counter() - t1) * 1e3 / 3
         ssb.ssb_release(h2)
         del phase2
         torch.cuda.empty_cache()
@@ -501,7 +506,7 @@ def main():
             "workload": f"{w2.name}: {n2}x{n2} scan, {w2.geometry.det_n}x{w2.geometry.det_n} detector, "
                         f"{w2.n_bf} BF, one trial per evaluation",
             "ms_per_eval": ms2, "samples_per_s": w2.n_bf * n2 * n2 / (ms2 * 1e-3), "loss": loss2,
-            "object_ms": obj2, "prepare_ms": prep2, "spectrum_gb": info2["spectrum_bytes"] / 1e9,
+            "object_ms": obj2, "loss_object_ms": lo2, "prepare_ms": prep2, "spectrum_gb": info2["spectrum_bytes"] / 1e9,
             "chunk_bf": info2["chunk_bf"],
             "roofline": {"bound": "hbm", "kernel": dom2, "achieved": round(r2[dom2]["gbs"], 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(r2[dom2]["gbs"] / PEAK_HBM_GBS, 4),
@@ -515,7 +520,7 @@ def main():
             "pages_context_ms": 168.538,
         }
         log(f"[bench] scan 1024: {ms2:.3f} ms/eval, pass1 {r2['pass1']['avg_launch_ms']:.3f} ms, "
-            f"pass2 {r2['pass2']['avg_launch_ms']:.3f} ms, object {obj2:.3f} ms")
+            f"pass2 {r2['pass2']['avg_launch_ms']:.3f} ms, object {obj2:.3f} ms, loss and object {lo2:.3f} ms")
 
     value = samples * args.steps / total_s
     pages_rate = samples / (PAGES_MS * 1e-3) if args.config == "full" else None
