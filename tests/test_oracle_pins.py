@@ -301,6 +301,34 @@ def test_phase_of_mean_linearity(tiny_counts):
     assert np.max(np.abs(phase - np.angle(acc))) < 1e-12
 
 
+def test_real_part_of_bf_object_depends_on_row_and_column_parity(tiny_counts):
+    """Away from its v = 0 and v = N/2 columns the extended plane is anti-Hermitian, so those
+    entries transform to a purely imaginary object; the v = 0 column (with the DC term) adds
+    a term constant along each row and the Nyquist column one that alternates in sign with x.
+    So Re O_b(y, x) depends on x only through its parity: the fact that lets a row pass carry
+    the object's real part as two sums per row."""
+    g = _geom("tiny")
+    kx, ky = O.bf_kvectors(g)
+    dc = O.dc_value(tiny_counts)
+    for b in (0, 17, 48):
+        t = O.transfer(g, (40.0, 5.0, 0.3), kx[b], ky[b])
+        c = O.corrected_spectrum(O.scan_spectrum(tiny_counts[b]), t, dc)
+        obj = O.bf_object(O.full_plane(c))
+        re = obj.real
+        scale = np.abs(obj).max()
+        assert np.max(np.abs(re - np.tile(re[:, :2], (1, 16)))) < 1e-12 * scale
+        # the two parity terms are the v = 0 and v = N/2 columns' transforms along the rows
+        col0 = np.fft.ifft(c[:, 0]) / 32
+        nyq = np.fft.ifft(c[:, 16]) / 32
+        assert np.max(np.abs(re[:, 0] - (col0.real + nyq.real))) < 1e-12 * scale
+        assert np.max(np.abs(re[:, 1] - (col0.real - nyq.real))) < 1e-12 * scale
+        # and with those columns removed the object is purely imaginary
+        c2 = c.copy()
+        c2[:, 0] = 0.0
+        c2[:, 16] = 0.0
+        assert np.max(np.abs(O.bf_object(O.full_plane(c2)).real)) < 1e-12 * scale
+
+
 # ------------------------------------------------------------------ physics (P13)
 @pytest.fixture(scope="module")
 def small_setup():
