@@ -527,6 +527,13 @@ def test_error_paths_on_device(small):
         ssb.ssb_moments(p.h, [40.0, 5.0, 0.3], 0, 5, s1[:64])
     with pytest.raises(ValueError):
         ssb.ssb_object(p.h, [40.0, 5.0, 0.3], t.full((128, 128), 0.0, dtype=t.float32, device="cuda").t())
+    ph = t.full((128, 128), float("nan"), dtype=t.float32, device="cuda")
+    with pytest.raises(ssb.SSBError) as ei:
+        ssb.ssb_loss_object(p.h, [float("inf"), 5.0, 0.3], ph)
+    assert ei.value.code == ssb._ssb.SSB_EINVAL
+    assert bool(t.isnan(ph).all())                    # nothing written on the error
+    with pytest.raises(ValueError):
+        ssb.ssb_loss_object(p.h, [40.0, 5.0, 0.3], ph[:64])
     dev = t.zeros((w.n_bf - 1, 128, 128), dtype=t.int32, device="cuda")
     with pytest.raises(ssb.SSBError) as ei:
         ssb.ssb_prepare(w.geometry, dev, w.n_bf - 1)
