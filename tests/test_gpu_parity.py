@@ -356,6 +356,22 @@ def test_loss_object_vs_oracle(fx, request):
         assert _rel(p.loss_obj(params, with_psi=False)[0], O.loss(g, counts, params)) <= LOSS_RTOL
 
 
+def test_loss_object_allocates_nothing_after_prepare():
+    """ssb_prepare reserves what ssb_loss_object needs, in both variants: the call leaves the
+    handle's workspace as it was."""
+    w = WORKLOADS["tiny"]
+    counts = cached_counts(w)
+    p = Prepared(w.geometry, counts)
+    try:
+        before = ssb.ssb_query(p.h)["workspace_bytes"]
+        p.loss_obj([40.0, 5.0, 0.3])
+        ssb.ssb_set_variant(p.h, ssb.SSB_VARIANT_FULL_PLANE)
+        p.loss_obj([40.0, 5.0, 0.3])
+        assert ssb.ssb_query(p.h)["workspace_bytes"] == before
+    finally:
+        p.release()
+
+
 def test_loss_object_chunked(small):
     """Chunks smaller than the BF set: the object sums carry over from chunk to chunk."""
     w, counts, p = small
