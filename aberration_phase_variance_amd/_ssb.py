@@ -116,7 +116,7 @@ class ssb_probe_fit(ctypes.Structure):
 EXPORTS = ("ssb_prepare", "ssb_reserve", "ssb_loss", "ssb_loss_noalloc", "ssb_moments", "ssb_object",
            "ssb_loss_object", "ssb_spectrum", "ssb_set_chunk",
            "ssb_profile", "ssb_query", "ssb_release", "ssb_last_error", "ssb_nelder_mead", "ssb_fit",
-           "ssb_detector_sum", "ssb_fit_probe", "ssb_gather_bf", "ssb_set_variant")
+           "ssb_detector_sum", "ssb_fit_probe", "ssb_fit_probe_device", "ssb_gather_bf", "ssb_set_variant")
 
 _lib = None
 
@@ -154,6 +154,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ssb_detector_sum.argtypes = [vp, i32, i32, vp, vp]
     lib.ssb_fit_probe.argtypes = [ctypes.POINTER(ctypes.c_uint64), i32, i32, ctypes.POINTER(ssb_probe_fit)]
     lib.ssb_gather_bf.argtypes = [vp, ctypes.POINTER(ssb_geometry), vp, i64, vp]
+    lib.ssb_fit_probe_device.argtypes = [vp, i32, i32, ctypes.POINTER(ssb_probe_fit), vp]
     for name in EXPORTS:
         if name not in ("ssb_release", "ssb_last_error"):
             getattr(lib, name).restype = ctypes.c_int
@@ -412,6 +413,14 @@ def ssb_fit_probe(sums, scan_n: int, det_n: int) -> dict:
     out = ssb_probe_fit()
     _check(load_library().ssb_fit_probe(s.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)), int(scan_n), int(det_n),
                                         ctypes.byref(out)))
+    return {name: getattr(out, name) for name, _ in ssb_probe_fit._fields_}
+
+
+def ssb_fit_probe_device(sums, scan_n: int, det_n: int, stream=None) -> dict:
+    """The same probe-disk fit on the device from the device sums (uint64 [det_n^2])."""
+    sp = _dev(sums, "sums", ("int64", "uint64"), int(det_n) ** 2)
+    out = ssb_probe_fit()
+    _check(load_library().ssb_fit_probe_device(sp, int(scan_n), int(det_n), ctypes.byref(out), _stream(stream)))
     return {name: getattr(out, name) for name, _ in ssb_probe_fit._fields_}
 
 

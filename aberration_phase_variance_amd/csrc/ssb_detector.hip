@@ -1,5 +1,6 @@
 // Detector side of the SSB path on gfx950: the exact detector sum over every scan
-// frame (the mean diffraction pattern), the probe-disk fit on the host, and the
+// frame (the mean diffraction pattern), the probe-disk fit (on the host, or on the
+// device from the device sums), and the
 // gather of the BF pixels into the BF-major counts ssb_prepare takes (declared in
 // ssb.h).
 //
@@ -146,6 +147,83 @@ __global__ __launch_bounds__(256) void k_gather(const uint32_t* __restrict__ fra
     }
 }
 
+// The probe-disk fit of ssb_fit_probe on the device, one workgroup: the mean and the
+// variance of the mean pattern summed by one thread in pixel order (the host fit's order,
+// so every double is the host's), then the mask's count and index sums and the disk's
+// pixel counts, exact integers, split over the threads.  out[0..6] takes the fit in the
+// order of ssb_probe_fit; out[7] is 1 when no pixel lies above the threshold.
+__global__ __launch_bounds__(256) void k_fit_probe(const unsigned long long* __restrict__ sums, double frames,
+                                                   int det_n, double* __restrict__ out) {
+    __shared__ double sh_thr;
+    __shared__ long long red[3][256];
+    const int tid = threadIdx.x;
+    const int64_t np = (int64_t)det_n * det_n;
+    if (tid == 0) {
+        double mu = 0.0;
+        for (int64_t p = 0; p < np; ++p) mu += (double)sums[p] / frames;
+        mu /= (double)np;
+        double var = 0.0;
+        for (int64_t p = 0; p < np; ++p) {
+            const double d = (double)sums[p] / frames - mu;
+            var = __dadd_rn(var, __dmul_rn(d, d));
+        }
+        sh_thr = mu + sqrt(var / (double)np);
+    }
+    __syncthreads();
+    const double thr = sh_thr;
+    long long n = 0, si = 0, sj = 0;
+    for (int64_t p = tid; p < np; p += 256)
+        if ((double)sums[p] / frames > thr) {
+            ++n;
+            si += p / det_n;
+            sj += p % det_n;
+        }
+    red[0][tid] = n;
+    red[1][tid] = si;
+    red[2][tid] = sj;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if (tid < w)
+            for (int k = 0; k < 3; ++k) red[k][tid] += red[k][tid + w];
+        __syncthreads();
+    }
+    const long long n_disk = red[0][0], ti = red[1][0], tj = red[2][0];
+    __syncthreads();
+    if (n_disk == 0) {
+        if (tid == 0) out[7] = 1.0;
+        return;
+    }
+    const double cy = (double)ti / (double)n_disk, cx = (double)tj / (double)n_disk;
+    const double r2 = (double)n_disk / M_PI;
+    // the BF rule: squares rounded on their own, then added (no fused multiply-add)
+    long long nbf = 0, nz = 0;
+    for (int64_t p = tid; p < np; p += 256) {
+        const double di = (double)(p / det_n) - cy, dj = (double)(p % det_n) - cx;
+        if (__dadd_rn(__dmul_rn(di, di), __dmul_rn(dj, dj)) <= r2) {
+            if (sums[p] > 0) ++nbf;
+            else ++nz;
+        }
+    }
+    red[0][tid] = nbf;
+    red[1][tid] = nz;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if (tid < w)
+            for (int k = 0; k < 2; ++k) red[k][tid] += red[k][tid + w];
+        __syncthreads();
+    }
+    if (tid == 0) {
+        out[0] = cy;
+        out[1] = cx;
+        out[2] = r2;
+        out[3] = thr;
+        out[4] = (double)n_disk;
+        out[5] = (double)red[0][0];
+        out[6] = (double)red[1][0];
+        out[7] = 0.0;
+    }
+}
+
 bool device_pointer(const void* p) {
     hipPointerAttribute_t attr;
     if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
@@ -240,6 +318,37 @@ extern "C" int ssb_fit_probe(const uint64_t* sums, int32_t scan_n, int32_t det_n
                 if (sums[(int64_t)i * det_n + j] > 0) ++f.n_bf;
                 else ++f.n_zero;
             }
+    *out = f;
+    return SSB_OK;
+}
+
+extern "C" int ssb_fit_probe_device(const uint64_t* sums, int32_t scan_n, int32_t det_n, ssb_probe_fit* out,
+                                    void* stream) {
+    ssb::clear_error();
+    if (!sums || !out) return ssb::set_error(SSB_EINVAL, "null argument");
+    if (scan_n < 1 || det_n < 1) return ssb::set_error(SSB_EINVAL, "scan_n and det_n must be positive");
+    if (!device_pointer(sums)) return ssb::set_error(SSB_EINVAL, "sums must be a device pointer");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    double* dev = nullptr;
+    hipError_t e = hipMalloc(&dev, 8 * sizeof(double));
+    if (e != hipSuccess) return ssb::set_error(SSB_ENOMEM, std::string("probe fit result: ") + hipGetErrorString(e));
+    double res[8];
+    hipLaunchKernelGGL(k_fit_probe, dim3(1), dim3(256), 0, st, reinterpret_cast<const unsigned long long*>(sums),
+                       (double)scan_n * (double)scan_n, det_n, dev);
+    e = hipGetLastError();
+    if (e == hipSuccess) e = hipMemcpyAsync(res, dev, sizeof(res), hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    (void)hipFree(dev);
+    if (e != hipSuccess) return ssb::set_error(SSB_EDEVICE, std::string("probe fit: ") + hipGetErrorString(e));
+    if (res[7] != 0.0) return ssb::set_error(SSB_EINVAL, "no detector pixel above the probe threshold");
+    ssb_probe_fit f;
+    f.det_cy = res[0];
+    f.det_cx = res[1];
+    f.bf_r2 = res[2];
+    f.threshold = res[3];
+    f.n_disk = (int64_t)res[4];
+    f.n_bf = (int64_t)res[5];
+    f.n_zero = (int64_t)res[6];
     *out = f;
     return SSB_OK;
 }

@@ -438,7 +438,10 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         sum_ms = e0.elapsed_time(e1) / reps
-        pfit = ssb.ssb_fit_probe(sums.cpu().numpy().view(np.uint64), n, g.det_n)
+        t1 = time.perf_counter()
+        pfit = ssb.ssb_fit_probe_device(sums, n, g.det_n)            # synchronizes
+        fit_ms = (time.perf_counter() - t1) * 1e3
+        host_fit_same = pfit == ssb.ssb_fit_probe(sums.cpu().numpy().view(np.uint64), n, g.det_n)
         geom = dataclasses.replace(g, det_cy=pfit["det_cy"], det_cx=pfit["det_cx"], bf_r2=pfit["bf_r2"])
         bfc = torch.empty((pfit["n_bf"], n, n), dtype=torch.int32, device=dev)
         ssb.ssb_gather_bf(frames, geom, bfc, pfit["n_bf"])
@@ -450,10 +453,12 @@ def main():
         detector = {"frames": [n * n, d2], "frame_bytes": frame_bytes,
                     "detector_sum_ms": sum_ms, "detector_sum_gbs": frame_bytes / sum_ms / 1e6,
                     "detector_sum_hbm_frac": round(frame_bytes / sum_ms / 1e6 / PEAK_HBM_GBS, 4),
-                    "fit": pfit, "gather_ms_host_clock": gather_ms,
+                    "fit": pfit, "fit_ms_device": fit_ms, "fit_same_as_host": bool(host_fit_same),
+                    "gather_ms_host_clock": gather_ms,
                     "gather_gbs": 2 * pfit["n_bf"] * n * n * 4 / gather_ms / 1e6}
-        log(f"[bench] detector sum {sum_ms:.3f} ms ({detector['detector_sum_gbs']:.0f} GB/s), fit n_bf "
-            f"{pfit['n_bf']} r^2 {pfit['bf_r2']:.2f}, gather {gather_ms:.3f} ms")
+        log(f"[bench] detector sum {sum_ms:.3f} ms ({detector['detector_sum_gbs']:.0f} GB/s), fit on the device "
+            f"{fit_ms:.3f} ms (bitwise the host fit: {host_fit_same}) n_bf {pfit['n_bf']} r^2 {pfit['bf_r2']:.2f}, "
+            f"gather {gather_ms:.3f} ms")
         del frames, bfc, sums
         torch.cuda.empty_cache()
 

@@ -315,6 +315,18 @@ typedef struct ssb_probe_fit {
 int ssb_fit_probe(const uint64_t* sums, int32_t scan_n, int32_t det_n, ssb_probe_fit* out);
 
 /*
+ * ssb_fit_probe_device: the same fit from DEVICE sums [det_n * det_n] (ssb_detector_sum's
+ * output, left on the device); out is a HOST struct.  One workgroup forms the mean and the
+ * variance of the mean pattern in pixel order, as the host fit does, so every field is
+ * bitwise ssb_fit_probe's on the same sums; the mask and disk counts are exact integers.
+ * Allocates and frees a 64-byte result buffer; synchronizes the stream.  Errors: SSB_EINVAL
+ * (null, sizes < 1, sums not a device pointer, no pixel above the threshold), SSB_ENOMEM,
+ * SSB_EDEVICE.
+ */
+int ssb_fit_probe_device(const uint64_t* sums, int32_t scan_n, int32_t det_n, ssb_probe_fit* out,
+                         void* stream);
+
+/*
  * ssb_gather_bf: BF-major counts [n_bf][scan_n][scan_n] (the layout ssb_prepare
  * takes, BF pixels in row-major detector order by the geometry's disk rule) from
  * the DEVICE frames.  counts is a DEVICE buffer, overwritten.  Only scan_n, det_n,

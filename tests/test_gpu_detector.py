@@ -111,6 +111,34 @@ def test_automatic_bf_chain(small_frames):
         ssb.ssb_release(h)
 
 
+def test_fit_probe_on_device(small_frames):
+    """The device fit from the device sums: every field bitwise the host fit's."""
+    t = _torch()
+    w, frames = small_frames
+    g = w.geometry
+    fdev = _dev_u32(t, frames)
+    s = t.full((g.det_n * g.det_n,), -1, dtype=t.int64, device="cuda")
+    ssb.ssb_detector_sum(fdev, g.scan_n, g.det_n, s)
+    dfit = ssb.ssb_fit_probe_device(s, g.scan_n, g.det_n)
+    hfit = ssb.ssb_fit_probe(s.cpu().numpy().view(np.uint64), g.scan_n, g.det_n)
+    assert dfit == hfit
+    assert dfit["n_disk"] > 0 and dfit["n_zero"] == 0
+    # a flat pattern has no pixel above mean + std: the same error on both sides
+    flat = t.full((g.det_n * g.det_n,), 7, dtype=t.int64, device="cuda")
+    for fit in (lambda: ssb.ssb_fit_probe_device(flat, g.scan_n, g.det_n),
+                lambda: ssb.ssb_fit_probe(flat.cpu().numpy().view(np.uint64), g.scan_n, g.det_n)):
+        with pytest.raises(ssb.SSBError) as e:
+            fit()
+        assert e.value.code == ssb._ssb.SSB_EINVAL
+    # host sums given to the device fit
+    host = np.zeros(g.det_n * g.det_n, dtype=np.uint64)
+    lib = ssb.load_library()
+    out = ssb._ssb.ssb_probe_fit()
+    import ctypes
+    assert lib.ssb_fit_probe_device(host.ctypes.data, g.scan_n, g.det_n, ctypes.byref(out), None) == \
+        ssb._ssb.SSB_EINVAL
+
+
 def test_detector_errors():
     t = _torch()
     s = t.full((64,), -1, dtype=t.int64, device="cuda")
