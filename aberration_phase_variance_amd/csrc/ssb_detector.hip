@@ -151,9 +151,12 @@ __global__ __launch_bounds__(256) void k_gather(const uint32_t* __restrict__ fra
 // variance of the mean pattern summed by one thread in pixel order (the host fit's order,
 // so every double is the host's), then the mask's count and index sums and the disk's
 // pixel counts, exact integers, split over the threads.  out[0..6] takes the fit in the
-// order of ssb_probe_fit; out[7] is 1 when no pixel lies above the threshold.
+// order of ssb_probe_fit; out[7] is 1 when no pixel lies above the threshold; out[8], out[9]
+// the mean and the summed squared deviations.
 __global__ __launch_bounds__(256) void k_fit_probe(const unsigned long long* __restrict__ sums, double frames,
                                                    int det_n, double* __restrict__ out) {
+    // every product rounded on its own, as in the host fit (no fused multiply-add)
+#pragma clang fp contract(off)
     __shared__ double sh_thr;
     __shared__ long long red[3][256];
     const int tid = threadIdx.x;
@@ -165,9 +168,18 @@ __global__ __launch_bounds__(256) void k_fit_probe(const unsigned long long* __r
         double var = 0.0;
         for (int64_t p = 0; p < np; ++p) {
             const double d = (double)sums[p] / frames - mu;
-            var = __dadd_rn(var, __dmul_rn(d, d));
+            var += d * d;
         }
-        sh_thr = mu + sqrt(var / (double)np);
+        // the correctly rounded square root (the host's): the hardware root's neighbour
+        // whose square lies nearest the argument, residuals formed exactly by an FMA
+        const double a = var / (double)np;
+        double r = sqrt(a);
+        const double lo = nextafter(r, 0.0), hi = nextafter(r, 2.0 * r + 1.0);
+        if (fabs(fma(lo, lo, -a)) < fabs(fma(r, r, -a))) r = lo;
+        if (fabs(fma(hi, hi, -a)) < fabs(fma(r, r, -a))) r = hi;
+        out[8] = mu;
+        out[9] = var;
+        sh_thr = mu + r;
     }
     __syncthreads();
     const double thr = sh_thr;
@@ -195,11 +207,11 @@ __global__ __launch_bounds__(256) void k_fit_probe(const unsigned long long* __r
     }
     const double cy = (double)ti / (double)n_disk, cx = (double)tj / (double)n_disk;
     const double r2 = (double)n_disk / M_PI;
-    // the BF rule: squares rounded on their own, then added (no fused multiply-add)
+    // the BF rule: squares rounded on their own, then added
     long long nbf = 0, nz = 0;
     for (int64_t p = tid; p < np; p += 256) {
         const double di = (double)(p / det_n) - cy, dj = (double)(p % det_n) - cx;
-        if (__dadd_rn(__dmul_rn(di, di), __dmul_rn(dj, dj)) <= r2) {
+        if (di * di + dj * dj <= r2) {
             if (sums[p] > 0) ++nbf;
             else ++nz;
         }
@@ -330,9 +342,9 @@ extern "C" int ssb_fit_probe_device(const uint64_t* sums, int32_t scan_n, int32_
     if (!device_pointer(sums)) return ssb::set_error(SSB_EINVAL, "sums must be a device pointer");
     hipStream_t st = static_cast<hipStream_t>(stream);
     double* dev = nullptr;
-    hipError_t e = hipMalloc(&dev, 8 * sizeof(double));
+    hipError_t e = hipMalloc(&dev, 10 * sizeof(double));
     if (e != hipSuccess) return ssb::set_error(SSB_ENOMEM, std::string("probe fit result: ") + hipGetErrorString(e));
-    double res[8];
+    double res[10];
     hipLaunchKernelGGL(k_fit_probe, dim3(1), dim3(256), 0, st, reinterpret_cast<const unsigned long long*>(sums),
                        (double)scan_n * (double)scan_n, det_n, dev);
     e = hipGetLastError();
