@@ -152,7 +152,7 @@ __global__ __launch_bounds__(256) void k_gather(const uint32_t* __restrict__ fra
 // so every double is the host's), then the mask's count and index sums and the disk's
 // pixel counts, exact integers, split over the threads.  out[0..6] takes the fit in the
 // order of ssb_probe_fit; out[7] is 1 when no pixel lies above the threshold; out[8], out[9]
-// the mean and the summed squared deviations.
+// the mean and the summed squared deviations; out[10..] the mean pattern.
 __global__ __launch_bounds__(256) void k_fit_probe(const unsigned long long* __restrict__ sums, double frames,
                                                    int det_n, double* __restrict__ out) {
     // every product rounded on its own, as in the host fit (no fused multiply-add)
@@ -161,13 +161,18 @@ __global__ __launch_bounds__(256) void k_fit_probe(const unsigned long long* __r
     __shared__ long long red[3][256];
     const int tid = threadIdx.x;
     const int64_t np = (int64_t)det_n * det_n;
+    // the mean pattern, one division per pixel, split over the threads (m: np doubles
+    // after the 10 result slots); the workgroup barrier makes it visible to thread 0
+    double* m = out + 10;
+    for (int64_t p = tid; p < np; p += 256) m[p] = (double)sums[p] / frames;
+    __syncthreads();
     if (tid == 0) {
         double mu = 0.0;
-        for (int64_t p = 0; p < np; ++p) mu += (double)sums[p] / frames;
+        for (int64_t p = 0; p < np; ++p) mu += m[p];
         mu /= (double)np;
         double var = 0.0;
         for (int64_t p = 0; p < np; ++p) {
-            const double d = (double)sums[p] / frames - mu;
+            const double d = m[p] - mu;
             var += d * d;
         }
         // the correctly rounded square root (the host's): the hardware root's neighbour
@@ -185,7 +190,7 @@ __global__ __launch_bounds__(256) void k_fit_probe(const unsigned long long* __r
     const double thr = sh_thr;
     long long n = 0, si = 0, sj = 0;
     for (int64_t p = tid; p < np; p += 256)
-        if ((double)sums[p] / frames > thr) {
+        if (m[p] > thr) {
             ++n;
             si += p / det_n;
             sj += p % det_n;
@@ -342,7 +347,7 @@ extern "C" int ssb_fit_probe_device(const uint64_t* sums, int32_t scan_n, int32_
     if (!device_pointer(sums)) return ssb::set_error(SSB_EINVAL, "sums must be a device pointer");
     hipStream_t st = static_cast<hipStream_t>(stream);
     double* dev = nullptr;
-    hipError_t e = hipMalloc(&dev, 10 * sizeof(double));
+    hipError_t e = hipMalloc(&dev, (10 + (size_t)det_n * det_n) * sizeof(double));
     if (e != hipSuccess) return ssb::set_error(SSB_ENOMEM, std::string("probe fit result: ") + hipGetErrorString(e));
     double res[10];
     hipLaunchKernelGGL(k_fit_probe, dim3(1), dim3(256), 0, st, reinterpret_cast<const unsigned long long*>(sums),

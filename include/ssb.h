@@ -319,7 +319,7 @@ int ssb_fit_probe(const uint64_t* sums, int32_t scan_n, int32_t det_n, ssb_probe
  * output, left on the device); out is a HOST struct.  One workgroup forms the mean and the
  * variance of the mean pattern in pixel order, as the host fit does, so every field is
  * bitwise ssb_fit_probe's on the same sums; the mask and disk counts are exact integers.
- * Allocates and frees a 64-byte result buffer; synchronizes the stream.  Errors: SSB_EINVAL
+ * Allocates and frees a result buffer of 8 (det_n^2 + 10) bytes; synchronizes the stream.  Errors: SSB_EINVAL
  * (null, sizes < 1, sums not a device pointer, no pixel above the threshold), SSB_ENOMEM,
  * SSB_EDEVICE.
  */
